@@ -1,0 +1,46 @@
+"""MI355X-native sparse-embedding lookup: dedup -> dynamic hash table -> gather.
+
+Python face of libhtl.so (include/htl.h).  The library implements, as HIP
+kernels for gfx950, the embedding path described by MTGenRec (arXiv
+2505.12663: dynamic hash embedding table, table merging, two-stage ID
+deduplication) and MTGR (arXiv 2505.18654, section 5): feature-ID dedup,
+find-or-insert into an open-addressing table with odd-step probing, row
+gather with optional bag sum-pooling, gradient segment-sum and row-wise Adam,
+erase and least-recently-used eviction.
+
+Build the library first: ``python -m hash_table_lookup_amd.build``.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._binding import (  # noqa: F401
+    ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, HTLError, INSERTED, LIB_PATH,
+    META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
+    gather_pool, lib, rowwise_adam, segment_sum, table_keys, table_tensor,
+)
+
+__all__ = [
+    "Table", "dedup_unique_inverse", "gather", "gather_pool", "segment_sum", "rowwise_adam",
+    "lookup", "lib", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
+]
+
+
+def lookup(table: Table, keys: torch.Tensor, step: int = 0,
+           offsets: Optional[torch.Tensor] = None, out_dtype=None):
+    """The forward hot path on one batch of feature IDs.
+
+    dedup_unique_inverse -> ht_find_or_insert (absent keys inserted) ->
+    emb_gather_pool.  Returns (out, unique, inverse, n_unique, slots, status);
+    out is per-ID rows, or per-bag sums when CSR ``offsets`` are given.
+    """
+    unique, inverse, n_unique = dedup_unique_inverse(keys)
+    slots, status = table.find_or_insert(unique, n_dev=n_unique, step=step)
+    if offsets is None:
+        out = gather(table, slots, inverse, out_dtype=out_dtype)
+    else:
+        out = gather_pool(table, slots, inverse, offsets,
+                          out_dtype=out_dtype if out_dtype is not None else table.dtype)
+    return out, unique, inverse, n_unique, slots, status

@@ -1,0 +1,362 @@
+"""ctypes binding of libhtl.so: argument marshalling only.
+
+Every step of the lookup path runs in the library's HIP kernels; this module
+checks tensor dtypes/devices, allocates outputs and workspaces with torch
+(device memory and streams are all torch is used for), and passes raw device
+pointers plus the current HIP stream through the C ABI declared in
+include/htl.h.  There is no CPU fallback: if the library is missing, or no
+GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhtl.so")
+
+HTL_OK, HTL_ERR_INVALID, HTL_ERR_NOMEM, HTL_ERR_DEVICE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+FOUND, INSERTED, FULL, RESERVED = 0, 1, 2, 3
+NOT_FOUND, ERASED = 0, 1
+META_LAST_SEEN, ADAM_STATE = 1, 2
+EMPTY_KEY, TOMBSTONE_KEY = -1, -2
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_I32 = ctypes.c_int
+_U32 = ctypes.c_uint32
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+
+class HTLError(RuntimeError):
+    """A libhtl call returned an error status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libhtl error {status}: {message}")
+        self.status = status
+
+
+class _View(ctypes.Structure):
+    _fields_ = [("capacity", _I64), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("keys", _P), ("rows", _P), ("last_seen", _P), ("adam_m", _P), ("adam_v", _P)]
+
+
+_SIGNATURES = {
+    "ht_create": [ctypes.POINTER(_P), _I32, _I32, _I32, _U64, _U32, _P],
+    "ht_destroy": [_P],
+    "ht_clear": [_P, _P],
+    "ht_find_or_insert": [_P, _P, _I64, _P, _U32, _P, _P, _P],
+    "ht_erase": [_P, _P, _I64, _P, _P],
+    "ht_scan": [_P, _P, _P, _P, _P, _P],
+    "lru_workspace_bytes": [_P],
+    "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
+    "ht_view": [_P, ctypes.POINTER(_View)],
+    "dedup_workspace_bytes": [_I64],
+    "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
+    "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
+    "segsum_workspace_bytes": [_I64, _I64, _I32],
+    "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
+    "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
+    "htl_last_error": [],
+}
+_SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes"}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhtl.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hash_table_lookup_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            if name in _SIZE_FUNCS:
+                f.restype = _SZ
+            elif name == "htl_last_error":
+                f.restype = ctypes.c_char_p
+            else:
+                f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != HTL_OK:
+        msg = lib().htl_last_error()
+        raise HTLError(status, msg.decode() if msg else "")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.contiguous()
+
+
+_ws_cache = {}
+
+
+def _workspace(tag: str, nbytes: int, device) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes (256-byte aligned by torch)."""
+    key = (tag, str(device))
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("f32", "fp32", "float32", torch.float32, F32):
+        return F32
+    if dtype in ("bf16", "bfloat16", torch.bfloat16, BF16):
+        return BF16
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class Table:
+    """A dynamic embedding table living in device memory (libhtl's ht_* calls)."""
+
+    def __init__(self, capacity_log2: int, dim: int, dtype="f32", init_seed: int = 0,
+                 last_seen: bool = False, adam: bool = False):
+        L = lib()
+        self.capacity_log2, self.dim = capacity_log2, dim
+        self.dtype = _dtype_code(dtype)
+        self.init_seed = init_seed
+        flags = (META_LAST_SEEN if last_seen else 0) | (ADAM_STATE if adam else 0)
+        h = _P()
+        _check(L.ht_create(ctypes.byref(h), capacity_log2, dim, self.dtype,
+                           init_seed & 0xFFFFFFFFFFFFFFFF, flags, _stream()))
+        self._h = h
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def capacity(self) -> int:
+        return 1 << self.capacity_log2
+
+    @property
+    def row_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPE[self.dtype]
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(lib().ht_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def clear(self):
+        _check(lib().ht_clear(self._h, _stream()))
+
+    def find_or_insert(self, keys: torch.Tensor, n_dev: Optional[torch.Tensor] = None,
+                       step: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+        keys = _dev(keys, torch.int64, "keys")
+        n = keys.numel()
+        slots = torch.empty(n, dtype=torch.int32, device=keys.device)
+        status = torch.empty(n, dtype=torch.uint8, device=keys.device)
+        if n_dev is not None:
+            n_dev = _dev(n_dev, torch.int64, "n_dev")
+        _check(lib().ht_find_or_insert(self._h, _ptr(keys), n, _ptr(n_dev), step, _ptr(slots),
+                                       _ptr(status), _stream()))
+        return slots, status
+
+    def erase(self, keys: torch.Tensor) -> torch.Tensor:
+        keys = _dev(keys, torch.int64, "keys")
+        status = torch.empty(keys.numel(), dtype=torch.uint8, device=keys.device)
+        _check(lib().ht_erase(self._h, _ptr(keys), keys.numel(), _ptr(status), _stream()))
+        return status
+
+    def scan(self):
+        """(keys, last_seen, slots, n_live) -- first n_live entries are valid."""
+        M = self.capacity
+        keys = torch.empty(M, dtype=torch.int64, device=self.device)
+        ls = torch.empty(M, dtype=torch.int32, device=self.device)
+        slots = torch.empty(M, dtype=torch.int32, device=self.device)
+        n = torch.empty(1, dtype=torch.int64, device=self.device)
+        _check(lib().ht_scan(self._h, _ptr(keys), _ptr(ls), _ptr(slots), _ptr(n), _stream()))
+        return keys, ls, slots, n
+
+    def lru_select(self, num: int, den: int, victims_cap: Optional[int] = None):
+        """(victims, n_victims): the floor(live*num/den) least recently used keys."""
+        cap = self.capacity if victims_cap is None else victims_cap
+        victims = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device)
+        n = torch.empty(1, dtype=torch.int64, device=self.device)
+        nb = lib().lru_workspace_bytes(self._h)
+        ws = _workspace("lru", nb, self.device)
+        _check(lib().ht_lru_select(self._h, num, den, _ptr(victims), cap, _ptr(n), _ptr(ws), nb,
+                                   _stream()))
+        return victims, n
+
+    def view(self) -> _View:
+        v = _View()
+        _check(lib().ht_view(self._h, ctypes.byref(v)))
+        return v
+
+
+def dedup_unique_inverse(keys: torch.Tensor):
+    """(unique int64[n], inverse int32[n], n_unique int64[1]) -- unique[:U] valid."""
+    keys = _dev(keys, torch.int64, "keys")
+    n = keys.numel()
+    unique = torch.empty(max(n, 1), dtype=torch.int64, device=keys.device)
+    inverse = torch.empty(n, dtype=torch.int32, device=keys.device)
+    n_unique = torch.empty(1, dtype=torch.int64, device=keys.device)
+    nb = lib().dedup_workspace_bytes(n)
+    ws = _workspace("dedup", nb, keys.device)
+    _check(lib().dedup_unique_inverse(_ptr(keys), n, _ptr(unique), _ptr(inverse), _ptr(n_unique),
+                                      _ptr(ws), nb, _stream()))
+    return unique, inverse, n_unique
+
+
+def gather(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor] = None,
+           out_dtype=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-ID rows: out[i] = rows[slots[inverse[i]]] (inverse None: identity)."""
+    slots = _dev(slots, torch.int32, "slots")
+    n = slots.numel() if inverse is None else inverse.numel()
+    if inverse is not None:
+        inverse = _dev(inverse, torch.int32, "inverse")
+    od = table.dtype if out_dtype is None else _dtype_code(out_dtype)
+    if out is None:
+        out = torch.empty((n, table.dim), dtype=_TORCH_DTYPE[od], device=slots.device)
+    _check(lib().emb_gather_pool(table.handle, _ptr(slots), _ptr(inverse), n, None, 0, od,
+                                 _ptr(out), _stream()))
+    return out
+
+
+def gather_pool(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor],
+                offsets: torch.Tensor, out_dtype="f32", out: Optional[torch.Tensor] = None):
+    """Bag sums: out[b] = sum of rows of IDs offsets[b]..offsets[b+1]-1."""
+    slots = _dev(slots, torch.int32, "slots")
+    offsets = _dev(offsets, torch.int32, "offsets")
+    n = slots.numel() if inverse is None else inverse.numel()
+    if inverse is not None:
+        inverse = _dev(inverse, torch.int32, "inverse")
+    nb = offsets.numel() - 1
+    od = _dtype_code(out_dtype)
+    if out is None:
+        out = torch.empty((nb, table.dim), dtype=_TORCH_DTYPE[od], device=offsets.device)
+    _check(lib().emb_gather_pool(table.handle, _ptr(slots), _ptr(inverse), n, _ptr(offsets), nb,
+                                 od, _ptr(out), _stream()))
+    return out
+
+
+def segment_sum(grad: torch.Tensor, inverse: torch.Tensor, n_unique: Optional[torch.Tensor],
+                u_max: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[u] = sum of grad[i] over inverse[i] == u, for u < n_unique (fp32)."""
+    grad = _dev(grad, torch.float32, "grad")
+    inverse = _dev(inverse, torch.int32, "inverse")
+    n, dim = grad.shape
+    if n_unique is not None:
+        n_unique = _dev(n_unique, torch.int64, "n_unique")
+    if out is None:
+        out = torch.empty((max(u_max, 1), dim), dtype=torch.float32, device=grad.device)
+    nb = lib().segsum_workspace_bytes(n, u_max, dim)
+    ws = _workspace("segsum", nb, grad.device)
+    _check(lib().emb_grad_segment_sum(_ptr(grad), _ptr(inverse), n, _ptr(n_unique), u_max, dim,
+                                      _ptr(out), _ptr(ws), nb, _stream()))
+    return out
+
+
+def rowwise_adam(table: Table, slots: torch.Tensor, g: torch.Tensor,
+                 n_unique: Optional[torch.Tensor], lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, step=1):
+    slots = _dev(slots, torch.int32, "slots")
+    g = _dev(g, torch.float32, "g")
+    if n_unique is not None:
+        n_unique = _dev(n_unique, torch.int64, "n_unique")
+    _check(lib().emb_rowwise_adam(table.handle, _ptr(slots), _ptr(g), slots.numel(),
+                                  _ptr(n_unique), lr, b1, b2, eps, step, _stream()))
+
+
+# ----------------------------------------------------------------- helpers --
+_hip = None
+
+
+def _hip_lib():
+    global _hip
+    if _hip is None:
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise ImportError("libamdhip64 not found")
+        _hip.hipMemcpyAsync.argtypes = [_P, _P, _SZ, _I32, _P]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    return _hip
+
+
+def copy_from_device_ptr(dst: torch.Tensor, src_ptr: int):
+    """Device-to-device copy of dst.nbytes bytes from a raw device pointer into dst."""
+    rc = _hip_lib().hipMemcpyAsync(dst.data_ptr(), src_ptr, dst.numel() * dst.element_size(), 3,
+                                   _stream())
+    if rc != 0:
+        raise HTLError(HTL_ERR_DEVICE, f"hipMemcpyAsync failed ({rc})")
+    return dst
+
+
+def copy_to_device_ptr(dst_ptr: int, src: torch.Tensor):
+    src = src.contiguous()
+    rc = _hip_lib().hipMemcpyAsync(dst_ptr, src.data_ptr(), src.numel() * src.element_size(), 3,
+                                   _stream())
+    if rc != 0:
+        raise HTLError(HTL_ERR_DEVICE, f"hipMemcpyAsync failed ({rc})")
+
+
+def table_keys(table: Table) -> torch.Tensor:
+    """A copy of the table's key array (int64[M])."""
+    v = table.view()
+    out = torch.empty(table.capacity, dtype=torch.int64, device=table.device)
+    return copy_from_device_ptr(out, v.keys)
+
+
+def table_tensor(table: Table, which: str) -> torch.Tensor:
+    """A copy of 'rows' ([M, dim]), 'last_seen' ([M]), 'adam_m' or 'adam_v' ([M, dim])."""
+    v = table.view()
+    M, d = table.capacity, table.dim
+    if which == "rows":
+        out = torch.empty((M, d), dtype=table.row_dtype, device=table.device)
+        ptr = v.rows
+    elif which == "last_seen":
+        out = torch.empty(M, dtype=torch.int32, device=table.device)
+        ptr = v.last_seen
+    elif which in ("adam_m", "adam_v"):
+        out = torch.empty((M, d), dtype=torch.float32, device=table.device)
+        ptr = getattr(v, which)
+    else:
+        raise ValueError(which)
+    if not ptr:
+        raise ValueError(f"table keeps no {which}")
+    return copy_from_device_ptr(out, ptr)

@@ -1,0 +1,166 @@
+// Internal definitions shared by the library's HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "htl.h"
+
+namespace htl {
+
+// ------------------------------------------------------------- errors ----
+void set_error(const std::string& msg);
+void clear_error();
+htl_status fail(htl_status code, const std::string& msg);
+htl_status check_launch(const char* what);   // hipGetLastError after enqueues
+
+#define HTL_REQUIRE(cond, msg)                                   \
+    do {                                                         \
+        if (!(cond)) return ::htl::fail(HTL_ERR_INVALID, (msg)); \
+    } while (0)
+
+#define HTL_HIP(call)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (call);                                                         \
+        if (e_ != hipSuccess)                                                           \
+            return ::htl::fail(HTL_ERR_DEVICE, std::string(#call ": ") + hipGetErrorString(e_)); \
+    } while (0)
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// -------------------------------------------------------------- table ----
+constexpr int64_t kEmpty = -1;       // HT_EMPTY_KEY
+constexpr int64_t kTomb = -2;        // HT_TOMBSTONE_KEY
+constexpr int kBucketLog2 = 4;       // 16 slots = 128 bytes of keys per bucket
+
+// Everything a kernel needs to know about a table, passed by value.
+struct TableDev {
+    int64_t* keys;
+    void* rows;
+    uint32_t* last_seen;   // nullable
+    float* m;              // nullable
+    float* v;              // nullable
+    int64_t capacity;
+    uint64_t bucket_mask;  // number of buckets - 1
+    int bucket_log2;       // slots per bucket = 1 << bucket_log2 (<= 4)
+    int dim;
+    int elem_bytes;        // 4 (fp32) or 2 (bf16)
+    int dtype;
+    uint64_t init_base;    // mix64(init_seed)
+    uint64_t salt;         // probe-hash salt
+};
+
+}  // namespace htl
+
+struct htl_table {
+    int device;
+    int capacity_log2;
+    int dim;
+    htl_dtype dtype;
+    uint64_t init_seed;
+    uint32_t flags;
+    htl::TableDev dev;
+};
+
+namespace htl {
+
+// --------------------------------------------------------- device math ----
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The closed-form initial row of a key, 16 bytes at a time.  Row words come
+// in pairs from one SplitMix64 output: output c (0-based) of the stream
+// seeded with base = mix64(key ^ mix64(seed)) is mix64(base + (c+1)*gamma);
+// its high half is word 2c, its low half word 2c+1.
+//   fp32 element j: ((word_j >> 8) - 2^23) * 2^-26
+//   bf16 element j: ((word_j >> 24) - 128) * 2^-10
+__device__ __forceinline__ uint64_t row_base(int64_t key, uint64_t init_base) {
+    return mix64((uint64_t)key ^ init_base);
+}
+__device__ __forceinline__ uint64_t row_word_pair(uint64_t base, uint32_t c) {
+    return mix64(base + (uint64_t)(c + 1) * kGamma);
+}
+__device__ __forceinline__ float init_f32(uint32_t w) {
+    return (float)((int32_t)(w >> 8) - (1 << 23)) * 0x1p-26f;
+}
+__device__ __forceinline__ uint32_t init_bf16_bits(uint32_t w) {
+    // exact: |q| <= 128 needs at most 8 significant bits
+    return __float_as_uint((float)((int32_t)(w >> 24) - 128) * 0x1p-10f) >> 16;
+}
+// 16-byte vector v of the initial row (elements [v*E, v*E + E) with E = 4
+// fp32 or 8 bf16).
+__device__ __forceinline__ u32x4 init_vec(uint64_t base, int v, int dtype) {
+    u32x4 out;
+    if (dtype == HTL_F32) {
+        uint64_t r0 = row_word_pair(base, 2 * v);
+        uint64_t r1 = row_word_pair(base, 2 * v + 1);
+        out.x = __float_as_uint(init_f32((uint32_t)(r0 >> 32)));
+        out.y = __float_as_uint(init_f32((uint32_t)r0));
+        out.z = __float_as_uint(init_f32((uint32_t)(r1 >> 32)));
+        out.w = __float_as_uint(init_f32((uint32_t)r1));
+    } else {
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint64_t r = row_word_pair(base, 4 * v + q);
+            o[q] = init_bf16_bits((uint32_t)(r >> 32)) | (init_bf16_bits((uint32_t)r) << 16);
+        }
+        out.x = o[0]; out.y = o[1]; out.z = o[2]; out.w = o[3];
+    }
+    return out;
+}
+// Element j of the initial row as raw bits (fp32 bits, or bf16 bits in the
+// low half) -- for rows whose byte length is not a multiple of 16.
+__device__ __forceinline__ uint32_t init_elem_bits(uint64_t base, int j, int dtype) {
+    uint64_t r = row_word_pair(base, (uint32_t)(j >> 1));
+    uint32_t w = (j & 1) ? (uint32_t)r : (uint32_t)(r >> 32);
+    return dtype == HTL_F32 ? __float_as_uint(init_f32(w)) : init_bf16_bits(w);
+}
+
+// ------------------------------------------------------ wave helpers ----
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int l = __lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Relaxed device-scope load of a table key (another workgroup may CAS it).
+__device__ __forceinline__ int64_t load_key(const int64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int64_t cas_key(int64_t* p, int64_t expected, int64_t desired) {
+    return (int64_t)atomicCAS((unsigned long long*)p, (unsigned long long)expected,
+                              (unsigned long long)desired);
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Launch-size helper: blocks for `items` work items of `per_block` each,
+// clamped to [1, cap] (kernels loop grid-stride beyond the cap).
+inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap = (1 << 20)) {
+    int64_t b = ceil_div(items, per_block);
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (unsigned)b;
+}
+
+}  // namespace htl

@@ -1,0 +1,242 @@
+/*
+ * htl.h -- C ABI of the MI355X (gfx950) sparse-embedding lookup library.
+ *
+ * The library implements the embedding hot path of a generative-recommendation
+ * training system: feature-ID deduplication, a dynamic open-addressing hash
+ * embedding table (find-or-insert, erase, scan), row gather with optional
+ * sum-pooling over multi-hot bags, and the backward gradient segment-sum with
+ * a row-wise Adam update.  Sources for each operation are cited below:
+ *
+ *   [MTGenRec] MTGenRec: An Efficient Distributed Training System for
+ *              Generative Recommendation Models in Meituan (arXiv 2505.12663).
+ *   [MTGR]     MTGR: Industrial-Scale Generative Recommendation Framework in
+ *              Meituan (arXiv 2505.18654).
+ *   [TF-PS]    Deep Customization of TensorFlow for Large-Scale Sparse Training
+ *              at Meituan (technical article).
+ *
+ * Conventions for every call:
+ *   - Pointers named in a signature are DEVICE pointers unless stated
+ *     otherwise; the caller owns them (inputs, outputs and workspaces).  The
+ *     library owns the table's storage.  No pointer is retained after return.
+ *   - Every call that takes a stream only enqueues work on it (asynchronous).
+ *     Calls on one table must be ordered on one stream, or synchronised by
+ *     the caller.  Concurrent calls on one table race.
+ *   - Sizes that depend on the data (unique count, live count, victim count)
+ *     are produced on the device as int64 values; host-visible sizes passed
+ *     in are upper bounds.
+ *   - Argument errors are reported synchronously as HTL_ERR_INVALID before
+ *     anything is enqueued; launch failures as HTL_ERR_DEVICE; allocation
+ *     failures as HTL_ERR_NOMEM.  htl_last_error() then returns a message
+ *     (thread-local, valid until the next call on the same thread).
+ *     Data-dependent outcomes (full table, reserved key, key not found) are
+ *     per-key status codes, never errors.
+ *   - Device pointers must be aligned to their element size; row buffers
+ *     (outputs of the gather, gradients) to 16 bytes.
+ */
+#ifndef HTL_H_
+#define HTL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct htl_table htl_table; /* opaque; created and owned by the library */
+
+typedef enum {
+    HTL_OK = 0,
+    HTL_ERR_INVALID = 1, /* bad argument; nothing was enqueued */
+    HTL_ERR_NOMEM = 2,   /* device allocation failed */
+    HTL_ERR_DEVICE = 3   /* HIP runtime or launch error */
+} htl_status;
+
+typedef enum { HTL_F32 = 0, HTL_BF16 = 1 } htl_dtype;
+
+/* Per-key status of ht_find_or_insert (uint8 each). */
+enum { HT_FOUND = 0, HT_INSERTED = 1, HT_FULL = 2, HT_RESERVED = 3 };
+/* Per-key status of ht_erase (uint8 each). */
+enum { HT_NOT_FOUND = 0, HT_ERASED = 1 };
+/* ht_create flags. */
+enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u };
+
+/* Key values the table keeps for itself (slot markers). */
+#define HT_EMPTY_KEY ((int64_t)-1)
+#define HT_TOMBSTONE_KEY ((int64_t)-2)
+/* Largest supported capacity_log2 (2^31 slots: slot indices are int32). */
+#define HT_MAX_CAPACITY_LOG2 31
+
+/* ------------------------------------------------------------------ table --
+ * ht_create -- allocate an empty dynamic embedding table.
+ * [MTGenRec] Abstract and Figure 5: a hash-based dynamic embedding table
+ * replaces static tables; [MTGR] section 5 "Embedding Management": keys map to
+ * embedding vectors and metadata.  Theorem 1 of [MTGenRec] fixes the shape:
+ * M = 2^capacity_log2 slots probed with an odd step.
+ *   capacity_log2  1..HT_MAX_CAPACITY_LOG2; M = 2^capacity_log2 slots.
+ *   dim            row length, 1..65536 elements.
+ *   dtype          HTL_F32 or HTL_BF16 row elements.
+ *   init_seed      seed of the closed-form initial row of every new key: the
+ *                  row is a function of (key, init_seed) only.
+ *   flags          HT_META_LAST_SEEN: keep a uint32 last_seen per slot;
+ *                  HT_ADAM_STATE: keep fp32 Adam moments m, v (needs HTL_F32).
+ *   stream         the table is cleared (all slots EMPTY) on this stream.
+ * Storage, all on the current device: keys int64[M]; rows dtype[M][dim];
+ * last_seen uint32[M]; m, v float[M][dim].  *t receives the handle.
+ * Errors: INVALID for a bad size/flag combination or null t; NOMEM. */
+htl_status ht_create(htl_table** t, int capacity_log2, int dim, htl_dtype dtype,
+                     uint64_t init_seed, uint32_t flags, hipStream_t stream);
+
+/* ht_destroy -- free the table (synchronises the device first).  Null is a no-op. */
+htl_status ht_destroy(htl_table* t);
+
+/* ht_clear -- mark every slot EMPTY again (rows, metadata are left as they are). */
+htl_status ht_clear(htl_table* t, hipStream_t stream);
+
+/* ht_find_or_insert -- look up keys, inserting the absent ones.
+ * [MTGenRec] Abstract (real-time insertion), Theorem 1 (odd-step probing of a
+ * power-of-two table visits every slot); [MTGR] section 5 (keys -> vectors and
+ * metadata).  Probing walks buckets of min(16, M) consecutive slots with an
+ * odd bucket step, so every slot is reachable (Theorem 1 at bucket level) and
+ * HT_FULL is only reported when no slot on the whole walk is free.
+ *   keys     int64[n_max], device.  Precondition: the first n keys are
+ *            pairwise distinct (dedup_unique_inverse produces such a list).
+ *   n_max    host upper bound on the number of keys (sizes the launch).
+ *   n_dev    nullable device int64: the actual count n <= n_max (e.g. the
+ *            unique count written by dedup_unique_inverse); null means n_max.
+ *   step     stamped into last_seen of FOUND and INSERTED keys (if kept).
+ *   slots    int32[n_max] out: slot of each key, -1 for FULL and RESERVED.
+ *   status   uint8[n_max] out: HT_FOUND, HT_INSERTED (row set to the closed-
+ *            form initial row, Adam moments zeroed), HT_FULL, or HT_RESERVED
+ *            (key equals HT_EMPTY_KEY or HT_TOMBSTONE_KEY).
+ * Entries at index >= n are not written.  Erased slots (tombstones) are
+ * reused by inserts. */
+htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max,
+                             const int64_t* n_dev, uint32_t step, int32_t* slots,
+                             uint8_t* status, hipStream_t stream);
+
+/* ht_erase -- delete keys ([MTGenRec] Abstract: real-time deletion).  A
+ * deleted slot becomes a tombstone: lookups walk past it, inserts reuse it.
+ *   keys    int64[n] device; duplicates allowed (one of them reports ERASED).
+ *   status  uint8[n] out: HT_ERASED or HT_NOT_FOUND; nullable. */
+htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* status,
+                    hipStream_t stream);
+
+/* ht_scan -- compact listing of live slots ([MTGR] section 5, "compact key
+ * scanning").  Writes, for each live slot in an unspecified order, its key,
+ * its last_seen (if kept) and its slot index.
+ *   keys       int64[M] out (nullable)    last_seen uint32[M] out (nullable)
+ *   slots      int32[M] out (nullable)    n_live_dev int64 out: live count. */
+htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32_t* slots,
+                   int64_t* n_live_dev, hipStream_t stream);
+
+/* ht_lru_select -- choose eviction victims for an online table: the
+ * floor(live * num / den) live keys smallest by (last_seen, key), last_seen
+ * compared as uint32 and keys as int64.  [MTGenRec] Abstract (deletions in
+ * real time); [MTGR] section 5 (metadata per key, key scanning).  The pages
+ * name no policy: least-recently-used with a key tie-break is this library's.
+ * Needs HT_META_LAST_SEEN.
+ *   victims        int64[victims_cap] out: the victim keys, unspecified order.
+ *   n_victims_dev  int64 out: the number of victims k (also when k exceeds
+ *                  victims_cap, in which case victims holds an arbitrary
+ *                  subset of victims_cap of them).
+ *   ws, ws_bytes   workspace of at least lru_workspace_bytes(t) bytes. */
+size_t lru_workspace_bytes(const htl_table* t);
+htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* victims,
+                         int64_t victims_cap, int64_t* n_victims_dev, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* ht_view -- raw device views of the table's storage (read-only use intended).
+ * Any output may be null.  rows is dtype[M][dim]; m, v are null unless the
+ * table keeps Adam state; last_seen is null unless it keeps metadata. */
+typedef struct {
+    int64_t capacity;
+    int32_t dim;
+    int32_t dtype;
+    int64_t* keys;
+    void* rows;
+    uint32_t* last_seen;
+    float* adam_m;
+    float* adam_v;
+} htl_view;
+htl_status ht_view(const htl_table* t, htl_view* out);
+
+/* ------------------------------------------------------------------ dedup --
+ * dedup_unique_inverse -- feature-ID deduplication in two stages.
+ * [MTGenRec] TL;DR and table of contents section 6: two-stage ID
+ * deduplication for faster embedding lookups; [MTGR] section 5 "Embedding
+ * Lookup": IDs are unique before and after the all-to-all.  On one device,
+ * stage 1 dedups each tile of keys in on-chip memory (one copy per tile
+ * leaves it, as one copy per sender leaves a device before the exchange), and
+ * stage 2 dedups the tile survivors device-wide.
+ *   keys          int64[n]; every 64-bit value is a valid key.
+ *   unique        int64[n] out: the U distinct keys, unspecified order.
+ *   inverse       int32[n] out: unique[inverse[i]] == keys[i].
+ *   n_unique_dev  int64 out: U.
+ *   ws, ws_bytes  workspace of at least dedup_workspace_bytes(n) bytes,
+ *                 256-byte aligned; contents on entry are ignored.
+ * n must be below 2^31.  n == 0 writes U = 0. */
+size_t dedup_workspace_bytes(int64_t n);
+htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique,
+                                int32_t* inverse, int64_t* n_unique_dev, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- gather --
+ * emb_gather_pool -- embedding row gather with optional bag sum-pooling.
+ * [MTGenRec] TL;DR: faster embedding lookups; pooling over multi-hot bags is
+ * this library's reading for bag-shaped features (the pages describe none).
+ *   slots     int32[U]: table slot per unique key (from ht_find_or_insert);
+ *             a negative slot stands for a zero row.
+ *   inverse   nullable int32[n]: per-ID index into slots; null means the
+ *             identity (ID i uses slots[i]).
+ *   n         number of IDs.
+ *   offsets   nullable int32[nbags + 1], non-decreasing, offsets[0] = 0,
+ *             offsets[nbags] = n: CSR bags over the IDs.  Null = no pooling.
+ *   out_dtype HTL_F32 or HTL_BF16.  Without pooling it must equal the table's
+ *             dtype, or be HTL_F32 for a bf16 table (exact widening).  With
+ *             pooling, sums accumulate in fp32 and are rounded to bf16 to
+ *             nearest even; an empty bag gives zeros.
+ *   out       without pooling: out_dtype[n][dim] = copies of the rows;
+ *             with pooling: out_dtype[nbags][dim]. */
+htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32_t* inverse,
+                           int64_t n, const int32_t* offsets, int64_t nbags,
+                           htl_dtype out_dtype, void* out, hipStream_t stream);
+
+/* --------------------------------------------------------------- backward --
+ * emb_grad_segment_sum -- backward gradient dedup: out[u] = sum of grad[i]
+ * over the IDs with inverse[i] == u, accumulated in fp32 (the backward of the
+ * deduplicated lookup; summation order is unspecified).
+ *   grad          float[n][dim]; inverse int32[n] with values < U.
+ *   n_unique_dev  device int64 U (nullable: then U = u_max); u_max host bound.
+ *   out           float[u_max][dim]: rows 0..U-1 written, the rest untouched.
+ *   ws, ws_bytes  at least segsum_workspace_bytes(n, u_max, dim) bytes,
+ *                 256-byte aligned. */
+size_t segsum_workspace_bytes(int64_t n, int64_t u_max, int dim);
+htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64_t n,
+                                const int64_t* n_unique_dev, int64_t u_max, int dim,
+                                float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* emb_rowwise_adam -- Adam update of the rows hit by a batch.  [TF-PS]
+ * section 3.2 (Adam with its beta terms kept per parameter server; here the
+ * bias corrections are per-call scalars).  Per element, in fp32:
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+ *   theta -= lr * ((m / c1) / (sqrt(v / c2) + eps)),
+ * c1 = 1 - b1^step, c2 = 1 - b2^step (computed in fp64 on the host).
+ *   slots   int32[u_max]: slot of each unique key (negative: skipped).
+ *   g       float[u_max][dim]: the summed gradient of each unique key.
+ *   n_unique_dev nullable device int64 U <= u_max.  step >= 1.
+ * Needs an HTL_F32 table with HT_ADAM_STATE. */
+htl_status emb_rowwise_adam(htl_table* t, const int32_t* slots, const float* g, int64_t u_max,
+                            const int64_t* n_unique_dev, float lr, float b1, float b2, float eps,
+                            int64_t step, hipStream_t stream);
+
+/* htl_last_error -- message of the last failed call on this thread ("" if none). */
+const char* htl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HTL_H_ */

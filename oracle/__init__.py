@@ -69,6 +69,8 @@ def lib():
             "orc_segment_sum": (None, [_P, _P, _I64, _I64, _I32, _P, _P]),
             "orc_adam": (None, [_P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
                                 ctypes.c_float, ctypes.c_float, _I64]),
+            "orc_adam_arrays": (None, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, _I64]),
             "orc_live": (_I64, [_P, _P, _P]),
             "orc_lru_victims": (_I64, [_P, _I64, _I64, _P]),
         }
@@ -148,6 +150,17 @@ def segment_sum(grad, inverse, n_unique: int, want_abs: bool = True):
     lib().orc_segment_sum(_ptr(grad), _ptr(inverse), n, n_unique, d, _ptr(s),
                           _ptr(a) if a is not None else None)
     return s, a
+
+
+def adam_arrays(theta, m, v, g, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, step=1):
+    """One Adam step on copies of fp32 arrays; returns (theta, m, v)."""
+    th = np.array(theta, dtype=np.float32, copy=True, order="C")
+    mm = np.array(m, dtype=np.float32, copy=True, order="C")
+    vv = np.array(v, dtype=np.float32, copy=True, order="C")
+    gg = _c(g, np.float32)
+    assert th.shape == mm.shape == vv.shape == gg.shape
+    lib().orc_adam_arrays(_ptr(th), _ptr(mm), _ptr(vv), _ptr(gg), th.size, lr, b1, b2, eps, step)
+    return th, mm, vv
 
 
 # ---------------------------------------------------------------------- table

@@ -359,37 +359,48 @@ void orc_segment_sum(const float* grad, const int32_t* inverse, int64_t n, int64
     }
 }
 
-// Row-wise Adam (Kingma & Ba, Algorithm 1) on the rows of the given
-// (distinct) keys, step t >= 1, evaluated in fp64 from the fp32 state:
+// Row-wise Adam (Kingma & Ba, Algorithm 1), one element, step t >= 1,
+// evaluated in fp64 from the fp32 state:
 //   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2;
 //   theta = theta - lr * (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps),
-// then theta, m and v are stored back rounded to fp32.  Only the rows named
-// by `keys` change (lazy update); keys that are not live are skipped.
-// Requires an fp32 table created with Adam state.
+// then theta, m and v are stored back rounded to fp32.
+static void adam_elem(float& th, float& mj, float& vj, float g, double lr, double b1, double b2,
+                      double eps, double c1, double c2) {
+    const double gj = g;
+    const double m2 = b1 * (double)mj + (1.0 - b1) * gj;
+    const double v2 = b2 * (double)vj + (1.0 - b2) * gj * gj;
+    const double upd = (m2 / c1) / (std::sqrt(v2 / c2) + eps);
+    th = (float)((double)th - lr * upd);
+    mj = (float)m2;
+    vj = (float)v2;
+}
+
+// Adam over the rows of the given (distinct) keys: only those rows change
+// (lazy update); keys that are not live are skipped.  Requires an fp32 table
+// created with Adam state.
 void orc_adam(void* h, const int64_t* keys, const float* g, int64_t n, float lr, float b1,
               float b2, float eps, int64_t step) {
     Table* t = (Table*)h;
     if (!t->adam || t->dtype != 0) return;
-    const double B1 = b1, B2 = b2, LR = lr, EPS = eps;
-    const double c1 = 1.0 - std::pow(B1, (double)step);
-    const double c2 = 1.0 - std::pow(B2, (double)step);
+    const double c1 = 1.0 - std::pow((double)b1, (double)step);
+    const double c2 = 1.0 - std::pow((double)b2, (double)step);
     for (int64_t i = 0; i < n; ++i) {
         auto it = t->index.find(keys[i]);
         if (it == t->index.end()) continue;
         int64_t e = it->second;
-        for (int j = 0; j < t->dim; ++j) {
-            const double gj = g[i * t->dim + j];
-            float& mj = t->m[e * t->dim + j];
-            float& vj = t->v[e * t->dim + j];
-            float& th = t->rows_f32[e * t->dim + j];
-            const double m2 = B1 * (double)mj + (1.0 - B1) * gj;
-            const double v2 = B2 * (double)vj + (1.0 - B2) * gj * gj;
-            const double upd = (m2 / c1) / (std::sqrt(v2 / c2) + EPS);
-            th = (float)((double)th - LR * upd);
-            mj = (float)m2;
-            vj = (float)v2;
-        }
+        for (int j = 0; j < t->dim; ++j)
+            adam_elem(t->rows_f32[e * t->dim + j], t->m[e * t->dim + j], t->v[e * t->dim + j],
+                      g[i * t->dim + j], lr, b1, b2, eps, c1, c2);
     }
+}
+
+// The same update on plain arrays of n elements (theta, m, v updated in place).
+void orc_adam_arrays(float* theta, float* m, float* v, const float* g, int64_t n, float lr,
+                     float b1, float b2, float eps, int64_t step) {
+    const double c1 = 1.0 - std::pow((double)b1, (double)step);
+    const double c2 = 1.0 - std::pow((double)b2, (double)step);
+    for (int64_t i = 0; i < n; ++i)
+        adam_elem(theta[i], m[i], v[i], g[i], lr, b1, b2, eps, c1, c2);
 }
 
 // Live keys with their last_seen (MTGR section 5, compact key scanning), in

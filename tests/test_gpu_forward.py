@@ -1,0 +1,264 @@
+"""GPU parity of the forward path against the CPU oracle.
+
+dedup_unique_inverse, ht_find_or_insert, emb_gather_pool are called through
+the C ABI (via the ctypes binding) and compared with the oracle on the same
+seeded inputs.  Slot placement and unique order depend on GPU scheduling, so
+what is compared is what is unique: the set of unique keys, the map
+ID -> key through the inverse, the status of every key, and every gathered or
+pooled row -- all bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from conftest import to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _dedup_check(htl, orc, keys_np):
+    keys = torch.from_numpy(keys_np).cuda()
+    uniq, inv, nu = htl.dedup_unique_inverse(keys)
+    U = int(nu.item())
+    u = to_np(uniq)[:U]
+    i = to_np(inv)
+    ref_u, ref_inv = orc.dedup(keys_np)
+    assert U == ref_u.size
+    assert np.array_equal(np.sort(u), ref_u)               # same set, no duplicates
+    if keys_np.size:
+        assert i.min() >= 0 and i.max() < U
+        assert np.array_equal(u[i], keys_np)               # inverse maps back
+        # canonical inverse: rank of each ID's key in the sorted unique list
+        assert np.array_equal(np.searchsorted(ref_u, u[i]).astype(np.int32), ref_inv)
+    return u, i, U
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 2047, 2048, 2049, 6144 + 5, 65536, 100_003])
+def test_dedup_sizes(htl, orc, n):
+    rng = np.random.default_rng(n)
+    keys = rng.integers(0, max(4, n // 3), n).astype(np.int64) * 977 - 5
+    _dedup_check(htl, orc, keys)
+
+
+def test_dedup_special_values(htl, orc):
+    i64 = np.iinfo(np.int64)
+    base = np.array([-1, -2, i64.min, i64.max, 0, 1, -1, i64.min], dtype=np.int64)
+    rng = np.random.default_rng(1)
+    keys = np.concatenate([base, rng.choice(base, 5000), rng.integers(-50, 50, 5000)])
+    rng.shuffle(keys)
+    _dedup_check(htl, orc, keys)
+    _dedup_check(htl, orc, np.full(70000, -1, np.int64))     # only the out-of-band key
+    _dedup_check(htl, orc, np.full(70000, 12345, np.int64))  # all equal
+    _dedup_check(htl, orc, rng.permutation(150000).astype(np.int64))   # all distinct
+
+
+def test_dedup_tiny_workload(htl, orc):
+    w = workloads.tiny()
+    _, _, U = _dedup_check(htl, orc, w.keys)
+    assert U == np.unique(w.keys).size
+
+
+def _lookup_parity(htl, orc, keys_np, capacity_log2, dim, dtype, prefill=None, step=0, seed=0):
+    """Run dedup -> find_or_insert -> gather on GPU and oracle; compare all outputs."""
+    odt = orc.F32 if dtype == "f32" else orc.BF16
+    table = htl.Table(capacity_log2, dim, dtype, init_seed=seed)
+    otab = orc.Table(1 << capacity_log2, dim, odt, seed=seed)
+    if prefill is not None and prefill.size:
+        pf = torch.from_numpy(prefill).cuda()
+        _, st = table.find_or_insert(pf)
+        assert np.all(to_np(st) == htl.INSERTED)
+        otab.find_or_insert(prefill)
+    keys = torch.from_numpy(keys_np).cuda()
+    out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=step)
+    U = int(nu.item())
+    u = to_np(uniq)[:U]
+    st = to_np(status)[:U]
+    sl = to_np(slots)[:U]
+    ref_u, _ = orc.dedup(keys_np)
+    assert np.array_equal(np.sort(u), ref_u)
+    ref_st = otab.find_or_insert(u, step=step)       # same call order: statuses are order-free here
+    assert np.array_equal(st, ref_st)
+    assert np.all(sl[st <= 1] >= 0) and np.unique(sl[st <= 1]).size == int((st <= 1).sum())
+    got = to_np(out)
+    ref = otab.gather(keys_np)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+    return table, otab, u, st, sl
+
+
+def test_tiny_insert_then_find(htl, orc):
+    w = workloads.tiny()
+    table, otab, u, st, sl = _lookup_parity(htl, orc, w.keys, w.capacity_log2, w.dim, w.dtype)
+    assert np.all(st == htl.INSERTED)
+    # the same batch again: every key FOUND, same slots
+    keys = torch.from_numpy(w.keys).cuda()
+    out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=1)
+    U = int(nu.item())
+    u2, st2, sl2 = to_np(uniq)[:U], to_np(status)[:U], to_np(slots)[:U]
+    assert np.all(st2 == htl.FOUND)
+    assert dict(zip(u.tolist(), sl.tolist())) == dict(zip(u2.tolist(), sl2.tolist()))
+    assert np.array_equal(to_np(out), otab.gather(w.keys))
+
+
+@pytest.mark.parametrize("dim,dtype", [(16, "f32"), (64, "f32"), (128, "bf16"), (64, "bf16"),
+                                       (3, "f32"), (5, "bf16"), (24, "bf16"), (200, "f32")])
+def test_row_shapes(htl, orc, dim, dtype):
+    rng = np.random.default_rng(dim)
+    keys = rng.integers(0, 5000, 20000).astype(np.int64) << np.int64(20)
+    _lookup_parity(htl, orc, keys, 14, dim, dtype, seed=dim)
+
+
+def test_single_large_table_shape_small(htl, orc):
+    # the large-table workload's shape at 1/64 scale: half the slots pre-filled
+    w = workloads.single_large_table(n=1 << 16, capacity_log2=18, prefill_count=1 << 17)
+    _, _, u, st, _ = _lookup_parity(htl, orc, w.keys, w.capacity_log2, w.dim, w.dtype, prefill=w.prefill)
+    pre = np.isin(u, w.prefill)
+    assert np.array_equal(st == htl.FOUND, pre)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6])
+def test_fill_to_full(htl, orc, k):
+    M = 1 << k
+    table = htl.Table(k, 4, "f32")
+    keys = torch.arange(M, dtype=torch.int64, device="cuda") * 1000 + 3
+    slots, st = table.find_or_insert(keys)
+    assert np.all(to_np(st) == htl.INSERTED)
+    assert sorted(to_np(slots).tolist()) == list(range(M))   # every slot reachable (Theorem 1)
+    _, st = table.find_or_insert(torch.tensor([999_999], dtype=torch.int64, device="cuda"))
+    assert to_np(st).tolist() == [htl.FULL]
+    _, st = table.find_or_insert(keys)
+    assert np.all(to_np(st) == htl.FOUND)
+    # more new keys than free slots in one call: exactly `free` of them get in
+    er = table.erase(keys[:3] if M >= 3 else keys[:1])
+    freed = int((to_np(er) == htl.ERASED).sum())
+    new = torch.arange(5, dtype=torch.int64, device="cuda") + 10**9
+    _, st = table.find_or_insert(new)
+    st = to_np(st)
+    assert int((st == htl.INSERTED).sum()) == freed and int((st == htl.FULL).sum()) == 5 - freed
+
+
+def test_reserved_keys(htl, orc):
+    table = htl.Table(8, 4, "f32")
+    keys = torch.tensor([-1, 7, -2, 8], dtype=torch.int64, device="cuda")
+    slots, st = table.find_or_insert(keys)
+    assert to_np(st).tolist() == [htl.RESERVED, htl.INSERTED, htl.RESERVED, htl.INSERTED]
+    assert to_np(slots)[[0, 2]].tolist() == [-1, -1]
+    assert to_np(table.erase(keys)).tolist() == [htl.NOT_FOUND, htl.ERASED, htl.NOT_FOUND, htl.ERASED]
+
+
+def test_erase_tombstones_and_reinsert(htl, orc):
+    rng = np.random.default_rng(5)
+    table = htl.Table(12, 8, "f32")
+    otab = orc.Table(1 << 12, 8)
+    for rnd in range(6):
+        ins = np.unique(rng.integers(0, 6000, 2500)).astype(np.int64)
+        rng.shuffle(ins)
+        _, st = table.find_or_insert(torch.from_numpy(ins).cuda(), step=rnd)
+        assert np.array_equal(to_np(st), otab.find_or_insert(ins, step=rnd))
+        er = np.unique(rng.integers(0, 6000, 1500)).astype(np.int64)
+        st = table.erase(torch.from_numpy(er).cuda())
+        assert np.array_equal(to_np(st), otab.erase(er))
+        keys, ls, slots, n = table.scan()
+        L = int(n.item())
+        assert L == len(otab)
+        assert np.array_equal(np.sort(to_np(keys)[:L]), otab.live()[0])
+    # rows of live keys are still their closed-form rows after tombstone reuse
+    lk = otab.live()[0]
+    slots, st = table.find_or_insert(torch.from_numpy(lk).cuda())
+    assert np.all(to_np(st) == htl.FOUND)
+    got = to_np(htl.gather(table, slots))
+    assert np.array_equal(got, otab.gather(lk))
+
+
+def test_duplicate_erase_reports_once(htl, orc):
+    table = htl.Table(10, 4, "f32")
+    table.find_or_insert(torch.tensor([5, 6], dtype=torch.int64, device="cuda"))
+    st = to_np(table.erase(torch.tensor([5] * 100 + [6], dtype=torch.int64, device="cuda")))
+    assert int((st[:100] == htl.ERASED).sum()) == 1 and st[100] == htl.ERASED
+
+
+def test_repeatable(htl, orc):
+    w = workloads.tiny(seed=3)
+    outs = []
+    for _ in range(5):
+        table = htl.Table(w.capacity_log2, w.dim, w.dtype)
+        keys = torch.from_numpy(w.keys).cuda()
+        out, uniq, inv, nu, slots, status = htl.lookup(table, keys)
+        outs.append(to_np(out))
+        U = int(nu.item())
+        assert np.all(to_np(status)[:U] == htl.INSERTED)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_pool_merged_tables_small(htl, orc):
+    w = workloads.merged_tables(batch=1024, capacity_log2=20)
+    for out_dtype, odt in (("bf16", orc.BF16), ("f32", orc.F32)):
+        table = htl.Table(w.capacity_log2, w.dim, w.dtype)
+        otab = orc.Table(1 << w.capacity_log2, w.dim, orc.BF16)
+        keys = torch.from_numpy(w.keys).cuda()
+        offs = torch.from_numpy(w.offsets).cuda()
+        out, uniq, inv, nu, slots, status = htl.lookup(table, keys, offsets=offs, out_dtype=out_dtype)
+        U = int(nu.item())
+        otab.find_or_insert(to_np(uniq)[:U])
+        ref = otab.gather_pool(w.keys, w.offsets, odt)
+        assert np.array_equal(to_np(out), ref)
+
+
+@pytest.mark.parametrize("dim,dtype", [(16, "f32"), (64, "bf16"), (6, "bf16"), (7, "f32"), (512, "bf16")])
+def test_pool_shapes_and_empty_bags(htl, orc, dim, dtype):
+    rng = np.random.default_rng(dim)
+    lens = rng.poisson(3, 3000)
+    lens[::7] = 0
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    keys = rng.integers(0, 800, offsets[-1]).astype(np.int64)
+    odt = orc.F32 if dtype == "f32" else orc.BF16
+    table = htl.Table(12, dim, dtype)
+    otab = orc.Table(1 << 12, dim, odt)
+    out, uniq, inv, nu, slots, status = htl.lookup(table, torch.from_numpy(keys).cuda(),
+                                                   offsets=torch.from_numpy(offsets).cuda(), out_dtype="f32")
+    otab.find_or_insert(np.unique(keys))
+    ref = otab.gather_pool(keys, offsets, orc.F32)
+    got = to_np(out)
+    if dtype == "bf16":
+        assert np.array_equal(got, ref)                 # exact sums
+    else:
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-7)
+    assert not got[lens == 0].any()
+
+
+def test_widening_gather(htl, orc):
+    rng = np.random.default_rng(9)
+    keys = rng.integers(0, 3000, 9000).astype(np.int64)
+    table = htl.Table(13, 64, "bf16")
+    out, uniq, inv, nu, slots, status = htl.lookup(table, torch.from_numpy(keys).cuda(), out_dtype="f32")
+    otab = orc.Table(1 << 13, 64, orc.BF16)
+    otab.find_or_insert(np.unique(keys))
+    ref = orc.bf16_bits_to_f32(otab.gather(keys))
+    assert np.array_equal(to_np(out), ref)
+
+
+@pytest.mark.slow
+def test_single_large_table_full_size(htl, orc):
+    """The 2^22-ID / 2^24-slot workload at full size, checked on what the oracle
+    can compute one by one: unique set, status of every key (FOUND iff pre-filled),
+    inverse of every ID, and the rows of a sample of IDs (closed form)."""
+    w = workloads.single_large_table()
+    table = htl.Table(w.capacity_log2, w.dim, w.dtype)
+    _, st = table.find_or_insert(torch.from_numpy(w.prefill).cuda())
+    assert np.all(to_np(st) == htl.INSERTED)
+    keys = torch.from_numpy(w.keys).cuda()
+    out, uniq, inv, nu, slots, status = htl.lookup(table, keys)
+    U = int(nu.item())
+    u = to_np(uniq)[:U]
+    ref_u = np.unique(w.keys)
+    assert np.array_equal(np.sort(u), ref_u)
+    assert np.array_equal(u[to_np(inv)], w.keys)
+    st = to_np(status)[:U]
+    assert np.array_equal(st == htl.FOUND, np.isin(u, w.prefill))
+    assert np.all(st <= 1)
+    rng = np.random.default_rng(0)
+    idx = np.concatenate([rng.integers(0, w.keys.size, 4096), [0, w.keys.size - 1]])
+    got = to_np(out[torch.from_numpy(idx).cuda()])
+    assert np.array_equal(got, orc.init_rows(w.keys[idx], w.dim, orc.F32))

@@ -1,0 +1,81 @@
+"""GPU parity of the online-table steps: find-or-insert with a step stamp,
+gather, least-recently-used victim choice, and erase -- over a drifting
+Zipf stream, step by step against the oracle.
+
+Victim sets are compared as sets (their order is unspecified); statuses per
+key, live key sets with their last_seen, and gathered bf16 rows bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from conftest import to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_online(htl, orc, spec, steps):
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+    otab = orc.Table(1 << spec.capacity_log2, spec.dim, orc.BF16)
+    for s in range(steps):
+        keys_np = workloads.dynamic_online_step(spec, s)
+        keys = torch.from_numpy(keys_np).cuda()
+        out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=s)
+        U = int(nu.item())
+        u = to_np(uniq)[:U]
+        assert np.array_equal(to_np(status)[:U], otab.find_or_insert(u, step=s))
+        assert np.array_equal(to_np(out), otab.gather(keys_np))
+        victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
+        k = int(nv.item())
+        ref_v = otab.lru_victims(spec.evict_num, spec.evict_den)
+        assert k == ref_v.size
+        assert np.array_equal(np.sort(to_np(victims)[:k]), np.sort(ref_v))
+        st = table.erase(victims[:k])
+        assert np.all(to_np(st) == htl.ERASED)
+        otab.erase(ref_v)
+        lk, ls, sl, n = table.scan()
+        L = int(n.item())
+        assert L == len(otab)
+        order = np.argsort(to_np(lk)[:L])
+        ref_k, ref_ls = otab.live()
+        assert np.array_equal(to_np(lk)[:L][order], ref_k)
+        assert np.array_equal(to_np(ls)[:L][order].astype(np.uint32), ref_ls)
+
+
+def test_online_small(htl, orc):
+    spec = workloads.DynamicOnlineSpec(window=1 << 14, n=1 << 12, capacity_log2=16, dim=64)
+    _run_online(htl, orc, spec, steps=8)
+
+
+def test_online_heavy_eviction(htl, orc):
+    spec = workloads.DynamicOnlineSpec(window=1 << 12, n=1 << 11, capacity_log2=13, dim=8,
+                                       evict_num=1, evict_den=3)
+    _run_online(htl, orc, spec, steps=6)
+
+
+def test_lru_edge_fractions(htl, orc):
+    table = htl.Table(10, 4, "bf16", last_seen=True)
+    otab = orc.Table(1 << 10, 4, orc.BF16)
+    rng = np.random.default_rng(4)
+    for s in range(5):
+        ks = np.unique(rng.integers(0, 600, 200)).astype(np.int64)
+        table.find_or_insert(torch.from_numpy(ks).cuda(), step=s * 300)   # last_seen above one byte
+        otab.find_or_insert(ks, step=s * 300)
+    for num, den in ((0, 1), (1, 1), (1, 2), (3, 7), (1, 1000)):
+        victims, nv = table.lru_select(num, den)
+        k = int(nv.item())
+        ref = otab.lru_victims(num, den)
+        assert k == ref.size
+        assert np.array_equal(np.sort(to_np(victims)[:k]), np.sort(ref))
+    # a victim buffer smaller than k holds some of the victims, n reports all
+    victims, nv = table.lru_select(1, 2, victims_cap=5)
+    ref = otab.lru_victims(1, 2)
+    assert int(nv.item()) == ref.size
+    assert set(to_np(victims)[:5].tolist()) <= set(ref.tolist())
+
+
+def test_lru_requires_metadata(htl):
+    table = htl.Table(6, 4, "f32")
+    with pytest.raises(htl.HTLError):
+        table.lru_select(1, 20)

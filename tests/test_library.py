@@ -1,0 +1,90 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/htl.h declares, size
+its workspaces, and reject bad arguments with HTL_ERR_INVALID before it
+touches the device.  No compute call is made here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "htl.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import hash_table_lookup_amd as h
+    return h.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("ht_create", "ht_destroy", "ht_find_or_insert", "ht_erase", "dedup_unique_inverse",
+                     "emb_gather_pool", "emb_grad_segment_sum"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    import hash_table_lookup_amd as h
+    names = _declared_functions()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(h.EXPORTED)
+
+
+def test_workspace_sizes(L):
+    a = L.dedup_workspace_bytes(1000)
+    b = L.dedup_workspace_bytes(1 << 22)
+    assert 0 < a < b and b % 256 == 0
+    assert L.dedup_workspace_bytes(0) > 0
+    s1 = L.segsum_workspace_bytes(1 << 20, 1 << 18, 128)
+    s2 = L.segsum_workspace_bytes(1 << 20, 1 << 18, 64)
+    assert s1 > s2 > 0
+    assert L.lru_workspace_bytes(None) == 0
+
+
+def test_invalid_arguments_rejected_on_host(L):
+    INVALID = 1
+    h = ctypes.c_void_p()
+    assert L.ht_create(None, 10, 16, 0, 0, 0, None) == INVALID
+    assert L.ht_create(ctypes.byref(h), 0, 16, 0, 0, 0, None) == INVALID
+    assert b"capacity_log2" in L.htl_last_error()
+    assert L.ht_create(ctypes.byref(h), 32, 16, 0, 0, 0, None) == INVALID
+    assert L.ht_create(ctypes.byref(h), 10, 0, 0, 0, 0, None) == INVALID
+    assert L.ht_create(ctypes.byref(h), 10, 16, 7, 0, 0, None) == INVALID
+    assert L.ht_create(ctypes.byref(h), 10, 16, 1, 0, 2, None) == INVALID   # Adam needs fp32
+    assert L.ht_create(ctypes.byref(h), 10, 16, 0, 0, 8, None) == INVALID   # unknown flag
+    assert not h.value
+    assert L.ht_find_or_insert(None, None, 4, None, 0, None, None, None) == INVALID
+    assert L.ht_erase(None, None, 4, None, None) == INVALID
+    assert L.ht_scan(None, None, None, None, None, None) == INVALID
+    assert L.dedup_unique_inverse(None, -1, None, None, None, None, 0, None) == INVALID
+    assert L.dedup_unique_inverse(None, 1 << 31, None, None, None, None, 0, None) == INVALID
+    assert L.emb_gather_pool(None, None, None, 1, None, 0, 0, None, None) == INVALID
+    assert L.emb_grad_segment_sum(None, None, 10, None, 11, 4, None, None, 0, None) == INVALID
+    assert L.emb_grad_segment_sum(None, None, 10, None, 5, 0, None, None, 0, None) == INVALID
+    assert L.emb_rowwise_adam(None, None, None, 1, None, 1e-3, 0.9, 0.999, 1e-8, 1, None) == INVALID
+    assert L.ht_lru_select(None, 1, 20, None, 0, None, None, 0, None) == INVALID
+    assert L.ht_view(None, None) == INVALID
+    assert L.ht_destroy(None) == 0
+
+
+def test_misaligned_workspace_rejected(L):
+    INVALID = 1
+    # host-visible checks only: a bogus but non-null pointer is never dereferenced
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1001)
+    n_dev = ctypes.c_void_p(0x2000)
+    assert L.dedup_unique_inverse(fake, 10, fake, fake, n_dev, odd, 1 << 20, None) == INVALID
+    assert L.dedup_unique_inverse(fake, 10, fake, fake, n_dev, fake, 16, None) == INVALID
+    assert b"workspace" in L.htl_last_error()

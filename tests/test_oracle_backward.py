@@ -82,3 +82,20 @@ def test_adam_touches_only_batch_rows_and_zero_grad_is_noop(orc):
     assert r2[1] != before[2][1]
     t.adam(np.array([999], np.int64), g, step=1)     # not live: ignored
     assert len(t) == 3
+
+
+def test_adam_array_form_matches_table_form(orc):
+    rng = np.random.default_rng(8)
+    t = orc.Table(64, 8, orc.F32, adam=True)
+    keys = np.array([4, 5, 6], np.int64)
+    t.find_or_insert(keys)
+    th = np.stack([t.lookup(k)[0] for k in keys])
+    m = np.zeros_like(th)
+    v = np.zeros_like(th)
+    for step in (1, 2, 3, 4):
+        g = rng.standard_normal(th.shape).astype(np.float32)
+        t.adam(keys, g, step=step)
+        th, m, v = orc.adam_arrays(th, m, v, g, step=step)
+        for i, k in enumerate(keys):
+            row, _, mk, vk = t.lookup(k)
+            assert np.array_equal(row, th[i]) and np.array_equal(mk, m[i]) and np.array_equal(vk, v[i])
