@@ -14,7 +14,7 @@
 //     the hottest key's thousands of global CASes into one per tile.
 //   stage 2 (k_dedup_global): every tile survivor is inserted into a
 //     device-wide open-addressing set (next_pow2(2n) slots, 64-bit CAS); the
-//     winner of each key takes the next dense id (one atomic per wavefront).
+//     winner of each key takes the next dense id.
 //   compose (k_dedup_compose): inverse[i] = id(set slot of tile survivor
 //     local[i]).
 //
@@ -177,13 +177,23 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
 
 constexpr int kGlobalThreads = 256;
 
+// Stage 2.  A slot is read before it is CASed: a key that is already in the
+// set (the usual case for Zipf-hot keys, which every tile carries) costs a
+// cacheable load instead of an atomic that would serialise with the same
+// key's CAS from every other tile.  A CAS is attempted only on a slot seen
+// EMPTY; if it loses, the value it returns decides (same key: found; other
+// key: walk on).  Dense ids for the winners come from one atomicAdd per block
+// iteration.
 __global__ __launch_bounds__(kGlobalThreads) void k_dedup_global(
     const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, int64_t ntiles,
     unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_ids, uint64_t set_mask,
     int32_t* __restrict__ tu_slot, int64_t* __restrict__ unique, unsigned long long* __restrict__ counter,
     int32_t* __restrict__ misc) {
+    __shared__ int s_wcnt[kGlobalThreads / 64];
+    __shared__ unsigned long long s_base;
     const int tid = threadIdx.x;
     const int lane = lane_id();
+    const int wid = tid >> 6;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int cnt = tu_count[tile];
         for (int jb = 0; jb < cnt; jb += kGlobalThreads) {
@@ -195,37 +205,49 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_global(
             if (valid) {
                 k = (uint64_t)tu_keys[tile * kTile + j];
                 if (k == kFree) {
-                    win = atomicCAS(&misc[0], 0, 1) == 0;
+                    if (__hip_atomic_load(&misc[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+                        win = atomicCAS(&misc[0], 0, 1) == 0;
                 } else {
                     const uint64_t h = mix64(k ^ kSalt2);
                     uint64_t p = h & set_mask;
                     const uint64_t stp = ((h >> 32) | 1ull) & set_mask;
                     for (uint64_t probe = 0; probe <= set_mask; ++probe) {
-                        const unsigned long long old = atomicCAS(&set_keys[p], kFree, (unsigned long long)k);
-                        if (old == kFree) {
-                            win = true;
-                            break;
+                        const uint64_t cur = peek_u64(&set_keys[p]);
+                        if (cur == k) break;
+                        if (cur == kFree) {
+                            const unsigned long long old = atomicCAS(&set_keys[p], kFree, (unsigned long long)k);
+                            if (old == kFree) {
+                                win = true;
+                                break;
+                            }
+                            if (old == k) break;
                         }
-                        if (old == k) break;
                         p = (p + stp) & set_mask;
                     }
                     slot = (int64_t)p;
                 }
             }
             const uint64_t wm = __ballot(win);
-            if (wm) {
-                const int leader = __ffsll((unsigned long long)wm) - 1;
-                unsigned long long b = 0;
-                if (lane == leader) b = atomicAdd(counter, (unsigned long long)__popcll(wm));
-                b = __shfl(b, leader);
-                if (win) {
-                    const int64_t gid = (int64_t)b + __popcll(wm & lanemask_lt());
-                    unique[gid] = (int64_t)k;
-                    if (slot >= 0) set_ids[slot] = (int32_t)gid;
-                    else misc[1] = (int32_t)gid;
+            if (lane == 0) s_wcnt[wid] = __popcll(wm);
+            __syncthreads();
+            if (tid == 0) {
+                int run = 0;
+                for (int w = 0; w < kGlobalThreads / 64; ++w) {
+                    const int c = s_wcnt[w];
+                    s_wcnt[w] = run;
+                    run += c;
                 }
+                s_base = run ? atomicAdd(counter, (unsigned long long)run) : 0ull;
+            }
+            __syncthreads();
+            if (win) {
+                const int64_t gid = (int64_t)s_base + s_wcnt[wid] + __popcll(wm & lanemask_lt());
+                unique[gid] = (int64_t)k;
+                if (slot >= 0) set_ids[slot] = (int32_t)gid;
+                else misc[1] = (int32_t)gid;
             }
             if (valid) tu_slot[tile * kTile + j] = (int32_t)slot;
+            __syncthreads();
         }
     }
 }

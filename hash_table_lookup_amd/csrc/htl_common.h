@@ -141,9 +141,18 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Relaxed device-scope load of a table key (another workgroup may CAS it).
-__device__ __forceinline__ int64_t load_key(const int64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cacheable single-copy-atomic load of a key slot that other workgroups may
+// CAS during the same kernel.  It may return an older value of the slot.
+// Within one kernel a slot only ever goes from free (EMPTY or TOMBSTONE) to a
+// key -- never back -- so an old value can only show a slot as free that is
+// already taken; every claim goes through a CAS whose returned value is the
+// slot's true content, and the probe loops act on that value.  Between
+// kernels the runtime's acquire/release makes every write visible.
+__device__ __forceinline__ int64_t peek_key(const int64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint64_t peek_u64(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 __device__ __forceinline__ int64_t cas_key(int64_t* p, int64_t expected, int64_t desired) {

@@ -16,12 +16,15 @@
 // min(16, M)-slot buckets, one 128-byte line of keys each.  A key's walk
 // visits bucket b_t = b_0 + t*S mod (M/16) with S odd, so by Theorem 1 over the
 // buckets every bucket -- hence every slot -- is on the walk.  Within a bucket
-// the slots are taken in order.  Sixteen lanes of a wavefront handle one key:
-// each loads one slot of the bucket (one coalesced 128-byte request) and
+// the slots are taken in order.  A group of G lanes (4, 8 or 16) works on one
+// key, each lane holding 16/G slots of the bucket, so a wavefront keeps 64/G
+// keys in flight; the group loads the bucket's 128-byte line together and
 // ballots decide found / first free slot / EMPTY seen.  An insert claims the
 // first free (EMPTY or TOMBSTONE) slot of the walk with a 64-bit CAS; if the
 // CAS loses, the returned key is either the key itself (FOUND) or another
 // key, and the walk resumes right after that slot.
+#include <cstdlib>
+
 #include "htl_common.h"
 
 namespace htl {
@@ -29,8 +32,17 @@ namespace htl {
 namespace {
 thread_local std::string g_last_error;
 constexpr uint64_t kProbeSalt = 0x2545F4914F6CDD1Dull;
-constexpr int kGroup = 16;          // lanes per key in the probe kernels
 constexpr int kProbeBlock = 256;
+
+// Lanes per key in the probe kernels (4, 8 or 16); HTL_PROBE_LANES overrides.
+int probe_lanes() {
+    static int lanes = [] {
+        const char* e = getenv("HTL_PROBE_LANES");
+        int v = e ? atoi(e) : 8;
+        return (v == 4 || v == 8 || v == 16) ? v : 8;
+    }();
+    return lanes;
+}
 }  // namespace
 
 void set_error(const std::string& msg) { g_last_error = msg; }
@@ -58,9 +70,10 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) 
         p[i] = value;
 }
 
-// The 16-bit slice of a wave ballot that belongs to this lane's group.
+// The G-bit slice of a wave ballot that belongs to this lane's group.
+template <int G>
 __device__ __forceinline__ uint32_t group_bits(uint64_t ballot, int gshift) {
-    return (uint32_t)(ballot >> gshift) & 0xFFFFu;
+    return (uint32_t)(ballot >> gshift) & ((1u << G) - 1u);
 }
 
 __device__ __forceinline__ int64_t clamp_count(int64_t n_max, const int64_t* n_dev) {
@@ -69,41 +82,79 @@ __device__ __forceinline__ int64_t clamp_count(int64_t n_max, const int64_t* n_d
     return c < 0 ? 0 : (c < n_max ? c : n_max);
 }
 
-// Writes the closed-form initial row of `key` into `slot` (all 16 lanes of
-// the group cooperate) and zeroes its Adam moments.
+// Writes the closed-form initial row of `key` into `slot` (the G lanes of a
+// group cooperate) and zeroes its Adam moments.
+template <int G>
 __device__ void write_initial_row(const TableDev& T, int64_t slot, int64_t key, int gl) {
     const uint64_t base = row_base(key, T.init_base);
     const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
     if ((row_bytes & 15) == 0) {
         const int vpr = (int)(row_bytes >> 4);
         u32x4* dst = reinterpret_cast<u32x4*>(T.rows) + slot * vpr;
-        for (int v = gl; v < vpr; v += kGroup) dst[v] = init_vec(base, v, T.dtype);
+        for (int v = gl; v < vpr; v += G) dst[v] = init_vec(base, v, T.dtype);
     } else if (T.dtype == HTL_F32) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(T.rows) + slot * T.dim;
-        for (int j = gl; j < T.dim; j += kGroup) dst[j] = init_elem_bits(base, j, T.dtype);
+        for (int j = gl; j < T.dim; j += G) dst[j] = init_elem_bits(base, j, T.dtype);
     } else {
         uint16_t* dst = reinterpret_cast<uint16_t*>(T.rows) + slot * T.dim;
-        for (int j = gl; j < T.dim; j += kGroup) dst[j] = (uint16_t)init_elem_bits(base, j, T.dtype);
+        for (int j = gl; j < T.dim; j += G) dst[j] = (uint16_t)init_elem_bits(base, j, T.dtype);
     }
     if (T.m) {
-        for (int j = gl; j < T.dim; j += kGroup) {
+        for (int j = gl; j < T.dim; j += G) {
             T.m[slot * T.dim + j] = 0.0f;
             T.v[slot * T.dim + j] = 0.0f;
         }
     }
 }
 
+// One bucket as seen by a group of G lanes: lane gl holds slots j*G + gl,
+// j < 16/G (so each load instruction of the group reads consecutive slots).
+// Slots outside [from, W) are not examined.  Returns, as bucket-relative
+// slot numbers (-1 for none), the first slot holding `k`, the first free
+// slot, and whether the bucket holds an EMPTY slot; *free_val receives the
+// content of that first free slot.
+template <int G>
+__device__ __forceinline__ void probe_bucket(const int64_t* bucket, int64_t k, int gl, int gshift, int from, int W,
+                                             int& hit, int& free_slot, int64_t& free_val, bool& has_empty) {
+    constexpr int SPL = 16 / G;
+    int64_t v[SPL];
+    bool act[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int s = j * G + gl;
+        act[j] = s < W && s >= from;
+        v[j] = act[j] ? peek_key(bucket + s) : 0;
+    }
+    hit = -1;
+    free_slot = -1;
+    free_val = 0;
+    has_empty = false;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const uint32_t mb = group_bits<G>(__ballot(act[j] && v[j] == k), gshift);
+        if (hit < 0 && mb) hit = j * G + __builtin_ctz(mb);
+        const uint32_t fb = group_bits<G>(__ballot(act[j] && (v[j] == kEmpty || v[j] == kTomb)), gshift);
+        if (free_slot < 0 && fb) {
+            const int l = __builtin_ctz(fb);
+            free_slot = j * G + l;
+            free_val = __shfl(v[j], gshift + l);
+        }
+        if (group_bits<G>(__ballot(act[j] && v[j] == kEmpty), gshift)) has_empty = true;
+    }
+}
+
+template <int G>
 __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
     TableDev T, const int64_t* __restrict__ keys, int64_t n_max, const int64_t* __restrict__ n_dev,
     uint32_t step, int32_t* __restrict__ slots, uint8_t* __restrict__ status) {
     const int64_t n = clamp_count(n_max, n_dev);
     const int lane = lane_id();
-    const int gl = lane & (kGroup - 1);
-    const int gshift = lane & ~(kGroup - 1);
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
     const int W = 1 << T.bucket_log2;
     const uint64_t nb = T.bucket_mask + 1;
-    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kGroup;
-    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / kGroup;
+    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
 
     for (int64_t i = group0; i < n; i += ngroups) {
         const int64_t k = keys[i];
@@ -126,25 +177,22 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
                 bool found = false;          // else: saw EMPTY, or walked every bucket
                 while (t < nb) {
                     const int64_t base = (int64_t)(b << T.bucket_log2);
-                    const bool act = gl < W && gl >= from;
-                    const int64_t v = act ? load_key(T.keys + base + gl) : 0;
-                    const uint32_t mm = group_bits(__ballot(act && v == k), gshift);
-                    if (mm) {
-                        slot = base + __builtin_ctz(mm);
+                    int hit, fs;
+                    int64_t fv;
+                    bool has_empty;
+                    probe_bucket<G>(T.keys + base, k, gl, gshift, from, W, hit, fs, fv, has_empty);
+                    if (hit >= 0) {
+                        slot = base + hit;
                         found = true;
                         break;
                     }
-                    if (ff < 0) {
-                        const uint32_t fm = group_bits(__ballot(act && (v == kEmpty || v == kTomb)), gshift);
-                        if (fm) {
-                            const int l = __builtin_ctz(fm);
-                            ff = base + l;
-                            ffv = __shfl(v, gshift + l);
-                            ff_b = b;
-                            ff_t = t;
-                        }
+                    if (ff < 0 && fs >= 0) {
+                        ff = base + fs;
+                        ffv = fv;
+                        ff_b = b;
+                        ff_t = t;
                     }
-                    if (group_bits(__ballot(act && v == kEmpty), gshift)) break;
+                    if (has_empty) break;
                     from = 0;
                     b = (b + S) & T.bucket_mask;
                     ++t;
@@ -182,7 +230,7 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
                 ff = -1;
             }
         }
-        if (st == HT_INSERTED) write_initial_row(T, slot, k, gl);
+        if (st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
         if (gl == 0) {
             if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
             slots[i] = (int32_t)slot;
@@ -191,15 +239,16 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t* __restrict__ keys,
                                                        int64_t n, uint8_t* __restrict__ status) {
     const int lane = lane_id();
-    const int gl = lane & (kGroup - 1);
-    const int gshift = lane & ~(kGroup - 1);
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
     const int W = 1 << T.bucket_log2;
     const uint64_t nb = T.bucket_mask + 1;
-    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kGroup;
-    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / kGroup;
+    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
     for (int64_t i = group0; i < n; i += ngroups) {
         const int64_t k = keys[i];
         int st = HT_NOT_FOUND;
@@ -209,17 +258,18 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
             uint64_t b = h & T.bucket_mask;
             for (uint64_t t = 0; t < nb; ++t) {
                 const int64_t base = (int64_t)(b << T.bucket_log2);
-                const bool act = gl < W;
-                const int64_t v = act ? load_key(T.keys + base + gl) : 0;
-                const uint32_t mm = group_bits(__ballot(act && v == k), gshift);
-                if (mm) {
+                int hit, fs;
+                int64_t fv;
+                bool has_empty;
+                probe_bucket<G>(T.keys + base, k, gl, gshift, 0, W, hit, fs, fv, has_empty);
+                if (hit >= 0) {
                     int64_t old = 0;
-                    if (gl == 0) old = cas_key(T.keys + base + __builtin_ctz(mm), k, kTomb);
+                    if (gl == 0) old = cas_key(T.keys + base + hit, k, kTomb);
                     old = __shfl(old, gshift);
                     st = (old == k) ? HT_ERASED : HT_NOT_FOUND;
                     break;
                 }
-                if (group_bits(__ballot(act && v == kEmpty), gshift)) break;
+                if (has_empty) break;
                 b = (b + S) & T.bucket_mask;
             }
         }
@@ -400,8 +450,17 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
     HTL_REQUIRE(keys && slots && status, "ht_find_or_insert: null keys/slots/status");
     HTL_REQUIRE(aligned(keys, 8) && aligned(slots, 4) && (!n_dev || aligned(n_dev, 8)),
                 "ht_find_or_insert: misaligned pointer");
-    hipLaunchKernelGGL(k_find_or_insert, dim3(grid_for(n_max, kProbeBlock / kGroup)), dim3(kProbeBlock),
-                       0, stream, t->dev, keys, n_max, n_dev, step, slots, status);
+    const int G = probe_lanes();
+    const unsigned grid = grid_for(n_max, kProbeBlock / G);
+    if (G == 4)
+        hipLaunchKernelGGL(k_find_or_insert<4>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev,
+                           step, slots, status);
+    else if (G == 16)
+        hipLaunchKernelGGL(k_find_or_insert<16>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max,
+                           n_dev, step, slots, status);
+    else
+        hipLaunchKernelGGL(k_find_or_insert<8>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev,
+                           step, slots, status);
     return check_launch("ht_find_or_insert");
 }
 
@@ -411,8 +470,8 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "ht_erase: n out of range");
     if (n == 0) return HTL_OK;
     HTL_REQUIRE(keys && aligned(keys, 8), "ht_erase: null or misaligned keys");
-    hipLaunchKernelGGL(k_erase, dim3(grid_for(n, kProbeBlock / kGroup)), dim3(kProbeBlock), 0, stream,
-                       t->dev, keys, n, status);
+    hipLaunchKernelGGL(k_erase<8>, dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream, t->dev, keys,
+                       n, status);
     return check_launch("ht_erase");
 }
 
