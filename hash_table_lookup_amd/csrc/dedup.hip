@@ -8,13 +8,18 @@
 //
 //   stage 1 (k_dedup_tile): each workgroup dedups one tile of kTile keys in an
 //     LDS open-addressing set (2*kTile slots, 64-bit ds CAS), writes the tile's
-//     distinct keys compactly to its own region, and a 16-bit local index per
-//     key.  One copy of each key leaves the tile, as one copy per sender would
-//     leave a device before the exchange; under Zipf traffic this also turns
-//     the hottest key's thousands of global CASes into one per tile.
-//   stage 2 (k_dedup_global): every tile survivor is inserted into a
-//     device-wide open-addressing set (next_pow2(2n) slots, 64-bit CAS); the
-//     winner of each key takes the next dense id.
+//     distinct keys compactly to its own region in order of first occurrence,
+//     and a 16-bit local index per key.  One copy of each key leaves the tile,
+//     as one copy per sender would leave a device before the exchange; under
+//     Zipf traffic this also turns the hottest key's thousands of global
+//     atomics into at most one per tile.
+//   stage 2 (k_dedup_claim, k_dedup_count, k_dedup_assign): every tile
+//     survivor is inserted into a device-wide open-addressing set
+//     (next_pow2(2n) slots, 64-bit CAS), which also records the lowest tile
+//     holding each key; per-tile counts of owned keys are prefix-summed and
+//     owned keys take dense ids in tile order.  No counter atomics: the ids,
+//     hence `unique`, follow the order of first occurrence in the batch and
+//     do not depend on scheduling.
 //   compose (k_dedup_compose): inverse[i] = id(set slot of tile survivor
 //     local[i]).
 //
@@ -22,7 +27,7 @@
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
 // 2n slots it always ends at a free slot.  Every int64 is a valid key: the
 // value -1, which both sets use as their empty marker, is carried out of band.
-#include "htl_common.h"
+#include "scan.h"
 
 namespace htl {
 namespace {
@@ -31,20 +36,24 @@ constexpr int kTile = 2048;            // keys per stage-1 tile
 constexpr int kTileLog2 = 11;
 constexpr int kTileThreads = 256;
 constexpr int kKeysPerThread = kTile / kTileThreads;
-constexpr int kLdsCap = 2 * kTile;     // LDS set slots (load <= 1/2)
+constexpr int kLdsCap = 2 * kTile;     // LDS set slots (load <= 1/2); slot kLdsCap holds key -1
 constexpr int kLdsCapLog2 = kTileLog2 + 1;
 constexpr uint64_t kFree = ~0ull;      // empty marker of both sets (key -1 is out of band)
 constexpr uint64_t kSalt1 = 0x6A09E667F3BCC909ull;
 constexpr uint64_t kSalt2 = 0xBB67AE8584CAA73Bull;
+constexpr int kNoOwner = 0x7FFFFFFF;
 
 struct DedupWs {
     unsigned long long* set_keys;   // [cap]
-    int32_t* set_ids;               // [cap]
-    int64_t* tu_keys;               // [ntiles * kTile]: per-tile distinct keys
-    int32_t* tu_slot;               // [ntiles * kTile]: their set slot (-1: key -1)
+    int32_t* set_owner;             // [cap + 1]: lowest tile holding the key (entry cap: key -1)
+    int32_t* set_ids;               // [cap + 1]: dense id of the key
+    int64_t* tu_keys;               // [ntiles * kTile]: per-tile distinct keys, first-occurrence order
+    int32_t* tu_slot;               // [ntiles * kTile]: their set slot (cap: key -1)
     int32_t* tu_count;              // [ntiles]
+    int32_t* tile_win;              // [ntiles]: keys each tile owns
+    int32_t* tile_off;              // [ntiles + 1]: exclusive prefix of tile_win
+    void* scan_tmp;
     uint16_t* local;                // [n]
-    int32_t* misc;                  // [0]: key -1 claimed, [1]: its dense id
     uint64_t cap;
     size_t bytes;
 };
@@ -62,50 +71,70 @@ DedupWs layout(int64_t n, char* base) {
         return p;
     };
     w.set_keys = (unsigned long long*)take(cap * 8);
-    w.set_ids = (int32_t*)take(cap * 4);
+    w.set_owner = (int32_t*)take((cap + 1) * 4);
+    w.set_ids = (int32_t*)take((cap + 1) * 4);
     w.tu_keys = (int64_t*)take((size_t)ntiles * kTile * 8);
     w.tu_slot = (int32_t*)take((size_t)ntiles * kTile * 4);
     w.tu_count = (int32_t*)take((size_t)ntiles * 4);
+    w.tile_win = (int32_t*)take((size_t)ntiles * 4);
+    w.tile_off = (int32_t*)take((size_t)(ntiles + 1) * 4);
+    w.scan_tmp = take(scan_temp_bytes(ntiles));
     w.local = (uint16_t*)take((size_t)n * 2);
-    w.misc = (int32_t*)take(256);
     w.bytes = off;
     return w;
 }
 
-__global__ void k_dedup_clear(unsigned long long* __restrict__ set_keys, uint64_t cap,
-                              unsigned long long* __restrict__ counter, int32_t* __restrict__ misc) {
+// Block-wide exclusive prefix count of `flag` over the block's threads in
+// thread order; returns this thread's prefix and leaves the block total in
+// *total.  Uses s_wave[kTileThreads / 64].
+__device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
+    const int lane = lane_id();
+    const int wid = threadIdx.x >> 6;
+    const uint64_t m = __ballot(flag);
+    if (lane == 0) s_wave[wid] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTileThreads / 64; ++w) {
+        const int c = s_wave[w];
+        before += (w < wid) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + __popcll(m & lanemask_lt());
+}
+
+__global__ void k_dedup_clear(unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_owner,
+                              uint64_t cap) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (int64_t)cap; i += stride)
-        set_keys[i] = kFree;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *counter = 0ull;
-        misc[0] = 0;
-        misc[1] = -1;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i <= (int64_t)cap; i += stride) {
+        if (i < (int64_t)cap) set_keys[i] = kFree;
+        set_owner[i] = kNoOwner;
     }
 }
 
+// Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
+// occurrence inside the tile (LDS atomicMin of the position, then a block
+// scan over positions), so the result does not depend on scheduling.
 __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __restrict__ keys, int64_t n,
                                                             int64_t* __restrict__ tu_keys,
                                                             int32_t* __restrict__ tu_count,
                                                             uint16_t* __restrict__ local) {
     __shared__ unsigned long long s_key[kLdsCap];
-    __shared__ uint16_t s_id[kLdsCap];
-    __shared__ int s_count, s_has_free_key, s_free_key_id;
+    __shared__ int32_t s_tag[kLdsCap + 1];   // first position of the key, then its tile-local id
+    __shared__ int s_wave[kTileThreads / 64];
     const int tid = threadIdx.x;
-    const int lane = lane_id();
 
     for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
         const int64_t base = tile * kTile;
         for (int i = tid; i < kLdsCap; i += kTileThreads) s_key[i] = kFree;
-        if (tid == 0) {
-            s_count = 0;
-            s_has_free_key = 0;
-        }
+        for (int i = tid; i <= kLdsCap; i += kTileThreads) s_tag[i] = kTile;
         __syncthreads();
 
         uint64_t k[kKeysPerThread];
         int pos[kKeysPerThread];
-        uint32_t valid = 0, win = 0;
+        uint32_t valid = 0;
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
             const int64_t idx = base + j * kTileThreads + tid;
@@ -119,147 +148,152 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
             if (!(valid & (1u << j))) continue;
-            if (k[j] == kFree) {                 // key -1: out of band
-                pos[j] = kLdsCap;
-                s_has_free_key = 1;
-                continue;
-            }
-            const uint64_t h = mix64(k[j] ^ kSalt1);
-            uint32_t p = (uint32_t)(h >> (64 - kLdsCapLog2));
-            const uint32_t stp = ((uint32_t)h | 1u) & (kLdsCap - 1);
-            for (int probe = 0; probe < kLdsCap; ++probe) {
-                const unsigned long long old = atomicCAS(&s_key[p], kFree, (unsigned long long)k[j]);
-                if (old == kFree) {
-                    win |= 1u << j;
-                    break;
+            int p = kLdsCap;                         // key -1: out of band
+            if (k[j] != kFree) {
+                const uint64_t h = mix64(k[j] ^ kSalt1);
+                uint32_t q = (uint32_t)(h >> (64 - kLdsCapLog2));
+                const uint32_t stp = ((uint32_t)h | 1u) & (kLdsCap - 1);
+                for (int probe = 0; probe < kLdsCap; ++probe) {
+                    const unsigned long long old = atomicCAS(&s_key[q], kFree, (unsigned long long)k[j]);
+                    if (old == kFree || old == k[j]) break;
+                    q = (q + stp) & (kLdsCap - 1);
                 }
-                if (old == k[j]) break;
-                p = (p + stp) & (kLdsCap - 1);
+                p = (int)q;
             }
-            pos[j] = (int)p;
+            pos[j] = p;
+            atomicMin(&s_tag[p], j * kTileThreads + tid);
         }
         __syncthreads();
-
-        // Dense tile-local ids for the CAS winners: one LDS atomic per wavefront.
+        uint32_t first = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j)
+            if ((valid & (1u << j)) && s_tag[pos[j]] == j * kTileThreads + tid) first |= 1u << j;
+        __syncthreads();
+        // ids in position order: positions j*256 + tid run j-major
+        int run = 0;
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
-            const bool w = (win >> j) & 1u;
-            const uint64_t wm = __ballot(w);
-            if (wm) {
-                const int leader = __ffsll((unsigned long long)wm) - 1;
-                int b = 0;
-                if (lane == leader) b = atomicAdd(&s_count, __popcll(wm));
-                b = __shfl(b, leader);
-                if (w) {
-                    const int id = b + __popcll(wm & lanemask_lt());
-                    s_id[pos[j]] = (uint16_t)id;
-                    tu_keys[base + id] = (int64_t)k[j];
-                }
+            const bool f = (first >> j) & 1u;
+            int tot;
+            const int r = block_rank(f, s_wave, &tot);
+            if (f) {
+                s_tag[pos[j]] = run + r;
+                tu_keys[base + run + r] = (int64_t)k[j];
             }
-        }
-        __syncthreads();
-        if (tid == 0 && s_has_free_key) {
-            const int id = s_count++;
-            s_free_key_id = id;
-            tu_keys[base + id] = (int64_t)kFree;
+            run += tot;
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
             if (!(valid & (1u << j))) continue;
-            const int id = pos[j] == kLdsCap ? s_free_key_id : (int)s_id[pos[j]];
-            local[base + j * kTileThreads + tid] = (uint16_t)id;
+            local[base + j * kTileThreads + tid] = (uint16_t)s_tag[pos[j]];
         }
-        if (tid == 0) tu_count[tile] = s_count;
+        if (tid == 0) tu_count[tile] = run;
         __syncthreads();
     }
 }
 
-constexpr int kGlobalThreads = 256;
+constexpr int kGlobalThreads = kTileThreads;
 
-// Stage 2.  A slot is read before it is CASed: a key that is already in the
-// set (the usual case for Zipf-hot keys, which every tile carries) costs a
-// cacheable load instead of an atomic that would serialise with the same
-// key's CAS from every other tile.  A CAS is attempted only on a slot seen
-// EMPTY; if it loses, the value it returns decides (same key: found; other
-// key: walk on).  Dense ids for the winners come from one atomicAdd per block
-// iteration.
-__global__ __launch_bounds__(kGlobalThreads) void k_dedup_global(
+// Stage 2a: every tile survivor is put in the device-wide set, and the set
+// slot records the lowest tile holding the key (atomicMin).  A slot is read
+// before any atomic: a key already in the set (the usual case for Zipf-hot
+// keys, which every tile carries) costs a cacheable load, not an atomic that
+// would serialise with the same key's atomics from every other tile.  A CAS
+// is attempted only on a slot seen EMPTY; if it loses, the value it returns
+// decides (same key: found; other key: walk on).
+__global__ __launch_bounds__(kGlobalThreads) void k_dedup_claim(
     const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, int64_t ntiles,
-    unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_ids, uint64_t set_mask,
-    int32_t* __restrict__ tu_slot, int64_t* __restrict__ unique, unsigned long long* __restrict__ counter,
-    int32_t* __restrict__ misc) {
-    __shared__ int s_wcnt[kGlobalThreads / 64];
-    __shared__ unsigned long long s_base;
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wid = tid >> 6;
+    unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_owner, uint64_t set_mask,
+    int32_t* __restrict__ tu_slot) {
+    const uint64_t cap = set_mask + 1;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int cnt = tu_count[tile];
-        for (int jb = 0; jb < cnt; jb += kGlobalThreads) {
-            const int j = jb + tid;
-            const bool valid = j < cnt;
-            uint64_t k = 0;
-            bool win = false;
-            int64_t slot = -1;
-            if (valid) {
-                k = (uint64_t)tu_keys[tile * kTile + j];
-                if (k == kFree) {
-                    if (__hip_atomic_load(&misc[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-                        win = atomicCAS(&misc[0], 0, 1) == 0;
-                } else {
-                    const uint64_t h = mix64(k ^ kSalt2);
-                    uint64_t p = h & set_mask;
-                    const uint64_t stp = ((h >> 32) | 1ull) & set_mask;
-                    for (uint64_t probe = 0; probe <= set_mask; ++probe) {
-                        const uint64_t cur = peek_u64(&set_keys[p]);
-                        if (cur == k) break;
-                        if (cur == kFree) {
-                            const unsigned long long old = atomicCAS(&set_keys[p], kFree, (unsigned long long)k);
-                            if (old == kFree) {
-                                win = true;
-                                break;
-                            }
-                            if (old == k) break;
-                        }
-                        p = (p + stp) & set_mask;
+        for (int j = threadIdx.x; j < cnt; j += kGlobalThreads) {
+            const uint64_t k = (uint64_t)tu_keys[tile * kTile + j];
+            uint64_t p = cap;                        // key -1: the extra entry
+            if (k != kFree) {
+                const uint64_t h = mix64(k ^ kSalt2);
+                p = h & set_mask;
+                const uint64_t stp = ((h >> 32) | 1ull) & set_mask;
+                for (uint64_t probe = 0; probe <= set_mask; ++probe) {
+                    const uint64_t cur = peek_u64(&set_keys[p]);
+                    if (cur == k) break;
+                    if (cur == kFree) {
+                        const unsigned long long old = atomicCAS(&set_keys[p], kFree, (unsigned long long)k);
+                        if (old == kFree || old == k) break;
                     }
-                    slot = (int64_t)p;
+                    p = (p + stp) & set_mask;
                 }
             }
-            const uint64_t wm = __ballot(win);
-            if (lane == 0) s_wcnt[wid] = __popcll(wm);
-            __syncthreads();
-            if (tid == 0) {
-                int run = 0;
-                for (int w = 0; w < kGlobalThreads / 64; ++w) {
-                    const int c = s_wcnt[w];
-                    s_wcnt[w] = run;
-                    run += c;
-                }
-                s_base = run ? atomicAdd(counter, (unsigned long long)run) : 0ull;
+            const int32_t t32 = (int32_t)tile;
+            if (__hip_atomic_load(&set_owner[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > t32)
+                atomicMin(&set_owner[p], t32);
+            tu_slot[tile * kTile + j] = (int32_t)p;
+        }
+    }
+}
+
+// Stage 2b: how many of its keys each tile owns.
+__global__ __launch_bounds__(kGlobalThreads) void k_dedup_count(const int32_t* __restrict__ tu_count,
+                                                               const int32_t* __restrict__ tu_slot, int64_t ntiles,
+                                                               const int32_t* __restrict__ set_owner,
+                                                               int32_t* __restrict__ tile_win) {
+    __shared__ int s_wave[kGlobalThreads / 64];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int cnt = tu_count[tile];
+        int mine = 0;
+        for (int j = threadIdx.x; j < cnt; j += kGlobalThreads)
+            mine += set_owner[tu_slot[tile * kTile + j]] == (int32_t)tile;
+        for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
+        if (lane_id() == 0) s_wave[threadIdx.x >> 6] = mine;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int tot = 0;
+            for (int w = 0; w < kGlobalThreads / 64; ++w) tot += s_wave[w];
+            tile_win[tile] = tot;
+        }
+        __syncthreads();
+    }
+}
+
+// Stage 2c: owned keys get dense ids in (tile, first occurrence) order, i.e.
+// in order of first occurrence in the whole batch.
+__global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
+    const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, const int32_t* __restrict__ tu_slot,
+    int64_t ntiles, const int32_t* __restrict__ set_owner, const int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ set_ids, int64_t* __restrict__ unique, int64_t* __restrict__ n_unique) {
+    __shared__ int s_wave[kGlobalThreads / 64];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *n_unique = tile_off[ntiles];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int cnt = tu_count[tile];
+        int run = tile_off[tile];
+        for (int jb = 0; jb < cnt; jb += kGlobalThreads) {
+            const int j = jb + threadIdx.x;
+            int32_t p = 0;
+            bool own = false;
+            if (j < cnt) {
+                p = tu_slot[tile * kTile + j];
+                own = set_owner[p] == (int32_t)tile;
             }
-            __syncthreads();
-            if (win) {
-                const int64_t gid = (int64_t)s_base + s_wcnt[wid] + __popcll(wm & lanemask_lt());
-                unique[gid] = (int64_t)k;
-                if (slot >= 0) set_ids[slot] = (int32_t)gid;
-                else misc[1] = (int32_t)gid;
+            int tot;
+            const int r = block_rank(own, s_wave, &tot);
+            if (own) {
+                set_ids[p] = run + r;
+                unique[run + r] = tu_keys[tile * kTile + j];
             }
-            if (valid) tu_slot[tile * kTile + j] = (int32_t)slot;
-            __syncthreads();
+            run += tot;
         }
     }
 }
 
 __global__ void k_dedup_compose(const uint16_t* __restrict__ local, int64_t n,
                                 const int32_t* __restrict__ tu_slot, const int32_t* __restrict__ set_ids,
-                                const int32_t* __restrict__ misc, int32_t* __restrict__ inverse) {
+                                int32_t* __restrict__ inverse) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         const int64_t tile = i >> kTileLog2;
-        const int32_t s = tu_slot[(tile << kTileLog2) + local[i]];
-        inverse[i] = s >= 0 ? set_ids[s] : misc[1];
+        inverse[i] = set_ids[tu_slot[(tile << kTileLog2) + local[i]]];
     }
 }
 
@@ -292,16 +326,22 @@ htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique,
     DedupWs w = layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "dedup_unique_inverse: workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
+    const unsigned gt = grid_for(ntiles, 1, 1 << 16);
 
-    hipLaunchKernelGGL(k_dedup_clear, dim3(grid_for((int64_t)w.cap, 256 * 8, 1 << 14)), dim3(256), 0, stream,
-                       w.set_keys, w.cap, (unsigned long long*)n_unique_dev, w.misc);
-    hipLaunchKernelGGL(k_dedup_tile, dim3(grid_for(ntiles, 1, 1 << 16)), dim3(kTileThreads), 0, stream,
-                       keys, n, w.tu_keys, w.tu_count, w.local);
-    hipLaunchKernelGGL(k_dedup_global, dim3(grid_for(ntiles, 1, 1 << 16)), dim3(kGlobalThreads), 0, stream,
-                       w.tu_keys, w.tu_count, ntiles, w.set_keys, w.set_ids, (uint64_t)(w.cap - 1), w.tu_slot,
-                       unique, (unsigned long long*)n_unique_dev, w.misc);
-    hipLaunchKernelGGL(k_dedup_compose, dim3(grid_for(n, 256 * 4, 1 << 16)), dim3(256), 0, stream,
-                       w.local, n, w.tu_slot, w.set_ids, w.misc, inverse);
+    hipLaunchKernelGGL(k_dedup_clear, dim3(grid_for((int64_t)w.cap + 1, 256 * 8, 1 << 14)), dim3(256), 0, stream,
+                       w.set_keys, w.set_owner, w.cap);
+    hipLaunchKernelGGL(k_dedup_tile, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
+                       w.local);
+    hipLaunchKernelGGL(k_dedup_claim, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count, ntiles,
+                       w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot);
+    hipLaunchKernelGGL(k_dedup_count, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_count, w.tu_slot, ntiles,
+                       w.set_owner, w.tile_win);
+    htl_status st = scan_exclusive_i32(w.tile_win, w.tile_off, ntiles, nullptr, kScanIdentity, 1, w.scan_tmp, stream);
+    if (st != HTL_OK) return st;
+    hipLaunchKernelGGL(k_dedup_assign, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count, w.tu_slot,
+                       ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
+    hipLaunchKernelGGL(k_dedup_compose, dim3(grid_for(n, 256 * 4, 1 << 16)), dim3(256), 0, stream, w.local, n,
+                       w.tu_slot, w.set_ids, inverse);
     return check_launch("dedup_unique_inverse");
 }
 

@@ -172,7 +172,8 @@ htl_status ht_view(const htl_table* t, htl_view* out);
  * leaves it, as one copy per sender leaves a device before the exchange), and
  * stage 2 dedups the tile survivors device-wide.
  *   keys          int64[n]; every 64-bit value is a valid key.
- *   unique        int64[n] out: the U distinct keys, unspecified order.
+ *   unique        int64[n] out: the U distinct keys in order of first
+ *                 occurrence in keys (deterministic, independent of scheduling).
  *   inverse       int32[n] out: unique[inverse[i]] == keys[i].
  *   n_unique_dev  int64 out: U.
  *   ws, ws_bytes  workspace of at least dedup_workspace_bytes(n) bytes,

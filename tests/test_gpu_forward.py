@@ -41,6 +41,18 @@ def test_dedup_sizes(htl, orc, n):
     _dedup_check(htl, orc, keys)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_dedup_first_occurrence_order(htl, orc, seed):
+    # unique[] lists keys in order of first occurrence, so the whole output is
+    # a function of the input alone; checked against numpy's first indices.
+    w = workloads.tiny(seed=seed, n=300_000 + seed * 777)
+    u, i, U = _dedup_check(htl, orc, w.keys)
+    _, first = np.unique(w.keys, return_index=True)
+    assert np.array_equal(u, w.keys[np.sort(first)])
+    u2, i2, _ = _dedup_check(htl, orc, w.keys)
+    assert np.array_equal(u, u2) and np.array_equal(i, i2)
+
+
 def test_dedup_special_values(htl, orc):
     i64 = np.iinfo(np.int64)
     base = np.array([-1, -2, i64.min, i64.max, 0, 1, -1, i64.min], dtype=np.int64)
