@@ -59,6 +59,7 @@ _SIGNATURES = {
     "ht_view": [_P, ctypes.POINTER(_View)],
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
+    "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
     "segsum_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
@@ -225,8 +226,10 @@ class Table:
         return v
 
 
-def dedup_unique_inverse(keys: torch.Tensor):
-    """(unique int64[n], inverse int32[n], n_unique int64[1]) -- unique[:U] valid."""
+def dedup_unique_inverse(keys: torch.Tensor, ordered: bool = False):
+    """(unique int64[n], inverse int32[n], n_unique int64[1]) -- unique[:U] valid.
+
+    ordered=True lists unique keys in order of first occurrence (reproducible)."""
     keys = _dev(keys, torch.int64, "keys")
     n = keys.numel()
     unique = torch.empty(max(n, 1), dtype=torch.int64, device=keys.device)
@@ -234,8 +237,8 @@ def dedup_unique_inverse(keys: torch.Tensor):
     n_unique = torch.empty(1, dtype=torch.int64, device=keys.device)
     nb = lib().dedup_workspace_bytes(n)
     ws = _workspace("dedup", nb, keys.device)
-    _check(lib().dedup_unique_inverse(_ptr(keys), n, _ptr(unique), _ptr(inverse), _ptr(n_unique),
-                                      _ptr(ws), nb, _stream()))
+    fn = lib().dedup_unique_inverse_ordered if ordered else lib().dedup_unique_inverse
+    _check(fn(_ptr(keys), n, _ptr(unique), _ptr(inverse), _ptr(n_unique), _ptr(ws), nb, _stream()))
     return unique, inverse, n_unique
 
 

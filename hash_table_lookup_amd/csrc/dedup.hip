@@ -13,15 +13,17 @@
 //     as one copy per sender would leave a device before the exchange; under
 //     Zipf traffic this also turns the hottest key's thousands of global
 //     atomics into at most one per tile.
-//   stage 2 (k_dedup_claim, k_dedup_count, k_dedup_assign): every tile
+//   stage 2 (k_dedup_claim, [k_dedup_count], k_dedup_assign): every tile
 //     survivor is inserted into a device-wide open-addressing set
-//     (next_pow2(2n) slots, 64-bit CAS), which also records the lowest tile
-//     holding each key; per-tile counts of owned keys are prefix-summed and
-//     owned keys take dense ids in tile order.  No counter atomics: the ids,
-//     hence `unique`, follow the order of first occurrence in the batch and
-//     do not depend on scheduling.
+//     (next_pow2(2n) slots, 64-bit CAS).  One survivor per key owns it: the
+//     one whose CAS inserted it, or, in ordered mode, the one in the lowest
+//     tile (atomicMin).  Per-tile counts of owned keys are prefix-summed and
+//     owned keys take dense ids in tile order -- no counter atomics.  In
+//     ordered mode the ids, hence `unique`, follow the order of first
+//     occurrence in the batch; that costs one more atomic per unique key and
+//     two more random reads per survivor.
 //   compose (k_dedup_compose): inverse[i] = id(set slot of tile survivor
-//     local[i]).
+//     local[i]), one workgroup per tile with the survivors' ids in LDS.
 //
 // Both sets probe with an odd step over a power-of-two capacity, so by
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
@@ -49,7 +51,9 @@ struct DedupWs {
     int32_t* set_ids;               // [cap + 1]: dense id of the key
     int64_t* tu_keys;               // [ntiles * kTile]: per-tile distinct keys, first-occurrence order
     int32_t* tu_slot;               // [ntiles * kTile]: their set slot (cap: key -1)
+    uint8_t* tu_own;                // [ntiles * kTile]: 1 if this survivor owns its key
     int32_t* tu_count;              // [ntiles]
+    int32_t* misc;                  // [0]: key -1 claimed (unordered mode)
     int32_t* tile_win;              // [ntiles]: keys each tile owns
     int32_t* tile_off;              // [ntiles + 1]: exclusive prefix of tile_win
     void* scan_tmp;
@@ -75,7 +79,9 @@ DedupWs layout(int64_t n, char* base) {
     w.set_ids = (int32_t*)take((cap + 1) * 4);
     w.tu_keys = (int64_t*)take((size_t)ntiles * kTile * 8);
     w.tu_slot = (int32_t*)take((size_t)ntiles * kTile * 4);
+    w.tu_own = (uint8_t*)take((size_t)ntiles * kTile);
     w.tu_count = (int32_t*)take((size_t)ntiles * 4);
+    w.misc = (int32_t*)take(256);
     w.tile_win = (int32_t*)take((size_t)ntiles * 4);
     w.tile_off = (int32_t*)take((size_t)(ntiles + 1) * 4);
     w.scan_tmp = take(scan_temp_bytes(ntiles));
@@ -105,13 +111,15 @@ __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
     return before + __popcll(m & lanemask_lt());
 }
 
+template <bool ORDERED>
 __global__ void k_dedup_clear(unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_owner,
-                              uint64_t cap) {
+                              uint64_t cap, int32_t* __restrict__ misc) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i <= (int64_t)cap; i += stride) {
         if (i < (int64_t)cap) set_keys[i] = kFree;
-        set_owner[i] = kNoOwner;
+        if (ORDERED) set_owner[i] = kNoOwner;
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0) misc[0] = 0;
 }
 
 // Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
@@ -195,23 +203,31 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
 
 constexpr int kGlobalThreads = kTileThreads;
 
-// Stage 2a: every tile survivor is put in the device-wide set, and the set
-// slot records the lowest tile holding the key (atomicMin).  A slot is read
-// before any atomic: a key already in the set (the usual case for Zipf-hot
-// keys, which every tile carries) costs a cacheable load, not an atomic that
-// would serialise with the same key's atomics from every other tile.  A CAS
-// is attempted only on a slot seen EMPTY; if it loses, the value it returns
-// decides (same key: found; other key: walk on).
+// Stage 2a: every tile survivor is put in the device-wide set.  A slot is
+// read before any atomic: a key already in the set (the usual case for
+// Zipf-hot keys, which every tile carries) costs a cacheable load, not an
+// atomic that would serialise with the same key's atomics from every other
+// tile.  A CAS is attempted only on a slot seen EMPTY; if it loses, the value
+// it returns decides (same key: found; other key: walk on).
+// Ownership: unordered mode -- the survivor whose CAS inserted the key owns
+// it, and the block counts its tile's owners right here; ordered mode -- the
+// lowest tile holding the key owns it (atomicMin on the slot's owner field,
+// again read first), counted by k_dedup_count once every tile is done.
+template <bool ORDERED>
 __global__ __launch_bounds__(kGlobalThreads) void k_dedup_claim(
     const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, int64_t ntiles,
     unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_owner, uint64_t set_mask,
-    int32_t* __restrict__ tu_slot) {
+    int32_t* __restrict__ tu_slot, uint8_t* __restrict__ tu_own, int32_t* __restrict__ tile_win,
+    int32_t* __restrict__ misc) {
+    __shared__ int s_wave[kGlobalThreads / 64];
     const uint64_t cap = set_mask + 1;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int cnt = tu_count[tile];
+        int owned = 0;
         for (int j = threadIdx.x; j < cnt; j += kGlobalThreads) {
             const uint64_t k = (uint64_t)tu_keys[tile * kTile + j];
             uint64_t p = cap;                        // key -1: the extra entry
+            bool won = false;
             if (k != kFree) {
                 const uint64_t h = mix64(k ^ kSalt2);
                 p = h & set_mask;
@@ -221,20 +237,43 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_claim(
                     if (cur == k) break;
                     if (cur == kFree) {
                         const unsigned long long old = atomicCAS(&set_keys[p], kFree, (unsigned long long)k);
-                        if (old == kFree || old == k) break;
+                        if (old == kFree) {
+                            won = true;
+                            break;
+                        }
+                        if (old == k) break;
                     }
                     p = (p + stp) & set_mask;
                 }
+            } else if (!ORDERED) {
+                if (__hip_atomic_load(&misc[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+                    won = atomicCAS(&misc[0], 0, 1) == 0;
             }
-            const int32_t t32 = (int32_t)tile;
-            if (__hip_atomic_load(&set_owner[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > t32)
-                atomicMin(&set_owner[p], t32);
+            if (ORDERED) {
+                const int32_t t32 = (int32_t)tile;
+                if (__hip_atomic_load(&set_owner[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > t32)
+                    atomicMin(&set_owner[p], t32);
+            } else {
+                tu_own[tile * kTile + j] = won ? 1 : 0;
+                owned += won;
+            }
             tu_slot[tile * kTile + j] = (int32_t)p;
+        }
+        if (!ORDERED) {
+            for (int off = 32; off > 0; off >>= 1) owned += __shfl_xor(owned, off);
+            if (lane_id() == 0) s_wave[threadIdx.x >> 6] = owned;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int tot = 0;
+                for (int w = 0; w < kGlobalThreads / 64; ++w) tot += s_wave[w];
+                tile_win[tile] = tot;
+            }
+            __syncthreads();
         }
     }
 }
 
-// Stage 2b: how many of its keys each tile owns.
+// Stage 2b (ordered mode): how many of its keys each tile owns.
 __global__ __launch_bounds__(kGlobalThreads) void k_dedup_count(const int32_t* __restrict__ tu_count,
                                                                const int32_t* __restrict__ tu_slot, int64_t ntiles,
                                                                const int32_t* __restrict__ set_owner,
@@ -257,12 +296,14 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_count(const int32_t* _
     }
 }
 
-// Stage 2c: owned keys get dense ids in (tile, first occurrence) order, i.e.
-// in order of first occurrence in the whole batch.
+// Stage 2c: owned keys get dense ids in (tile, position in tile) order.  In
+// ordered mode that is the order of first occurrence in the whole batch.
+template <bool ORDERED>
 __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
     const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, const int32_t* __restrict__ tu_slot,
-    int64_t ntiles, const int32_t* __restrict__ set_owner, const int32_t* __restrict__ tile_off,
-    int32_t* __restrict__ set_ids, int64_t* __restrict__ unique, int64_t* __restrict__ n_unique) {
+    const uint8_t* __restrict__ tu_own, int64_t ntiles, const int32_t* __restrict__ set_owner,
+    const int32_t* __restrict__ tile_off, int32_t* __restrict__ set_ids, int64_t* __restrict__ unique,
+    int64_t* __restrict__ n_unique) {
     __shared__ int s_wave[kGlobalThreads / 64];
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_unique = tile_off[ntiles];
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -274,7 +315,7 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
             bool own = false;
             if (j < cnt) {
                 p = tu_slot[tile * kTile + j];
-                own = set_owner[p] == (int32_t)tile;
+                own = ORDERED ? set_owner[p] == (int32_t)tile : tu_own[tile * kTile + j] != 0;
             }
             int tot;
             const int r = block_rank(own, s_wave, &tot);
@@ -287,13 +328,24 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
     }
 }
 
-__global__ void k_dedup_compose(const uint16_t* __restrict__ local, int64_t n,
-                                const int32_t* __restrict__ tu_slot, const int32_t* __restrict__ set_ids,
-                                int32_t* __restrict__ inverse) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int64_t tile = i >> kTileLog2;
-        inverse[i] = set_ids[tu_slot[(tile << kTileLog2) + local[i]]];
+// inverse[i] = id of the set slot of tile survivor local[i]: each block takes
+// one tile, fetches its survivors' ids once into LDS, then maps its IDs.
+__global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* __restrict__ local, int64_t n,
+                                                               const int32_t* __restrict__ tu_count,
+                                                               const int32_t* __restrict__ tu_slot,
+                                                               const int32_t* __restrict__ set_ids,
+                                                               int32_t* __restrict__ inverse) {
+    __shared__ int32_t s_gid[kTile];
+    for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
+        const int cnt = tu_count[tile];
+        for (int j = threadIdx.x; j < cnt; j += kTileThreads) s_gid[j] = set_ids[tu_slot[tile * kTile + j]];
+        __syncthreads();
+        const int64_t base = tile * kTile;
+        for (int q = threadIdx.x; q < kTile; q += kTileThreads) {
+            const int64_t i = base + q;
+            if (i < n) inverse[i] = s_gid[local[i]];
+        }
+        __syncthreads();
     }
 }
 
@@ -311,38 +363,65 @@ size_t dedup_workspace_bytes(int64_t n) {
     return layout(n, nullptr).bytes;
 }
 
-htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
-                                int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, int64_t n, int64_t* unique,
+                            int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
     clear_error();
-    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "dedup_unique_inverse: n must be in [0, 2^31)");
-    HTL_REQUIRE(n_unique_dev && aligned(n_unique_dev, 8), "dedup_unique_inverse: null or misaligned n_unique_dev");
+    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 30), std::string(who) + ": n must be in [0, 2^30)");
+    HTL_REQUIRE(n_unique_dev && aligned(n_unique_dev, 8), std::string(who) + ": null or misaligned n_unique_dev");
     if (n == 0) {
         hipLaunchKernelGGL(k_write_zero, dim3(1), dim3(1), 0, stream, n_unique_dev);
-        return check_launch("dedup_unique_inverse");
+        return check_launch(who);
     }
-    HTL_REQUIRE(keys && unique && inverse && ws, "dedup_unique_inverse: null pointer");
+    HTL_REQUIRE(keys && unique && inverse && ws, std::string(who) + ": null pointer");
     HTL_REQUIRE(aligned(keys, 8) && aligned(unique, 8) && aligned(inverse, 4) && aligned(ws, 256),
-                "dedup_unique_inverse: misaligned pointer");
+                std::string(who) + ": misaligned pointer");
     DedupWs w = layout(n, (char*)ws);
-    HTL_REQUIRE(ws_bytes >= w.bytes, "dedup_unique_inverse: workspace too small");
+    HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
+    const unsigned gclear = grid_for((int64_t)w.cap + 1, 256 * 8, 1 << 14);
 
-    hipLaunchKernelGGL(k_dedup_clear, dim3(grid_for((int64_t)w.cap + 1, 256 * 8, 1 << 14)), dim3(256), 0, stream,
-                       w.set_keys, w.set_owner, w.cap);
+    if (ordered)
+        hipLaunchKernelGGL(k_dedup_clear<true>, dim3(gclear), dim3(256), 0, stream, w.set_keys, w.set_owner, w.cap,
+                           w.misc);
+    else
+        hipLaunchKernelGGL(k_dedup_clear<false>, dim3(gclear), dim3(256), 0, stream, w.set_keys, w.set_owner, w.cap,
+                           w.misc);
     hipLaunchKernelGGL(k_dedup_tile, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
                        w.local);
-    hipLaunchKernelGGL(k_dedup_claim, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count, ntiles,
-                       w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot);
-    hipLaunchKernelGGL(k_dedup_count, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_count, w.tu_slot, ntiles,
-                       w.set_owner, w.tile_win);
+    if (ordered) {
+        hipLaunchKernelGGL(k_dedup_claim<true>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
+                           ntiles, w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot, w.tu_own, w.tile_win,
+                           w.misc);
+        hipLaunchKernelGGL(k_dedup_count, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_count, w.tu_slot, ntiles,
+                           w.set_owner, w.tile_win);
+    } else {
+        hipLaunchKernelGGL(k_dedup_claim<false>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
+                           ntiles, w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot, w.tu_own, w.tile_win,
+                           w.misc);
+    }
     htl_status st = scan_exclusive_i32(w.tile_win, w.tile_off, ntiles, nullptr, kScanIdentity, 1, w.scan_tmp, stream);
     if (st != HTL_OK) return st;
-    hipLaunchKernelGGL(k_dedup_assign, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count, w.tu_slot,
-                       ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
-    hipLaunchKernelGGL(k_dedup_compose, dim3(grid_for(n, 256 * 4, 1 << 16)), dim3(256), 0, stream, w.local, n,
-                       w.tu_slot, w.set_ids, inverse);
-    return check_launch("dedup_unique_inverse");
+    if (ordered)
+        hipLaunchKernelGGL(k_dedup_assign<true>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
+                           w.tu_slot, w.tu_own, ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
+    else
+        hipLaunchKernelGGL(k_dedup_assign<false>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
+                           w.tu_slot, w.tu_own, ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
+    hipLaunchKernelGGL(k_dedup_compose, dim3(gt), dim3(kTileThreads), 0, stream, w.local, n, w.tu_count, w.tu_slot,
+                       w.set_ids, inverse);
+    return check_launch(who);
+}
+
+htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
+                                int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return run_dedup("dedup_unique_inverse", false, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream);
+}
+
+htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
+                                        int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return run_dedup("dedup_unique_inverse_ordered", true, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes,
+                     stream);
 }
 
 }  // extern "C"

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_apply(const int32_t* __restri
     }
     int32_t v = sum;
     block_exclusive(v, s_warp);
-    int32_t run = totals[blockIdx.x] + v;
+    int32_t run = (totals ? totals[blockIdx.x] : 0) + v;
     for (int j = 0; j < kItems; ++j) {
         const int64_t i = base + (int64_t)threadIdx.x * kItems + j;
         if (i <= n) out[i] = run;       // out[n] receives the grand total
@@ -123,6 +123,11 @@ htl_status scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n_max, co
                               int param, void* temp, hipStream_t s) {
     // Blocks cover indices 0..n_max inclusive so that out[n] is always written.
     const int64_t nblocks = ceil_div(n_max + 1, kPerBlock);
+    if (nblocks == 1) {             // one block: no carries to compute
+        hipLaunchKernelGGL(k_scan_apply, dim3(1), dim3(kThreads), 0, s, in, n_max, n_dev, mode, param,
+                           (const int32_t*)nullptr, out);
+        return check_launch("prefix sum");
+    }
     int32_t* totals = (int32_t*)temp;
     hipLaunchKernelGGL(k_block_totals, dim3((unsigned)nblocks), dim3(kThreads), 0, s, in, n_max, n_dev, mode,
                        param, totals);

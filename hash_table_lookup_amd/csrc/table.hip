@@ -16,9 +16,9 @@
 // min(16, M)-slot buckets, one 128-byte line of keys each.  A key's walk
 // visits bucket b_t = b_0 + t*S mod (M/16) with S odd, so by Theorem 1 over the
 // buckets every bucket -- hence every slot -- is on the walk.  Within a bucket
-// the slots are taken in order.  A group of G lanes (4, 8 or 16) works on one
-// key, each lane holding 16/G slots of the bucket, so a wavefront keeps 64/G
-// keys in flight; the group loads the bucket's 128-byte line together and
+// the slots are taken in order.  A group of G lanes (1, 2, 4, 8 or 16) works
+// on one key, each lane holding 16/G consecutive slots of the bucket, so a
+// wavefront keeps 64/G keys in flight; the group loads the bucket's 128-byte line together and
 // ballots decide found / first free slot / EMPTY seen.  An insert claims the
 // first free (EMPTY or TOMBSTONE) slot of the walk with a 64-bit CAS; if the
 // CAS loses, the returned key is either the key itself (FOUND) or another
@@ -34,12 +34,13 @@ thread_local std::string g_last_error;
 constexpr uint64_t kProbeSalt = 0x2545F4914F6CDD1Dull;
 constexpr int kProbeBlock = 256;
 
-// Lanes per key in the probe kernels (4, 8 or 16); HTL_PROBE_LANES overrides.
+// Lanes per key in the probe kernels (1, 2, 4, 8 or 16); HTL_PROBE_LANES
+// overrides the default.
 int probe_lanes() {
     static int lanes = [] {
         const char* e = getenv("HTL_PROBE_LANES");
-        int v = e ? atoi(e) : 8;
-        return (v == 4 || v == 8 || v == 16) ? v : 8;
+        int v = e ? atoi(e) : 4;
+        return (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 4;
     }();
     return lanes;
 }
@@ -107,40 +108,62 @@ __device__ void write_initial_row(const TableDev& T, int64_t slot, int64_t key, 
     }
 }
 
-// One bucket as seen by a group of G lanes: lane gl holds slots j*G + gl,
-// j < 16/G (so each load instruction of the group reads consecutive slots).
-// Slots outside [from, W) are not examined.  Returns, as bucket-relative
-// slot numbers (-1 for none), the first slot holding `k`, the first free
-// slot, and whether the bucket holds an EMPTY slot; *free_val receives the
-// content of that first free slot.
+// One bucket as seen by a group of G lanes: lane gl holds the SPL = 16/G
+// consecutive slots [gl*SPL, gl*SPL + SPL), read with 16-byte loads when the
+// bucket is a full 16 slots.  Slots outside [from, W) are not examined.
+// Returns, as bucket-relative slot numbers (-1 for none), the first slot
+// holding `k` and the first free slot, and whether the bucket holds an EMPTY
+// slot; *free_val receives the content of that first free slot.
+typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+
 template <int G>
 __device__ __forceinline__ void probe_bucket(const int64_t* bucket, int64_t k, int gl, int gshift, int from, int W,
                                              int& hit, int& free_slot, int64_t& free_val, bool& has_empty) {
     constexpr int SPL = 16 / G;
     int64_t v[SPL];
-    bool act[SPL];
+    const int s0 = gl * SPL;
+    if (W == 16 && SPL >= 2) {
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const int s = j * G + gl;
-        act[j] = s < W && s >= from;
-        v[j] = act[j] ? peek_key(bucket + s) : 0;
+        for (int q = 0; q < SPL / 2; ++q) {
+            const i64x2 x = *reinterpret_cast<const i64x2*>(bucket + s0 + 2 * q);
+            v[2 * q] = x.x;
+            v[2 * q + 1] = x.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) v[j] = (s0 + j < W) ? peek_key(bucket + s0 + j) : kEmpty;
+    }
+    int mj = SPL, fj = SPL;
+    bool emp = false;
+#pragma unroll
+    for (int j = SPL - 1; j >= 0; --j) {
+        const int s = s0 + j;
+        if (s >= from && s < W) {
+            if (v[j] == k) mj = j;
+            if (v[j] == kEmpty || v[j] == kTomb) fj = j;
+            if (v[j] == kEmpty) emp = true;
+        }
     }
     hit = -1;
     free_slot = -1;
     free_val = 0;
-    has_empty = false;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const uint32_t mb = group_bits<G>(__ballot(act[j] && v[j] == k), gshift);
-        if (hit < 0 && mb) hit = j * G + __builtin_ctz(mb);
-        const uint32_t fb = group_bits<G>(__ballot(act[j] && (v[j] == kEmpty || v[j] == kTomb)), gshift);
-        if (free_slot < 0 && fb) {
-            const int l = __builtin_ctz(fb);
-            free_slot = j * G + l;
-            free_val = __shfl(v[j], gshift + l);
-        }
-        if (group_bits<G>(__ballot(act[j] && v[j] == kEmpty), gshift)) has_empty = true;
+    const uint32_t mb = group_bits<G>(__ballot(mj < SPL), gshift);
+    if (mb) {
+        const int l = __builtin_ctz(mb);
+        hit = l * SPL + __shfl(mj, gshift + l);
     }
+    const uint32_t fb = group_bits<G>(__ballot(fj < SPL), gshift);
+    if (fb) {
+        const int l = __builtin_ctz(fb);
+        int64_t fv = 0;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j)
+            if (j == fj) fv = v[j];
+        const int fjl = __shfl(fj, gshift + l);
+        free_slot = l * SPL + fjl;
+        free_val = __shfl(fv, gshift + l);
+    }
+    has_empty = group_bits<G>(__ballot(emp), gshift) != 0;
 }
 
 template <int G>
@@ -452,15 +475,17 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
                 "ht_find_or_insert: misaligned pointer");
     const int G = probe_lanes();
     const unsigned grid = grid_for(n_max, kProbeBlock / G);
-    if (G == 4)
-        hipLaunchKernelGGL(k_find_or_insert<4>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev,
-                           step, slots, status);
-    else if (G == 16)
-        hipLaunchKernelGGL(k_find_or_insert<16>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max,
-                           n_dev, step, slots, status);
-    else
-        hipLaunchKernelGGL(k_find_or_insert<8>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev,
-                           step, slots, status);
+#define HTL_FOI(GG)                                                                                        \
+    hipLaunchKernelGGL(k_find_or_insert<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, \
+                       n_dev, step, slots, status)
+    switch (G) {
+        case 1: HTL_FOI(1); break;
+        case 2: HTL_FOI(2); break;
+        case 8: HTL_FOI(8); break;
+        case 16: HTL_FOI(16); break;
+        default: HTL_FOI(4); break;
+    }
+#undef HTL_FOI
     return check_launch("ht_find_or_insert");
 }
 

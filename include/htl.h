@@ -172,17 +172,25 @@ htl_status ht_view(const htl_table* t, htl_view* out);
  * leaves it, as one copy per sender leaves a device before the exchange), and
  * stage 2 dedups the tile survivors device-wide.
  *   keys          int64[n]; every 64-bit value is a valid key.
- *   unique        int64[n] out: the U distinct keys in order of first
- *                 occurrence in keys (deterministic, independent of scheduling).
+ *   unique        int64[n] out: the U distinct keys.  Order: unspecified
+ *                 (it depends on which tile's insert wins a race).
  *   inverse       int32[n] out: unique[inverse[i]] == keys[i].
  *   n_unique_dev  int64 out: U.
  *   ws, ws_bytes  workspace of at least dedup_workspace_bytes(n) bytes,
  *                 256-byte aligned; contents on entry are ignored.
- * n must be below 2^31.  n == 0 writes U = 0. */
+ * n must be below 2^30.  n == 0 writes U = 0. */
 size_t dedup_workspace_bytes(int64_t n);
 htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique,
                                 int32_t* inverse, int64_t* n_unique_dev, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
+
+/* dedup_unique_inverse_ordered -- the same, with `unique` in order of first
+ * occurrence in keys: the output is a function of the input alone
+ * (reproducible run to run).  Same arguments and workspace; slower (one more
+ * atomic per unique key). */
+htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t* unique,
+                                        int32_t* inverse, int64_t* n_unique_dev, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------- gather --
  * emb_gather_pool -- embedding row gather with optional bag sum-pooling.

@@ -17,9 +17,9 @@ from conftest import to_np
 pytestmark = pytest.mark.gpu
 
 
-def _dedup_check(htl, orc, keys_np):
+def _dedup_check(htl, orc, keys_np, ordered=False):
     keys = torch.from_numpy(keys_np).cuda()
-    uniq, inv, nu = htl.dedup_unique_inverse(keys)
+    uniq, inv, nu = htl.dedup_unique_inverse(keys, ordered=ordered)
     U = int(nu.item())
     u = to_np(uniq)[:U]
     i = to_np(inv)
@@ -34,11 +34,15 @@ def _dedup_check(htl, orc, keys_np):
     return u, i, U
 
 
+@pytest.mark.parametrize("ordered", [False, True])
 @pytest.mark.parametrize("n", [0, 1, 2, 2047, 2048, 2049, 6144 + 5, 65536, 100_003])
-def test_dedup_sizes(htl, orc, n):
+def test_dedup_sizes(htl, orc, n, ordered):
     rng = np.random.default_rng(n)
     keys = rng.integers(0, max(4, n // 3), n).astype(np.int64) * 977 - 5
-    _dedup_check(htl, orc, keys)
+    u, _, _ = _dedup_check(htl, orc, keys, ordered)
+    if ordered and n:
+        _, first = np.unique(keys, return_index=True)
+        assert np.array_equal(u, keys[np.sort(first)])
 
 
 @pytest.mark.parametrize("seed", [0, 1])
@@ -46,23 +50,24 @@ def test_dedup_first_occurrence_order(htl, orc, seed):
     # unique[] lists keys in order of first occurrence, so the whole output is
     # a function of the input alone; checked against numpy's first indices.
     w = workloads.tiny(seed=seed, n=300_000 + seed * 777)
-    u, i, U = _dedup_check(htl, orc, w.keys)
+    u, i, U = _dedup_check(htl, orc, w.keys, ordered=True)
     _, first = np.unique(w.keys, return_index=True)
     assert np.array_equal(u, w.keys[np.sort(first)])
-    u2, i2, _ = _dedup_check(htl, orc, w.keys)
+    u2, i2, _ = _dedup_check(htl, orc, w.keys, ordered=True)
     assert np.array_equal(u, u2) and np.array_equal(i, i2)
 
 
-def test_dedup_special_values(htl, orc):
+@pytest.mark.parametrize("ordered", [False, True])
+def test_dedup_special_values(htl, orc, ordered):
     i64 = np.iinfo(np.int64)
     base = np.array([-1, -2, i64.min, i64.max, 0, 1, -1, i64.min], dtype=np.int64)
     rng = np.random.default_rng(1)
     keys = np.concatenate([base, rng.choice(base, 5000), rng.integers(-50, 50, 5000)])
     rng.shuffle(keys)
-    _dedup_check(htl, orc, keys)
-    _dedup_check(htl, orc, np.full(70000, -1, np.int64))     # only the out-of-band key
-    _dedup_check(htl, orc, np.full(70000, 12345, np.int64))  # all equal
-    _dedup_check(htl, orc, rng.permutation(150000).astype(np.int64))   # all distinct
+    _dedup_check(htl, orc, keys, ordered)
+    _dedup_check(htl, orc, np.full(70000, -1, np.int64), ordered)     # only the out-of-band key
+    _dedup_check(htl, orc, np.full(70000, 12345, np.int64), ordered)  # all equal
+    _dedup_check(htl, orc, rng.permutation(150000).astype(np.int64), ordered)   # all distinct
 
 
 def test_dedup_tiny_workload(htl, orc):
