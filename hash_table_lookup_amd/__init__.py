@@ -29,21 +29,18 @@ __all__ = [
 
 
 def lookup(table: Table, keys: torch.Tensor, step: int = 0,
-           offsets: Optional[torch.Tensor] = None, out_dtype=None, ordered: bool = False,
-           fresh: bool = True, out: Optional[torch.Tensor] = None):
+           offsets: Optional[torch.Tensor] = None, out_dtype=None):
     """The forward hot path on one batch of feature IDs.
 
     dedup_unique_inverse -> ht_find_or_insert (absent keys inserted) ->
-    emb_gather_pool(_fresh).  Returns (out, unique, inverse, n_unique, slots,
-    status); out is per-ID rows, or per-bag sums when CSR ``offsets`` are
-    given.  fresh=True lets the gather recompute just-inserted rows.
+    emb_gather_pool.  Returns (out, unique, inverse, n_unique, slots, status);
+    out is per-ID rows, or per-bag sums when CSR ``offsets`` are given.
     """
-    unique, inverse, n_unique = dedup_unique_inverse(keys, ordered=ordered)
+    unique, inverse, n_unique = dedup_unique_inverse(keys)
     slots, status = table.find_or_insert(unique, n_dev=n_unique, step=step)
-    fk = dict(unique=unique, status=status) if fresh else {}
     if offsets is None:
-        out = gather(table, slots, inverse, out_dtype=out_dtype, out=out, **fk)
+        out = gather(table, slots, inverse, out_dtype=out_dtype)
     else:
         out = gather_pool(table, slots, inverse, offsets,
-                          out_dtype=out_dtype if out_dtype is not None else table.dtype, out=out, **fk)
+                          out_dtype=out_dtype if out_dtype is not None else table.dtype)
     return out, unique, inverse, n_unique, slots, status

@@ -61,7 +61,6 @@ _SIGNATURES = {
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
-    "emb_gather_pool_fresh": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P, _P, _P],
     "segsum_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
     "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
@@ -243,50 +242,35 @@ def dedup_unique_inverse(keys: torch.Tensor, ordered: bool = False):
     return unique, inverse, n_unique
 
 
-def _fresh_args(unique, status):
-    if (unique is None) != (status is None):
-        raise ValueError("unique and status go together")
-    if unique is None:
-        return None, None
-    return _dev(unique, torch.int64, "unique"), _dev(status, torch.uint8, "status")
-
-
 def gather(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor] = None,
-           out_dtype=None, out: Optional[torch.Tensor] = None,
-           unique: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-ID rows: out[i] = rows[slots[inverse[i]]] (inverse None: identity).
-
-    unique/status: the keys and statuses of the find_or_insert call that made
-    `slots`; rows it inserted are recomputed instead of read back."""
+           out_dtype=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-ID rows: out[i] = rows[slots[inverse[i]]] (inverse None: identity)."""
     slots = _dev(slots, torch.int32, "slots")
     n = slots.numel() if inverse is None else inverse.numel()
     if inverse is not None:
         inverse = _dev(inverse, torch.int32, "inverse")
-    unique, status = _fresh_args(unique, status)
     od = table.dtype if out_dtype is None else _dtype_code(out_dtype)
     if out is None:
         out = torch.empty((n, table.dim), dtype=_TORCH_DTYPE[od], device=slots.device)
-    _check(lib().emb_gather_pool_fresh(table.handle, _ptr(slots), _ptr(inverse), n, None, 0, od,
-                                       _ptr(out), _ptr(unique), _ptr(status), _stream()))
+    _check(lib().emb_gather_pool(table.handle, _ptr(slots), _ptr(inverse), n, None, 0, od,
+                                 _ptr(out), _stream()))
     return out
 
 
 def gather_pool(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor],
-                offsets: torch.Tensor, out_dtype="f32", out: Optional[torch.Tensor] = None,
-                unique: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None):
+                offsets: torch.Tensor, out_dtype="f32", out: Optional[torch.Tensor] = None):
     """Bag sums: out[b] = sum of rows of IDs offsets[b]..offsets[b+1]-1."""
     slots = _dev(slots, torch.int32, "slots")
     offsets = _dev(offsets, torch.int32, "offsets")
     n = slots.numel() if inverse is None else inverse.numel()
     if inverse is not None:
         inverse = _dev(inverse, torch.int32, "inverse")
-    unique, status = _fresh_args(unique, status)
     nb = offsets.numel() - 1
     od = _dtype_code(out_dtype)
     if out is None:
         out = torch.empty((nb, table.dim), dtype=_TORCH_DTYPE[od], device=offsets.device)
-    _check(lib().emb_gather_pool_fresh(table.handle, _ptr(slots), _ptr(inverse), n, _ptr(offsets),
-                                       nb, od, _ptr(out), _ptr(unique), _ptr(status), _stream()))
+    _check(lib().emb_gather_pool(table.handle, _ptr(slots), _ptr(inverse), n, _ptr(offsets), nb,
+                                 od, _ptr(out), _stream()))
     return out
 
 

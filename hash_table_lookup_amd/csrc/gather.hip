@@ -28,45 +28,28 @@ __device__ __forceinline__ u32x4 zero4() {
     return z;
 }
 
-// Rows of keys the same find-or-insert call just inserted (ustatus ==
-// HT_INSERTED) are their closed-form initial rows: those are recomputed from
-// the key (ukeys) instead of read back from HBM.
 template <int TEAM>
 __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ rows, int vpr, int64_t M,
                                                   const int32_t* __restrict__ slots,
                                                   const int32_t* __restrict__ inverse, int64_t n,
-                                                  const int64_t* __restrict__ ukeys,
-                                                  const uint8_t* __restrict__ ustatus, uint64_t init_base,
-                                                  int dtype, u32x4* __restrict__ out) {
+                                                  u32x4* __restrict__ out) {
     const int tl = threadIdx.x & (TEAM - 1);
     const int64_t team = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / TEAM;
     const int64_t nteams = (int64_t)gridDim.x * kBlock / TEAM;
     for (int64_t rb = team; rb < n; rb += nteams * kUnroll) {
         int32_t s[kUnroll];
-        uint64_t fresh_base[kUnroll];
-        bool fresh[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t r = rb + u * nteams;
             s[u] = -1;
-            fresh[u] = false;
-            fresh_base[u] = 0;
-            if (r < n) {
-                const int32_t idx = inverse ? inverse[r] : (int32_t)r;
-                s[u] = slots[idx];
-                if (ustatus && s[u] >= 0 && ustatus[idx] == HT_INSERTED) {
-                    fresh[u] = true;
-                    fresh_base[u] = row_base(ukeys[idx], init_base);
-                }
-            }
+            if (r < n) s[u] = slots[inverse ? inverse[r] : r];
             if (s[u] >= M) s[u] = -1;            // not a slot of this table: zero row
         }
         for (int v = tl; v < vpr; v += TEAM) {
             u32x4 val[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                val[u] = fresh[u] ? init_vec(fresh_base[u], v, dtype)
-                                  : (s[u] >= 0 ? rows[(int64_t)s[u] * vpr + v] : zero4());
+                val[u] = s[u] >= 0 ? rows[(int64_t)s[u] * vpr + v] : zero4();
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t r = rb + u * nteams;
@@ -125,8 +108,6 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
                                                 const int32_t* __restrict__ slots,
                                                 const int32_t* __restrict__ inverse,
                                                 const int32_t* __restrict__ offsets, int64_t nbags,
-                                                const int64_t* __restrict__ ukeys,
-                                                const uint8_t* __restrict__ ustatus, uint64_t init_base,
                                                 bool out_bf16, void* __restrict__ out) {
     constexpr int E = IN_BF16 ? 8 : 4;            // elements per 16-byte vector
     constexpr int TEAMS = 64 / TEAM;
@@ -143,17 +124,14 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
             for (int e = 0; e < E; ++e) acc[a][e] = 0.0f;
         const int32_t beg = offsets[bag], end = offsets[bag + 1];
         for (int32_t i = beg + q; i < end; i += TEAMS) {
-            const int32_t idx = inverse ? inverse[i] : i;
-            const int32_t s = slots[idx];
+            const int32_t s = slots[inverse ? inverse[i] : i];
             if (s < 0 || s >= M) continue;
-            const bool fresh = ustatus && ustatus[idx] == HT_INSERTED;
-            const uint64_t fbase = fresh ? row_base(ukeys[idx], init_base) : 0;
             const u32x4* src = rows + (int64_t)s * vpr;
 #pragma unroll
             for (int a = 0; a < QMAX; ++a) {
                 const int v = tl + a * TEAM;
                 if (v >= vpr) break;
-                const u32x4 x = fresh ? init_vec(fbase, v, IN_BF16 ? HTL_BF16 : HTL_F32) : src[v];
+                const u32x4 x = src[v];
                 if (IN_BF16) {
                     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -241,29 +219,26 @@ int team_for(int vpr) {
 
 template <int TEAM>
 void launch_gather(const TableDev& T, int vpr, const int32_t* slots, const int32_t* inverse, int64_t n,
-                   const int64_t* ukeys, const uint8_t* ustatus, void* out, bool widen, hipStream_t s) {
+                   void* out, bool widen, hipStream_t s) {
     const unsigned grid = grid_for(n, (kBlock / TEAM) * (widen ? 1 : kUnroll));
     if (widen)
         hipLaunchKernelGGL(k_gather_widen<TEAM>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows, vpr,
                            T.capacity, slots, inverse, n, (u32x4*)out);
     else
         hipLaunchKernelGGL(k_gather<TEAM>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows, vpr,
-                           T.capacity, slots, inverse, n, ukeys, ustatus, T.init_base, T.dtype, (u32x4*)out);
+                           T.capacity, slots, inverse, n, (u32x4*)out);
 }
 
 template <int TEAM, int QMAX>
 void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t* inverse,
-                 const int32_t* offsets, int64_t nbags, const int64_t* ukeys, const uint8_t* ustatus,
-                 bool out_bf16, void* out, hipStream_t s) {
+                 const int32_t* offsets, int64_t nbags, bool out_bf16, void* out, hipStream_t s) {
     const unsigned grid = grid_for(nbags, kBlock / 64);
     if (T.dtype == HTL_BF16)
         hipLaunchKernelGGL((k_pool<TEAM, QMAX, true>), dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
-                           vpr, T.capacity, slots, inverse, offsets, nbags, ukeys, ustatus, T.init_base, out_bf16,
-                           out);
+                           vpr, T.capacity, slots, inverse, offsets, nbags, out_bf16, out);
     else
         hipLaunchKernelGGL((k_pool<TEAM, QMAX, false>), dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
-                           vpr, T.capacity, slots, inverse, offsets, nbags, ukeys, ustatus, T.init_base, out_bf16,
-                           out);
+                           vpr, T.capacity, slots, inverse, offsets, nbags, out_bf16, out);
 }
 
 }  // namespace
@@ -276,15 +251,7 @@ extern "C" {
 htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32_t* inverse, int64_t n,
                            const int32_t* offsets, int64_t nbags, htl_dtype out_dtype, void* out,
                            hipStream_t stream) {
-    return emb_gather_pool_fresh(t, slots, inverse, n, offsets, nbags, out_dtype, out, nullptr, nullptr, stream);
-}
-
-htl_status emb_gather_pool_fresh(const htl_table* t, const int32_t* slots, const int32_t* inverse, int64_t n,
-                                 const int32_t* offsets, int64_t nbags, htl_dtype out_dtype, void* out,
-                                 const int64_t* ukeys, const uint8_t* ustatus, hipStream_t stream) {
     clear_error();
-    HTL_REQUIRE((ukeys == nullptr) == (ustatus == nullptr),
-                "emb_gather_pool_fresh: unique keys and status go together");
     HTL_REQUIRE(t != nullptr, "emb_gather_pool: null table");
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "emb_gather_pool: n must be in [0, 2^31)");
     HTL_REQUIRE(out_dtype == HTL_F32 || out_dtype == HTL_BF16, "emb_gather_pool: bad out_dtype");
@@ -302,13 +269,13 @@ htl_status emb_gather_pool_fresh(const htl_table* t, const int32_t* slots, const
         const bool widen = out_dtype != t->dtype;
         if (vec) {
             switch (team_for(vpr)) {
-                case 1: launch_gather<1>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                case 2: launch_gather<2>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                case 4: launch_gather<4>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                case 8: launch_gather<8>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                case 16: launch_gather<16>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                case 32: launch_gather<32>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
-                default: launch_gather<64>(T, vpr, slots, inverse, n, ukeys, ustatus, out, widen, stream); break;
+                case 1: launch_gather<1>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                case 2: launch_gather<2>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                case 4: launch_gather<4>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                case 8: launch_gather<8>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                case 16: launch_gather<16>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                case 32: launch_gather<32>(T, vpr, slots, inverse, n, out, widen, stream); break;
+                default: launch_gather<64>(T, vpr, slots, inverse, n, out, widen, stream); break;
             }
         } else {
             const unsigned grid = grid_for(n * T.dim, 256 * 4);
@@ -334,16 +301,16 @@ htl_status emb_gather_pool_fresh(const htl_table* t, const int32_t* slots, const
     if (vec && vpr <= 256) {
         const int team = team_for(vpr);
         switch (team) {
-            case 1: launch_pool<1, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
-            case 2: launch_pool<2, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
-            case 4: launch_pool<4, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
-            case 8: launch_pool<8, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
-            case 16: launch_pool<16, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
-            case 32: launch_pool<32, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream); break;
+            case 1: launch_pool<1, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 2: launch_pool<2, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 4: launch_pool<4, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 8: launch_pool<8, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 16: launch_pool<16, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 32: launch_pool<32, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
             default:
-                if (vpr <= 64) launch_pool<64, 1>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream);
-                else if (vpr <= 128) launch_pool<64, 2>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream);
-                else launch_pool<64, 4>(T, vpr, slots, inverse, offsets, nbags, ukeys, ustatus, out_bf16, out, stream);
+                if (vpr <= 64) launch_pool<64, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
+                else if (vpr <= 128) launch_pool<64, 2>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
+                else launch_pool<64, 4>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
                 break;
         }
     } else {

@@ -213,20 +213,6 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
                            int64_t n, const int32_t* offsets, int64_t nbags,
                            htl_dtype out_dtype, void* out, hipStream_t stream);
 
-/* emb_gather_pool_fresh -- emb_gather_pool that also takes the unique keys
- * and per-key statuses of the ht_find_or_insert call that produced `slots`.
- * Rows of keys that call INSERTED are, by definition, their closed-form
- * initial rows; the gather recomputes them from the key instead of reading
- * them back (the same bits, less HBM traffic).  Valid only while those rows
- * are unmodified since that call (no Adam update in between).
- *   ukeys    int64[U]: the keys passed to ht_find_or_insert (nullable).
- *   ustatus  uint8[U]: its status output (nullable; null iff ukeys is null).
- * With both null this is emb_gather_pool. */
-htl_status emb_gather_pool_fresh(const htl_table* t, const int32_t* slots, const int32_t* inverse,
-                                 int64_t n, const int32_t* offsets, int64_t nbags,
-                                 htl_dtype out_dtype, void* out, const int64_t* ukeys,
-                                 const uint8_t* ustatus, hipStream_t stream);
-
 /* --------------------------------------------------------------- backward --
  * emb_grad_segment_sum -- backward gradient dedup: out[u] = sum of grad[i]
  * over the IDs with inverse[i] == u, accumulated in fp32 (the backward of the

@@ -211,26 +211,6 @@ def test_duplicate_erase_reports_once(htl, orc):
     assert int((st[:100] == htl.ERASED).sum()) == 1 and st[100] == htl.ERASED
 
 
-@pytest.mark.parametrize("dim,dtype", [(64, "f32"), (128, "bf16"), (16, "f32")])
-def test_fresh_rows_match_stored_rows(htl, orc, dim, dtype):
-    # recomputing just-inserted rows gives the bits the table stores
-    w = workloads.single_large_table(n=1 << 15, capacity_log2=17, prefill_count=1 << 15, dim=dim)
-    table = htl.Table(w.capacity_log2, dim, dtype)
-    table.find_or_insert(torch.from_numpy(w.prefill).cuda())
-    keys = torch.from_numpy(w.keys).cuda()
-    uniq, inv, nu = htl.dedup_unique_inverse(keys)
-    slots, status = table.find_or_insert(uniq, n_dev=nu)
-    assert bool((status[: int(nu.item())] == htl.INSERTED).any())
-    a = htl.gather(table, slots, inv, unique=uniq, status=status)
-    b = htl.gather(table, slots, inv)
-    assert torch.equal(a.view(torch.int16) if dtype == "bf16" else a, b.view(torch.int16) if dtype == "bf16" else b)
-    offs = torch.arange(0, keys.numel() + 1, 7, dtype=torch.int32, device="cuda")
-    offs[-1] = keys.numel()
-    p1 = htl.gather_pool(table, slots, inv, offs, unique=uniq, status=status)
-    p2 = htl.gather_pool(table, slots, inv, offs)
-    assert torch.equal(p1, p2)
-
-
 def test_repeatable(htl, orc):
     w = workloads.tiny(seed=3)
     outs = []
