@@ -186,9 +186,30 @@ def main():
     found_map[:] = st == htl.FOUND
     result["path"]["hit_rate_per_id"] = round(float(found_map[inv.long()].float().mean().item()), 4)
 
+    result["copy_reference"] = _copy_reference(torch, htl, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(w, args.cpu_sample)
     print(json.dumps(result), flush=True)
+
+
+def _copy_reference(torch, htl, dev, nbytes=1 << 30, reps=5):
+    """Achievable streaming bandwidth: a 1 GiB device-to-device copy (read + write)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        htl._binding.copy_to_device_ptr(dst.data_ptr(), src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    gbs = 2 * nbytes / (best * 1e-3) / 1e9
+    return {"kind": "hipMemcpyAsync device-to-device, 1 GiB", "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def _cpu_baseline(w, sample):
