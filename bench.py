@@ -27,6 +27,29 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
+GATHER_SOURCES = [os.path.join(ROOT, "hash_table_lookup_amd", "csrc", f) for f in ("gather.hip", "htl_common.h")]
+
+
+def _measured_traffic():
+    """Counter-measured HBM bytes per gather launch, or None if the gather's
+    source changed since the counters were taken (or no record exists)."""
+    import hashlib
+    try:
+        rec = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                rec[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in GATHER_SOURCES:
+            h.update(open(f, "rb").read())
+        if h.hexdigest() != rec.get("source_sha256"):
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _parse():
@@ -176,7 +199,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": _measured_traffic() if w.name == "single_large_table" else None,
             "algorithmic_bytes_per_launch": gather_bytes,
             "avg_launch_ms": round(g_ms, 4),
         },
