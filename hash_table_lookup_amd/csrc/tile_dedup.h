@@ -1,0 +1,126 @@
+// Stage 1 of the feature-ID dedup: one workgroup dedups one tile of keys in
+// LDS (internal header, shared by the dedup and fused lookup entry points).
+//
+// MTGenRec (arXiv 2505.12663) TL;DR: two-stage ID deduplication; MTGR (arXiv
+// 2505.18654) section 5, "Embedding Lookup": IDs are unique before the
+// exchange.  One copy of each key leaves the tile.
+#pragma once
+
+#include "htl_common.h"
+
+namespace htl {
+namespace {
+
+constexpr int kTile = 2048;            // keys per stage-1 tile
+constexpr int kTileLog2 = 11;
+constexpr int kTileThreads = 256;
+constexpr int kKeysPerThread = kTile / kTileThreads;
+constexpr int kLdsCap = 2 * kTile;     // LDS set slots (load <= 1/2); slot kLdsCap holds key -1
+constexpr int kLdsCapLog2 = kTileLog2 + 1;
+constexpr uint64_t kFree = ~0ull;      // empty marker of both sets (key -1 is out of band)
+constexpr uint64_t kSalt1 = 0x6A09E667F3BCC909ull;
+constexpr uint64_t kSalt2 = 0xBB67AE8584CAA73Bull;
+constexpr int kNoOwner = 0x7FFFFFFF;
+
+// Block-wide exclusive prefix count of `flag` over the block's threads in
+// thread order; returns this thread's prefix and leaves the block total in
+// *total.  Uses s_wave[kTileThreads / 64].
+__device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
+    const int lane = lane_id();
+    const int wid = threadIdx.x >> 6;
+    const uint64_t m = __ballot(flag);
+    if (lane == 0) s_wave[wid] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTileThreads / 64; ++w) {
+        const int c = s_wave[w];
+        before += (w < wid) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + __popcll(m & lanemask_lt());
+}
+
+// Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
+// occurrence inside the tile (LDS atomicMin of the position, then a block
+// scan over positions), so the result does not depend on scheduling.
+__global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __restrict__ keys, int64_t n,
+                                                            int64_t* __restrict__ tu_keys,
+                                                            int32_t* __restrict__ tu_count,
+                                                            uint16_t* __restrict__ local) {
+    __shared__ unsigned long long s_key[kLdsCap];
+    __shared__ int32_t s_tag[kLdsCap + 1];   // first position of the key, then its tile-local id
+    __shared__ int s_wave[kTileThreads / 64];
+    const int tid = threadIdx.x;
+
+    for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
+        const int64_t base = tile * kTile;
+        for (int i = tid; i < kLdsCap; i += kTileThreads) s_key[i] = kFree;
+        for (int i = tid; i <= kLdsCap; i += kTileThreads) s_tag[i] = kTile;
+        __syncthreads();
+
+        uint64_t k[kKeysPerThread];
+        int pos[kKeysPerThread];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j) {
+            const int64_t idx = base + j * kTileThreads + tid;
+            k[j] = 0;
+            pos[j] = 0;
+            if (idx < n) {
+                valid |= 1u << j;
+                k[j] = (uint64_t)keys[idx];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j) {
+            if (!(valid & (1u << j))) continue;
+            int p = kLdsCap;                         // key -1: out of band
+            if (k[j] != kFree) {
+                const uint64_t h = mix64(k[j] ^ kSalt1);
+                uint32_t q = (uint32_t)(h >> (64 - kLdsCapLog2));
+                const uint32_t stp = ((uint32_t)h | 1u) & (kLdsCap - 1);
+                for (int probe = 0; probe < kLdsCap; ++probe) {
+                    const unsigned long long old = atomicCAS(&s_key[q], kFree, (unsigned long long)k[j]);
+                    if (old == kFree || old == k[j]) break;
+                    q = (q + stp) & (kLdsCap - 1);
+                }
+                p = (int)q;
+            }
+            pos[j] = p;
+            atomicMin(&s_tag[p], j * kTileThreads + tid);
+        }
+        __syncthreads();
+        uint32_t first = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j)
+            if ((valid & (1u << j)) && s_tag[pos[j]] == j * kTileThreads + tid) first |= 1u << j;
+        __syncthreads();
+        // ids in position order: positions j*256 + tid run j-major
+        int run = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j) {
+            const bool f = (first >> j) & 1u;
+            int tot;
+            const int r = block_rank(f, s_wave, &tot);
+            if (f) {
+                s_tag[pos[j]] = run + r;
+                tu_keys[base + run + r] = (int64_t)k[j];
+            }
+            run += tot;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j) {
+            if (!(valid & (1u << j))) continue;
+            local[base + j * kTileThreads + tid] = (uint16_t)s_tag[pos[j]];
+        }
+        if (tid == 0) tu_count[tile] = run;
+        __syncthreads();
+    }
+}
+
+}  // namespace
+}  // namespace htl
