@@ -22,8 +22,8 @@
 //   k_lookup_words        map bytes -> 64-bit words + popcounts
 //   prefix sum            word offsets (rank base per word)
 //   k_lookup_emit         unique / slots / status per rank; re-zero the map
-//   k_lookup_gather<TEAM> per tile: survivors' (slot, id) into LDS, then
-//                         inverse and the row copy for each ID of the tile
+//   k_lookup_ids          per survivor: dense id (rank), INSERTED status
+//   k_lookup_gather<TEAM> per ID: tile-local survivor record -> inverse + row
 //
 // Pseudo-slots: table slot p < M; key -1 -> M, key -2 -> M + 1 (RESERVED);
 // FULL key in spill slot q -> 64 * words_table + q.
@@ -43,6 +43,7 @@ struct LookupWs {
     uint16_t* local;       // [n]
     int32_t* tu_slot;      // [ntiles * kTile]: pseudo-slot of each survivor
     uint8_t* tu_ins;       // [ntiles * kTile]: 1 if this survivor inserted its key
+    int32_t* tu_gid;       // [ntiles * kTile]: dense id of each survivor's key
     uint64_t* word_bits;   // [nwords]
     int32_t* word_cnt;     // [nwords]
     int32_t* word_off;     // [nwords + 1]
@@ -74,6 +75,7 @@ LookupWs lookup_layout(int64_t M, int64_t n, char* base) {
     w.local = (uint16_t*)take((size_t)n * 2);
     w.tu_slot = (int32_t*)take((size_t)ntiles * kTile * 4);
     w.tu_ins = (uint8_t*)take((size_t)ntiles * kTile);
+    w.tu_gid = (int32_t*)take((size_t)ntiles * kTile * 4);
     w.word_bits = (uint64_t*)take((size_t)w.nwords * 8);
     w.word_cnt = (int32_t*)take((size_t)w.nwords * 4);
     w.word_off = (int32_t*)take((size_t)(w.nwords + 1) * 4);
@@ -85,50 +87,57 @@ LookupWs lookup_layout(int64_t M, int64_t n, char* base) {
     return w;
 }
 
+__device__ __forceinline__ u32x4 zero4() {
+    u32x4 z;
+    z.x = z.y = z.z = z.w = 0u;
+    return z;
+}
+
 __global__ void k_lookup_reset(int32_t* flags) { flags[0] = 0; }
 __global__ void k_write_zero_i64(int64_t* p) { *p = 0; }
 
-// Survivors find-or-insert into the table, G lanes per survivor, one block
-// per tile.  The slot a survivor lands on is marked in the table's byte map
-// (read first: a hot key's slot is written once, not once per tile).
+// Survivors find-or-insert into the table, G lanes per survivor, over a flat
+// grid of survivor positions (tile * kTile + j; positions past a tile's
+// count are skipped).  The slot a survivor lands on is marked in the table's
+// byte map (read first: a hot key's slot is written once, not once per tile).
 template <int G>
 __global__ __launch_bounds__(kBlock) void k_lookup_claim(TableDev T, const int64_t* __restrict__ tu_keys,
-                                                        const int32_t* __restrict__ tu_count, int64_t ntiles,
+                                                        const int32_t* __restrict__ tu_count, int64_t npos,
                                                         uint32_t step, int32_t* __restrict__ tu_slot,
                                                         uint8_t* __restrict__ tu_ins, int32_t* __restrict__ flags) {
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
-    const int group = threadIdx.x / G;
-    constexpr int kGroups = kBlock / G;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int cnt = tu_count[tile];
-        for (int j = group; j < cnt; j += kGroups) {
-            const int64_t k = tu_keys[tile * kTile + j];
-            int64_t p;
-            int st;
-            if (k == kEmpty) {
-                p = T.capacity;
-                st = HT_RESERVED;
-            } else if (k == kTomb) {
-                p = T.capacity + 1;
-                st = HT_RESERVED;
+    const int64_t group0 = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * kBlock / G;
+    for (int64_t pos = group0; pos < npos; pos += ngroups) {
+        const int64_t tile = pos >> kTileLog2;
+        const int j = (int)(pos & (kTile - 1));
+        if (j >= tu_count[tile]) continue;
+        const int64_t k = tu_keys[pos];
+        int64_t p;
+        int st;
+        if (k == kEmpty) {
+            p = T.capacity;
+            st = HT_RESERVED;
+        } else if (k == kTomb) {
+            p = T.capacity + 1;
+            st = HT_RESERVED;
+        } else {
+            int64_t slot;
+            st = find_or_insert_key<G>(T, k, gl, gshift, &slot);
+            if (st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
+            p = (st == HT_FULL) ? -1 : slot;
+        }
+        if (gl == 0) {
+            if (p >= 0) {
+                if (T.mark[p] == 0) T.mark[p] = 1;
+                if (p < T.capacity && T.last_seen) T.last_seen[p] = step;
             } else {
-                int64_t slot;
-                st = find_or_insert_key<G>(T, k, gl, gshift, &slot);
-                if (st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
-                p = (st == HT_FULL) ? -1 : slot;
+                flags[0] = 1;
             }
-            if (gl == 0) {
-                if (p >= 0) {
-                    if (T.mark[p] == 0) T.mark[p] = 1;
-                    if (p < T.capacity && T.last_seen) T.last_seen[p] = step;
-                } else {
-                    flags[0] = 1;
-                }
-                tu_slot[tile * kTile + j] = (int32_t)p;
-                tu_ins[tile * kTile + j] = st == HT_INSERTED ? 1 : 0;
-            }
+            tu_slot[pos] = (int32_t)p;
+            tu_ins[pos] = st == HT_INSERTED ? 1 : 0;
         }
     }
 }
@@ -253,88 +262,79 @@ __global__ void k_lookup_emit(TableDev T, const int64_t* __restrict__ spill_keys
     }
 }
 
-__device__ __forceinline__ u32x4 zero4() {
-    u32x4 z;
-    z.x = z.y = z.z = z.w = 0u;
-    return z;
+// Per survivor position: its dense id (rank of its pseudo-slot) into tu_gid,
+// its table slot (or -1) back into tu_slot, and INSERTED status for keys it
+// inserted.
+__global__ void k_lookup_ids(int64_t M, const int32_t* __restrict__ tu_count, int64_t npos,
+                             int32_t* __restrict__ tu_slot, const uint8_t* __restrict__ tu_ins,
+                             const uint64_t* __restrict__ word_bits, const int32_t* __restrict__ word_off,
+                             int32_t* __restrict__ tu_gid, uint8_t* __restrict__ status) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t pos = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; pos < npos; pos += stride) {
+        if ((int)(pos & (kTile - 1)) >= tu_count[pos >> kTileLog2]) continue;
+        const int64_t p = tu_slot[pos];
+        const int64_t w = p >> 6;
+        const int32_t gid = word_off[w] + __popcll(word_bits[w] & ((1ull << (p & 63)) - 1ull));
+        tu_gid[pos] = gid;
+        tu_slot[pos] = p < M ? (int32_t)p : -1;
+        if (tu_ins[pos]) status[gid] = HT_INSERTED;
+    }
 }
 
-// One block per tile: the survivors' (slot, dense id) go to LDS, then every
-// ID of the tile gets its inverse and its row (TEAM lanes x 16 bytes per row,
-// kUnroll rows in flight per team, non-temporal stores).  Keys this call
-// inserted get their status set to INSERTED here.
+// Per ID: its survivor record is tile-local (tile * kTile + local index), so
+// the slot and id reads stay in a few cache lines per tile; then inverse and
+// the row copy (TEAM lanes x 16 bytes per row, kUnroll rows in flight per
+// team, non-temporal stores).
 template <int TEAM>
-__global__ __launch_bounds__(kBlock) void k_lookup_gather(
-    TableDev T, const int32_t* __restrict__ tu_count, const int32_t* __restrict__ tu_slot,
-    const uint8_t* __restrict__ tu_ins, const uint16_t* __restrict__ local, int64_t n, int64_t ntiles,
-    const uint64_t* __restrict__ word_bits, const int32_t* __restrict__ word_off, uint8_t* __restrict__ status,
-    int32_t* __restrict__ inverse, void* __restrict__ out) {
-    __shared__ int32_t s_slot[kTile];
-    __shared__ int32_t s_gid[kTile];
+__global__ __launch_bounds__(kBlock) void k_lookup_gather(TableDev T, const uint16_t* __restrict__ local, int64_t n,
+                                                         const int32_t* __restrict__ tu_slot,
+                                                         const int32_t* __restrict__ tu_gid,
+                                                         int32_t* __restrict__ inverse, void* __restrict__ out) {
     const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
-    const bool vec = (row_bytes & 15) == 0;
-    const int vpr = (int)(row_bytes >> 4);
     const int tl = threadIdx.x & (TEAM - 1);
-    const int team = threadIdx.x / TEAM;
-    constexpr int kTeams = kBlock / TEAM;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int cnt = tu_count[tile];
-        for (int j = threadIdx.x; j < cnt; j += kBlock) {
-            const int64_t p = tu_slot[tile * kTile + j];
-            const int64_t w = p >> 6;
-            const uint64_t below = word_bits[w] & ((1ull << (p & 63)) - 1ull);
-            const int32_t gid = word_off[w] + __popcll(below);
-            s_slot[j] = p < T.capacity ? (int32_t)p : -1;
-            s_gid[j] = gid;
-            if (tu_ins[tile * kTile + j]) status[gid] = HT_INSERTED;
-        }
-        __syncthreads();
-        const int64_t base = tile * kTile;
-        const int rows = (int)min((int64_t)kTile, n - base);
-        if (vec) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(T.rows);
-            u32x4* dst = reinterpret_cast<u32x4*>(out);
-            for (int r0 = team; r0 < rows; r0 += kTeams * kUnroll) {
-                int32_t s[kUnroll];
+    const int64_t team = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / TEAM;
+    const int64_t nteams = (int64_t)gridDim.x * kBlock / TEAM;
+    if ((row_bytes & 15) == 0) {
+        const int vpr = (int)(row_bytes >> 4);
+        const u32x4* src = reinterpret_cast<const u32x4*>(T.rows);
+        u32x4* dst = reinterpret_cast<u32x4*>(out);
+        for (int64_t rb = team; rb < n; rb += nteams * kUnroll) {
+            int32_t s[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t r = rb + u * nteams;
+                s[u] = -1;
+                if (r < n) {
+                    const int64_t pos = ((r >> kTileLog2) << kTileLog2) + local[r];
+                    s[u] = tu_slot[pos];
+                    if (tl == 0) inverse[r] = tu_gid[pos];
+                }
+            }
+            for (int v = tl; v < vpr; v += TEAM) {
+                u32x4 val[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) val[u] = s[u] >= 0 ? src[(int64_t)s[u] * vpr + v] : zero4();
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const int r = r0 + u * kTeams;
-                    s[u] = -1;
-                    if (r < rows) {
-                        const int j = local[base + r];
-                        s[u] = s_slot[j];
-                        if (tl == 0) inverse[base + r] = s_gid[j];
-                    }
-                }
-                for (int v = tl; v < vpr; v += TEAM) {
-                    u32x4 val[kUnroll];
-#pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
-                        val[u] = s[u] >= 0 ? src[(int64_t)s[u] * vpr + v] : zero4();
-#pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) {
-                        const int r = r0 + u * kTeams;
-                        if (r < rows) __builtin_nontemporal_store(val[u], dst + (base + r) * vpr + v);
-                    }
-                }
-            }
-        } else {
-            // rows whose byte length is not a multiple of 16: element by element
-            const int esz = T.elem_bytes;
-            for (int r = threadIdx.x; r < rows; r += kBlock) inverse[base + r] = s_gid[local[base + r]];
-            for (int64_t e = threadIdx.x; e < (int64_t)rows * T.dim; e += kBlock) {
-                const int r = (int)(e / T.dim);
-                const int c = (int)(e - (int64_t)r * T.dim);
-                const int32_t s = s_slot[local[base + r]];
-                const int64_t o = (base + r) * T.dim + c;
-                if (esz == 4) {
-                    ((uint32_t*)out)[o] = s >= 0 ? ((const uint32_t*)T.rows)[(int64_t)s * T.dim + c] : 0u;
-                } else {
-                    ((uint16_t*)out)[o] = s >= 0 ? ((const uint16_t*)T.rows)[(int64_t)s * T.dim + c] : (uint16_t)0;
+                    const int64_t r = rb + u * nteams;
+                    if (r < n) __builtin_nontemporal_store(val[u], dst + r * vpr + v);
                 }
             }
         }
-        __syncthreads();
+    } else {
+        // rows whose byte length is not a multiple of 16: one thread per element
+        const int64_t stride = (int64_t)gridDim.x * kBlock;
+        for (int64_t e = blockIdx.x * (int64_t)kBlock + threadIdx.x; e < n * T.dim; e += stride) {
+            const int64_t r = e / T.dim;
+            const int c = (int)(e - r * T.dim);
+            const int64_t pos = ((r >> kTileLog2) << kTileLog2) + local[r];
+            const int32_t s = tu_slot[pos];
+            if (c == 0) inverse[r] = tu_gid[pos];
+            if (T.elem_bytes == 4)
+                ((uint32_t*)out)[e] = s >= 0 ? ((const uint32_t*)T.rows)[(int64_t)s * T.dim + c] : 0u;
+            else
+                ((uint16_t*)out)[e] = s >= 0 ? ((const uint16_t*)T.rows)[(int64_t)s * T.dim + c] : (uint16_t)0;
+        }
     }
 }
 
@@ -376,6 +376,7 @@ htl_status ht_lookup_prepare(htl_table* t, const int64_t* keys, int64_t n, uint3
     LookupWs w = lookup_layout(T.capacity, n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "ht_lookup_prepare: workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
+    const int64_t npos = ntiles * kTile;
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
 
     hipLaunchKernelGGL(k_lookup_reset, dim3(1), dim3(1), 0, stream, w.flags);
@@ -383,8 +384,8 @@ htl_status ht_lookup_prepare(htl_table* t, const int64_t* keys, int64_t n, uint3
                        w.local);
     switch (probe_lanes()) {
 #define HTL_CLAIM(GG)                                                                                        \
-    hipLaunchKernelGGL(k_lookup_claim<GG>, dim3(gt), dim3(kBlock), 0, stream, T, w.tu_keys, w.tu_count, ntiles, \
-                       step, w.tu_slot, w.tu_ins, w.flags)
+    hipLaunchKernelGGL(k_lookup_claim<GG>, dim3(grid_for(npos, kBlock / GG)), dim3(kBlock), 0, stream, T, w.tu_keys, \
+                       w.tu_count, npos, step, w.tu_slot, w.tu_ins, w.flags)
         case 1: HTL_CLAIM(1); break;
         case 2: HTL_CLAIM(2); break;
         case 8: HTL_CLAIM(8); break;
@@ -419,13 +420,17 @@ htl_status ht_lookup_gather(htl_table* t, int64_t n, int32_t* inverse, uint8_t* 
     LookupWs w = lookup_layout(T.capacity, n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "ht_lookup_gather: workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
-    const unsigned gt = grid_for(ntiles, 1, 1 << 16);
+    const int64_t npos = ntiles * kTile;
+    hipLaunchKernelGGL(k_lookup_ids, dim3(grid_for(npos, 256 * 4)), dim3(256), 0, stream, T.capacity, w.tu_count,
+                       npos, w.tu_slot, w.tu_ins, w.word_bits, w.word_off, w.tu_gid, status);
     const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
     const int vpr = (int)(row_bytes / 16);
-    switch ((row_bytes % 16) ? 1 : team_for(vpr)) {
-#define HTL_GATHER(TT)                                                                                          \
-    hipLaunchKernelGGL(k_lookup_gather<TT>, dim3(gt), dim3(kBlock), 0, stream, T, w.tu_count, w.tu_slot, w.tu_ins, \
-                       w.local, n, ntiles, w.word_bits, w.word_off, status, inverse, out)
+    const int team = (row_bytes % 16) ? 1 : team_for(vpr);
+    const unsigned grid = (row_bytes % 16) ? grid_for(n * T.dim, 256 * 4) : grid_for(n, (kBlock / team) * kUnroll);
+    switch (team) {
+#define HTL_GATHER(TT)                                                                                        \
+    hipLaunchKernelGGL(k_lookup_gather<TT>, dim3(grid), dim3(kBlock), 0, stream, T, w.local, n, w.tu_slot, w.tu_gid, \
+                       inverse, out)
         case 1: HTL_GATHER(1); break;
         case 2: HTL_GATHER(2); break;
         case 4: HTL_GATHER(4); break;
