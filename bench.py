@@ -2,9 +2,8 @@
 
 A step is one pass of the forward hot path over one batch: two-stage dedup
 -> find-or-insert of the unique keys into the dynamic table (misses inserted)
--> per-ID row gather.  --path fused (default) runs it as ht_lookup_prepare +
-ht_lookup_gather; --path separate as dedup_unique_inverse ->
-ht_find_or_insert -> emb_gather_pool.  The default workload is the large-table lookup: 2^22 IDs
+-> per-ID row gather, as dedup_unique_inverse -> ht_find_or_insert ->
+emb_gather_pool.  The default workload is the large-table lookup: 2^22 IDs
 drawn Zipf(1.05) over a 2^40 key universe against a 2^24-slot fp32 table of
 dim 64 pre-filled (untimed) with the 2^23 most popular keys.
 
@@ -30,19 +29,15 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
-TRAFFIC = {
-    "separate": (os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt"),
-                 [os.path.join(CSRC, f) for f in ("gather.hip", "htl_common.h")]),
-    "fused": (os.path.join(ROOT, "profiles", "lookup_gather_single_large_table_traffic.txt"),
-              [os.path.join(CSRC, f) for f in ("lookup.hip", "htl_common.h")]),
-}
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
+TRAFFIC_SOURCES = [os.path.join(CSRC, f) for f in ("gather.hip", "htl_common.h")]
 
 
-def _measured_traffic(path_kind):
+def _measured_traffic():
     """Counter-measured HBM bytes per gather launch, or None if the gather's
     source changed since the counters were taken (or no record exists)."""
     import hashlib
-    record, sources = TRAFFIC[path_kind]
+    record, sources = TRAFFIC_RECORD, TRAFFIC_SOURCES
     try:
         rec = {}
         for line in open(record):
@@ -66,34 +61,25 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="single_large_table",
                     choices=["single_large_table", "tiny"])
-    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
-                    help="fused: ht_lookup (prepare + gather); separate: dedup_unique_inverse -> "
-                         "ht_find_or_insert -> emb_gather_pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="IDs of the batch the CPU oracle processes (timed)")
     return ap.parse_args()
 
 
-def _algorithmic_bytes(n, U, hits, misses, dim, esz, path_kind):
+def _algorithmic_bytes(n, U, hits, misses, dim, esz):
     """Minimum HBM bytes of the whole path and of its gather kernel.
 
-    Whole path (either implementation): per ID 8 (key read) + 4 (inverse
-    write) + 4 (inverse read) + row (output); per unique key 8 (unique write)
-    + 8 (unique read) + 4 + 4 (slot write/read) + 1 (status) + 8 (table key
-    probe); per hit one row read; per miss one key claim (8) and one
-    initial-row write.
-    Gather kernel, separate path (k_gather): per ID 4 (inverse) + row
-    (output); per unique 4 (slot) + row (read).  Fused path
-    (k_lookup_gather): per ID 2 (local index) + 4 (inverse write) + row
-    (output); per unique row (read).
+    Whole path: per ID 8 (key read) + 4 (inverse write) + 4 (inverse read) +
+    row (output); per unique key 8 (unique write) + 8 (unique read) + 4 + 4
+    (slot write/read) + 1 (status) + 8 (table key probe); per hit one row
+    read; per miss one key claim (8) and one initial-row write.
+    Gather kernel (k_gather): per ID 4 (inverse) + row (output); per unique
+    4 (slot) + row (read).
     """
     row = dim * esz
     path = n * (8 + 4 + 4 + row) + U * (8 + 8 + 4 + 4 + 1 + 8) + hits * row + misses * (8 + row)
-    if path_kind == "fused":
-        gather = n * (2 + 4 + row) + U * row
-    else:
-        gather = n * (4 + row) + U * (4 + row)
+    gather = n * (4 + row) + U * (4 + row)
     return path, gather
 
 
@@ -136,15 +122,11 @@ def main():
 
     def step(e_gather=None):
         """One pass of the hot path; records e_gather just before the gather kernel."""
-        mark = (lambda: e_gather.record(stream)) if e_gather is not None else None
-        if args.path == "fused":
-            _, uniq, inv, nu, slots, status = table.lookup(keys, out=out, phases=True, between=mark)
-        else:
-            uniq, inv, nu = htl.dedup_unique_inverse(keys)
-            slots, status = table.find_or_insert(uniq, n_dev=nu)
-            if mark:
-                mark()
-            htl.gather(table, slots, inv, out=out)
+        uniq, inv, nu = htl.dedup_unique_inverse(keys)
+        slots, status = table.find_or_insert(uniq, n_dev=nu)
+        if e_gather is not None:
+            e_gather.record(stream)
+        htl.gather(table, slots, inv, out=out)
         return uniq, inv, nu, slots, status
 
     for _ in range(args.warmup):
@@ -172,7 +154,7 @@ def main():
     hits = int((st == htl.FOUND).sum().item())
     misses = int((st == htl.INSERTED).sum().item())
     esz = 4 if w.dtype == "f32" else 2
-    path_bytes, gather_bytes = _algorithmic_bytes(n, U, hits, misses, w.dim, esz, args.path)
+    path_bytes, gather_bytes = _algorithmic_bytes(n, U, hits, misses, w.dim, esz)
     mean_ms = float(step_ms.mean())
     mkeys = n / (mean_ms * 1e-3) / 1e6
     g_ms = float(gather_ms.mean())
@@ -210,20 +192,18 @@ def main():
             "frac_of_hbm_peak": round(path_bytes / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "ms_median": round(float(np.median(step_ms)), 4),
             "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
-            "implementation": ("ht_lookup_prepare + ht_lookup_gather (fused)" if args.path == "fused" else
-                               "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool"),
+            "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool",
             "timing": "HIP events around dedup+find_or_insert+gather per step on the launch stream; "
                       "table keys restored by a D2D copy between steps, outside the events",
         },
         "roofline": {
-            "kernel": ("k_lookup_gather (ht_lookup_gather: inverse + per-ID rows)" if args.path == "fused"
-                       else "k_gather (emb_gather_pool: per-ID rows)"),
+            "kernel": "k_gather (emb_gather_pool: per-ID rows)",
             "bound": "hbm",
             "achieved": round(g_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-            "traffic": _measured_traffic(args.path) if w.name == "single_large_table" else None,
+            "traffic": _measured_traffic() if w.name == "single_large_table" else None,
             "algorithmic_bytes_per_launch": gather_bytes,
             "avg_launch_ms": round(g_ms, 4),
         },

@@ -61,17 +61,12 @@ _SIGNATURES = {
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
-    "lookup_workspace_bytes": [_P, _I64],
-    "ht_lookup": [_P, _P, _I64, _U32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
-    "ht_lookup_prepare": [_P, _P, _I64, _U32, _P, _P, _P, _P, _P, _SZ, _P],
-    "ht_lookup_gather": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "segsum_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
     "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
     "htl_last_error": [],
 }
-_SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes",
-               "lookup_workspace_bytes"}
+_SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes"}
 EXPORTED = tuple(_SIGNATURES)
 
 _lib = None
@@ -224,37 +219,6 @@ class Table:
         _check(lib().ht_lru_select(self._h, num, den, _ptr(victims), cap, _ptr(n), _ptr(ws), nb,
                                    _stream()))
         return victims, n
-
-    def lookup(self, keys: torch.Tensor, step: int = 0, out: Optional[torch.Tensor] = None,
-               phases: bool = False, between=None):
-        """Fused forward (ht_lookup): (out, unique, inverse, n_unique, slots, status).
-
-        phases=True issues ht_lookup_prepare and ht_lookup_gather separately
-        and calls between() (e.g. to record an event) in between."""
-        keys = _dev(keys, torch.int64, "keys")
-        n = keys.numel()
-        dev = keys.device
-        unique = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
-        inverse = torch.empty(n, dtype=torch.int32, device=dev)
-        n_unique = torch.empty(1, dtype=torch.int64, device=dev)
-        slots = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-        status = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-        if out is None:
-            out = torch.empty((n, self.dim), dtype=self.row_dtype, device=dev)
-        nb = lib().lookup_workspace_bytes(self._h, n)
-        ws = _workspace("lookup", nb, dev)
-        if phases:
-            _check(lib().ht_lookup_prepare(self._h, _ptr(keys), n, step, _ptr(unique), _ptr(n_unique),
-                                           _ptr(slots), _ptr(status), _ptr(ws), nb, _stream()))
-            if between is not None:
-                between()
-            _check(lib().ht_lookup_gather(self._h, n, _ptr(inverse), _ptr(status), _ptr(out), _ptr(ws), nb,
-                                          _stream()))
-        else:
-            _check(lib().ht_lookup(self._h, _ptr(keys), n, step, _ptr(unique), _ptr(inverse),
-                                   _ptr(n_unique), _ptr(slots), _ptr(status), _ptr(out), _ptr(ws), nb,
-                                   _stream()))
-        return out, unique, inverse, n_unique, slots, status
 
     def view(self) -> _View:
         v = _View()

@@ -42,7 +42,6 @@ struct TableDev {
     uint32_t* last_seen;   // nullable
     float* m;              // nullable
     float* v;              // nullable
-    uint8_t* mark;         // [capacity + 64] touch map of the fused lookup; all zero between calls
     int64_t capacity;
     uint64_t bucket_mask;  // number of buckets - 1
     int bucket_log2;       // slots per bucket = 1 << bucket_log2 (<= 4)

@@ -62,14 +62,6 @@ __global__ void k_fill_i64(int64_t* __restrict__ p, int64_t n, int64_t value) {
         p[i] = value;
 }
 
-__global__ void k_fill_u8x16(u32x4* __restrict__ p, int64_t n16) {
-    u32x4 z;
-    z.x = z.y = z.z = z.w = 0u;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = z;
-}
-
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -203,8 +195,6 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_live(TableDev T, int64_t* _
 htl_status fill_keys_empty(const TableDev& T, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_i64, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, s,
                        T.keys, T.capacity, kEmpty);
-    const int64_t n16 = (T.capacity + 64) / 16;
-    hipLaunchKernelGGL(k_fill_u8x16, dim3(grid_for(n16, 256 * 8, 1 << 16)), dim3(256), 0, s, (u32x4*)T.mark, n16);
     return check_launch("clear table keys");
 }
 
@@ -252,13 +242,12 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
         if (T.last_seen) (void)hipFree(T.last_seen);
         if (T.m) (void)hipFree(T.m);
         if (T.v) (void)hipFree(T.v);
-        if (T.mark) (void)hipFree(T.mark);
         delete t;
     };
     const size_t M = (size_t)T.capacity;
     const size_t row_bytes = M * (size_t)dim * (size_t)T.elem_bytes;
     if (hipMalloc((void**)&T.keys, M * sizeof(int64_t)) != hipSuccess ||
-        hipMalloc(&T.rows, row_bytes) != hipSuccess || hipMalloc((void**)&T.mark, M + 64) != hipSuccess ||
+        hipMalloc(&T.rows, row_bytes) != hipSuccess ||
         ((flags & HT_META_LAST_SEEN) && hipMalloc((void**)&T.last_seen, M * 4) != hipSuccess) ||
         ((flags & HT_ADAM_STATE) && (hipMalloc((void**)&T.m, M * dim * 4) != hipSuccess ||
                                      hipMalloc((void**)&T.v, M * dim * 4) != hipSuccess))) {
@@ -294,7 +283,6 @@ htl_status ht_destroy(htl_table* t) {
     if (T.last_seen) (void)hipFree(T.last_seen);
     if (T.m) (void)hipFree(T.m);
     if (T.v) (void)hipFree(T.v);
-    (void)hipFree(T.mark);
     delete t;
     HTL_HIP(hipSetDevice(cur));
     return HTL_OK;

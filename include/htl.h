@@ -213,44 +213,6 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
                            int64_t n, const int32_t* offsets, int64_t nbags,
                            htl_dtype out_dtype, void* out, hipStream_t stream);
 
-/* ------------------------------------------------------------ fused path --
- * ht_lookup -- the whole forward lookup in one call: dedup -> find-or-insert
- * (absent keys inserted) -> per-ID row gather.  [MTGenRec] TL;DR (dynamic
- * hash table, two-stage ID dedup), [MTGR] section 5 (IDs unique before and
- * after the exchange; keys map to vectors and metadata).  The outputs equal
- * those of dedup_unique_inverse + ht_find_or_insert(unique, U) +
- * emb_gather_pool(slots, inverse) except for the order of the unique keys:
- * table keys in slot order, then -1 / -2 (RESERVED), then FULL keys.  The
- * table itself serves as the stage-2 dedup set.
- *   keys          int64[n]; any values (the table's reserved keys come back
- *                 RESERVED, keys that find the table full come back FULL).
- *   step          stamped into last_seen of FOUND and INSERTED keys.
- *   unique        int64[n] out;  inverse int32[n] out;  n_unique_dev int64 out.
- *   slots         int32[n] out: slot per unique key (-1: FULL / RESERVED).
- *   status        uint8[n] out: HT_FOUND / HT_INSERTED / HT_FULL / HT_RESERVED.
- *   out           table dtype [n][dim] out: the row of each ID (zeros for
- *                 FULL / RESERVED keys); 16-byte aligned.
- *   ws, ws_bytes  at least lookup_workspace_bytes(t, n) bytes, 256-aligned.
- * Needs capacity_log2 <= 30 and n < 2^28.  The table keeps a per-slot touch
- * map that this call leaves all zero; calls on one table must not overlap. */
-size_t lookup_workspace_bytes(const htl_table* t, int64_t n);
-htl_status ht_lookup(htl_table* t, const int64_t* keys, int64_t n, uint32_t step,
-                     int64_t* unique, int32_t* inverse, int64_t* n_unique_dev,
-                     int32_t* slots, uint8_t* status, void* out, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
-
-/* ht_lookup in two phases over the same workspace (same results):
- * ht_lookup_prepare -- dedup, find-or-insert, unique / slots / status /
- *   n_unique (status of inserted keys still reads FOUND);
- * ht_lookup_gather  -- inverse, the rows, and INSERTED statuses.
- * Call them in this order on one stream with the same n and workspace; the
- * table must not change in between. */
-htl_status ht_lookup_prepare(htl_table* t, const int64_t* keys, int64_t n, uint32_t step,
-                             int64_t* unique, int64_t* n_unique_dev, int32_t* slots,
-                             uint8_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
-htl_status ht_lookup_gather(htl_table* t, int64_t n, int32_t* inverse, uint8_t* status, void* out,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
-
 /* --------------------------------------------------------------- backward --
  * emb_grad_segment_sum -- backward gradient dedup: out[u] = sum of grad[i]
  * over the IDs with inverse[i] == u, accumulated in fp32 (the backward of the
