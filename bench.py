@@ -1,18 +1,28 @@
 """Benchmark of the sparse-embedding lookup hot path on one MI355X.
 
-A step is one pass of the forward hot path over one batch: two-stage dedup
--> find-or-insert of the unique keys into the dynamic table (misses inserted)
--> per-ID row gather, as dedup_unique_inverse -> ht_find_or_insert ->
-emb_gather_pool.  The default workload is the large-table lookup: 2^22 IDs
-drawn Zipf(1.05) over a 2^40 key universe against a 2^24-slot fp32 table of
-dim 64 pre-filled (untimed) with the 2^23 most popular keys.
+Default workload (the one the headline metric is quoted on): the large-table
+lookup -- 2^22 IDs drawn Zipf(1.05) over a 2^40 key universe against a
+2^24-slot fp32 table of dim 64 pre-filled (untimed) with the 2^23 most popular
+keys.  A step is one pass of the forward hot path over the batch:
+dedup_unique_inverse -> ht_find_or_insert (misses inserted) ->
+emb_gather_pool.
 
-Timing: each step is bracketed by HIP events on the stream the library
-launches on; between steps the table's key array is restored to its
-pre-filled state by a device-to-device copy that lies outside the events, so
-every step sees the same table.  The K timed steps as a whole are also
-bracketed by torch.cuda.synchronize() and reported as wall time (restores
-included).  value = IDs per second over the hot path (Mkeys/s).
+Other workloads (--workload), each its own hot-path rows:
+  tiny            the same forward path, 65,536 IDs, 2^18-slot table
+  merged_tables   26 tables merged into one 2^26-slot bf16 table (dim 128),
+                  65,536 samples x 26 bags of Poisson(20) IDs: dedup ->
+                  find-or-insert -> gather + sum-pool (bf16 out)
+  backward        2^23 IDs Zipf(1.2), fp32 gradients [N, 128]: segment-sum
+                  by the forward's inverse -> row-wise Adam (forward untimed)
+  dynamic_online  2^27-slot bf16 table (dim 64), steps of 2^22 IDs over a
+                  drifting window: dedup -> find-or-insert -> gather, then
+                  LRU selection of 5% of the live keys and their erase
+
+Timing: HIP events on the stream the library launches on bracket each step
+(and the dominant kernel inside it); table state that a step changes is
+restored between steps outside the events (forward workloads), so every step
+sees the same table.  The K timed steps are bracketed by
+torch.cuda.synchronize() and reported as wall time too.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -31,27 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
 TRAFFIC_SOURCES = [os.path.join(CSRC, f) for f in ("gather.hip", "htl_common.h")]
-
-
-def _measured_traffic():
-    """Counter-measured HBM bytes per gather launch, or None if the gather's
-    source changed since the counters were taken (or no record exists)."""
-    import hashlib
-    record, sources = TRAFFIC_RECORD, TRAFFIC_SOURCES
-    try:
-        rec = {}
-        for line in open(record):
-            if "=" in line and not line.lstrip().startswith("#"):
-                k, v = line.split("=", 1)
-                rec[k.strip()] = v.strip()
-        h = hashlib.sha256()
-        for f in sources:
-            h.update(open(f, "rb").read())
-        if h.hexdigest() != rec.get("source_sha256"):
-            return None
-        return int(rec["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+METRIC = "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X"
 
 
 def _parse():
@@ -60,15 +50,64 @@ def _parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="single_large_table",
-                    choices=["single_large_table", "tiny"])
+                    choices=["single_large_table", "tiny", "merged_tables", "backward", "dynamic_online"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="IDs of the batch the CPU oracle processes (timed)")
     return ap.parse_args()
 
 
-def _algorithmic_bytes(n, U, hits, misses, dim, esz):
-    """Minimum HBM bytes of the whole path and of its gather kernel.
+def _measured_traffic():
+    """Counter-measured HBM bytes per gather launch, or None if the gather's
+    source changed since the counters were taken (or no record exists)."""
+    import hashlib
+    try:
+        rec = {}
+        for line in open(TRAFFIC_RECORD):
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                rec[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            h.update(open(f, "rb").read())
+        if h.hexdigest() != rec.get("source_sha256"):
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Per-step HIP events (start, mark, end) on one stream."""
+
+    def __init__(self, torch, steps):
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        self.ev = [(E(), E(), E()) for _ in range(steps)]
+
+    def step_ms(self):
+        return np.array([a.elapsed_time(c) for a, b, c in self.ev])
+
+    def kernel_ms(self):
+        return np.array([b.elapsed_time(c) for a, b, c in self.ev])
+
+
+def _roofline(kernel, alg_bytes, ms, traffic=None):
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(alg_bytes), "avg_launch_ms": round(ms, 4)}
+
+
+def _result(args, value, ms, config, dtype, path, roofline, unit="Mkeys/s"):
+    return {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic: seeded Zipf ID streams (numpy PCG64), closed-form table rows",
+            "config": config, "path": path, "roofline": roofline}
+
+
+def _lookup_bytes(n, U, hits, misses, row):
+    """Minimum HBM bytes of the forward path and of its gather kernel.
 
     Whole path: per ID 8 (key read) + 4 (inverse write) + 4 (inverse read) +
     row (output); per unique key 8 (unique write) + 8 (unique read) + 4 + 4
@@ -77,33 +116,40 @@ def _algorithmic_bytes(n, U, hits, misses, dim, esz):
     Gather kernel (k_gather): per ID 4 (inverse) + row (output); per unique
     4 (slot) + row (read).
     """
-    row = dim * esz
     path = n * (8 + 4 + 4 + row) + U * (8 + 8 + 4 + 4 + 1 + 8) + hits * row + misses * (8 + row)
     gather = n * (4 + row) + U * (4 + row)
     return path, gather
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the sharded design is described, not built). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def _statuses(htl, status, U):
+    st = status[:U]
+    return int((st == htl.FOUND).sum().item()), int((st == htl.INSERTED).sum().item())
 
-    import torch
-    import workloads
-    import hash_table_lookup_amd as htl
 
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
+def _timed(torch, args, step, restore=None):
+    """Warm-up, then K steps with events; step(mark_event) runs one step."""
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step(None)
+        if restore:
+            restore()
+    T = Timer(torch, args.steps)
+    last = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in T.ev:
+        a.record(stream)
+        last = step(b)
+        c.record(stream)
+        if restore:
+            restore()
+    torch.cuda.synchronize()
+    return T, time.perf_counter() - t0, last
 
-    if args.workload == "single_large_table":
-        w = workloads.single_large_table()
-    else:
-        w = workloads.tiny()
+
+# ------------------------------------------------------------------ forward
+def run_lookup(args, torch, htl, workloads, dev):
+    w = workloads.single_large_table() if args.workload == "single_large_table" else workloads.tiny()
     n = w.keys.size
     keys = torch.from_numpy(w.keys).to(dev)
     table = htl.Table(w.capacity_log2, w.dim, w.dtype)
@@ -113,112 +159,199 @@ def main():
     saved_keys = htl.table_keys(table).clone()
     view = table.view()
     stream = torch.cuda.current_stream()
+    out = torch.empty((n, w.dim), dtype=table.row_dtype, device=dev)   # the timed region allocates nothing
 
     def restore():
         htl._binding.copy_to_device_ptr(view.keys, saved_keys)
 
-    # outputs preallocated once: the timed region allocates nothing
-    out = torch.empty((n, w.dim), dtype=table.row_dtype, device=dev)
-
-    def step(e_gather=None):
-        """One pass of the hot path; records e_gather just before the gather kernel."""
+    def step(mark):
         uniq, inv, nu = htl.dedup_unique_inverse(keys)
         slots, status = table.find_or_insert(uniq, n_dev=nu)
-        if e_gather is not None:
-            e_gather.record(stream)
+        if mark is not None:
+            mark.record(stream)
         htl.gather(table, slots, inv, out=out)
         return uniq, inv, nu, slots, status
 
-    for _ in range(args.warmup):
-        step()
-        restore()
-    torch.cuda.synchronize()
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        e_start, e_gather, e_end = ev[i]
-        e_start.record(stream)
-        uniq, inv, nu, slots, status = step(e_gather)
-        e_end.record(stream)
-        restore()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    step_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
-    gather_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
+    T, wall, (uniq, inv, nu, slots, status) = _timed(torch, args, step, restore)
+    ms = float(T.step_ms().mean())
+    g_ms = float(T.kernel_ms().mean())
     U = int(nu.item())
-    st = status[:U]
-    hits = int((st == htl.FOUND).sum().item())
-    misses = int((st == htl.INSERTED).sum().item())
-    esz = 4 if w.dtype == "f32" else 2
-    path_bytes, gather_bytes = _algorithmic_bytes(n, U, hits, misses, w.dim, esz)
-    mean_ms = float(step_ms.mean())
-    mkeys = n / (mean_ms * 1e-3) / 1e6
-    g_ms = float(gather_ms.mean())
-    g_gbs = gather_bytes / (g_ms * 1e-3) / 1e9
-
-    result = {
-        "metric": "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X",
-        "value": round(mkeys, 2),
-        "unit": "Mkeys/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(mean_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int64 keys, " + ("fp32" if w.dtype == "f32" else "bf16") + " rows",
-        "data": "synthetic: seeded Zipf ID stream (numpy PCG64), closed-form table rows",
-        "config": {
-            "workload": w.name,
-            "ids_per_step": n,
-            "zipf_a": w.meta.get("zipf_a"),
-            "key_universe_log2": w.meta.get("universe_log2"),
-            "table_slots_log2": w.capacity_log2,
-            "prefilled_keys": 0 if w.prefill is None else int(w.prefill.size),
-            "dim": w.dim,
-            "row_dtype": w.dtype,
-            "parallelism": "single GPU",
-        },
-        "path": {
-            "unique": U, "hits": hits, "misses": misses,
-            "hit_rate_per_id": None,
+    hits, misses = _statuses(htl, status, U)
+    row = w.dim * (4 if w.dtype == "f32" else 2)
+    path_bytes, gather_bytes = _lookup_bytes(n, U, hits, misses, row)
+    found = (status[:U] == htl.FOUND)[inv.long()].float().mean().item()
+    config = {"workload": w.name, "ids_per_step": n, "zipf_a": w.meta.get("zipf_a"),
+              "key_universe_log2": w.meta.get("universe_log2"), "table_slots_log2": w.capacity_log2,
+              "prefilled_keys": 0 if w.prefill is None else int(w.prefill.size), "dim": w.dim,
+              "row_dtype": w.dtype, "parallelism": "single GPU"}
+    path = {"unique": U, "hits": hits, "misses": misses, "hit_rate_per_id": round(found, 4),
             "algorithmic_bytes": path_bytes,
-            "achieved_gbs": round(path_bytes / (mean_ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(path_bytes / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "ms_median": round(float(np.median(step_ms)), 4),
+            "achieved_gbs": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_median": round(float(np.median(T.step_ms())), 4),
             "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
             "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool",
-            "timing": "HIP events around dedup+find_or_insert+gather per step on the launch stream; "
-                      "table keys restored by a D2D copy between steps, outside the events",
-        },
-        "roofline": {
-            "kernel": "k_gather (emb_gather_pool: per-ID rows)",
-            "bound": "hbm",
-            "achieved": round(g_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-            "traffic": _measured_traffic() if w.name == "single_large_table" else None,
-            "algorithmic_bytes_per_launch": gather_bytes,
-            "avg_launch_ms": round(g_ms, 4),
-        },
-    }
-    # hit rate per ID: fraction of IDs whose key was FOUND
-    found_map = torch.zeros(U, dtype=torch.bool, device=dev)
-    found_map[:] = st == htl.FOUND
-    result["path"]["hit_rate_per_id"] = round(float(found_map[inv.long()].float().mean().item()), 4)
-
-    result["copy_reference"] = _copy_reference(torch, htl, dev)
+            "timing": "HIP events around dedup+find_or_insert+gather per step on the launch stream; table keys "
+                      "restored by a D2D copy between steps, outside the events"}
+    traffic = _measured_traffic() if w.name == "single_large_table" else None
+    res = _result(args, n / (ms * 1e-3) / 1e6, ms, config,
+                  "int64 keys, " + ("fp32" if w.dtype == "f32" else "bf16") + " rows", path,
+                  _roofline("k_gather (emb_gather_pool: per-ID rows)", gather_bytes, g_ms, traffic))
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(w, args.cpu_sample)
-    print(json.dumps(result), flush=True)
+        res["cpu_baseline"] = _cpu_baseline_lookup(w, args.cpu_sample)
+    return res
 
 
+def run_pooled(args, torch, htl, workloads, dev):
+    w = workloads.merged_tables()
+    warm = workloads.merged_tables(seed=1)
+    n, nb = w.keys.size, w.nbags
+    keys = torch.from_numpy(w.keys).to(dev)
+    offsets = torch.from_numpy(w.offsets).to(dev)
+    table = htl.Table(w.capacity_log2, w.dim, w.dtype)
+    wk = torch.from_numpy(warm.keys).to(dev)             # a previous batch populates the table (untimed)
+    u0, _, nu0 = htl.dedup_unique_inverse(wk)
+    table.find_or_insert(u0, n_dev=nu0)
+    del wk, u0
+    saved_keys = htl.table_keys(table).clone()
+    view = table.view()
+    stream = torch.cuda.current_stream()
+    out = torch.empty((nb, w.dim), dtype=torch.bfloat16, device=dev)
+
+    def restore():
+        htl._binding.copy_to_device_ptr(view.keys, saved_keys)
+
+    def step(mark):
+        uniq, inv, nu = htl.dedup_unique_inverse(keys)
+        slots, status = table.find_or_insert(uniq, n_dev=nu)
+        if mark is not None:
+            mark.record(stream)
+        htl.gather_pool(table, slots, inv, offsets, out_dtype="bf16", out=out)
+        return uniq, inv, nu, slots, status
+
+    T, wall, (uniq, inv, nu, slots, status) = _timed(torch, args, step, restore)
+    ms, p_ms = float(T.step_ms().mean()), float(T.kernel_ms().mean())
+    U = int(nu.item())
+    hits, misses = _statuses(htl, status, U)
+    row = w.dim * 2
+    # per ID: key 8 + inverse 4 + 4; per bag: offsets 4 + pooled row; per unique: 33 + a row read
+    # (hits) or a key claim and a row write (misses)
+    path_bytes = n * 16 + nb * (4 + row) + U * 33 + hits * row + misses * (8 + row)
+    pool_bytes = n * 4 + nb * (4 + row) + U * (4 + row)
+    config = {"workload": w.name, "ids_per_step": n, "bags": nb, "tables": w.meta["n_tables"],
+              "zipf_a": w.meta["zipf_a"], "mean_bag": w.meta["mean_bag"], "table_slots_log2": w.capacity_log2,
+              "dim": w.dim, "row_dtype": "bf16", "pooled_dtype": "bf16", "parallelism": "single GPU"}
+    path = {"unique": U, "hits": hits, "misses": misses, "algorithmic_bytes": path_bytes,
+            "achieved_gbs": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
+            "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool (pooled)",
+            "timing": "HIP events per step; table keys restored between steps outside the events"}
+    return _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
+                   _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms))
+
+
+# ----------------------------------------------------------------- backward
+def run_backward(args, torch, htl, workloads, dev):
+    w = workloads.backward(with_grad=False)
+    n, dim = w.keys.size, w.dim
+    keys = torch.from_numpy(w.keys).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1_000_003)
+    grad = torch.randn((n, dim), generator=gen, dtype=torch.float32, device=dev)
+    table = htl.Table(w.capacity_log2, dim, "f32", adam=True)
+    # the forward (untimed): its dedup (unique, inverse) and slots are what the backward consumes
+    uniq, inv, nu = htl.dedup_unique_inverse(keys)
+    slots, status = table.find_or_insert(uniq, n_dev=nu)
+    stream = torch.cuda.current_stream()
+    g = torch.empty((n, dim), dtype=torch.float32, device=dev)
+    state = {"t": 0}
+
+    def step(mark):
+        htl.segment_sum(grad, inv, nu, u_max=n, out=g)
+        if mark is not None:
+            mark.record(stream)
+        state["t"] += 1
+        htl.rowwise_adam(table, slots, g, nu, 1e-3, 0.9, 0.999, 1e-8, state["t"])
+        return nu
+
+    T, wall, nq = _timed(torch, args, step)
+    ms = float(T.step_ms().mean())
+    adam_ms = float(T.kernel_ms().mean())
+    seg_ms = ms - adam_ms
+    U = int(nq.item())
+    row = dim * 4
+    # segment-sum: per ID inverse 4 + gradient row, per unique the summed row written;
+    # Adam: per unique slot 4 + g read + theta, m, v read and written
+    path_bytes = n * (4 + row) + U * row + U * (4 + 7 * row)
+    seg_bytes = n * (4 + row) + U * row
+    config = {"workload": w.name, "ids_per_step": n, "zipf_a": w.meta["zipf_a"],
+              "table_slots_log2": w.capacity_log2, "dim": dim, "grad_dtype": "fp32",
+              "optimizer": "row-wise Adam lr=1e-3 b1=0.9 b2=0.999 eps=1e-8", "parallelism": "single GPU"}
+    path = {"unique": U, "algorithmic_bytes": path_bytes,
+            "achieved_gbs": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "segment_sum_ms": round(seg_ms, 4), "adam_ms": round(adam_ms, 4),
+            "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+            "implementation": "emb_grad_segment_sum + emb_rowwise_adam over the forward's dedup",
+            "grad": "torch.randn on the GPU, seeded generator (1000003)",
+            "timing": "HIP events per step (segment-sum + Adam); the forward's dedup and find-or-insert run "
+                      "once, untimed; Adam's step counter advances"}
+    return _result(args, n / (ms * 1e-3) / 1e6, ms, config, "fp32 gradients and rows", path,
+                   _roofline("emb_grad_segment_sum (CSR + segmented reduce)", seg_bytes, seg_ms))
+
+
+# ------------------------------------------------------------------- online
+def run_online(args, torch, htl, workloads, dev):
+    spec = workloads.DynamicOnlineSpec()
+    steps = args.warmup + args.steps
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((spec.n, spec.dim), dtype=torch.bfloat16, device=dev)
+    fwd, lru, ers = [], [], []
+    U_last = 0
+    gen = workloads.DynamicOnlineStream(spec, steps)
+    for s in range(steps):
+        keys = torch.from_numpy(gen.keys(s)).to(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        uniq, inv, nu = htl.dedup_unique_inverse(keys)
+        slots, status = table.find_or_insert(uniq, n_dev=nu, step=s)
+        htl.gather(table, slots, inv, out=out)
+        e[1].record(stream)
+        victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
+        e[2].record(stream)
+        k = int(nv.item())                                # the host needs k to size the erase
+        table.erase(victims[:k])
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if s >= args.warmup:
+            fwd.append(e[0].elapsed_time(e[1]))
+            lru.append(e[1].elapsed_time(e[2]))
+            ers.append(e[2].elapsed_time(e[3]))
+            U_last = int(nu.item())
+        print(f"online step {s} done", file=sys.stderr, flush=True)
+    ms = float(np.mean(fwd))
+    M = 1 << spec.capacity_log2
+    row = spec.dim * 2
+    fwd_bytes = spec.n * (16 + row) + U_last * (33 + row)
+    lru_bytes = M * 12
+    config = {"workload": "dynamic_online", "ids_per_step": spec.n, "window": spec.window,
+              "new_ids_per_step": spec.delta, "zipf_a": spec.zipf_a, "table_slots_log2": spec.capacity_log2,
+              "dim": spec.dim, "row_dtype": "bf16", "evict_fraction": f"{spec.evict_num}/{spec.evict_den}",
+              "parallelism": "single GPU"}
+    path = {"unique_last_step": U_last, "forward_ms": round(ms, 4),
+            "lru_select_ms": round(float(np.mean(lru)), 4), "erase_ms": round(float(np.mean(ers)), 4),
+            "forward_algorithmic_bytes": fwd_bytes,
+            "implementation": "dedup + find_or_insert(step) + gather, then ht_lru_select + ht_erase",
+            "timing": f"per-step HIP events over steps {args.warmup}..{steps - 1} of the drifting stream "
+                      "(the warm-up steps fill the table); value = forward IDs/s"}
+    return _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
+                   _roofline("ht_lru_select (full-table scan + radix select)", lru_bytes, float(np.mean(lru))))
+
+
+# -------------------------------------------------------------- references
 def _copy_reference(torch, htl, dev, nbytes=1 << 30, reps=5):
     """Achievable streaming bandwidth: a 1 GiB device-to-device copy (read + write)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -239,7 +372,7 @@ def _copy_reference(torch, htl, dev, nbytes=1 << 30, reps=5):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def _cpu_baseline(w, sample):
+def _cpu_baseline_lookup(w, sample):
     """The oracle timed on the host (single thread) on the first `sample` IDs."""
     import oracle
     m = min(sample, w.keys.size)
@@ -255,6 +388,29 @@ def _cpu_baseline(w, sample):
     return {"value": round(m / dt / 1e6, 3), "unit": "Mkeys/s", "cores": 1, "kind": "oracle",
             "sample": f"first {m} IDs of the same batch, dedup+find_or_insert+gather, table pre-filled "
                       f"untimed; {dt:.2f} s", "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the sharded design is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import hash_table_lookup_amd as htl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    runner = {"single_large_table": run_lookup, "tiny": run_lookup, "merged_tables": run_pooled,
+              "backward": run_backward, "dynamic_online": run_online}[args.workload]
+    result = runner(args, torch, htl, workloads, dev)
+    result["copy_reference"] = _copy_reference(torch, htl, dev)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

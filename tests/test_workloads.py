@@ -120,3 +120,10 @@ def test_dynamic_online_window_drifts():
         assert np.all(np.isin(keys, allowed.astype(np.int64)))
         inv_keys[s] = set(allowed.tolist())
     assert len(inv_keys[1] - inv_keys[0]) == spec.delta
+
+
+def test_dynamic_online_stream_matches_per_step_definition():
+    spec = workloads.DynamicOnlineSpec(window=1 << 12, n=1 << 10, steps=6)
+    stream = workloads.DynamicOnlineStream(spec, 6)
+    for s in (0, 1, 5):
+        assert np.array_equal(stream.keys(s), workloads.dynamic_online_step(spec, s))

@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "scramble", "zipf_ranks", "tiny", "single_large_table", "merged_tables",
-    "backward", "dynamic_online_step", "DynamicOnlineSpec", "LookupWorkload",
+    "backward", "dynamic_online_step", "DynamicOnlineSpec", "DynamicOnlineStream", "LookupWorkload",
     "PooledWorkload", "BackwardWorkload", "merged_vocab_sizes", "WORKLOADS",
 ]
 
@@ -211,6 +211,30 @@ def dynamic_online_step(spec: DynamicOnlineSpec, step: int) -> np.ndarray:
     r = zipf_ranks(rng, spec.zipf_a, spec.window, spec.n)
     ids = active[order[r - 1]]
     return scramble(ids, 40).astype(np.int64)
+
+
+class DynamicOnlineStream:
+    """The same key batches as :func:`dynamic_online_step`, for steps
+    0..steps-1, computed from one sort of every id the stream can reach
+    (scramble64 is a bijection, so the order restricted to each window is the
+    window's own order)."""
+
+    def __init__(self, spec: DynamicOnlineSpec, steps: int):
+        self.spec = spec
+        self.steps = steps
+        span = (steps - 1) * spec.delta + spec.window
+        ids = np.arange(span, dtype=np.uint64)
+        self._order = ids[np.argsort(scramble(ids, 64), kind="stable")]
+
+    def keys(self, step: int) -> np.ndarray:
+        assert 0 <= step < self.steps
+        spec = self.spec
+        lo = np.uint64(step * spec.delta)
+        in_window = (self._order >= lo) & (self._order < lo + np.uint64(spec.window))
+        ordered = self._order[in_window]
+        rng = np.random.Generator(np.random.PCG64(step))
+        r = zipf_ranks(rng, spec.zipf_a, spec.window, spec.n)
+        return scramble(ordered[r - 1], 40).astype(np.int64)
 
 
 WORKLOADS = {
