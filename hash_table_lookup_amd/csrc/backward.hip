@@ -14,6 +14,11 @@
 //             the tile's places inside that unique's segment (hot keys cost
 //             one atomic per tile, not one per ID);
 //   scan   -- segment offsets = exclusive prefix sum of the counts;
+//   (segments are laid out in a spread order q(u) = (u mod S) * C + u / S,
+//   C = ceil(U / S): the dedup gives the hottest keys small, adjacent ids,
+//   and their counters would otherwise share a few cache lines, so that
+//   every tile's atomics queue on the same L2 channels; measured on MI355X
+//   with a Zipf(1.2) batch of 2^23 IDs the count pass ran 3x slower);
 //   fill   -- perm[offset[u] + place] = i (CSR of IDs grouped by unique);
 //   small  -- one wavefront per segment of <= kSmallMax IDs sums its rows;
 //   large  -- longer segments (Zipf's head: the hottest key of a 2^23-ID
@@ -37,10 +42,18 @@ constexpr int kCCapLog2 = 12;
 constexpr int kSmallMax = 256;             // longest segment summed by one wavefront
 constexpr int kChunk = 1024;               // rows per workgroup in long segments
 constexpr int kRBlock = 256;
+constexpr int kSpread = 1024;              // S of the spread segment order
+
+// Spread order: q(u) = (u mod S) * C + u / S with C = ceil(U / S), a
+// bijection from [0, U) into [0, S * C); qinv inverts it on that range.
+__device__ __forceinline__ int64_t spread_c(int64_t U) { return (U + kSpread - 1) / kSpread; }
+__device__ __forceinline__ int64_t spread_q(int64_t u, int64_t C) { return (u % kSpread) * C + u / kSpread; }
+__device__ __forceinline__ int64_t spread_u(int64_t q, int64_t C) { return (q % C) * kSpread + q / C; }
 
 struct SegWs {
-    int32_t* counts;       // [u_max]
-    int32_t* seg_off;      // [u_max + 1]
+    int32_t* counts;       // [u_max + S], spread order
+    int32_t* seg_off;      // [u_max + S + 1]
+    int64_t* n_seg;        // S * C: segments in spread order
     int32_t* rel;          // [n]
     int32_t* perm;         // [n]
     int32_t* large;        // [large_max]
@@ -62,14 +75,16 @@ SegWs seg_layout(int64_t n, int64_t u_max, int dim, char* base) {
         off = align_up(off + bytes, 256);
         return p;
     };
-    w.counts = (int32_t*)take((size_t)u_max * 4);
-    w.seg_off = (int32_t*)take((size_t)(u_max + 1) * 4);
+    const int64_t q_max = u_max + kSpread;
+    w.counts = (int32_t*)take((size_t)q_max * 4);
+    w.seg_off = (int32_t*)take((size_t)(q_max + 1) * 4);
+    w.n_seg = (int64_t*)take(8);
     w.rel = (int32_t*)take((size_t)n * 4);
     w.perm = (int32_t*)take((size_t)n * 4);
     w.large = (int32_t*)take((size_t)w.large_max * 4);
     w.large_off = (int32_t*)take((size_t)(w.large_max + 1) * 4);
     w.n_large = (unsigned long long*)take(8);
-    w.scan_tmp = take(scan_temp_bytes(u_max));
+    w.scan_tmp = take(scan_temp_bytes(q_max));
     w.partial = (float*)take((size_t)w.max_chunks * dim * 4);
     w.bytes = off;
     return w;
@@ -82,11 +97,14 @@ __device__ __forceinline__ int64_t dev_count(int64_t n_max, const int64_t* n_dev
 }
 
 __global__ void k_seg_zero(int32_t* __restrict__ counts, int64_t u_max, const int64_t* __restrict__ n_dev,
-                           unsigned long long* __restrict__ n_large) {
-    const int64_t U = dev_count(u_max, n_dev);
+                           unsigned long long* __restrict__ n_large, int64_t* __restrict__ n_seg) {
+    const int64_t Q = kSpread * spread_c(dev_count(u_max, n_dev));
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < U; i += stride) counts[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *n_large = 0ull;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < Q; i += stride) counts[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *n_large = 0ull;
+        *n_seg = Q;
+    }
 }
 
 __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restrict__ inverse, int64_t n,
@@ -97,6 +115,7 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
     __shared__ int32_t s_base[kCCap];
     const int tid = threadIdx.x;
     const int64_t U = dev_count(u_max, n_dev);
+    const int64_t C = spread_c(U);
     for (int64_t tile = blockIdx.x; tile * kCTile < n; tile += gridDim.x) {
         const int64_t base = tile * kCTile;
         for (int i = tid; i < kCCap; i += kCThreads) {
@@ -127,7 +146,7 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
         __syncthreads();
         for (int i = tid; i < kCCap; i += kCThreads) {
             const int32_t u = s_u[i];
-            if (u >= 0) s_base[i] = atomicAdd(&counts[u], s_cnt[i]);
+            if (u >= 0) s_base[i] = atomicAdd(&counts[spread_q(u, C)], s_cnt[i]);
         }
         __syncthreads();
 #pragma unroll
@@ -143,10 +162,11 @@ __global__ void k_seg_fill(const int32_t* __restrict__ inverse, const int32_t* _
                            int64_t u_max, const int64_t* __restrict__ n_dev, const int32_t* __restrict__ seg_off,
                            int32_t* __restrict__ perm) {
     const int64_t U = dev_count(u_max, n_dev);
+    const int64_t C = spread_c(U);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         const int32_t u = inverse[i];
-        if (u >= 0 && u < U) perm[seg_off[u] + rel[i]] = (int32_t)i;
+        if (u >= 0 && u < U) perm[seg_off[spread_q(u, C)] + rel[i]] = (int32_t)i;
     }
 }
 
@@ -200,8 +220,8 @@ __device__ __forceinline__ void store_row(float* __restrict__ dst, int vpr, int 
     }
 }
 
-// One wavefront per segment; segments longer than kSmallMax are listed for
-// the chunked path instead.
+// One wavefront per segment (in spread order); segments longer than
+// kSmallMax are listed, by their spread index, for the chunked path.
 template <int TEAM, int QMAX>
 __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__ grad, int vpr,
                                                       const int32_t* __restrict__ perm,
@@ -210,16 +230,19 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
                                                       int32_t* __restrict__ large,
                                                       unsigned long long* __restrict__ n_large) {
     const int64_t U = dev_count(u_max, n_dev);
+    const int64_t C = spread_c(U);
     const int lane = lane_id();
     const int tl = lane & (TEAM - 1);
     const int team = lane / TEAM;
     constexpr int TEAMS = 64 / TEAM;
     const int64_t wave = (blockIdx.x * (int64_t)kRBlock + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * kRBlock) >> 6;
-    for (int64_t u = wave; u < U; u += nwaves) {
-        const int32_t beg = seg_off[u], end = seg_off[u + 1];
+    for (int64_t q = wave; q < kSpread * C; q += nwaves) {
+        const int64_t u = spread_u(q, C);
+        if (u >= U) continue;                    // a hole of the spread order
+        const int32_t beg = seg_off[q], end = seg_off[q + 1];
         if (end - beg > kSmallMax) {
-            if (lane == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)u;
+            if (lane == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
             continue;
         }
         float acc[QMAX][4];
@@ -250,8 +273,8 @@ __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__
         const int64_t i = b0 + threadIdx.x;
         int32_t x = 0;
         if (i < nl) {
-            const int32_t u = large[i];
-            x = (seg_off[u + 1] - seg_off[u] + kChunk - 1) / kChunk;
+            const int32_t q = large[i];
+            x = (seg_off[q + 1] - seg_off[q] + kChunk - 1) / kChunk;
         }
         const int lane = lane_id();
         const int wid = threadIdx.x >> 6;
@@ -298,10 +321,10 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
             if (large_off[mid] <= c) lo = mid;
             else hi = mid;
         }
-        const int32_t u = large[lo];
+        const int32_t q = large[lo];
         const int32_t part = (int32_t)(c - large_off[lo]);
-        const int32_t beg = seg_off[u] + part * kChunk;
-        const int32_t end = min(seg_off[u + 1], beg + kChunk);
+        const int32_t beg = seg_off[q] + part * kChunk;
+        const int32_t end = min(seg_off[q + 1], beg + kChunk);
         float acc[QMAX][4];
 #pragma unroll
         for (int a = 0; a < QMAX; ++a) acc[a][0] = acc[a][1] = acc[a][2] = acc[a][3] = 0.0f;
@@ -322,20 +345,72 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
     }
 }
 
-// One workgroup per long segment: out[u] = sum of its chunk partials in order.
-__global__ __launch_bounds__(kRBlock) void k_large_combine(const float* __restrict__ partial, int dim,
-                                                          const int32_t* __restrict__ large,
-                                                          const unsigned long long* __restrict__ n_large,
-                                                          const int32_t* __restrict__ large_off,
-                                                          float* __restrict__ out) {
+// One workgroup per long segment: out[u] = sum of its chunk partials.  The
+// block's kCombThreads threads are vpr-wide column lanes times groups; each
+// group adds every groups-th partial (several loads in flight per thread),
+// then the groups are added in LDS.  The hottest segment of a Zipf batch has
+// over a thousand partials, so a serial walk over them would dominate.
+constexpr int kCombThreads = 1024;
+
+__global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __restrict__ partial, int vpr,
+                                                               int lanes, const int32_t* __restrict__ large,
+                                                               const unsigned long long* __restrict__ n_large,
+                                                               const int32_t* __restrict__ large_off, int64_t u_max,
+                                                               const int64_t* __restrict__ n_dev,
+                                                               u32x4* __restrict__ out) {
+    __shared__ float4 s_red[kCombThreads];
     const int64_t nl = (int64_t)*n_large;
+    const int64_t C = spread_c(dev_count(u_max, n_dev));
+    const int groups = kCombThreads / lanes;
+    const int l = threadIdx.x % lanes, g = threadIdx.x / lanes;
     for (int64_t i = blockIdx.x; i < nl; i += gridDim.x) {
-        const int32_t u = large[i];
+        const int64_t u = spread_u(large[i], C);
         const int32_t c0 = large_off[i], c1 = large_off[i + 1];
-        for (int e = threadIdx.x; e < dim; e += kRBlock) {
-            float s = 0.0f;
-            for (int32_t c = c0; c < c1; ++c) s += partial[(int64_t)c * dim + e];
-            out[(int64_t)u * dim + e] = s;
+        for (int v0 = 0; v0 < vpr; v0 += lanes) {
+            const int v = v0 + l;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (v < vpr) {
+                constexpr int U = 4;
+                int32_t c = c0 + g;
+                for (; c + (U - 1) * groups < c1; c += U * groups) {
+                    u32x4 x[U];
+#pragma unroll
+                    for (int q = 0; q < U; ++q) x[q] = partial[(int64_t)(c + q * groups) * vpr + v];
+#pragma unroll
+                    for (int q = 0; q < U; ++q) {
+                        acc.x += __uint_as_float(x[q].x);
+                        acc.y += __uint_as_float(x[q].y);
+                        acc.z += __uint_as_float(x[q].z);
+                        acc.w += __uint_as_float(x[q].w);
+                    }
+                }
+                for (; c < c1; c += groups) {
+                    const u32x4 x = partial[(int64_t)c * vpr + v];
+                    acc.x += __uint_as_float(x.x);
+                    acc.y += __uint_as_float(x.y);
+                    acc.z += __uint_as_float(x.z);
+                    acc.w += __uint_as_float(x.w);
+                }
+            }
+            s_red[threadIdx.x] = acc;
+            __syncthreads();
+            if (g == 0 && v < vpr) {
+                float4 s4 = s_red[l];
+                for (int q = 1; q < groups; ++q) {
+                    const float4 y = s_red[q * lanes + l];
+                    s4.x += y.x;
+                    s4.y += y.y;
+                    s4.z += y.z;
+                    s4.w += y.w;
+                }
+                u32x4 w;
+                w.x = __float_as_uint(s4.x);
+                w.y = __float_as_uint(s4.y);
+                w.z = __float_as_uint(s4.z);
+                w.w = __float_as_uint(s4.w);
+                out[(int64_t)u * vpr + v] = w;
+            }
+            __syncthreads();
         }
     }
 }
@@ -345,12 +420,14 @@ __global__ void k_seg_elem(const float* __restrict__ grad, int dim, const int32_
                            const int32_t* __restrict__ seg_off, int64_t u_max, const int64_t* __restrict__ n_dev,
                            float* __restrict__ out) {
     const int64_t U = dev_count(u_max, n_dev);
+    const int64_t C = spread_c(U);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < U * dim; e += stride) {
         const int64_t u = e / dim;
         const int j = (int)(e - u * dim);
+        const int64_t q = spread_q(u, C);
         float s = 0.0f;
-        for (int32_t i = seg_off[u]; i < seg_off[u + 1]; ++i) s += grad[(int64_t)perm[i] * dim + j];
+        for (int32_t i = seg_off[q]; i < seg_off[q + 1]; ++i) s += grad[(int64_t)perm[i] * dim + j];
         out[e] = s;
     }
 }
@@ -358,18 +435,65 @@ __global__ void k_seg_elem(const float* __restrict__ grad, int dim, const int32_
 template <int TEAM, int QMAX>
 void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, const int64_t* n_dev, float* out,
                    hipStream_t s) {
-    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX>), dim3(grid_for(u_max, kRBlock / 64)), dim3(kRBlock), 0, s,
-                       (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, out, w.large, w.n_large);
+    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX>), dim3(grid_for(u_max + kSpread, kRBlock / 64)), dim3(kRBlock), 0,
+                       s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, out, w.large, w.n_large);
     hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off);
     hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX>), dim3(grid_for(w.max_chunks, 1, 1 << 16)), dim3(kRBlock), 0,
                        s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off,
                        w.max_chunks, w.partial);
-    hipLaunchKernelGGL(k_large_combine, dim3(grid_for(w.large_max, 1, 1 << 14)), dim3(kRBlock), 0, s, w.partial,
-                       vpr * 4, w.large, w.n_large, w.large_off, out);
+    int lanes = 1;
+    while (lanes < vpr && lanes < kCombThreads / 4) lanes <<= 1;
+    hipLaunchKernelGGL(k_large_combine, dim3(grid_for(w.large_max, 1, 1 << 14)), dim3(kCombThreads), 0, s,
+                       (const u32x4*)w.partial, vpr, lanes, w.large, w.n_large, w.large_off, u_max, n_dev,
+                       (u32x4*)out);
 }
 
 // ---------------------------------------------------------------- Adam --
+// Same arithmetic per element in both kernels; contraction off so that every
+// product and sum rounds on its own, as written.
 #pragma clang fp contract(off)
+__device__ __forceinline__ void adam_elem(float& th, float& mo, float& vo, float gj, float b1, float b2, float omb1,
+                                          float omb2, float lr, float eps, float c1, float c2) {
+    const float mj = b1 * mo + omb1 * gj;
+    const float vj = b2 * vo + omb2 * (gj * gj);
+    const float mhat = mj / c1;
+    const float vhat = vj / c2;
+    th = th - lr * (mhat / (sqrtf(vhat) + eps));
+    mo = mj;
+    vo = vj;
+}
+
+// Rows of 4k floats: TEAM lanes per row, 16 bytes per lane access.
+template <int TEAM>
+__global__ __launch_bounds__(256) void k_adam4(float4* __restrict__ theta, float4* __restrict__ m,
+                                              float4* __restrict__ v, int vpr, int64_t M,
+                                              const int32_t* __restrict__ slots, const float4* __restrict__ g,
+                                              int64_t u_max, const int64_t* __restrict__ n_dev, float lr, float b1,
+                                              float b2, float eps, float c1, float c2) {
+    const int64_t U = dev_count(u_max, n_dev);
+    const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
+    const int tl = threadIdx.x & (TEAM - 1);
+    const int64_t team = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / TEAM;
+    const int64_t nteams = (int64_t)gridDim.x * blockDim.x / TEAM;
+    for (int64_t u = team; u < U; u += nteams) {
+        const int32_t s = slots[u];
+        if (s < 0 || s >= M) continue;
+        for (int j = tl; j < vpr; j += TEAM) {
+            const int64_t o = (int64_t)s * vpr + j;
+            const float4 gj = g[u * vpr + j];
+            float4 th = theta[o], mo = m[o], vo = v[o];
+            adam_elem(th.x, mo.x, vo.x, gj.x, b1, b2, omb1, omb2, lr, eps, c1, c2);
+            adam_elem(th.y, mo.y, vo.y, gj.y, b1, b2, omb1, omb2, lr, eps, c1, c2);
+            adam_elem(th.z, mo.z, vo.z, gj.z, b1, b2, omb1, omb2, lr, eps, c1, c2);
+            adam_elem(th.w, mo.w, vo.w, gj.w, b1, b2, omb1, omb2, lr, eps, c1, c2);
+            theta[o] = th;
+            m[o] = mo;
+            v[o] = vo;
+        }
+    }
+}
+
+// Any dim: one thread per (u, j).
 __global__ void k_adam(float* __restrict__ theta, float* __restrict__ m, float* __restrict__ v, int dim, int64_t M,
                        const int32_t* __restrict__ slots, const float* __restrict__ g, int64_t u_max,
                        const int64_t* __restrict__ n_dev, float lr, float b1, float b2, float eps, float c1,
@@ -383,15 +507,16 @@ __global__ void k_adam(float* __restrict__ theta, float* __restrict__ m, float* 
         const int32_t s = slots[u];
         if (s < 0 || s >= M) continue;
         const int64_t o = (int64_t)s * dim + j;
-        const float gj = g[e];
-        const float mj = b1 * m[o] + omb1 * gj;
-        const float vj = b2 * v[o] + omb2 * (gj * gj);
-        const float mhat = mj / c1;
-        const float vhat = vj / c2;
-        theta[o] = theta[o] - lr * (mhat / (sqrtf(vhat) + eps));
-        m[o] = mj;
-        v[o] = vj;
+        adam_elem(theta[o], m[o], v[o], g[e], b1, b2, omb1, omb2, lr, eps, c1, c2);
     }
+}
+
+template <int TEAM>
+void launch_adam4(const TableDev& T, const int32_t* slots, const float* g, int64_t u_max, const int64_t* n_dev,
+                  float lr, float b1, float b2, float eps, float c1, float c2, hipStream_t s) {
+    hipLaunchKernelGGL(k_adam4<TEAM>, dim3(grid_for(u_max, 256 / TEAM, 1 << 16)), dim3(256), 0, s, (float4*)T.rows,
+                       (float4*)T.m, (float4*)T.v, T.dim / 4, T.capacity, slots, (const float4*)g, u_max, n_dev, lr,
+                       b1, b2, eps, c1, c2);
 }
 
 int team_for(int vpr) {
@@ -418,7 +543,7 @@ htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64
                                 const int64_t* n_unique_dev, int64_t u_max, int dim, float* out, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
     clear_error();
-    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "emb_grad_segment_sum: n must be in [0, 2^31)");
+    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31) - kSpread, "emb_grad_segment_sum: n must be in [0, 2^31 - 1024)");
     HTL_REQUIRE(u_max >= 0 && u_max <= n, "emb_grad_segment_sum: u_max must be in [0, n]");
     HTL_REQUIRE(dim >= 1 && dim <= 65536, "emb_grad_segment_sum: dim must be in [1, 65536]");
     if (n == 0 || u_max == 0) return HTL_OK;
@@ -429,11 +554,12 @@ htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64
     SegWs w = seg_layout(n, u_max, dim, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "emb_grad_segment_sum: workspace too small");
 
-    hipLaunchKernelGGL(k_seg_zero, dim3(grid_for(u_max, 256 * 4, 1 << 14)), dim3(256), 0, stream, w.counts, u_max,
-                       n_unique_dev, w.n_large);
+    hipLaunchKernelGGL(k_seg_zero, dim3(grid_for(u_max + kSpread, 256 * 4, 1 << 14)), dim3(256), 0, stream, w.counts,
+                       u_max, n_unique_dev, w.n_large, w.n_seg);
     hipLaunchKernelGGL(k_seg_count, dim3(grid_for(ceil_div(n, kCTile), 1, 1 << 16)), dim3(kCThreads), 0, stream,
                        inverse, n, u_max, n_unique_dev, w.counts, w.rel);
-    htl_status st = scan_exclusive_i32(w.counts, w.seg_off, u_max, n_unique_dev, kScanIdentity, 1, w.scan_tmp, stream);
+    htl_status st = scan_exclusive_i32(w.counts, w.seg_off, u_max + kSpread, w.n_seg, kScanIdentity, 1, w.scan_tmp,
+                                       stream);
     if (st != HTL_OK) return st;
     hipLaunchKernelGGL(k_seg_fill, dim3(grid_for(n, 256 * 4)), dim3(256), 0, stream, inverse, w.rel, n, u_max,
                        n_unique_dev, w.seg_off, w.perm);
@@ -472,8 +598,20 @@ htl_status emb_rowwise_adam(htl_table* t, const int32_t* slots, const float* g, 
     const float c1 = (float)(1.0 - std::pow((double)b1, (double)step));
     const float c2 = (float)(1.0 - std::pow((double)b2, (double)step));
     const TableDev& T = t->dev;
-    hipLaunchKernelGGL(k_adam, dim3(grid_for(u_max * T.dim, 256 * 4)), dim3(256), 0, stream, (float*)T.rows, T.m,
-                       T.v, T.dim, T.capacity, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2);
+    if (T.dim % 4 == 0 && aligned(g, 16)) {
+        switch (team_for(T.dim / 4)) {
+            case 1: launch_adam4<1>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            case 2: launch_adam4<2>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            case 4: launch_adam4<4>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            case 8: launch_adam4<8>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            case 16: launch_adam4<16>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            case 32: launch_adam4<32>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+            default: launch_adam4<64>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
+        }
+    } else {
+        hipLaunchKernelGGL(k_adam, dim3(grid_for(u_max * T.dim, 256 * 4)), dim3(256), 0, stream, (float*)T.rows,
+                           T.m, T.v, T.dim, T.capacity, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2);
+    }
     return check_launch("emb_rowwise_adam");
 }
 

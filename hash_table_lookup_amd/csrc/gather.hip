@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kUnroll = 4;
+constexpr int kPoolUnroll = 4;         // IDs per team in flight in the pooling loop
 
 __device__ __forceinline__ u32x4 zero4() {
     u32x4 z;
@@ -101,8 +102,10 @@ __global__ void k_gather_elem(const TIn* __restrict__ rows, int dim, int64_t M, 
 
 // ------------------------------------------------------------- pooling --
 // One wavefront per bag.  The wave splits into 64/TEAM teams; team q takes
-// IDs q, q + 64/TEAM, ... of the bag; every lane accumulates its 16-byte
-// vectors in fp32; a butterfly over the teams then combines the partial sums.
+// IDs q, q + 64/TEAM, ... of the bag, kPoolUnroll of them per round so that
+// their three dependent loads (inverse, slot, row) overlap; every lane
+// accumulates its 16-byte vectors in fp32; a butterfly over the teams then
+// combines the partial sums.
 template <int TEAM, int QMAX, bool IN_BF16>
 __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows, int vpr, int64_t M,
                                                 const int32_t* __restrict__ slots,
@@ -123,27 +126,41 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[a][e] = 0.0f;
         const int32_t beg = offsets[bag], end = offsets[bag + 1];
-        for (int32_t i = beg + q; i < end; i += TEAMS) {
-            const int32_t s = slots[inverse ? inverse[i] : i];
-            if (s < 0 || s >= M) continue;
-            const u32x4* src = rows + (int64_t)s * vpr;
+        for (int32_t i0 = beg + q; i0 < end; i0 += TEAMS * kPoolUnroll) {
+            // kPoolUnroll IDs per team in flight: inverse, then slots, then rows
+            int32_t s[kPoolUnroll];
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) {
+                const int32_t i = i0 + u * TEAMS;
+                s[u] = i < end ? (inverse ? inverse[i] : i) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) {
+                if (s[u] >= 0) s[u] = slots[s[u]];
+                if (s[u] >= M) s[u] = -1;            // not a slot of this table: adds nothing
+            }
 #pragma unroll
             for (int a = 0; a < QMAX; ++a) {
                 const int v = tl + a * TEAM;
                 if (v >= vpr) break;
-                const u32x4 x = src[v];
-                if (IN_BF16) {
-                    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                u32x4 x[kPoolUnroll];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        acc[a][2 * c] += bf16_lo(w[c]);
-                        acc[a][2 * c + 1] += bf16_hi(w[c]);
+                for (int u = 0; u < kPoolUnroll; ++u) x[u] = s[u] >= 0 ? rows[(int64_t)s[u] * vpr + v] : zero4();
+#pragma unroll
+                for (int u = 0; u < kPoolUnroll; ++u) {
+                    if (IN_BF16) {
+                        const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            acc[a][2 * c] += bf16_lo(w[c]);
+                            acc[a][2 * c + 1] += bf16_hi(w[c]);
+                        }
+                    } else {
+                        acc[a][0] += __uint_as_float(x[u].x);
+                        acc[a][1] += __uint_as_float(x[u].y);
+                        acc[a][2] += __uint_as_float(x[u].z);
+                        acc[a][3] += __uint_as_float(x[u].w);
                     }
-                } else {
-                    acc[a][0] += __uint_as_float(x.x);
-                    acc[a][1] += __uint_as_float(x.y);
-                    acc[a][2] += __uint_as_float(x.z);
-                    acc[a][3] += __uint_as_float(x.w);
                 }
             }
         }

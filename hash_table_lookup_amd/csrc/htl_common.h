@@ -61,6 +61,7 @@ struct htl_table {
     htl_dtype dtype;
     uint64_t init_seed;
     uint32_t flags;
+    uint32_t max_step;   // largest step any find-or-insert stamped since create/clear
     htl::TableDev dev;
 };
 

@@ -7,51 +7,73 @@
 // pages name no eviction policy; least recently used, ties broken by the key
 // value, is this library's.
 //
-// Steps, all on the device (no host synchronisation):
-//   collect  -- compact the live slots' (last_seen, key) into candidate lists
-//               and take the maximum last_seen;
-//   select   -- radix select with 8-bit digits: per digit, LDS histograms of
-//               the candidates that match the digits chosen so far, summed
-//               into one 256-bin histogram, and one block picks the bucket
-//               that holds the k-th smallest.  last_seen digits go first
-//               (only as many as its maximum needs), then the 64-bit keys
-//               (sign bit flipped so unsigned order is signed order), the
-//               latter over the compacted list of candidates that tie on
-//               last_seen;
-//   emit     -- every candidate at or below the selected (last_seen, key)
-//               is a victim.
-#include "htl_common.h"
+// All on the device, no host synchronisation and no counter atomics (a
+// counter that every block bumps serialises on MI355X):
+//   collect -- the table is cut into chunks of kChunk slots; each chunk
+//              compacts its live slots' (last_seen, key) into its own fixed
+//              region of the candidate arrays and records its count and its
+//              largest last_seen;
+//   init    -- one block sums the counts (live L), takes the maximum
+//              last_seen and sets k = floor(L * num / den);
+//   select  -- radix select with 8-bit digits: per digit, LDS histograms of
+//              the candidates that match the digits chosen so far (a
+//              persistent grid, so each of the 256 global bins, one cache
+//              line apart, gets one add per block), then one block scans the
+//              bins for the bucket holding the k-th smallest.  last_seen
+//              digits go first (only as many as its maximum needs), then the
+//              64-bit keys (sign bit flipped so unsigned order is signed
+//              order) over the candidates that tie on last_seen, compacted
+//              per chunk the same way, and compacted again in place to those
+//              matching the top key digit before the second one is counted.
+//              (A pick fused into the histogram pass by a last-block ticket
+//              needs a device-scope fence per block, which writes back L2 on
+//              this multi-die part and cost far more than the extra launch.)
+//   emit    -- victims (candidates at or below the selected (last_seen,
+//              key)) are counted per chunk, the counts prefix-summed, and
+//              written densely.
+#include "scan.h"
 
 namespace htl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = 16;
+constexpr int kChunk = 4096;               // table slots per chunk (one block pass)
+constexpr int kPerThread = kChunk / kThreads;
+constexpr int kHistBlocks = 1024;          // persistent grid of the histogram passes
+constexpr int kBinStride = 32;             // words between global histogram bins
 
 struct LruState {
-    unsigned long long n_live;
-    unsigned long long n_ties;
-    unsigned long long n_out;
+    int64_t n_live;
     int64_t k;            // victims wanted
     int64_t k_rem;        // rank (1-based) still to find inside the current prefix
     uint32_t ls_max;
     uint32_t ls_digits;   // last_seen digits in use
-    uint32_t ls_prefix;   // selected last_seen (complete after the last digit)
+    uint32_t ls_prefix;   // selected last_seen (complete after its last digit)
     uint32_t pad;
     uint64_t key_prefix;  // selected biased key
-    uint32_t hist[256];
+    unsigned long long key_and, key_or;   // over the biased keys of the ties
+    uint32_t hist[256 * kBinStride];
 };
 
 struct LruWs {
     LruState* st;
-    uint32_t* cand_ls;    // [M]
-    uint64_t* cand_key;   // [M], biased keys
-    uint64_t* ties;       // [M]
+    uint32_t* cand_ls;     // [nchunks * kChunk]: per chunk, its live slots first
+    uint64_t* cand_key;    // [nchunks * kChunk], biased keys
+    uint64_t* ties;        // [nchunks * kChunk]: per chunk, candidates tying on last_seen
+    int32_t* chunk_cnt;    // [nchunks]
+    uint32_t* chunk_max;   // [nchunks]
+    int32_t* tie_cnt;      // [nchunks]
+    int32_t* vic_cnt;      // [nchunks]
+    int32_t* vic_off;      // [nchunks + 1]
+    void* scan_tmp;
+    int64_t nchunks;
     size_t bytes;
 };
 
 LruWs lru_layout(int64_t M, char* base) {
     LruWs w{};
+    w.nchunks = ceil_div(M, kChunk);
+    const size_t cap = (size_t)w.nchunks * kChunk;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char* p = base ? base + off : nullptr;
@@ -59,205 +81,383 @@ LruWs lru_layout(int64_t M, char* base) {
         return p;
     };
     w.st = (LruState*)take(sizeof(LruState));
-    w.cand_ls = (uint32_t*)take((size_t)M * 4);
-    w.cand_key = (uint64_t*)take((size_t)M * 8);
-    w.ties = (uint64_t*)take((size_t)M * 8);
+    w.cand_ls = (uint32_t*)take(cap * 4);
+    w.cand_key = (uint64_t*)take(cap * 8);
+    w.ties = (uint64_t*)take(cap * 8);
+    w.chunk_cnt = (int32_t*)take((size_t)w.nchunks * 4);
+    w.chunk_max = (uint32_t*)take((size_t)w.nchunks * 4);
+    w.tie_cnt = (int32_t*)take((size_t)w.nchunks * 4);
+    w.vic_cnt = (int32_t*)take((size_t)w.nchunks * 4);
+    w.vic_off = (int32_t*)take((size_t)(w.nchunks + 1) * 4);
+    w.scan_tmp = take(scan_temp_bytes(w.nchunks));
     w.bytes = off;
     return w;
 }
 
 __device__ __forceinline__ uint64_t bias(int64_t k) { return (uint64_t)k ^ 0x8000000000000000ull; }
 
-__global__ void k_lru_reset(LruState* st) {
-    if (threadIdx.x == 0) {
-        st->n_live = st->n_ties = st->n_out = 0ull;
-        st->ls_max = 0u;
-        st->ls_prefix = 0u;
-        st->key_prefix = 0ull;
+// Block-wide exclusive prefix of v over thread order; returns the total.
+__device__ __forceinline__ int block_prefix(int& v, int* s_wave) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    int incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
     }
-    st->hist[threadIdx.x] = 0u;
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        const int c = s_wave[w];
+        before += (w < wid) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    v = before + incl - v;
+    return tot;
 }
 
-// Compaction of live slots (block-level counting, one atomic per block).
-__global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, LruState* __restrict__ st,
+// Each chunk compacts its live slots into its own region (order within the
+// region: by thread, then by the thread's slots).  Loads are coalesced: slot
+// j * kThreads + tid of the chunk belongs to thread tid.
+__global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nchunks,
                                                          uint32_t* __restrict__ cand_ls,
-                                                         uint64_t* __restrict__ cand_key) {
-    __shared__ int s_warp[kThreads / 64];
-    __shared__ unsigned long long s_base;
-    const int tid = threadIdx.x, wid = tid >> 6, lane = lane_id();
-    constexpr int kPerBlock = kThreads * kPerThread;
-    uint32_t my_max = 0;
-    for (int64_t blk = blockIdx.x; blk * kPerBlock < T.capacity; blk += gridDim.x) {
-        const int64_t start = blk * kPerBlock;
+                                                         uint64_t* __restrict__ cand_key,
+                                                         int32_t* __restrict__ chunk_cnt,
+                                                         uint32_t* __restrict__ chunk_max) {
+    __shared__ int s_wave[kThreads / 64];
+    __shared__ uint32_t s_max[kThreads / 64];
+    const int tid = threadIdx.x;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t base = c * kChunk;
         int64_t k[kPerThread];
         uint32_t live = 0;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const int64_t s = start + (int64_t)j * kThreads + tid;
+            const int64_t s = base + (int64_t)j * kThreads + tid;
             k[j] = s < T.capacity ? T.keys[s] : kEmpty;
             if (k[j] != kEmpty && k[j] != kTomb) live |= 1u << j;
         }
-        const int mine = __popc(live);
-        int incl = mine;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-        }
-        if (lane == 63) s_warp[wid] = incl;
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int w = 0; w < kThreads / 64; ++w) {
-                const int c = s_warp[w];
-                s_warp[w] = run;
-                run += c;
-            }
-            s_base = run ? atomicAdd(&st->n_live, (unsigned long long)run) : 0ull;
-        }
-        __syncthreads();
-        int64_t pos = (int64_t)s_base + s_warp[wid] + (incl - mine);
+        int pos = __popc(live);
+        const int total = block_prefix(pos, s_wave);
+        uint32_t my_max = 0;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             if (live & (1u << j)) {
-                const int64_t s = start + (int64_t)j * kThreads + tid;
-                const uint32_t ls = T.last_seen[s];
+                const uint32_t ls = T.last_seen[base + (int64_t)j * kThreads + tid];
                 my_max = ls > my_max ? ls : my_max;
-                cand_ls[pos] = ls;
-                cand_key[pos] = bias(k[j]);
+                cand_ls[base + pos] = ls;
+                cand_key[base + pos] = bias(k[j]);
                 ++pos;
             }
         }
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint32_t y = __shfl_xor(my_max, off);
+            my_max = y > my_max ? y : my_max;
+        }
+        if (lane_id() == 0) s_max[tid >> 6] = my_max;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t m = 0;
+            for (int w = 0; w < kThreads / 64; ++w) m = s_max[w] > m ? s_max[w] : m;
+            chunk_cnt[c] = total;
+            chunk_max[c] = m;
+        }
         __syncthreads();
     }
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t y = __shfl_xor(my_max, off);
-        my_max = y > my_max ? y : my_max;
+}
+
+// One block: live count, maximum last_seen, k, and a cleared histogram.
+__global__ __launch_bounds__(1024) void k_lru_init(LruState* st, const int32_t* __restrict__ chunk_cnt,
+                                                  const uint32_t* __restrict__ chunk_max, int64_t nchunks,
+                                                  int64_t num, int64_t den) {
+    __shared__ unsigned long long s_sum[1024 / 64];
+    __shared__ uint32_t s_max[1024 / 64];
+    unsigned long long sum = 0;
+    uint32_t mx = 0;
+    for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
+        sum += (unsigned long long)chunk_cnt[c];
+        mx = chunk_max[c] > mx ? chunk_max[c] : mx;
     }
-    if (lane == 0 && my_max) atomicMax(&st->ls_max, my_max);
+    for (int off = 32; off > 0; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        const uint32_t y = __shfl_xor(mx, off);
+        mx = y > mx ? y : mx;
+    }
+    if (lane_id() == 0) {
+        s_sum[threadIdx.x >> 6] = sum;
+        s_max[threadIdx.x >> 6] = mx;
+    }
+    if (threadIdx.x < 256) st->hist[threadIdx.x * kBinStride] = 0u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long L = 0;
+        uint32_t m = 0;
+        for (int w = 0; w < 1024 / 64; ++w) {
+            L += s_sum[w];
+            m = s_max[w] > m ? s_max[w] : m;
+        }
+        st->n_live = (int64_t)L;
+        st->k = ((int64_t)L * num) / den;
+        st->k_rem = st->k;
+        st->ls_max = m;
+        uint32_t d = 1;
+        while (d < 4 && (m >> (8 * d)) != 0u) ++d;
+        st->ls_digits = d;
+        st->ls_prefix = 0u;
+        st->key_prefix = 0ull;
+        st->key_and = ~0ull;
+        st->key_or = 0ull;
+    }
 }
 
-__global__ void k_lru_init(LruState* st, int64_t num, int64_t den) {
-    const int64_t L = (int64_t)st->n_live;
-    st->k = (L * num) / den;
-    st->k_rem = st->k;
-    uint32_t d = 1;
-    while (d < 4 && (st->ls_max >> (8 * d)) != 0u) ++d;
-    st->ls_digits = d;
+// A block's LDS histogram (s_h, 256 bins, complete) is added into the
+// global one; the bins sit kBinStride words apart, one cache line each, so
+// that the blocks' atomics spread over the L2 channels.
+__device__ __forceinline__ void commit_hist(LruState* st, const uint32_t* s_h) {
+    const uint32_t c = s_h[threadIdx.x];
+    if (c) atomicAdd(&st->hist[threadIdx.x * kBinStride], c);
 }
 
-// Histogram of last_seen digit `d` over candidates matching the higher digits.
+// One block of 256 threads after each digit's histogram: a block-wide scan
+// of the 256 bins finds the bucket that holds rank k_rem; the prefix is
+// narrowed and the histogram cleared for the next digit.
+__global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d, int is_key) {
+    __shared__ int64_t s_wave[4];
+    const int t = threadIdx.x, lane = lane_id(), wid = t >> 6;
+    const bool active = st->k > 0 && (is_key || (uint32_t)d < st->ls_digits);
+    const int64_t rem = st->k_rem;                // read before any thread may update it
+    const int64_t c = st->hist[t * kBinStride];
+    st->hist[t * kBinStride] = 0u;
+    if (is_key && active && (((st->key_or ^ st->key_and) >> (8 * d)) & 255u) == 0) {
+        // every tie has this digit (the top digit's histogram is taken all
+        // the same, the others are skipped): the rank within stays
+        if (t == 0) st->key_prefix |= st->key_and & (0xFFull << (8 * d));
+        return;
+    }
+    int64_t incl = c;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    for (int w = 0; w < wid; ++w) incl += s_wave[w];
+    const int64_t excl = incl - c;
+    if (active && excl < rem && (incl >= rem || t == 255)) {
+        st->k_rem = rem - excl;
+        if (is_key) st->key_prefix |= (uint64_t)t << (8 * d);
+        else st->ls_prefix |= (uint32_t)t << (8 * d);
+    }
+}
+
+// Calls f(c, cnt) for each chunk c = blockIdx.x + i * gridDim.x whose count
+// is nonzero.  The block's counts are loaded kThreads at a time in one round
+// (a chain of one dependent load per chunk costs microseconds per block once
+// the lists are sparse).  When zero_out is given, zero_out[c] = 0 is stored
+// for the chunks skipped.  f may use block barriers: cnt is block-uniform.
+template <class F>
+__device__ __forceinline__ void for_my_chunks(const int32_t* __restrict__ cnts, int64_t nchunks,
+                                              int32_t* __restrict__ zero_out, F&& f) {
+    __shared__ int32_t s_cnt[kThreads];
+    const int64_t G = gridDim.x;
+    const int64_t mine = nchunks > (int64_t)blockIdx.x ? (nchunks - blockIdx.x + G - 1) / G : 0;
+    for (int64_t i0 = 0; i0 < mine; i0 += kThreads) {
+        const int64_t i = i0 + threadIdx.x;
+        int32_t cnt = 0;
+        if (i < mine) {
+            cnt = cnts[blockIdx.x + i * G];
+            if (cnt <= 0 && zero_out) zero_out[blockIdx.x + i * G] = 0;
+        }
+        s_cnt[threadIdx.x] = cnt;
+        __syncthreads();
+        const int nb = (int)(mine - i0 < kThreads ? mine - i0 : kThreads);
+        for (int j = 0; j < nb; ++j) {
+            const int c = s_cnt[j];
+            if (c > 0) f(blockIdx.x + (i0 + j) * G, c);
+        }
+        __syncthreads();
+    }
+}
+
+// last_seen digit d over the candidates matching the higher digits.
 __global__ __launch_bounds__(kThreads) void k_lru_hist_ls(LruState* __restrict__ st,
-                                                         const uint32_t* __restrict__ cand_ls, int d) {
-    if ((uint32_t)d >= st->ls_digits) return;
+                                                         const uint32_t* __restrict__ cand_ls,
+                                                         const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
+                                                         int d) {
+    if ((uint32_t)d >= st->ls_digits || st->k <= 0) return;
     __shared__ uint32_t s_h[256];
     s_h[threadIdx.x] = 0u;
     __syncthreads();
-    const int64_t L = (int64_t)st->n_live;
     const uint32_t hi_shift = 8u * (uint32_t)(d + 1);
     const uint32_t want = hi_shift >= 32 ? 0u : (st->ls_prefix >> hi_shift);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < L; i += stride) {
-        const uint32_t x = cand_ls[i];
-        const uint32_t hi = hi_shift >= 32 ? 0u : (x >> hi_shift);
-        if (hi == want) atomicAdd(&s_h[(x >> (8 * d)) & 255u], 1u);
-    }
-    __syncthreads();
-    if (s_h[threadIdx.x]) atomicAdd(&st->hist[threadIdx.x], s_h[threadIdx.x]);
-}
-
-// Histogram of key digit `d` over the tied candidates matching higher digits.
-__global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict__ st,
-                                                          const uint64_t* __restrict__ ties, int d) {
-    __shared__ uint32_t s_h[256];
-    s_h[threadIdx.x] = 0u;
-    __syncthreads();
-    const int64_t L = (int64_t)st->n_ties;
-    const uint32_t hi_shift = 8u * (uint32_t)(d + 1);
-    const uint64_t want = hi_shift >= 64 ? 0ull : (st->key_prefix >> hi_shift);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < L; i += stride) {
-        const uint64_t x = ties[i];
-        const uint64_t hi = hi_shift >= 64 ? 0ull : (x >> hi_shift);
-        if (hi == want) atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
-    }
-    __syncthreads();
-    if (s_h[threadIdx.x]) atomicAdd(&st->hist[threadIdx.x], s_h[threadIdx.x]);
-}
-
-// One block of 256: pick the bucket holding rank k_rem, narrow the prefix,
-// clear the histogram for the next digit.
-__global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d, int is_key) {
-    __shared__ uint32_t s_c[256];
-    const int t = threadIdx.x;
-    const bool active = is_key ? true : ((uint32_t)d < st->ls_digits);
-    const uint32_t h = st->hist[t];
-    s_c[t] = h;
-    __syncthreads();
-    if (t == 0 && active && st->k > 0) {
-        int64_t rem = st->k_rem;
-        int b = 0;
-        for (; b < 255; ++b) {
-            if ((int64_t)s_c[b] >= rem) break;
-            rem -= s_c[b];
+    for_my_chunks(chunk_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
+        for (int j = threadIdx.x; j < cnt; j += kThreads) {
+            const uint32_t x = cand_ls[c * kChunk + j];
+            const uint32_t hi = hi_shift >= 32 ? 0u : (x >> hi_shift);
+            if (hi == want) atomicAdd(&s_h[(x >> (8 * d)) & 255u], 1u);
         }
-        st->k_rem = rem;
-        if (is_key) st->key_prefix |= (uint64_t)b << (8 * d);
-        else st->ls_prefix |= (uint32_t)b << (8 * d);
-    }
+    });
     __syncthreads();
-    st->hist[t] = 0u;
+    commit_hist(st, s_h);
 }
 
+// Candidates tying on the selected last_seen, compacted per chunk; the
+// histogram of their top key digit (7); and the AND and OR of all their keys
+// (digits where the two agree are the same in every tie and need no pass).
 __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st,
                                                       const uint32_t* __restrict__ cand_ls,
                                                       const uint64_t* __restrict__ cand_key,
-                                                      uint64_t* __restrict__ ties) {
-    const int64_t L = (int64_t)st->n_live;
-    if (st->k <= 0) return;
-    const uint32_t thr = st->ls_prefix;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i0 = blockIdx.x * (int64_t)kThreads; i0 < L; i0 += stride) {
-        const int64_t i = i0 + threadIdx.x;
-        const bool tie = i < L && cand_ls[i] == thr;
-        const uint64_t m = __ballot(tie);
-        if (!m) continue;
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        unsigned long long b = 0;
-        if (lane_id() == leader) b = atomicAdd(&st->n_ties, (unsigned long long)__popcll(m));
-        b = __shfl(b, leader);
-        if (tie) ties[b + __popcll(m & lanemask_lt())] = cand_key[i];
+                                                      const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
+                                                      uint64_t* __restrict__ ties, int32_t* __restrict__ tie_cnt) {
+    __shared__ int s_wave[kThreads / 64];
+    __shared__ uint32_t s_h[256];
+    __shared__ unsigned long long s_and[kThreads / 64], s_or[kThreads / 64];
+    if (st->k <= 0) {
+        for (int64_t c = blockIdx.x * (int64_t)kThreads + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * kThreads)
+            tie_cnt[c] = 0;
+        return;
     }
+    const uint32_t thr = st->ls_prefix;
+    s_h[threadIdx.x] = 0u;
+    unsigned long long k_and = ~0ull, k_or = 0ull;
+    __syncthreads();
+    for_my_chunks(chunk_cnt, nchunks, tie_cnt, [&](int64_t c, int cnt) {
+        int run = 0;
+        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
+            const int j = j0 + threadIdx.x;
+            const bool tie = j < cnt && cand_ls[c * kChunk + j] == thr;
+            uint64_t key = 0;
+            if (tie) {
+                key = cand_key[c * kChunk + j];
+                atomicAdd(&s_h[(uint32_t)(key >> 56)], 1u);
+                k_and &= key;
+                k_or |= key;
+            }
+            int pos = tie ? 1 : 0;
+            const int tot = block_prefix(pos, s_wave);
+            if (tie) ties[c * kChunk + run + pos] = key;
+            run += tot;
+        }
+        if (threadIdx.x == 0) tie_cnt[c] = run;
+    });
+    for (int off = 32; off > 0; off >>= 1) {
+        k_and &= __shfl_xor(k_and, off);
+        k_or |= __shfl_xor(k_or, off);
+    }
+    if (lane_id() == 0) {
+        s_and[threadIdx.x >> 6] = k_and;
+        s_or[threadIdx.x >> 6] = k_or;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kThreads / 64; ++w) {
+            k_and &= s_and[w];
+            k_or |= s_or[w];
+        }
+        if (k_and != ~0ull) atomicAnd(&st->key_and, k_and);
+        if (k_or != 0ull) atomicOr(&st->key_or, k_or);
+    }
+    commit_hist(st, s_h);
 }
 
-__global__ __launch_bounds__(kThreads) void k_lru_emit(LruState* __restrict__ st,
-                                                      const uint32_t* __restrict__ cand_ls,
-                                                      const uint64_t* __restrict__ cand_key,
-                                                      int64_t* __restrict__ victims, int64_t cap,
-                                                      int64_t* __restrict__ n_victims) {
-    const int64_t L = (int64_t)st->n_live;
+// Key digit d over the tied candidates matching the higher digits.  Skipped
+// when every tie has the same digit d.  When a higher digit varied among the
+// ties, the entries that match the prefix chosen so far are first compacted
+// in place in each chunk, so the passes after it read only those.
+__global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict__ st, uint64_t* __restrict__ ties,
+                                                          int32_t* __restrict__ tie_cnt, int64_t nchunks, int d) {
+    if (st->k <= 0) return;
+    const uint64_t diff = st->key_or ^ st->key_and;
+    if (((diff >> (8 * d)) & 255u) == 0) return;
+    const bool compact = (diff >> (8 * (d + 1))) != 0;     // d < 7 here: digit 7 is counted by k_lru_ties
+    __shared__ int s_wave[kThreads / 64];
+    __shared__ uint32_t s_h[256];
+    s_h[threadIdx.x] = 0u;
+    __syncthreads();
+    const uint64_t want = st->key_prefix >> (8 * (d + 1));
+    for_my_chunks(tie_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
+        if (!compact) {
+            for (int j = threadIdx.x; j < cnt; j += kThreads) {
+                const uint64_t x = ties[c * kChunk + j];
+                atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
+            }
+            return;
+        }
+        // in place: the writes of a round land below the round's reads,
+        // and block_prefix's barriers order every read before them
+        int run = 0;
+        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
+            const int j = j0 + threadIdx.x;
+            uint64_t x = 0;
+            bool keep = false;
+            if (j < cnt) {
+                x = ties[c * kChunk + j];
+                keep = (x >> (8 * (d + 1))) == want;
+                if (keep) atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
+            }
+            int pos = keep ? 1 : 0;
+            const int tot = block_prefix(pos, s_wave);
+            if (keep) ties[c * kChunk + run + pos] = x;
+            run += tot;
+        }
+        if (threadIdx.x == 0) tie_cnt[c] = run;
+    });
+    __syncthreads();
+    commit_hist(st, s_h);
+}
+
+__device__ __forceinline__ bool is_victim(uint32_t ls, uint64_t key, uint32_t thr, uint64_t kthr) {
+    return ls < thr || (ls == thr && key <= kthr);
+}
+
+__global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* __restrict__ st,
+                                                               const uint32_t* __restrict__ cand_ls,
+                                                               const uint64_t* __restrict__ cand_key,
+                                                               const int32_t* __restrict__ chunk_cnt,
+                                                               int64_t nchunks, int32_t* __restrict__ vic_cnt) {
+    __shared__ int s_wave[kThreads / 64];
     const bool any = st->k > 0;
     const uint32_t thr = st->ls_prefix;
     const uint64_t kthr = st->key_prefix;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int cnt = any ? chunk_cnt[c] : 0;
+        int mine = 0;
+        for (int j = threadIdx.x; j < cnt; j += kThreads)
+            mine += is_victim(cand_ls[c * kChunk + j], cand_key[c * kChunk + j], thr, kthr);
+        const int tot = block_prefix(mine, s_wave);
+        if (threadIdx.x == 0) vic_cnt[c] = tot;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restrict__ st,
+                                                      const uint32_t* __restrict__ cand_ls,
+                                                      const uint64_t* __restrict__ cand_key,
+                                                      const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
+                                                      const int32_t* __restrict__ vic_off, int64_t* __restrict__ victims,
+                                                      int64_t cap, int64_t* __restrict__ n_victims) {
+    __shared__ int s_wave[kThreads / 64];
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_victims = st->k;
-    if (!any) return;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i0 = blockIdx.x * (int64_t)kThreads; i0 < L; i0 += stride) {
-        const int64_t i = i0 + threadIdx.x;
-        bool v = false;
-        uint64_t key = 0;
-        if (i < L) {
-            const uint32_t ls = cand_ls[i];
-            key = cand_key[i];
-            v = ls < thr || (ls == thr && key <= kthr);
+    const bool any = st->k > 0;
+    const uint32_t thr = st->ls_prefix;
+    const uint64_t kthr = st->key_prefix;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int cnt = any ? chunk_cnt[c] : 0;
+        int64_t run = vic_off[c];
+        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
+            const int j = j0 + threadIdx.x;
+            uint64_t key = 0;
+            bool v = false;
+            if (j < cnt) {
+                key = cand_key[c * kChunk + j];
+                v = is_victim(cand_ls[c * kChunk + j], key, thr, kthr);
+            }
+            int pos = v ? 1 : 0;
+            const int tot = block_prefix(pos, s_wave);
+            if (v && run + pos < cap) victims[run + pos] = (int64_t)(key ^ 0x8000000000000000ull);
+            run += tot;
         }
-        const uint64_t m = __ballot(v);
-        if (!m) continue;
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        unsigned long long b = 0;
-        if (lane_id() == leader) b = atomicAdd(&st->n_out, (unsigned long long)__popcll(m));
-        b = __shfl(b, leader);
-        const int64_t pos = (int64_t)b + __popcll(m & lanemask_lt());
-        if (v && pos < cap) victims[pos] = (int64_t)(key ^ 0x8000000000000000ull);
     }
 }
 
@@ -284,25 +484,40 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     HTL_REQUIRE(n_victims_dev && aligned(n_victims_dev, 8) && ws && aligned(ws, 256) &&
                     (victims_cap == 0 || (victims && aligned(victims, 8))),
                 "ht_lru_select: null or misaligned pointer");
+    HTL_REQUIRE(t->capacity_log2 <= 30, "ht_lru_select: needs capacity_log2 <= 30");
     LruWs w = lru_layout(t->dev.capacity, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "ht_lru_select: workspace too small");
     const TableDev& T = t->dev;
-    const unsigned gscan = grid_for(T.capacity, kThreads * kPerThread, 1 << 15);
-    const unsigned gcand = grid_for(T.capacity, kThreads * 8, 1 << 14);
-    hipLaunchKernelGGL(k_lru_reset, dim3(1), dim3(256), 0, stream, w.st);
-    hipLaunchKernelGGL(k_lru_collect, dim3(gscan), dim3(kThreads), 0, stream, T, w.st, w.cand_ls, w.cand_key);
-    hipLaunchKernelGGL(k_lru_init, dim3(1), dim3(1), 0, stream, w.st, num, den);
-    for (int d = 3; d >= 0; --d) {
-        hipLaunchKernelGGL(k_lru_hist_ls, dim3(gcand), dim3(kThreads), 0, stream, w.st, w.cand_ls, d);
+    const unsigned gchunk = grid_for(w.nchunks, 1, 1 << 16);
+    const unsigned ghist = grid_for(w.nchunks, 1, kHistBlocks);
+    hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_key,
+                       w.chunk_cnt, w.chunk_max);
+    hipLaunchKernelGGL(k_lru_init, dim3(1), dim3(1024), 0, stream, w.st, w.chunk_cnt, w.chunk_max, w.nchunks, num,
+                       den);
+    // last_seen digits: as many as the largest step stamped needs (the
+    // kernels also skip digits above the live maximum)
+    int ls_digits = 1;
+    while (ls_digits < 4 && (t->max_step >> (8 * ls_digits)) != 0u) ++ls_digits;
+    for (int d = ls_digits - 1; d >= 0; --d) {
+        hipLaunchKernelGGL(k_lru_hist_ls, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.chunk_cnt,
+                           w.nchunks, d);
         hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 0);
     }
-    hipLaunchKernelGGL(k_lru_ties, dim3(gcand), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key, w.ties);
-    for (int d = 7; d >= 0; --d) {
-        hipLaunchKernelGGL(k_lru_hist_key, dim3(gcand), dim3(kThreads), 0, stream, w.st, w.ties, d);
+    hipLaunchKernelGGL(k_lru_ties, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key,
+                       w.chunk_cnt, w.nchunks, w.ties, w.tie_cnt);
+    hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, 7, 1);
+    for (int d = 6; d >= 0; --d) {
+        hipLaunchKernelGGL(k_lru_hist_key, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.ties, w.tie_cnt,
+                           w.nchunks, d);
         hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 1);
     }
-    hipLaunchKernelGGL(k_lru_emit, dim3(gcand), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key, victims,
-                       victims_cap, n_victims_dev);
+    hipLaunchKernelGGL(k_lru_count_victims, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key,
+                       w.chunk_cnt, w.nchunks, w.vic_cnt);
+    htl_status st = scan_exclusive_i32(w.vic_cnt, w.vic_off, w.nchunks, nullptr, kScanIdentity, 1, w.scan_tmp,
+                                       stream);
+    if (st != HTL_OK) return st;
+    hipLaunchKernelGGL(k_lru_emit, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key, w.chunk_cnt,
+                       w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev);
     return check_launch("ht_lru_select");
 }
 

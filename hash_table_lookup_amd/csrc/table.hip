@@ -291,6 +291,7 @@ htl_status ht_destroy(htl_table* t) {
 htl_status ht_clear(htl_table* t, hipStream_t stream) {
     clear_error();
     HTL_REQUIRE(t != nullptr, "ht_clear: null table");
+    t->max_step = 0u;
     return fill_keys_empty(t->dev, stream);
 }
 
@@ -303,6 +304,7 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
     HTL_REQUIRE(keys && slots && status, "ht_find_or_insert: null keys/slots/status");
     HTL_REQUIRE(aligned(keys, 8) && aligned(slots, 4) && (!n_dev || aligned(n_dev, 8)),
                 "ht_find_or_insert: misaligned pointer");
+    if (step > t->max_step) t->max_step = step;
     const int G = probe_lanes();
     const unsigned grid = grid_for(n_max, kProbeBlock / G);
 #define HTL_FOI(GG)                                                                                        \

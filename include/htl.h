@@ -137,7 +137,7 @@ htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32
  * compared as uint32 and keys as int64.  [MTGenRec] Abstract (deletions in
  * real time); [MTGR] section 5 (metadata per key, key scanning).  The pages
  * name no policy: least-recently-used with a key tie-break is this library's.
- * Needs HT_META_LAST_SEEN.
+ * Needs HT_META_LAST_SEEN and capacity_log2 <= 30 (HTL_ERR_INVALID otherwise).
  *   victims        int64[victims_cap] out: the victim keys, unspecified order.
  *   n_victims_dev  int64 out: the number of victims k (also when k exceeds
  *                  victims_cap, in which case victims holds an arbitrary
@@ -217,7 +217,10 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
  * emb_grad_segment_sum -- backward gradient dedup: out[u] = sum of grad[i]
  * over the IDs with inverse[i] == u, accumulated in fp32 (the backward of the
  * deduplicated lookup; summation order is unspecified).
- *   grad          float[n][dim]; inverse int32[n] with values < U.
+ *   grad          float[n][dim]; inverse int32[n] with values < U; entries
+ *                 outside [0, U) contribute nowhere.  n < 2^31 - 1024,
+ *                 1 <= dim <= 65536, 0 <= u_max <= n (HTL_ERR_INVALID
+ *                 otherwise).
  *   n_unique_dev  device int64 U (nullable: then U = u_max); u_max host bound.
  *   out           float[u_max][dim]: rows 0..U-1 written, the rest untouched.
  *   ws, ws_bytes  at least segsum_workspace_bytes(n, u_max, dim) bytes,

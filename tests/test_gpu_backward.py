@@ -61,13 +61,14 @@ def test_segment_sum_backward_workload_small(htl, orc):
     _segsum_check(htl, orc, w.keys, w.grad)
 
 
-def test_adam_decoupled(htl, orc):
+@pytest.mark.parametrize("dim,cap_log2", [(128, 18), (6, 16), (1028, 16)])
+def test_adam_decoupled(htl, orc, dim, cap_log2):
     """Each step is checked from identical states: the oracle's array Adam gets
     the GPU table's theta, m, v before the step and the GPU's own summed
     gradient.  Tolerance: 1e-5 times the magnitudes of the terms each update
     adds (m and theta updates can cancel), so |err| <= 1e-5 * (|b1 m| + |(1-b1) g|)
     for m, likewise for v, and 1e-5 * (|theta| + |theta' - theta|) for theta."""
-    w = workloads.backward(n=1 << 15, dim=128, capacity_log2=18)
+    w = workloads.backward(n=1 << 15, dim=dim, capacity_log2=cap_log2)
     lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
     table = htl.Table(w.capacity_log2, w.dim, "f32", adam=True)
     keys = torch.from_numpy(w.keys).cuda()

@@ -79,3 +79,27 @@ def test_lru_requires_metadata(htl):
     table = htl.Table(6, 4, "f32")
     with pytest.raises(htl.HTLError):
         table.lru_select(1, 20)
+
+
+def test_lru_many_ties(htl, orc):
+    # 40,000 keys share the newest last_seen, so the victim cut falls inside
+    # one last_seen value: the key digits decide, over ties spread across all
+    # 16 chunks of 4096 slots; half the keys are small (their top digits all
+    # equal), half span the whole signed range
+    table = htl.Table(16, 4, "bf16", last_seen=True)
+    otab = orc.Table(1 << 16, 4, orc.BF16)
+    rng = np.random.default_rng(9)
+    old = rng.integers(-(1 << 62), 1 << 62, 10_000).astype(np.int64)
+    small = np.arange(20_000, dtype=np.int64)
+    wide = rng.integers(-(1 << 63), (1 << 63) - 1, 20_000, dtype=np.int64)
+    new = np.unique(np.concatenate([small, wide]))
+    old = np.setdiff1d(old, new)
+    for ks, step in ((old, 3), (new, 5)):
+        table.find_or_insert(torch.from_numpy(ks).cuda(), step=step)
+        otab.find_or_insert(ks, step=step)
+    for num, den in ((1, 2), (3, 4), (1, 5), (999, 1000)):
+        victims, nv = table.lru_select(num, den)
+        k = int(nv.item())
+        ref = otab.lru_victims(num, den)
+        assert k == ref.size
+        assert np.array_equal(np.sort(to_np(victims)[:k]), np.sort(ref))

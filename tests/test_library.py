@@ -72,6 +72,7 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.dedup_unique_inverse(None, 1 << 31, None, None, None, None, 0, None) == INVALID
     assert L.emb_gather_pool(None, None, None, 1, None, 0, 0, None, None) == INVALID
     assert L.emb_grad_segment_sum(None, None, 10, None, 11, 4, None, None, 0, None) == INVALID
+    assert L.emb_grad_segment_sum(None, None, (1 << 31) - 1024, None, 1, 4, None, None, 0, None) == INVALID
     assert L.emb_grad_segment_sum(None, None, 10, None, 5, 0, None, None, 0, None) == INVALID
     assert L.emb_rowwise_adam(None, None, None, 1, None, 1e-3, 0.9, 0.999, 1e-8, 1, None) == INVALID
     assert L.ht_lru_select(None, 1, 20, None, 0, None, None, 0, None) == INVALID
