@@ -20,7 +20,7 @@
 //   every tile's atomics queue on the same L2 channels; measured on MI355X
 //   with a Zipf(1.2) batch of 2^23 IDs the count pass ran 3x slower);
 //   fill   -- perm[offset[u] + place] = i (CSR of IDs grouped by unique);
-//   small  -- one wavefront per segment of <= kSmallMax IDs sums its rows;
+//   small  -- one team of lanes per segment of <= kSmallMax IDs sums its rows;
 //   large  -- longer segments (Zipf's head: the hottest key of a 2^23-ID
 //             Zipf(1.2) batch owns ~18% of all rows) are cut into kChunk-row
 //             chunks, one workgroup each, and the chunk partials are then
@@ -39,7 +39,7 @@ constexpr int kCThreads = 256;
 constexpr int kCPerThread = kCTile / kCThreads;
 constexpr int kCCap = 2 * kCTile;          // LDS hash slots
 constexpr int kCCapLog2 = 12;
-constexpr int kSmallMax = 256;             // longest segment summed by one wavefront
+constexpr int kSmallMax = 32;              // longest segment summed by one team
 constexpr int kChunk = 1024;               // rows per workgroup in long segments
 constexpr int kRBlock = 256;
 constexpr int kSpread = 1024;              // S of the spread segment order
@@ -57,11 +57,12 @@ struct SegWs {
     int32_t* rel;          // [n]
     int32_t* perm;         // [n]
     int32_t* large;        // [large_max]
-    int32_t* large_off;    // [large_max + 1]
+    int32_t* large_off;    // [large_max + 1]: chunks before each listed segment
+    int32_t* part_off;     // [large_max + 1]: the same, counting multi-chunk segments only
     unsigned long long* n_large;
     void* scan_tmp;
-    float* partial;        // [max_chunks][dim]
-    int64_t large_max, max_chunks;
+    float* partial;        // [part_max][dim]
+    int64_t large_max, max_chunks, part_max;
     size_t bytes;
 };
 
@@ -69,6 +70,7 @@ SegWs seg_layout(int64_t n, int64_t u_max, int dim, char* base) {
     SegWs w{};
     w.large_max = n / (kSmallMax + 1) + 1;
     w.max_chunks = n / kChunk + w.large_max;
+    w.part_max = 2 * (n / kChunk) + 2;     // multi-chunk segments hold > kChunk IDs each
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char* p = base ? base + off : nullptr;
@@ -83,9 +85,10 @@ SegWs seg_layout(int64_t n, int64_t u_max, int dim, char* base) {
     w.perm = (int32_t*)take((size_t)n * 4);
     w.large = (int32_t*)take((size_t)w.large_max * 4);
     w.large_off = (int32_t*)take((size_t)(w.large_max + 1) * 4);
+    w.part_off = (int32_t*)take((size_t)(w.large_max + 1) * 4);
     w.n_large = (unsigned long long*)take(8);
     w.scan_tmp = take(scan_temp_bytes(q_max));
-    w.partial = (float*)take((size_t)w.max_chunks * dim * 4);
+    w.partial = (float*)take((size_t)w.part_max * dim * 4);
     w.bytes = off;
     return w;
 }
@@ -220,8 +223,11 @@ __device__ __forceinline__ void store_row(float* __restrict__ dst, int vpr, int 
     }
 }
 
-// One wavefront per segment (in spread order); segments longer than
-// kSmallMax are listed, by their spread index, for the chunked path.
+// One team of TEAM lanes per segment (in spread order): most segments of a
+// Zipf batch hold one to a few IDs, so a team, not a whole wavefront, takes
+// each, and a wavefront keeps 64/TEAM segments' rows in flight.  Segments
+// longer than kSmallMax are listed, by their spread index, for the chunked
+// path.
 template <int TEAM, int QMAX>
 __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__ grad, int vpr,
                                                       const int32_t* __restrict__ perm,
@@ -231,43 +237,37 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
                                                       unsigned long long* __restrict__ n_large) {
     const int64_t U = dev_count(u_max, n_dev);
     const int64_t C = spread_c(U);
-    const int lane = lane_id();
-    const int tl = lane & (TEAM - 1);
-    const int team = lane / TEAM;
-    constexpr int TEAMS = 64 / TEAM;
-    const int64_t wave = (blockIdx.x * (int64_t)kRBlock + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kRBlock) >> 6;
-    for (int64_t q = wave; q < kSpread * C; q += nwaves) {
+    const int tl = threadIdx.x & (TEAM - 1);
+    const int64_t team = (blockIdx.x * (int64_t)kRBlock + threadIdx.x) / TEAM;
+    const int64_t nteams = (int64_t)gridDim.x * kRBlock / TEAM;
+    for (int64_t q = team; q < kSpread * C; q += nteams) {
         const int64_t u = spread_u(q, C);
         if (u >= U) continue;                    // a hole of the spread order
         const int32_t beg = seg_off[q], end = seg_off[q + 1];
         if (end - beg > kSmallMax) {
-            if (lane == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
+            if (tl == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
             continue;
         }
         float acc[QMAX][4];
 #pragma unroll
         for (int a = 0; a < QMAX; ++a) acc[a][0] = acc[a][1] = acc[a][2] = acc[a][3] = 0.0f;
-        sum_rows<TEAM, QMAX>(grad, vpr, perm, beg, end, team, TEAMS, tl, acc);
-#pragma unroll
-        for (int off = TEAM; off < 64; off <<= 1)
-#pragma unroll
-            for (int a = 0; a < QMAX; ++a)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[a][e] += __shfl_xor(acc[a][e], off);
-        if (team == 0) store_row<TEAM, QMAX>(out + u * (int64_t)vpr * 4, vpr, tl, acc);
+        sum_rows<TEAM, QMAX>(grad, vpr, perm, beg, end, 0, 1, tl, acc);
+        store_row<TEAM, QMAX>(out + u * (int64_t)vpr * 4, vpr, tl, acc);
     }
 }
 
-// One block: large_off = exclusive scan of ceil(count / kChunk) over the list.
+// One block: large_off = exclusive scan of the chunk counts ceil(count /
+// kChunk) over the list, part_off = the same over the segments of more than
+// one chunk only (a one-chunk segment's sum goes straight to the output).
 __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__ large,
                                                     const unsigned long long* __restrict__ n_large,
                                                     const int32_t* __restrict__ seg_off,
-                                                    int32_t* __restrict__ large_off) {
-    __shared__ int32_t s_warp[16];
-    __shared__ int32_t s_carry;
+                                                    int32_t* __restrict__ large_off,
+                                                    int32_t* __restrict__ part_off) {
+    __shared__ int32_t s_warp[16], s_warp2[16];
+    __shared__ int32_t s_carry, s_carry2;
     const int64_t nl = (int64_t)*n_large;
-    if (threadIdx.x == 0) s_carry = 0;
+    if (threadIdx.x == 0) s_carry = s_carry2 = 0;
     __syncthreads();
     for (int64_t b0 = 0; b0 <= nl; b0 += 1024) {
         const int64_t i = b0 + threadIdx.x;
@@ -276,41 +276,63 @@ __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__
             const int32_t q = large[i];
             x = (seg_off[q + 1] - seg_off[q] + kChunk - 1) / kChunk;
         }
+        const int32_t x2 = x > 1 ? x : 0;
         const int lane = lane_id();
         const int wid = threadIdx.x >> 6;
-        int32_t incl = x;
+        int32_t incl = x, incl2 = x2;
         for (int off = 1; off < 64; off <<= 1) {
             const int32_t y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
+            const int32_t y2 = __shfl_up(incl2, off);
+            if (lane >= off) {
+                incl += y;
+                incl2 += y2;
+            }
         }
-        if (lane == 63) s_warp[wid] = incl;
+        if (lane == 63) {
+            s_warp[wid] = incl;
+            s_warp2[wid] = incl2;
+        }
         __syncthreads();
-        int32_t before = 0, total = 0;
+        int32_t before = 0, total = 0, before2 = 0, total2 = 0;
         for (int w = 0; w < 16; ++w) {
-            if (w < wid) before += s_warp[w];
+            if (w < wid) {
+                before += s_warp[w];
+                before2 += s_warp2[w];
+            }
             total += s_warp[w];
+            total2 += s_warp2[w];
         }
-        const int32_t carry = s_carry;
-        if (i <= nl) large_off[i] = carry + before + incl - x;
+        const int32_t carry = s_carry, carry2 = s_carry2;
+        if (i <= nl) {
+            large_off[i] = carry + before + incl - x;
+            part_off[i] = carry2 + before2 + incl2 - x2;
+        }
         __syncthreads();
-        if (threadIdx.x == 0) s_carry = carry + total;
+        if (threadIdx.x == 0) {
+            s_carry = carry + total;
+            s_carry2 = carry2 + total2;
+        }
         __syncthreads();
     }
 }
 
-// One workgroup per chunk of a long segment -> partial[chunk].
+// One workgroup per chunk of a long segment -> partial[part_off + chunk],
+// or straight to out[u] when the segment is a single chunk.
 template <int TEAM, int QMAX>
 __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restrict__ grad, int vpr,
                                                          const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ seg_off,
                                                          const int32_t* __restrict__ large,
                                                          const unsigned long long* __restrict__ n_large,
-                                                         const int32_t* __restrict__ large_off, int64_t max_chunks,
-                                                         float* __restrict__ partial) {
+                                                         const int32_t* __restrict__ large_off,
+                                                         const int32_t* __restrict__ part_off, int64_t max_chunks,
+                                                         int64_t u_max, const int64_t* __restrict__ n_dev,
+                                                         float* __restrict__ partial, float* __restrict__ out) {
     constexpr int TEAMS = kRBlock / TEAM;
     __shared__ float s_acc[TEAMS][QMAX * TEAM * 4];
     const int64_t nl = (int64_t)*n_large;
     const int32_t total = large_off[nl];
+    const int64_t C = spread_c(dev_count(u_max, n_dev));
     const int tl = threadIdx.x & (TEAM - 1);
     const int team = threadIdx.x / TEAM;
     for (int64_t c = blockIdx.x; c < total && c < max_chunks; c += gridDim.x) {
@@ -334,18 +356,21 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) s_acc[team][(a * TEAM + tl) * 4 + e] = acc[a][e];
         __syncthreads();
-        float* dst = partial + c * (int64_t)vpr * 4;
+        float* dst = large_off[lo + 1] - large_off[lo] == 1
+                         ? out + spread_u(q, C) * vpr * 4
+                         : partial + (int64_t)(part_off[lo] + part) * vpr * 4;
         for (int e = threadIdx.x; e < vpr * 4; e += kRBlock) {
             const int a = (e / 4) / TEAM, l = (e / 4) % TEAM;
             float s = 0.0f;
-            for (int q = 0; q < TEAMS; ++q) s += s_acc[q][(a * TEAM + l) * 4 + (e & 3)];
+            for (int t = 0; t < TEAMS; ++t) s += s_acc[t][(a * TEAM + l) * 4 + (e & 3)];
             dst[e] = s;
         }
         __syncthreads();
     }
 }
 
-// One workgroup per long segment: out[u] = sum of its chunk partials.  The
+// One workgroup per segment of several chunks: out[u] = sum of its chunk
+// partials.  The
 // block's kCombThreads threads are vpr-wide column lanes times groups; each
 // group adds every groups-th partial (several loads in flight per thread),
 // then the groups are added in LDS.  The hottest segment of a Zipf batch has
@@ -355,7 +380,7 @@ constexpr int kCombThreads = 1024;
 __global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __restrict__ partial, int vpr,
                                                                int lanes, const int32_t* __restrict__ large,
                                                                const unsigned long long* __restrict__ n_large,
-                                                               const int32_t* __restrict__ large_off, int64_t u_max,
+                                                               const int32_t* __restrict__ part_off, int64_t u_max,
                                                                const int64_t* __restrict__ n_dev,
                                                                u32x4* __restrict__ out) {
     __shared__ float4 s_red[kCombThreads];
@@ -364,8 +389,9 @@ __global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __r
     const int groups = kCombThreads / lanes;
     const int l = threadIdx.x % lanes, g = threadIdx.x / lanes;
     for (int64_t i = blockIdx.x; i < nl; i += gridDim.x) {
+        const int32_t c0 = part_off[i], c1 = part_off[i + 1];
+        if (c1 == c0) continue;                  // a single chunk, already written
         const int64_t u = spread_u(large[i], C);
-        const int32_t c0 = large_off[i], c1 = large_off[i + 1];
         for (int v0 = 0; v0 < vpr; v0 += lanes) {
             const int v = v0 + l;
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -435,16 +461,17 @@ __global__ void k_seg_elem(const float* __restrict__ grad, int dim, const int32_
 template <int TEAM, int QMAX>
 void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, const int64_t* n_dev, float* out,
                    hipStream_t s) {
-    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX>), dim3(grid_for(u_max + kSpread, kRBlock / 64)), dim3(kRBlock), 0,
+    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM)), dim3(kRBlock), 0,
                        s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, out, w.large, w.n_large);
-    hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off);
+    hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off,
+                       w.part_off);
     hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX>), dim3(grid_for(w.max_chunks, 1, 1 << 16)), dim3(kRBlock), 0,
-                       s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off,
-                       w.max_chunks, w.partial);
+                       s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off, w.part_off,
+                       w.max_chunks, u_max, n_dev, w.partial, out);
     int lanes = 1;
     while (lanes < vpr && lanes < kCombThreads / 4) lanes <<= 1;
     hipLaunchKernelGGL(k_large_combine, dim3(grid_for(w.large_max, 1, 1 << 14)), dim3(kCombThreads), 0, s,
-                       (const u32x4*)w.partial, vpr, lanes, w.large, w.n_large, w.large_off, u_max, n_dev,
+                       (const u32x4*)w.partial, vpr, lanes, w.large, w.n_large, w.part_off, u_max, n_dev,
                        (u32x4*)out);
 }
 

@@ -15,8 +15,8 @@
 //     atomics into at most one per tile.
 //   stage 2 (k_dedup_claim, [k_dedup_count], k_dedup_assign): every tile
 //     survivor is inserted into a device-wide open-addressing set
-//     (next_pow2(2n) slots, 64-bit CAS).  One survivor per key owns it: the
-//     one whose CAS inserted it, or, in ordered mode, the one in the lowest
+//     (next_pow2(3n/2 + 1) slots, 64-bit CAS).  One survivor per key owns
+//     it: the one whose CAS inserted it, or, in ordered mode, the one in the lowest
 //     tile (atomicMin).  Per-tile counts of owned keys are prefix-summed and
 //     owned keys take dense ids in tile order -- no counter atomics.  In
 //     ordered mode the ids, hence `unique`, follow the order of first
@@ -27,8 +27,10 @@
 //
 // Both sets probe with an odd step over a power-of-two capacity, so by
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
-// 2n slots it always ends at a free slot.  Every int64 is a valid key: the
-// value -1, which both sets use as their empty marker, is carried out of band.
+// more than 3n/2 slots it always ends at a free slot (load at most 2/3: the
+// set is cleared on every call, so its size is traded against that clear).
+// Every int64 is a valid key: the value -1, which both sets use as their
+// empty marker, is carried out of band.
 #include "scan.h"
 #include "tile_dedup.h"
 
@@ -56,7 +58,7 @@ DedupWs layout(int64_t n, char* base) {
     DedupWs w{};
     const int64_t ntiles = ceil_div(n, kTile);
     uint64_t cap = 256;
-    while (cap < (uint64_t)(2 * n)) cap <<= 1;
+    while (cap <= (uint64_t)(n + n / 2)) cap <<= 1;
     w.cap = cap;
     size_t off = 0;
     auto take = [&](size_t bytes) {
