@@ -64,9 +64,12 @@ _SIGNATURES = {
     "segsum_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
     "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
+    "segsum_adam_workspace_bytes": [_I64, _I64, _I32],
+    "emb_grad_segment_sum_adam": [_P, _P, _P, _P, _I64, _P, _I64, _F, _F, _F, _F, _I64, _P, _SZ, _P],
     "htl_last_error": [],
 }
-_SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes"}
+_SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes",
+               "segsum_adam_workspace_bytes"}
 EXPORTED = tuple(_SIGNATURES)
 
 _lib = None
@@ -299,6 +302,24 @@ def rowwise_adam(table: Table, slots: torch.Tensor, g: torch.Tensor,
         n_unique = _dev(n_unique, torch.int64, "n_unique")
     _check(lib().emb_rowwise_adam(table.handle, _ptr(slots), _ptr(g), slots.numel(),
                                   _ptr(n_unique), lr, b1, b2, eps, step, _stream()))
+
+
+def segment_sum_adam(table: Table, slots: torch.Tensor, grad: torch.Tensor, inverse: torch.Tensor,
+                     n_unique: Optional[torch.Tensor], u_max: int, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8,
+                     step=1):
+    """Segment-sum of grad by inverse, then Adam on each unique key's table row,
+    without writing the summed gradients (emb_grad_segment_sum_adam)."""
+    slots = _dev(slots, torch.int32, "slots")
+    grad = _dev(grad, torch.float32, "grad")
+    inverse = _dev(inverse, torch.int32, "inverse")
+    n = grad.shape[0]
+    if n_unique is not None:
+        n_unique = _dev(n_unique, torch.int64, "n_unique")
+    nb = lib().segsum_adam_workspace_bytes(n, u_max, table.dim)
+    ws = _workspace("segsum_adam", nb, grad.device)
+    _check(lib().emb_grad_segment_sum_adam(table.handle, _ptr(slots), _ptr(grad), _ptr(inverse), n,
+                                           _ptr(n_unique), u_max, lr, b1, b2, eps, step, _ptr(ws), nb,
+                                           _stream()))
 
 
 # ----------------------------------------------------------------- helpers --

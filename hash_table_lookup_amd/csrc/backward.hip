@@ -173,6 +173,76 @@ __global__ void k_seg_fill(const int32_t* __restrict__ inverse, const int32_t* _
     }
 }
 
+// Adam on one element: contraction off, so every product and sum rounds on
+// its own as written (the same arithmetic in every kernel that applies it).
+__device__ __forceinline__ void adam_elem(float& th, float& mo, float& vo, float gj, float b1, float b2, float omb1,
+                                          float omb2, float lr, float eps, float c1, float c2) {
+#pragma clang fp contract(off)
+    const float mj = b1 * mo + omb1 * gj;
+    const float vj = b2 * vo + omb2 * (gj * gj);
+    const float mhat = mj / c1;
+    const float vhat = vj / c2;
+    th = th - lr * (mhat / (sqrtf(vhat) + eps));
+    mo = mj;
+    vo = vj;
+}
+
+// Where a finished 16-byte vector v of unique u's summed gradient goes:
+// into out[u] (ADAM false), or straight into Adam on the table row of
+// slot[u] (ADAM true: the summed gradient is never written).
+struct AdamArgs {
+    float4* theta;
+    float4* m;
+    float4* v;
+    const int32_t* slots;
+    int64_t M;
+    float lr, b1, b2, eps, c1, c2;
+};
+
+// Adam's state of one 16-byte vector of a row, loaded ahead of the gradient
+// sum it waits for (the loads do not depend on it), then updated and stored.
+struct AdamVec {
+    int64_t o;      // vector index in the table's arrays; -1: not a slot of the table
+    float4 th, m, v;
+};
+
+template <bool ADAM>
+__device__ __forceinline__ AdamVec adam_load(int vpr, int64_t u, int v, const AdamArgs& A) {
+    AdamVec r;
+    r.o = -1;
+    if (!ADAM) return r;
+    const int32_t s = A.slots[u];
+    if (s < 0 || s >= A.M) return r;
+    r.o = (int64_t)s * vpr + v;
+    r.th = A.theta[r.o];
+    r.m = A.m[r.o];
+    r.v = A.v[r.o];
+    return r;
+}
+
+template <bool ADAM>
+__device__ __forceinline__ void emit4(u32x4* __restrict__ out, int vpr, int64_t u, int v, float4 g,
+                                      const AdamArgs& A, AdamVec st) {
+    if (!ADAM) {
+        u32x4 w;
+        w.x = __float_as_uint(g.x);
+        w.y = __float_as_uint(g.y);
+        w.z = __float_as_uint(g.z);
+        w.w = __float_as_uint(g.w);
+        out[u * vpr + v] = w;
+        return;
+    }
+    if (st.o < 0) return;
+    const float omb1 = 1.0f - A.b1, omb2 = 1.0f - A.b2;
+    adam_elem(st.th.x, st.m.x, st.v.x, g.x, A.b1, A.b2, omb1, omb2, A.lr, A.eps, A.c1, A.c2);
+    adam_elem(st.th.y, st.m.y, st.v.y, g.y, A.b1, A.b2, omb1, omb2, A.lr, A.eps, A.c1, A.c2);
+    adam_elem(st.th.z, st.m.z, st.v.z, g.z, A.b1, A.b2, omb1, omb2, A.lr, A.eps, A.c1, A.c2);
+    adam_elem(st.th.w, st.m.w, st.v.w, g.w, A.b1, A.b2, omb1, omb2, A.lr, A.eps, A.c1, A.c2);
+    A.theta[st.o] = st.th;
+    A.m[st.o] = st.m;
+    A.v[st.o] = st.v;
+}
+
 // Sums rows perm[beg..end) of `grad` into acc, TEAM lanes per row, the
 // TEAMS teams of `nthreads` lanes taking every TEAMS-th row.
 template <int TEAM, int QMAX>
@@ -208,32 +278,17 @@ __device__ __forceinline__ void sum_rows(const u32x4* __restrict__ grad, int vpr
     }
 }
 
-template <int TEAM, int QMAX>
-__device__ __forceinline__ void store_row(float* __restrict__ dst, int vpr, int tl, const float (&acc)[QMAX][4]) {
-#pragma unroll
-    for (int a = 0; a < QMAX; ++a) {
-        const int v = tl + a * TEAM;
-        if (v >= vpr) break;
-        u32x4 w;
-        w.x = __float_as_uint(acc[a][0]);
-        w.y = __float_as_uint(acc[a][1]);
-        w.z = __float_as_uint(acc[a][2]);
-        w.w = __float_as_uint(acc[a][3]);
-        reinterpret_cast<u32x4*>(dst)[v] = w;
-    }
-}
-
 // One team of TEAM lanes per segment (in spread order): most segments of a
 // Zipf batch hold one to a few IDs, so a team, not a whole wavefront, takes
 // each, and a wavefront keeps 64/TEAM segments' rows in flight.  Segments
 // longer than kSmallMax are listed, by their spread index, for the chunked
 // path.
-template <int TEAM, int QMAX>
+template <int TEAM, int QMAX, bool ADAM>
 __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__ grad, int vpr,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ seg_off, int64_t u_max,
-                                                      const int64_t* __restrict__ n_dev, float* __restrict__ out,
-                                                      int32_t* __restrict__ large,
+                                                      const int64_t* __restrict__ n_dev, u32x4* __restrict__ out,
+                                                      AdamArgs A, int32_t* __restrict__ large,
                                                       unsigned long long* __restrict__ n_large) {
     const int64_t U = dev_count(u_max, n_dev);
     const int64_t C = spread_c(U);
@@ -248,11 +303,22 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
             if (tl == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
             continue;
         }
+        AdamVec st[QMAX];
+#pragma unroll
+        for (int a = 0; a < QMAX; ++a) {
+            st[a].o = -1;
+            if (tl + a * TEAM < vpr) st[a] = adam_load<ADAM>(vpr, u, tl + a * TEAM, A);
+        }
         float acc[QMAX][4];
 #pragma unroll
         for (int a = 0; a < QMAX; ++a) acc[a][0] = acc[a][1] = acc[a][2] = acc[a][3] = 0.0f;
         sum_rows<TEAM, QMAX>(grad, vpr, perm, beg, end, 0, 1, tl, acc);
-        store_row<TEAM, QMAX>(out + u * (int64_t)vpr * 4, vpr, tl, acc);
+#pragma unroll
+        for (int a = 0; a < QMAX; ++a) {
+            const int v = tl + a * TEAM;
+            if (v >= vpr) break;
+            emit4<ADAM>(out, vpr, u, v, make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]), A, st[a]);
+        }
     }
 }
 
@@ -318,7 +384,7 @@ __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__
 
 // One workgroup per chunk of a long segment -> partial[part_off + chunk],
 // or straight to out[u] when the segment is a single chunk.
-template <int TEAM, int QMAX>
+template <int TEAM, int QMAX, bool ADAM>
 __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restrict__ grad, int vpr,
                                                          const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ seg_off,
@@ -327,7 +393,8 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
                                                          const int32_t* __restrict__ large_off,
                                                          const int32_t* __restrict__ part_off, int64_t max_chunks,
                                                          int64_t u_max, const int64_t* __restrict__ n_dev,
-                                                         float* __restrict__ partial, float* __restrict__ out) {
+                                                         u32x4* __restrict__ partial, u32x4* __restrict__ out,
+                                                         AdamArgs A) {
     constexpr int TEAMS = kRBlock / TEAM;
     __shared__ float s_acc[TEAMS][QMAX * TEAM * 4];
     const int64_t nl = (int64_t)*n_large;
@@ -347,6 +414,11 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
         const int32_t part = (int32_t)(c - large_off[lo]);
         const int32_t beg = seg_off[q] + part * kChunk;
         const int32_t end = min(seg_off[q + 1], beg + kChunk);
+        const bool single = large_off[lo + 1] - large_off[lo] == 1;
+        const int64_t u = spread_u(q, C);
+        AdamVec st;
+        st.o = -1;
+        if (single && (int)threadIdx.x < vpr) st = adam_load<ADAM>(vpr, u, threadIdx.x, A);
         float acc[QMAX][4];
 #pragma unroll
         for (int a = 0; a < QMAX; ++a) acc[a][0] = acc[a][1] = acc[a][2] = acc[a][3] = 0.0f;
@@ -356,14 +428,27 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) s_acc[team][(a * TEAM + tl) * 4 + e] = acc[a][e];
         __syncthreads();
-        float* dst = large_off[lo + 1] - large_off[lo] == 1
-                         ? out + spread_u(q, C) * vpr * 4
-                         : partial + (int64_t)(part_off[lo] + part) * vpr * 4;
-        for (int e = threadIdx.x; e < vpr * 4; e += kRBlock) {
-            const int a = (e / 4) / TEAM, l = (e / 4) % TEAM;
-            float s = 0.0f;
-            for (int t = 0; t < TEAMS; ++t) s += s_acc[t][(a * TEAM + l) * 4 + (e & 3)];
-            dst[e] = s;
+        u32x4* dst = partial + (int64_t)(part_off[lo] + part) * vpr;
+        for (int v = threadIdx.x; v < vpr; v += kRBlock) {
+            const int a = v / TEAM, l = v % TEAM;
+            float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int t = 0; t < TEAMS; ++t) {
+                const float* x = &s_acc[t][(a * TEAM + l) * 4];
+                g.x += x[0];
+                g.y += x[1];
+                g.z += x[2];
+                g.w += x[3];
+            }
+            if (single) {
+                emit4<ADAM>(out, vpr, u, v, g, A, st);     // v == threadIdx.x: vpr <= kRBlock
+            } else {
+                u32x4 w;
+                w.x = __float_as_uint(g.x);
+                w.y = __float_as_uint(g.y);
+                w.z = __float_as_uint(g.z);
+                w.w = __float_as_uint(g.w);
+                dst[v] = w;
+            }
         }
         __syncthreads();
     }
@@ -377,12 +462,13 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
 // over a thousand partials, so a serial walk over them would dominate.
 constexpr int kCombThreads = 1024;
 
+template <bool ADAM>
 __global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __restrict__ partial, int vpr,
                                                                int lanes, const int32_t* __restrict__ large,
                                                                const unsigned long long* __restrict__ n_large,
                                                                const int32_t* __restrict__ part_off, int64_t u_max,
                                                                const int64_t* __restrict__ n_dev,
-                                                               u32x4* __restrict__ out) {
+                                                               u32x4* __restrict__ out, AdamArgs A) {
     __shared__ float4 s_red[kCombThreads];
     const int64_t nl = (int64_t)*n_large;
     const int64_t C = spread_c(dev_count(u_max, n_dev));
@@ -394,6 +480,9 @@ __global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __r
         const int64_t u = spread_u(large[i], C);
         for (int v0 = 0; v0 < vpr; v0 += lanes) {
             const int v = v0 + l;
+            AdamVec st;
+            st.o = -1;
+            if (g == 0 && v < vpr) st = adam_load<ADAM>(vpr, u, v, A);
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
             if (v < vpr) {
                 constexpr int U = 4;
@@ -429,12 +518,7 @@ __global__ __launch_bounds__(kCombThreads) void k_large_combine(const u32x4* __r
                     s4.z += y.z;
                     s4.w += y.w;
                 }
-                u32x4 w;
-                w.x = __float_as_uint(s4.x);
-                w.y = __float_as_uint(s4.y);
-                w.z = __float_as_uint(s4.z);
-                w.w = __float_as_uint(s4.w);
-                out[(int64_t)u * vpr + v] = w;
+                emit4<ADAM>(out, vpr, u, v, s4, A, st);
             }
             __syncthreads();
         }
@@ -458,38 +542,49 @@ __global__ void k_seg_elem(const float* __restrict__ grad, int dim, const int32_
     }
 }
 
-template <int TEAM, int QMAX>
+int team_for(int vpr) {
+    int t = 1;
+    while (t < vpr && t < 64) t <<= 1;
+    return t;
+}
+
+template <int TEAM, int QMAX, bool ADAM>
 void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, const int64_t* n_dev, float* out,
-                   hipStream_t s) {
-    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM)), dim3(kRBlock), 0,
-                       s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, out, w.large, w.n_large);
+                   const AdamArgs& A, hipStream_t s) {
+    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM)),
+                       dim3(kRBlock), 0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, (u32x4*)out, A,
+                       w.large, w.n_large);
     hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off,
                        w.part_off);
-    hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX>), dim3(grid_for(w.max_chunks, 1, 1 << 16)), dim3(kRBlock), 0,
-                       s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off, w.part_off,
-                       w.max_chunks, u_max, n_dev, w.partial, out);
+    hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX, ADAM>), dim3(grid_for(w.max_chunks, 1, 1 << 16)), dim3(kRBlock),
+                       0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off, w.part_off,
+                       w.max_chunks, u_max, n_dev, (u32x4*)w.partial, (u32x4*)out, A);
     int lanes = 1;
     while (lanes < vpr && lanes < kCombThreads / 4) lanes <<= 1;
-    hipLaunchKernelGGL(k_large_combine, dim3(grid_for(w.large_max, 1, 1 << 14)), dim3(kCombThreads), 0, s,
+    hipLaunchKernelGGL(k_large_combine<ADAM>, dim3(grid_for(w.large_max, 1, 1 << 14)), dim3(kCombThreads), 0, s,
                        (const u32x4*)w.partial, vpr, lanes, w.large, w.n_large, w.part_off, u_max, n_dev,
-                       (u32x4*)out);
+                       (u32x4*)out, A);
+}
+
+template <bool ADAM>
+void launch_reduce_any(const float* grad, int vpr, const SegWs& w, int64_t u_max, const int64_t* n_dev, float* out,
+                       const AdamArgs& A, hipStream_t s) {
+    switch (team_for(vpr)) {
+        case 1: launch_reduce<1, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        case 2: launch_reduce<2, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        case 4: launch_reduce<4, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        case 8: launch_reduce<8, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        case 16: launch_reduce<16, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        case 32: launch_reduce<32, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s); break;
+        default:
+            if (vpr <= 64) launch_reduce<64, 1, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s);
+            else if (vpr <= 128) launch_reduce<64, 2, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s);
+            else launch_reduce<64, 4, ADAM>(grad, vpr, w, u_max, n_dev, out, A, s);
+            break;
+    }
 }
 
 // ---------------------------------------------------------------- Adam --
-// Same arithmetic per element in both kernels; contraction off so that every
-// product and sum rounds on its own, as written.
-#pragma clang fp contract(off)
-__device__ __forceinline__ void adam_elem(float& th, float& mo, float& vo, float gj, float b1, float b2, float omb1,
-                                          float omb2, float lr, float eps, float c1, float c2) {
-    const float mj = b1 * mo + omb1 * gj;
-    const float vj = b2 * vo + omb2 * (gj * gj);
-    const float mhat = mj / c1;
-    const float vhat = vj / c2;
-    th = th - lr * (mhat / (sqrtf(vhat) + eps));
-    mo = mj;
-    vo = vj;
-}
-
 // Rows of 4k floats: TEAM lanes per row, 16 bytes per lane access.
 template <int TEAM>
 __global__ __launch_bounds__(256) void k_adam4(float4* __restrict__ theta, float4* __restrict__ m,
@@ -546,16 +641,70 @@ void launch_adam4(const TableDev& T, const int32_t* slots, const float* g, int64
                        b1, b2, eps, c1, c2);
 }
 
-int team_for(int vpr) {
-    int t = 1;
-    while (t < vpr && t < 64) t <<= 1;
-    return t;
-}
 
 }  // namespace
 }  // namespace htl
 
 using namespace htl;
+
+namespace htl {
+namespace {
+
+bool fused_fallback(int dim) { return dim % 4 != 0 || dim > 1024; }
+
+// Count, scan and fill: the CSR of IDs grouped by unique (spread order).
+htl_status build_csr(const int32_t* inverse, int64_t n, const int64_t* n_dev, int64_t u_max, const SegWs& w,
+                     hipStream_t stream) {
+    hipLaunchKernelGGL(k_seg_zero, dim3(grid_for(u_max + kSpread, 256 * 4, 1 << 14)), dim3(256), 0, stream, w.counts,
+                       u_max, n_dev, w.n_large, w.n_seg);
+    hipLaunchKernelGGL(k_seg_count, dim3(grid_for(ceil_div(n, kCTile), 1, 1 << 16)), dim3(kCThreads), 0, stream,
+                       inverse, n, u_max, n_dev, w.counts, w.rel);
+    htl_status st = scan_exclusive_i32(w.counts, w.seg_off, u_max + kSpread, w.n_seg, kScanIdentity, 1, w.scan_tmp,
+                                       stream);
+    if (st != HTL_OK) return st;
+    hipLaunchKernelGGL(k_seg_fill, dim3(grid_for(n, 256 * 4)), dim3(256), 0, stream, inverse, w.rel, n, u_max, n_dev,
+                       w.seg_off, w.perm);
+    return HTL_OK;
+}
+
+AdamArgs adam_args(const htl_table* t, const int32_t* slots, float lr, float b1, float b2, float eps,
+                   int64_t step) {
+    AdamArgs A{};
+    A.theta = (float4*)t->dev.rows;
+    A.m = (float4*)t->dev.m;
+    A.v = (float4*)t->dev.v;
+    A.slots = slots;
+    A.M = t->dev.capacity;
+    A.lr = lr;
+    A.b1 = b1;
+    A.b2 = b2;
+    A.eps = eps;
+    A.c1 = (float)(1.0 - std::pow((double)b1, (double)step));
+    A.c2 = (float)(1.0 - std::pow((double)b2, (double)step));
+    return A;
+}
+
+void launch_adam(const htl_table* t, const int32_t* slots, const float* g, int64_t u_max, const int64_t* n_dev,
+                 const AdamArgs& A, hipStream_t stream) {
+    const TableDev& T = t->dev;
+    if (T.dim % 4 == 0 && aligned(g, 16)) {
+        switch (team_for(T.dim / 4)) {
+            case 1: launch_adam4<1>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            case 2: launch_adam4<2>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            case 4: launch_adam4<4>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            case 8: launch_adam4<8>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            case 16: launch_adam4<16>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            case 32: launch_adam4<32>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+            default: launch_adam4<64>(T, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2, stream); break;
+        }
+    } else {
+        hipLaunchKernelGGL(k_adam, dim3(grid_for(u_max * T.dim, 256 * 4)), dim3(256), 0, stream, (float*)T.rows, T.m,
+                           T.v, T.dim, T.capacity, slots, g, u_max, n_dev, A.lr, A.b1, A.b2, A.eps, A.c1, A.c2);
+    }
+}
+
+}  // namespace
+}  // namespace htl
 
 extern "C" {
 
@@ -564,6 +713,15 @@ size_t segsum_workspace_bytes(int64_t n, int64_t u_max, int dim) {
     if (u_max < 0) u_max = 0;
     if (dim < 1) dim = 1;
     return seg_layout(n, u_max, dim, nullptr).bytes;
+}
+
+size_t segsum_adam_workspace_bytes(int64_t n, int64_t u_max, int dim) {
+    if (n < 0) n = 0;
+    if (u_max < 0) u_max = 0;
+    if (dim < 1) dim = 1;
+    size_t b = seg_layout(n, u_max, dim, nullptr).bytes;
+    if (fused_fallback(dim)) b += align_up((size_t)u_max * dim * 4, 256);
+    return b;
 }
 
 htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64_t n,
@@ -580,35 +738,14 @@ htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64
                 "emb_grad_segment_sum: misaligned pointer (grad/out need 16 bytes, ws 256)");
     SegWs w = seg_layout(n, u_max, dim, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, "emb_grad_segment_sum: workspace too small");
-
-    hipLaunchKernelGGL(k_seg_zero, dim3(grid_for(u_max + kSpread, 256 * 4, 1 << 14)), dim3(256), 0, stream, w.counts,
-                       u_max, n_unique_dev, w.n_large, w.n_seg);
-    hipLaunchKernelGGL(k_seg_count, dim3(grid_for(ceil_div(n, kCTile), 1, 1 << 16)), dim3(kCThreads), 0, stream,
-                       inverse, n, u_max, n_unique_dev, w.counts, w.rel);
-    htl_status st = scan_exclusive_i32(w.counts, w.seg_off, u_max + kSpread, w.n_seg, kScanIdentity, 1, w.scan_tmp,
-                                       stream);
+    htl_status st = build_csr(inverse, n, n_unique_dev, u_max, w, stream);
     if (st != HTL_OK) return st;
-    hipLaunchKernelGGL(k_seg_fill, dim3(grid_for(n, 256 * 4)), dim3(256), 0, stream, inverse, w.rel, n, u_max,
-                       n_unique_dev, w.seg_off, w.perm);
-    if (dim % 4 != 0 || dim > 1024) {
+    if (fused_fallback(dim)) {
         hipLaunchKernelGGL(k_seg_elem, dim3(grid_for(u_max * dim, 256 * 4)), dim3(256), 0, stream, grad, dim, w.perm,
                            w.seg_off, u_max, n_unique_dev, out);
         return check_launch("emb_grad_segment_sum");
     }
-    const int vpr = dim / 4;
-    switch (team_for(vpr)) {
-        case 1: launch_reduce<1, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        case 2: launch_reduce<2, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        case 4: launch_reduce<4, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        case 8: launch_reduce<8, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        case 16: launch_reduce<16, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        case 32: launch_reduce<32, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream); break;
-        default:
-            if (vpr <= 64) launch_reduce<64, 1>(grad, vpr, w, u_max, n_unique_dev, out, stream);
-            else if (vpr <= 128) launch_reduce<64, 2>(grad, vpr, w, u_max, n_unique_dev, out, stream);
-            else launch_reduce<64, 4>(grad, vpr, w, u_max, n_unique_dev, out, stream);
-            break;
-    }
+    launch_reduce_any<false>(grad, dim / 4, w, u_max, n_unique_dev, out, AdamArgs{}, stream);
     return check_launch("emb_grad_segment_sum");
 }
 
@@ -622,24 +759,43 @@ htl_status emb_rowwise_adam(htl_table* t, const int32_t* slots, const float* g, 
     HTL_REQUIRE(step >= 1, "emb_rowwise_adam: step must be >= 1");
     if (u_max == 0) return HTL_OK;
     HTL_REQUIRE(slots && g && aligned(slots, 4) && aligned(g, 4), "emb_rowwise_adam: null or misaligned pointer");
-    const float c1 = (float)(1.0 - std::pow((double)b1, (double)step));
-    const float c2 = (float)(1.0 - std::pow((double)b2, (double)step));
-    const TableDev& T = t->dev;
-    if (T.dim % 4 == 0 && aligned(g, 16)) {
-        switch (team_for(T.dim / 4)) {
-            case 1: launch_adam4<1>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            case 2: launch_adam4<2>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            case 4: launch_adam4<4>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            case 8: launch_adam4<8>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            case 16: launch_adam4<16>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            case 32: launch_adam4<32>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-            default: launch_adam4<64>(T, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2, stream); break;
-        }
-    } else {
-        hipLaunchKernelGGL(k_adam, dim3(grid_for(u_max * T.dim, 256 * 4)), dim3(256), 0, stream, (float*)T.rows,
-                           T.m, T.v, T.dim, T.capacity, slots, g, u_max, n_unique_dev, lr, b1, b2, eps, c1, c2);
-    }
+    launch_adam(t, slots, g, u_max, n_unique_dev, adam_args(t, slots, lr, b1, b2, eps, step), stream);
     return check_launch("emb_rowwise_adam");
+}
+
+htl_status emb_grad_segment_sum_adam(htl_table* t, const int32_t* slots, const float* grad, const int32_t* inverse,
+                                     int64_t n, const int64_t* n_unique_dev, int64_t u_max, float lr, float b1,
+                                     float b2, float eps, int64_t step, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(t != nullptr, "emb_grad_segment_sum_adam: null table");
+    HTL_REQUIRE(t->dev.m != nullptr && t->dtype == HTL_F32, "emb_grad_segment_sum_adam: table has no Adam state");
+    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31) - kSpread,
+                "emb_grad_segment_sum_adam: n must be in [0, 2^31 - 1024)");
+    HTL_REQUIRE(u_max >= 0 && u_max <= n, "emb_grad_segment_sum_adam: u_max must be in [0, n]");
+    HTL_REQUIRE(step >= 1, "emb_grad_segment_sum_adam: step must be >= 1");
+    if (n == 0 || u_max == 0) return HTL_OK;
+    const int dim = t->dim;
+    HTL_REQUIRE(slots && grad && inverse && ws, "emb_grad_segment_sum_adam: null pointer");
+    HTL_REQUIRE(aligned(grad, 16) && aligned(slots, 4) && aligned(inverse, 4) && aligned(ws, 256) &&
+                    (!n_unique_dev || aligned(n_unique_dev, 8)),
+                "emb_grad_segment_sum_adam: misaligned pointer (grad needs 16 bytes, ws 256)");
+    SegWs w = seg_layout(n, u_max, dim, (char*)ws);
+    HTL_REQUIRE(ws_bytes >= segsum_adam_workspace_bytes(n, u_max, dim),
+                "emb_grad_segment_sum_adam: workspace too small");
+    const AdamArgs A = adam_args(t, slots, lr, b1, b2, eps, step);
+    htl_status st = build_csr(inverse, n, n_unique_dev, u_max, w, stream);
+    if (st != HTL_OK) return st;
+    if (fused_fallback(dim)) {
+        // rows not in 16-byte vectors: the summed gradient goes through the workspace
+        float* g = (float*)((char*)ws + w.bytes);
+        hipLaunchKernelGGL(k_seg_elem, dim3(grid_for(u_max * dim, 256 * 4)), dim3(256), 0, stream, grad, dim, w.perm,
+                           w.seg_off, u_max, n_unique_dev, g);
+        launch_adam(t, slots, g, u_max, n_unique_dev, A, stream);
+        return check_launch("emb_grad_segment_sum_adam");
+    }
+    launch_reduce_any<true>(grad, dim / 4, w, u_max, n_unique_dev, nullptr, A, stream);
+    return check_launch("emb_grad_segment_sum_adam");
 }
 
 }  // extern "C"

@@ -244,6 +244,25 @@ htl_status emb_rowwise_adam(htl_table* t, const int32_t* slots, const float* g, 
                             const int64_t* n_unique_dev, float lr, float b1, float b2, float eps,
                             int64_t step, hipStream_t stream);
 
+/* emb_grad_segment_sum_adam -- emb_grad_segment_sum and then emb_rowwise_adam
+ * in one pass: each unique key's summed gradient is handed to Adam on its
+ * table row as soon as it is complete, so the summed gradients are never
+ * written to memory (the same arithmetic and results as the two calls, up to
+ * the summation order, which is unspecified in both).  Backward of the
+ * deduplicated lookup ([MTGenRec] TL;DR; [MTGR] section 5) with Adam as in
+ * [TF-PS] section 3.2.
+ *   t, slots      as emb_rowwise_adam; dim is the table's.
+ *   grad, inverse, n, n_unique_dev, u_max  as emb_grad_segment_sum
+ *                 (n < 2^31 - 1024, u_max <= n).
+ *   ws, ws_bytes  at least segsum_adam_workspace_bytes(n, u_max, dim) bytes,
+ *                 256-byte aligned.
+ * Needs an HTL_F32 table with HT_ADAM_STATE; HTL_ERR_INVALID otherwise. */
+size_t segsum_adam_workspace_bytes(int64_t n, int64_t u_max, int dim);
+htl_status emb_grad_segment_sum_adam(htl_table* t, const int32_t* slots, const float* grad,
+                                     const int32_t* inverse, int64_t n, const int64_t* n_unique_dev,
+                                     int64_t u_max, float lr, float b1, float b2, float eps,
+                                     int64_t step, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* htl_last_error -- message of the last failed call on this thread ("" if none). */
 const char* htl_last_error(void);
 

@@ -118,3 +118,55 @@ def test_segment_sum_backward_full_size(htl, orc):
     """2^23 IDs, Zipf(1.2), dim 128: the full-size workload, every element checked."""
     w = workloads.backward()
     _segsum_check(htl, orc, w.keys, w.grad)
+
+
+def _exact_grad(rng, n, dim):
+    # multiples of 2^-6 in [-0.125, 0.125]: every fp32 sum of fewer than 2^17
+    # of them is exact in any order, so the summed gradient does not depend
+    # on the summation order and the fused and two-call paths see the same g
+    return (rng.integers(-8, 9, (n, dim)) * 2.0 ** -6).astype(np.float32)
+
+
+@pytest.mark.parametrize("dim,zipf", [(128, True), (16, True), (64, False), (6, True), (1028, False)])
+def test_segment_sum_adam_fused_matches_two_calls(htl, orc, dim, zipf):
+    """Fused segment-sum + Adam against segment_sum then rowwise_adam on a
+    twin table: theta, m, v bit-equal over three steps (exact-sum gradients),
+    and against the oracle's array Adam fed the oracle's segment sums."""
+    rng = np.random.default_rng(dim)
+    n = 1 << 15 if dim < 1024 else 1 << 12
+    if zipf:
+        keys_np = workloads.backward(n=n, dim=4, with_grad=False).keys
+    else:
+        keys_np = rng.integers(0, n // 3, n).astype(np.int64)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    fused = htl.Table(16, dim, "f32", adam=True)
+    twin = htl.Table(16, dim, "f32", adam=True)
+    keys = torch.from_numpy(keys_np).cuda()
+    for step in (1, 2, 3):
+        grad_np = _exact_grad(rng, n, dim)
+        grad = torch.from_numpy(grad_np).cuda()
+        uniq, inv, nu = htl.dedup_unique_inverse(keys)
+        U = int(nu.item())
+        slots, _ = fused.find_or_insert(uniq, n_dev=nu, step=step)
+        slots2, _ = twin.find_or_insert(uniq, n_dev=nu, step=step)
+        sl = to_np(slots)[:U]
+        th0 = to_np(htl.table_tensor(fused, "rows"))[sl]
+        m0 = to_np(htl.table_tensor(fused, "adam_m"))[sl]
+        v0 = to_np(htl.table_tensor(fused, "adam_v"))[sl]
+        htl.segment_sum_adam(fused, slots, grad, inv, nu, n, lr, b1, b2, eps, step)
+        g = htl.segment_sum(grad, inv, nu, u_max=n)
+        htl.rowwise_adam(twin, slots2[:U], g[:U], nu, lr, b1, b2, eps, step)
+        sl2 = to_np(slots2)[:U]
+        for name in ("rows", "adam_m", "adam_v"):
+            a = to_np(htl.table_tensor(fused, name))[sl]
+            b = to_np(htl.table_tensor(twin, name))[sl2]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (name, step)
+        # the oracle: exact segment sums, then its own Adam from the same state
+        ref_g, _ = orc.segment_sum(grad_np, to_np(inv), U)
+        rth, rm, rv = orc.adam_arrays(th0, m0, v0, ref_g.astype(np.float32), lr, b1, b2, eps, step)
+        th1 = to_np(htl.table_tensor(fused, "rows"))[sl]
+        d = np.float64
+        assert np.array_equal(to_np(g)[:U].astype(d), ref_g)          # the sums are exact
+        assert np.all(np.abs(to_np(htl.table_tensor(fused, "adam_m"))[sl].astype(d) - rm) <=
+                      1e-5 * (b1 * np.abs(m0.astype(d)) + (1 - b1) * np.abs(ref_g)) + 1e-38)
+        assert np.all(np.abs(th1.astype(d) - rth) <= 1e-5 * (np.abs(th0.astype(d)) + np.abs(rth - th0)) + 1e-38)

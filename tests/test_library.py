@@ -50,6 +50,11 @@ def test_workspace_sizes(L):
     s1 = L.segsum_workspace_bytes(1 << 20, 1 << 18, 128)
     s2 = L.segsum_workspace_bytes(1 << 20, 1 << 18, 64)
     assert s1 > s2 > 0
+    # the fused backward needs no more than the segment-sum, except where rows
+    # are not 16-byte vectors and the summed gradient goes through it
+    assert L.segsum_adam_workspace_bytes(1 << 20, 1 << 18, 128) == s1
+    assert L.segsum_adam_workspace_bytes(1 << 20, 1 << 18, 6) >= \
+        L.segsum_workspace_bytes(1 << 20, 1 << 18, 6) + (1 << 18) * 6 * 4
     assert L.lru_workspace_bytes(None) == 0
 
 
@@ -75,6 +80,8 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.emb_grad_segment_sum(None, None, (1 << 31) - 1024, None, 1, 4, None, None, 0, None) == INVALID
     assert L.emb_grad_segment_sum(None, None, 10, None, 5, 0, None, None, 0, None) == INVALID
     assert L.emb_rowwise_adam(None, None, None, 1, None, 1e-3, 0.9, 0.999, 1e-8, 1, None) == INVALID
+    assert L.emb_grad_segment_sum_adam(None, None, None, None, 10, None, 5, 1e-3, 0.9, 0.999, 1e-8, 1,
+                                       None, 0, None) == INVALID
     assert L.ht_lru_select(None, 1, 20, None, 0, None, None, 0, None) == INVALID
     assert L.ht_view(None, None) == INVALID
     assert L.ht_destroy(None) == 0
