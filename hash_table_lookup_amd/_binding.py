@@ -22,7 +22,7 @@ HTL_OK, HTL_ERR_INVALID, HTL_ERR_NOMEM, HTL_ERR_DEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 FOUND, INSERTED, FULL, RESERVED = 0, 1, 2, 3
 NOT_FOUND, ERASED = 0, 1
-META_LAST_SEEN, ADAM_STATE = 1, 2
+META_LAST_SEEN, ADAM_STATE, GROWABLE = 1, 2, 4
 EMPTY_KEY, TOMBSTONE_KEY = -1, -2
 
 _P = ctypes.c_void_p
@@ -44,13 +44,15 @@ class HTLError(RuntimeError):
 
 class _View(ctypes.Structure):
     _fields_ = [("capacity", _I64), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("keys", _P), ("rows", _P), ("last_seen", _P), ("adam_m", _P), ("adam_v", _P)]
+                ("keys", _P), ("rows", _P), ("last_seen", _P), ("adam_m", _P), ("adam_v", _P),
+                ("row_of_slot", _P)]
 
 
 _SIGNATURES = {
     "ht_create": [ctypes.POINTER(_P), _I32, _I32, _I32, _U64, _U32, _P],
     "ht_destroy": [_P],
     "ht_clear": [_P, _P],
+    "ht_resize": [_P, _I32, _P],
     "ht_find_or_insert": [_P, _P, _I64, _P, _U32, _P, _P, _P],
     "ht_erase": [_P, _P, _I64, _P, _P],
     "ht_scan": [_P, _P, _P, _P, _P, _P],
@@ -143,15 +145,20 @@ _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
 
 class Table:
-    """A dynamic embedding table living in device memory (libhtl's ht_* calls)."""
+    """A dynamic embedding table living in device memory (libhtl's ht_* calls).
+
+    growable=True: rows live apart from the key index, slots returned are row
+    handles, and resize() grows the index without moving rows."""
 
     def __init__(self, capacity_log2: int, dim: int, dtype="f32", init_seed: int = 0,
-                 last_seen: bool = False, adam: bool = False):
+                 last_seen: bool = False, adam: bool = False, growable: bool = False):
         L = lib()
         self.capacity_log2, self.dim = capacity_log2, dim
         self.dtype = _dtype_code(dtype)
         self.init_seed = init_seed
-        flags = (META_LAST_SEEN if last_seen else 0) | (ADAM_STATE if adam else 0)
+        self.growable = growable
+        flags = ((META_LAST_SEEN if last_seen else 0) | (ADAM_STATE if adam else 0)
+                 | (GROWABLE if growable else 0))
         h = _P()
         _check(L.ht_create(ctypes.byref(h), capacity_log2, dim, self.dtype,
                            init_seed & 0xFFFFFFFFFFFFFFFF, flags, _stream()))
@@ -183,6 +190,11 @@ class Table:
 
     def clear(self):
         _check(lib().ht_clear(self._h, _stream()))
+
+    def resize(self, capacity_log2: int):
+        """Grow a growable table to 2^capacity_log2 slots (rows stay in place)."""
+        _check(lib().ht_resize(self._h, capacity_log2, _stream()))
+        self.capacity_log2 = capacity_log2
 
     def find_or_insert(self, keys: torch.Tensor, n_dev: Optional[torch.Tensor] = None,
                        step: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -367,10 +379,17 @@ def table_keys(table: Table) -> torch.Tensor:
 
 
 def table_tensor(table: Table, which: str) -> torch.Tensor:
-    """A copy of 'rows' ([M, dim]), 'last_seen' ([M]), 'adam_m' or 'adam_v' ([M, dim])."""
+    """A copy of 'rows' ([M, dim]), 'last_seen' ([M]), 'adam_m' or 'adam_v' ([M, dim]),
+    'keys' ([M]) or, for a growable table, 'row_of_slot' ([M])."""
     v = table.view()
     M, d = table.capacity, table.dim
-    if which == "rows":
+    if which == "keys":
+        out = torch.empty(M, dtype=torch.int64, device=table.device)
+        ptr = v.keys
+    elif which == "row_of_slot":
+        out = torch.empty(M, dtype=torch.int32, device=table.device)
+        ptr = v.row_of_slot
+    elif which == "rows":
         out = torch.empty((M, d), dtype=table.row_dtype, device=table.device)
         ptr = v.rows
     elif which == "last_seen":

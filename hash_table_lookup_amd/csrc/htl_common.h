@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <vector>
 
 #include "htl.h"
 
@@ -50,6 +51,35 @@ struct TableDev {
     int dtype;
     uint64_t init_base;    // mix64(init_seed)
     uint64_t salt;         // probe-hash salt
+    int32_t* rowid;        // growable tables: row handle of each live slot; null: row = slot
+};
+
+// Row-space index of a live slot.
+__device__ __forceinline__ int64_t row_of(const TableDev& T, int64_t slot) {
+    return T.rowid ? (int64_t)T.rowid[slot] : slot;
+}
+
+// A device array in a reserved virtual range that grows by mapping more
+// physical memory at its end (growable tables' row space).
+struct VmArray {
+    void* base = nullptr;
+    size_t reserved = 0;   // bytes of address space
+    size_t mapped = 0;     // bytes mapped from base
+    std::vector<hipMemGenericAllocationHandle_t> handles;
+    std::vector<size_t> sizes;
+};
+
+// Row-handle bookkeeping of a growable table (device memory).
+struct RowAlloc {
+    int64_t* state = nullptr;      // [0] next never-used row, [1] handles on the free stack
+    int32_t* free_stack = nullptr; // [rows]
+    int32_t* chunk_cnt = nullptr;  // per-call temporaries: per 64-key chunk counts ...
+    int32_t* chunk_off = nullptr;  // ... their exclusive prefix ...
+    int32_t* row_tmp = nullptr;    // ... a row handle per key (erase)
+    uint8_t* status_tmp = nullptr; // ... and a status per key (erase without status)
+    void* scan_tmp = nullptr;
+    void* tmp_base = nullptr;      // one allocation holding the temporaries
+    int64_t tmp_keys = 0;          // keys the temporaries are sized for
 };
 
 }  // namespace htl
@@ -63,6 +93,10 @@ struct htl_table {
     uint32_t flags;
     uint32_t max_step;   // largest step any find-or-insert stamped since create/clear
     htl::TableDev dev;
+    // growable tables only
+    int max_capacity_log2;
+    htl::VmArray vm_rows, vm_last_seen, vm_m, vm_v;
+    htl::RowAlloc alloc;
 };
 
 namespace htl {

@@ -12,6 +12,16 @@
 // dtype[M][dim] indexed by slot, optional last_seen uint32[M], optional Adam
 // moments float[M][dim].
 //
+// Growable tables (MTGR section 5: capacity grows by copying the key
+// storage, not the embeddings) add a row handle int32[M] per slot; rows,
+// last_seen and the moments are indexed by handle and live in a reserved
+// virtual range that grows by mapping physical memory at its end
+// (hipMemAddressReserve / hipMemCreate / hipMemMap), so a resize rehashes
+// only the 12-byte index entries and no row moves.  Handles come from a free
+// stack (handles of erased keys) and then a bump pointer; an insert pass
+// takes its handles with a count / prefix-sum / assign sequence, so no
+// counter is shared by the keys of a call.
+//
 // Probing (this library's layout, not the pages'): the M slots form
 // min(16, M)-slot buckets, one 128-byte line of keys each.  A key's walk
 // visits bucket b_t = b_0 + t*S mod (M/16) with S odd, so by Theorem 1 over the
@@ -26,6 +36,7 @@
 #include <cstdlib>
 
 #include "probe.h"
+#include "scan.h"
 
 namespace htl {
 
@@ -94,7 +105,8 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
 
 template <int G>
 __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t* __restrict__ keys,
-                                                       int64_t n, uint8_t* __restrict__ status) {
+                                                       int64_t n, uint8_t* __restrict__ status,
+                                                       int32_t* __restrict__ row_tmp) {
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
@@ -120,6 +132,7 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
                     if (gl == 0) old = cas_key(T.keys + base + hit, k, kTomb);
                     old = __shfl(old, gshift);
                     st = (old == k) ? HT_ERASED : HT_NOT_FOUND;
+                    if (gl == 0 && st == HT_ERASED && row_tmp) row_tmp[i] = T.rowid[base + hit];
                     break;
                 }
                 if (has_empty) break;
@@ -127,6 +140,156 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
             }
         }
         if (gl == 0 && status) status[i] = (uint8_t)st;
+    }
+}
+
+// --------------------------------------------------- growable tables --
+constexpr int kChunkKeys = 64;    // keys per handle-allocation chunk
+constexpr int kAssignLanes = 4;   // lanes per key in the assign pass: 64 keys per 256-thread block
+
+// Pass 1 of an insert into a growable table: probe and claim slots; the
+// slot goes to slots[i] for pass 3, no row is written yet.
+template <int G>
+__global__ __launch_bounds__(kProbeBlock) void k_foi_claim(TableDev T, const int64_t* __restrict__ keys,
+                                                          int64_t n_max, const int64_t* __restrict__ n_dev,
+                                                          int32_t* __restrict__ slots, uint8_t* __restrict__ status) {
+    const int64_t n = clamp_count(n_max, n_dev);
+    const int lane = lane_id();
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
+    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
+    for (int64_t i = group0; i < n; i += ngroups) {
+        int64_t slot;
+        const int st = find_or_insert_key<G>(T, keys[i], gl, gshift, &slot);
+        if (gl == 0) {
+            slots[i] = (int32_t)slot;
+            status[i] = (uint8_t)st;
+        }
+    }
+}
+
+// Per chunk of kChunkKeys keys (one wavefront each): how many of its first
+// n keys have status `want`.  Writes every one of the nchunks counts.
+__global__ void k_chunk_count(const uint8_t* __restrict__ status, int64_t n_max, const int64_t* __restrict__ n_dev,
+                              int want, int32_t* __restrict__ cnt, int64_t nchunks) {
+    const int64_t n = clamp_count(n_max, n_dev);
+    const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t c = wave; c < nchunks; c += nwaves) {
+        const int64_t i = c * kChunkKeys + lane_id();
+        const bool f = i < n && status[i] == want;
+        const int k = __popcll(__ballot(f));
+        if (lane_id() == 0) cnt[c] = k;
+    }
+}
+
+// The handle for the r-th new row of a call: the top of the free stack
+// first, then never-used rows.
+__device__ __forceinline__ int32_t take_handle(int64_t r, int64_t bump, int64_t nfree,
+                                               const int32_t* __restrict__ free_stack) {
+    return r < nfree ? free_stack[nfree - 1 - r] : (int32_t)(bump + (r - nfree));
+}
+
+// Pass 3: INSERTED keys take handles in key order (rank within the chunk +
+// the chunk's prefix), record them at their slot, get their initial row and
+// last_seen; slots[i] becomes the handle.
+__global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const int64_t* __restrict__ keys,
+                                                           int64_t n_max, const int64_t* __restrict__ n_dev,
+                                                           uint32_t step, const int32_t* __restrict__ chunk_off,
+                                                           const int64_t* __restrict__ state,
+                                                           const int32_t* __restrict__ free_stack,
+                                                           int32_t* __restrict__ slots,
+                                                           const uint8_t* __restrict__ status) {
+    constexpr int G = kAssignLanes;
+    __shared__ int s_wave[kProbeBlock / 64];
+    const int64_t n = clamp_count(n_max, n_dev);
+    const int64_t bump = state[0], nfree = state[1];
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
+    for (int64_t c = blockIdx.x; c * kChunkKeys < n; c += gridDim.x) {
+        const int64_t i = c * kChunkKeys + threadIdx.x / G;
+        const int st = i < n ? (int)status[i] : -1;
+        const bool ins = st == HT_INSERTED;
+        const uint64_t m = __ballot(gl == 0 && ins);
+        if (lane == 0) s_wave[wid] = __popcll(m);
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wid; ++w) before += s_wave[w];
+        __syncthreads();
+        if (ins) {
+            const int64_t slot = slots[i];
+            const int64_t r = chunk_off[c] + before + __popcll(m & ((1ull << gshift) - 1ull));
+            const int64_t row = take_handle(r, bump, nfree, free_stack);
+            write_initial_row<G>(T, row, keys[i], gl);
+            if (gl == 0) {
+                T.rowid[slot] = (int32_t)row;
+                if (T.last_seen) T.last_seen[row] = step;
+                slots[i] = (int32_t)row;
+            }
+        }
+    }
+}
+
+// Pass 4: FOUND keys read their slot's handle (after pass 3, so a key that
+// another entry of the same call inserted reads the handle just recorded)
+// and stamp last_seen; slots[i] becomes the handle.
+__global__ void k_foi_found(const TableDev T, int64_t n_max, const int64_t* __restrict__ n_dev, uint32_t step,
+                            int32_t* __restrict__ slots, const uint8_t* __restrict__ status) {
+    const int64_t n = clamp_count(n_max, n_dev);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        if (status[i] != HT_FOUND) continue;
+        const int32_t row = T.rowid[slots[i]];
+        if (T.last_seen) T.last_seen[row] = step;
+        slots[i] = row;
+    }
+}
+
+// Pass 5 (one thread): the handles taken leave the free stack / bump pointer.
+__global__ void k_foi_finish(int64_t* __restrict__ state, const int32_t* __restrict__ total) {
+    const int64_t t = *total, nfree = state[1];
+    const int64_t take = t < nfree ? t : nfree;
+    state[1] = nfree - take;
+    state[0] += t - take;
+}
+
+// Erase of a growable table: handles of the erased keys go on the free
+// stack (rank in key order, after the current top).
+__global__ void k_erase_push(const uint8_t* __restrict__ status, const int32_t* __restrict__ row_tmp, int64_t n,
+                             const int32_t* __restrict__ chunk_off, const int64_t* __restrict__ state,
+                             int32_t* __restrict__ free_stack) {
+    const int64_t nfree = state[1];
+    const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t c = wave; c * kChunkKeys < n; c += nwaves) {
+        const int64_t i = c * kChunkKeys + lane_id();
+        const bool f = i < n && status[i] == HT_ERASED;
+        const uint64_t m = __ballot(f);
+        if (f) free_stack[nfree + chunk_off[c] + __popcll(m & lanemask_lt())] = row_tmp[i];
+    }
+}
+
+__global__ void k_erase_finish(int64_t* __restrict__ state, const int32_t* __restrict__ total) {
+    state[1] += *total;
+}
+
+// Resize: one group of G lanes per old slot re-inserts its live key, with
+// its handle, into the new index (keys are distinct, so every one lands in
+// a free slot; the new index holds no tombstones).
+template <int G>
+__global__ __launch_bounds__(kProbeBlock) void k_rehash(TableDev O, TableDev N) {
+    const int lane = lane_id();
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
+    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
+    for (int64_t s = group0; s < O.capacity; s += ngroups) {
+        const int64_t k = O.keys[s];
+        if (k == kEmpty || k == kTomb) continue;
+        int64_t ns;
+        const int st = find_or_insert_key<G>(N, k, gl, gshift, &ns);
+        if (gl == 0 && st == HT_INSERTED) N.rowid[ns] = O.rowid[s];
     }
 }
 
@@ -182,8 +345,9 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_live(TableDev T, int64_t* _
             if (live & (1u << j)) {
                 const int64_t s = start + (int64_t)j * kScanBlock + tid;
                 if (out_keys) out_keys[pos] = k[j];
-                if (out_ls) out_ls[pos] = T.last_seen ? T.last_seen[s] : 0u;
-                if (out_slots) out_slots[pos] = (int32_t)s;
+                const int64_t row = row_of(T, s);
+                if (out_ls) out_ls[pos] = T.last_seen ? T.last_seen[row] : 0u;
+                if (out_slots) out_slots[pos] = (int32_t)row;
                 ++pos;
             }
         }
@@ -196,6 +360,150 @@ htl_status fill_keys_empty(const TableDev& T, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_i64, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, s,
                        T.keys, T.capacity, kEmpty);
     return check_launch("clear table keys");
+}
+
+hipMemAllocationProp vm_prop(int device) {
+    hipMemAllocationProp prop = {};
+    prop.type = hipMemAllocationTypePinned;
+    prop.location.type = hipMemLocationTypeDevice;
+    prop.location.id = device;
+    return prop;
+}
+
+size_t vm_granularity(int device) {
+    const hipMemAllocationProp prop = vm_prop(device);
+    size_t g = 0;
+    if (hipMemGetAllocationGranularity(&g, &prop, hipMemAllocationGranularityMinimum) != hipSuccess || g == 0)
+        g = (size_t)2 << 20;
+    return g;
+}
+
+htl_status vm_reserve(VmArray& a, size_t bytes, int device) {
+    const size_t g = vm_granularity(device);
+    a.reserved = align_up(bytes, g);
+    if (hipMemAddressReserve(&a.base, a.reserved, 0, nullptr, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        a.base = nullptr;
+        a.reserved = 0;
+        return fail(HTL_ERR_DEVICE, "growable table: cannot reserve device address space");
+    }
+    return HTL_OK;
+}
+
+// Maps physical memory so that the first `bytes` of the range are usable.
+htl_status vm_map_to(VmArray& a, size_t bytes, int device) {
+    const size_t g = vm_granularity(device);
+    const size_t need = align_up(bytes, g);
+    if (need <= a.mapped) return HTL_OK;
+    if (need > a.reserved) return fail(HTL_ERR_INVALID, "growable table: beyond the reserved row space");
+    const size_t size = need - a.mapped;
+    const hipMemAllocationProp prop = vm_prop(device);
+    hipMemGenericAllocationHandle_t h;
+    if (hipMemCreate(&h, size, &prop, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(HTL_ERR_NOMEM, "growable table: hipMemCreate failed");
+    }
+    char* at = (char*)a.base + a.mapped;
+    if (hipMemMap(at, size, 0, h, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipMemRelease(h);
+        return fail(HTL_ERR_DEVICE, "growable table: hipMemMap failed");
+    }
+    // Access is set over the whole mapped range from the base: on this
+    // runtime, setting it on the new chunk alone is refused ("invalid
+    // argument") for many chunk sequences, while the whole range never was
+    // in repeated trials on MI355X.
+    hipMemAccessDesc d = {};
+    d.location = prop.location;
+    d.flags = hipMemAccessFlagsProtReadWrite;
+    if (hipMemSetAccess(a.base, need, &d, 1) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipMemUnmap(at, size);
+        (void)hipMemRelease(h);
+        return fail(HTL_ERR_DEVICE, "growable table: hipMemSetAccess failed");
+    }
+    a.handles.push_back(h);
+    a.sizes.push_back(size);
+    a.mapped = need;
+    return HTL_OK;
+}
+
+void vm_free(VmArray& a) {
+    size_t off = 0;
+    for (size_t i = 0; i < a.handles.size(); ++i) {
+        (void)hipMemUnmap((char*)a.base + off, a.sizes[i]);
+        (void)hipMemRelease(a.handles[i]);
+        off += a.sizes[i];
+    }
+    if (a.base) (void)hipMemAddressFree(a.base, a.reserved);
+    a = VmArray{};
+}
+
+// Maps the row space of a growable table for `rows` handles; new last_seen
+// entries start at 0.
+htl_status grow_row_space(htl_table* t, int64_t rows, hipStream_t stream) {
+    TableDev& T = t->dev;
+    const size_t rb = (size_t)t->dim * T.elem_bytes;
+    const int64_t old_rows = (int64_t)(t->vm_rows.mapped / rb);
+    htl_status st = vm_map_to(t->vm_rows, (size_t)rows * rb, t->device);
+    if (st == HTL_OK && T.last_seen) st = vm_map_to(t->vm_last_seen, (size_t)rows * 4, t->device);
+    if (st == HTL_OK && T.m) st = vm_map_to(t->vm_m, (size_t)rows * t->dim * 4, t->device);
+    if (st == HTL_OK && T.v) st = vm_map_to(t->vm_v, (size_t)rows * t->dim * 4, t->device);
+    if (st != HTL_OK) return st;
+    if (T.last_seen && rows > old_rows) {
+        hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(rows - old_rows, 256 * 8, 1 << 16)), dim3(256), 0, stream,
+                           T.last_seen + old_rows, rows - old_rows, 0u);
+        return check_launch("clear last_seen");
+    }
+    return HTL_OK;
+}
+
+// Per-call temporaries of a growable table for up to n keys.
+htl_status ensure_tmp(htl_table* t, int64_t n) {
+    RowAlloc& A = t->alloc;
+    if (n <= A.tmp_keys) return HTL_OK;
+    if (A.tmp_base) {
+        HTL_HIP(hipDeviceSynchronize());
+        (void)hipFree(A.tmp_base);
+        A.tmp_base = nullptr;
+        A.tmp_keys = 0;
+    }
+    const int64_t nchunks = ceil_div(n, kChunkKeys);
+    size_t off = 0;
+    auto take = [&](size_t b) {
+        const size_t o = off;
+        off = align_up(off + b, 256);
+        return o;
+    };
+    const size_t o_cnt = take((size_t)nchunks * 4), o_off = take((size_t)(nchunks + 1) * 4);
+    const size_t o_row = take((size_t)n * 4), o_st = take((size_t)n), o_scan = take(scan_temp_bytes(nchunks));
+    if (hipMalloc(&A.tmp_base, off) != hipSuccess) {
+        (void)hipGetLastError();
+        A.tmp_base = nullptr;
+        return fail(HTL_ERR_NOMEM, "growable table: temporaries allocation failed");
+    }
+    char* b = (char*)A.tmp_base;
+    A.chunk_cnt = (int32_t*)(b + o_cnt);
+    A.chunk_off = (int32_t*)(b + o_off);
+    A.row_tmp = (int32_t*)(b + o_row);
+    A.status_tmp = (uint8_t*)(b + o_st);
+    A.scan_tmp = b + o_scan;
+    A.tmp_keys = n;
+    return HTL_OK;
+}
+
+void free_growable(htl_table* t) {
+    vm_free(t->vm_rows);
+    vm_free(t->vm_last_seen);
+    vm_free(t->vm_m);
+    vm_free(t->vm_v);
+    RowAlloc& A = t->alloc;
+    if (A.state) (void)hipFree(A.state);
+    if (A.free_stack) (void)hipFree(A.free_stack);
+    if (A.tmp_base) (void)hipFree(A.tmp_base);
+    A = RowAlloc{};
+    if (t->dev.rowid) (void)hipFree(t->dev.rowid);
+    t->dev.rowid = nullptr;
 }
 
 }  // namespace htl
@@ -215,8 +523,11 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
                 "ht_create: capacity_log2 must be in [1, 31]");
     HTL_REQUIRE(dim >= 1 && dim <= 65536, "ht_create: dim must be in [1, 65536]");
     HTL_REQUIRE(dtype == HTL_F32 || dtype == HTL_BF16, "ht_create: dtype must be HTL_F32 or HTL_BF16");
-    HTL_REQUIRE((flags & ~(uint32_t)(HT_META_LAST_SEEN | HT_ADAM_STATE)) == 0, "ht_create: unknown flag");
+    HTL_REQUIRE((flags & ~(uint32_t)(HT_META_LAST_SEEN | HT_ADAM_STATE | HT_GROWABLE)) == 0,
+                "ht_create: unknown flag");
     HTL_REQUIRE(!(flags & HT_ADAM_STATE) || dtype == HTL_F32, "ht_create: Adam state needs an fp32 table");
+    const bool growable = (flags & HT_GROWABLE) != 0;
+    HTL_REQUIRE(!growable || capacity_log2 <= 30, "ht_create: a growable table needs capacity_log2 <= 30");
 
     htl_table* t = new htl_table();
     t->capacity_log2 = capacity_log2;
@@ -224,6 +535,7 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
     t->dtype = dtype;
     t->init_seed = init_seed;
     t->flags = flags;
+    t->max_capacity_log2 = growable ? (capacity_log2 + 8 < 30 ? capacity_log2 + 8 : 30) : capacity_log2;
     HTL_HIP(hipGetDevice(&t->device));
     TableDev& T = t->dev;
     T = TableDev{};
@@ -238,14 +550,59 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
 
     auto cleanup = [&]() {
         if (T.keys) (void)hipFree(T.keys);
-        if (T.rows) (void)hipFree(T.rows);
-        if (T.last_seen) (void)hipFree(T.last_seen);
-        if (T.m) (void)hipFree(T.m);
-        if (T.v) (void)hipFree(T.v);
+        if (growable) {
+            free_growable(t);
+        } else {
+            if (T.rows) (void)hipFree(T.rows);
+            if (T.last_seen) (void)hipFree(T.last_seen);
+            if (T.m) (void)hipFree(T.m);
+            if (T.v) (void)hipFree(T.v);
+        }
         delete t;
     };
     const size_t M = (size_t)T.capacity;
     const size_t row_bytes = M * (size_t)dim * (size_t)T.elem_bytes;
+    if (growable) {
+        int vmm = 0;
+        if (hipDeviceGetAttribute(&vmm, hipDeviceAttributeVirtualMemoryManagementSupported, t->device) !=
+                hipSuccess ||
+            !vmm) {
+            (void)hipGetLastError();
+            cleanup();
+            return fail(HTL_ERR_DEVICE, "ht_create: the device does not support virtual memory management");
+        }
+        const size_t R = (size_t)1 << t->max_capacity_log2;
+        htl_status st = vm_reserve(t->vm_rows, R * (size_t)dim * T.elem_bytes, t->device);
+        if (st == HTL_OK && (flags & HT_META_LAST_SEEN)) st = vm_reserve(t->vm_last_seen, R * 4, t->device);
+        if (st == HTL_OK && (flags & HT_ADAM_STATE)) st = vm_reserve(t->vm_m, R * dim * 4, t->device);
+        if (st == HTL_OK && (flags & HT_ADAM_STATE)) st = vm_reserve(t->vm_v, R * dim * 4, t->device);
+        if (st == HTL_OK) {
+            T.rows = t->vm_rows.base;
+            T.last_seen = (uint32_t*)t->vm_last_seen.base;
+            T.m = (float*)t->vm_m.base;
+            T.v = (float*)t->vm_v.base;
+            st = grow_row_space(t, (int64_t)M, stream);
+        }
+        if (st == HTL_OK && (hipMalloc((void**)&T.keys, M * sizeof(int64_t)) != hipSuccess ||
+                             hipMalloc((void**)&T.rowid, M * 4) != hipSuccess ||
+                             hipMalloc((void**)&t->alloc.free_stack, M * 4) != hipSuccess ||
+                             hipMalloc((void**)&t->alloc.state, 2 * sizeof(int64_t)) != hipSuccess)) {
+            (void)hipGetLastError();
+            st = fail(HTL_ERR_NOMEM, "ht_create: device allocation failed");
+        }
+        if (st == HTL_OK) {
+            hipLaunchKernelGGL(k_fill_i64, dim3(1), dim3(64), 0, stream, t->alloc.state, (int64_t)2, (int64_t)0);
+            st = check_launch("ht_create: row allocator");
+        }
+        if (st == HTL_OK) st = fill_keys_empty(T, stream);
+        if (st != HTL_OK) {
+            std::string msg = g_last_error;
+            cleanup();
+            return fail(st, msg);
+        }
+        *out = t;
+        return HTL_OK;
+    }
     if (hipMalloc((void**)&T.keys, M * sizeof(int64_t)) != hipSuccess ||
         hipMalloc(&T.rows, row_bytes) != hipSuccess ||
         ((flags & HT_META_LAST_SEEN) && hipMalloc((void**)&T.last_seen, M * 4) != hipSuccess) ||
@@ -279,10 +636,14 @@ htl_status ht_destroy(htl_table* t) {
     HTL_HIP(hipDeviceSynchronize());
     TableDev& T = t->dev;
     (void)hipFree(T.keys);
-    (void)hipFree(T.rows);
-    if (T.last_seen) (void)hipFree(T.last_seen);
-    if (T.m) (void)hipFree(T.m);
-    if (T.v) (void)hipFree(T.v);
+    if (t->flags & HT_GROWABLE) {
+        free_growable(t);
+    } else {
+        (void)hipFree(T.rows);
+        if (T.last_seen) (void)hipFree(T.last_seen);
+        if (T.m) (void)hipFree(T.m);
+        if (T.v) (void)hipFree(T.v);
+    }
     delete t;
     HTL_HIP(hipSetDevice(cur));
     return HTL_OK;
@@ -292,7 +653,69 @@ htl_status ht_clear(htl_table* t, hipStream_t stream) {
     clear_error();
     HTL_REQUIRE(t != nullptr, "ht_clear: null table");
     t->max_step = 0u;
+    if (t->flags & HT_GROWABLE) {
+        hipLaunchKernelGGL(k_fill_i64, dim3(1), dim3(64), 0, stream, t->alloc.state, (int64_t)2, (int64_t)0);
+        htl_status st = check_launch("ht_clear: row allocator");
+        if (st != HTL_OK) return st;
+    }
     return fill_keys_empty(t->dev, stream);
+}
+
+htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(t != nullptr, "ht_resize: null table");
+    HTL_REQUIRE(t->flags & HT_GROWABLE, "ht_resize: the table was not created with HT_GROWABLE");
+    HTL_REQUIRE(new_capacity_log2 >= t->capacity_log2 && new_capacity_log2 <= t->max_capacity_log2,
+                "ht_resize: new_capacity_log2 must be in [current, created + 8] and <= 30");
+    TableDev& O = t->dev;
+    TableDev N = O;
+    N.capacity = (int64_t)1 << new_capacity_log2;
+    N.bucket_log2 = new_capacity_log2 < kBucketLog2 ? new_capacity_log2 : kBucketLog2;
+    N.bucket_mask = (uint64_t)(N.capacity >> N.bucket_log2) - 1;
+    N.keys = nullptr;
+    N.rowid = nullptr;
+    int32_t* new_stack = nullptr;
+    const size_t M2 = (size_t)N.capacity;
+    htl_status st = grow_row_space(t, N.capacity, stream);
+    if (st != HTL_OK) return st;
+    if (hipMalloc((void**)&N.keys, M2 * sizeof(int64_t)) != hipSuccess ||
+        hipMalloc((void**)&N.rowid, M2 * 4) != hipSuccess || hipMalloc((void**)&new_stack, M2 * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        if (N.keys) (void)hipFree(N.keys);
+        if (N.rowid) (void)hipFree(N.rowid);
+        if (new_stack) (void)hipFree(new_stack);
+        return fail(HTL_ERR_NOMEM, "ht_resize: device allocation failed");
+    }
+    st = fill_keys_empty(N, stream);
+    if (st == HTL_OK && hipMemcpyAsync(new_stack, t->alloc.free_stack, (size_t)O.capacity * 4,
+                                       hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        st = fail(HTL_ERR_DEVICE, "ht_resize: copy of the free handles failed");
+    }
+    if (st == HTL_OK) {
+        hipLaunchKernelGGL(k_rehash<4>, dim3(grid_for(O.capacity, kProbeBlock / 4, 1 << 16)), dim3(kProbeBlock), 0,
+                           stream, O, N);
+        st = check_launch("ht_resize: rehash");
+    }
+    if (st == HTL_OK && hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        st = fail(HTL_ERR_DEVICE, "ht_resize: stream synchronisation failed");
+    }
+    if (st != HTL_OK) {
+        std::string msg = g_last_error;
+        (void)hipStreamSynchronize(stream);
+        (void)hipFree(N.keys);
+        (void)hipFree(N.rowid);
+        (void)hipFree(new_stack);
+        return fail(st, msg);
+    }
+    (void)hipFree(O.keys);
+    (void)hipFree(O.rowid);
+    (void)hipFree(t->alloc.free_stack);
+    t->alloc.free_stack = new_stack;
+    t->dev = N;
+    t->capacity_log2 = new_capacity_log2;
+    return HTL_OK;
 }
 
 htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, const int64_t* n_dev,
@@ -307,6 +730,34 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
     if (step > t->max_step) t->max_step = step;
     const int G = probe_lanes();
     const unsigned grid = grid_for(n_max, kProbeBlock / G);
+    if (t->flags & HT_GROWABLE) {
+        // claim slots, count the inserts per chunk, prefix them, hand out rows
+        htl_status st = ensure_tmp(t, n_max);
+        if (st != HTL_OK) return st;
+        RowAlloc& A = t->alloc;
+        const int64_t nchunks = ceil_div(n_max, kChunkKeys);
+#define HTL_CLAIM(GG)                                                                                        \
+    hipLaunchKernelGGL(k_foi_claim<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev, \
+                       slots, status)
+        switch (G) {
+            case 1: HTL_CLAIM(1); break;
+            case 2: HTL_CLAIM(2); break;
+            case 8: HTL_CLAIM(8); break;
+            case 16: HTL_CLAIM(16); break;
+            default: HTL_CLAIM(4); break;
+        }
+#undef HTL_CLAIM
+        hipLaunchKernelGGL(k_chunk_count, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, status, n_max,
+                           n_dev, (int)HT_INSERTED, A.chunk_cnt, nchunks);
+        st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
+        if (st != HTL_OK) return st;
+        hipLaunchKernelGGL(k_foi_assign, dim3(grid_for(nchunks, 1, 1 << 16)), dim3(kProbeBlock), 0, stream, t->dev,
+                           keys, n_max, n_dev, step, A.chunk_off, A.state, A.free_stack, slots, status);
+        hipLaunchKernelGGL(k_foi_found, dim3(grid_for(n_max, 256 * 4)), dim3(256), 0, stream, t->dev, n_max, n_dev,
+                           step, slots, status);
+        hipLaunchKernelGGL(k_foi_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
+        return check_launch("ht_find_or_insert");
+    }
 #define HTL_FOI(GG)                                                                                        \
     hipLaunchKernelGGL(k_find_or_insert<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, \
                        n_dev, step, slots, status)
@@ -327,8 +778,26 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "ht_erase: n out of range");
     if (n == 0) return HTL_OK;
     HTL_REQUIRE(keys && aligned(keys, 8), "ht_erase: null or misaligned keys");
+    if (t->flags & HT_GROWABLE) {
+        // erased keys' row handles go back on the free stack, in key order
+        htl_status st = ensure_tmp(t, n);
+        if (st != HTL_OK) return st;
+        RowAlloc& A = t->alloc;
+        uint8_t* stat = status ? status : A.status_tmp;
+        const int64_t nchunks = ceil_div(n, kChunkKeys);
+        hipLaunchKernelGGL(k_erase<8>, dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream, t->dev,
+                           keys, n, stat, A.row_tmp);
+        hipLaunchKernelGGL(k_chunk_count, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, stat, n,
+                           (const int64_t*)nullptr, (int)HT_ERASED, A.chunk_cnt, nchunks);
+        st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
+        if (st != HTL_OK) return st;
+        hipLaunchKernelGGL(k_erase_push, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, stat, A.row_tmp,
+                           n, A.chunk_off, A.state, A.free_stack);
+        hipLaunchKernelGGL(k_erase_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
+        return check_launch("ht_erase");
+    }
     hipLaunchKernelGGL(k_erase<8>, dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream, t->dev, keys,
-                       n, status);
+                       n, status, (int32_t*)nullptr);
     return check_launch("ht_erase");
 }
 
@@ -356,6 +825,7 @@ htl_status ht_view(const htl_table* t, htl_view* out) {
     out->last_seen = t->dev.last_seen;
     out->adam_m = t->dev.m;
     out->adam_v = t->dev.v;
+    out->row_of_slot = t->dev.rowid;
     return HTL_OK;
 }
 

@@ -61,7 +61,7 @@ enum { HT_FOUND = 0, HT_INSERTED = 1, HT_FULL = 2, HT_RESERVED = 3 };
 /* Per-key status of ht_erase (uint8 each). */
 enum { HT_NOT_FOUND = 0, HT_ERASED = 1 };
 /* ht_create flags. */
-enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u };
+enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u };
 
 /* Key values the table keeps for itself (slot markers). */
 #define HT_EMPTY_KEY ((int64_t)-1)
@@ -81,19 +81,47 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u };
  *   init_seed      seed of the closed-form initial row of every new key: the
  *                  row is a function of (key, init_seed) only.
  *   flags          HT_META_LAST_SEEN: keep a uint32 last_seen per slot;
- *                  HT_ADAM_STATE: keep fp32 Adam moments m, v (needs HTL_F32).
+ *                  HT_ADAM_STATE: keep fp32 Adam moments m, v (needs HTL_F32);
+ *                  HT_GROWABLE: a table that ht_resize can grow (below).
  *   stream         the table is cleared (all slots EMPTY) on this stream.
  * Storage, all on the current device: keys int64[M]; rows dtype[M][dim];
  * last_seen uint32[M]; m, v float[M][dim].  *t receives the handle.
- * Errors: INVALID for a bad size/flag combination or null t; NOMEM. */
+ *
+ * Growable tables ([MTGR] section 5: keys map to vectors and metadata, and
+ * capacity grows by copying the key storage, not the embeddings): the key
+ * index (keys int64[M] + a row handle int32[M] per slot) is separate from the
+ * row space (rows, last_seen, m, v indexed by row handle).  The row space is
+ * a reserved virtual range of up to 2^min(30, capacity_log2 + 8) rows, of
+ * which M are mapped; ht_resize maps more and rehashes only the index.  In
+ * such a table every "slot" that a call returns or takes (ht_find_or_insert,
+ * ht_scan, emb_gather_pool, emb_rowwise_adam) is a row handle: stable for as
+ * long as its key stays live, across resizes; the handle of an erased key is
+ * reused by a later insert.  capacity_log2 <= 30 (the row handles are int32
+ * and the reservation must fit).
+ * Errors: INVALID for a bad size/flag combination or null t; NOMEM; DEVICE
+ * if the device cannot map virtual memory (HT_GROWABLE only). */
 htl_status ht_create(htl_table** t, int capacity_log2, int dim, htl_dtype dtype,
                      uint64_t init_seed, uint32_t flags, hipStream_t stream);
 
 /* ht_destroy -- free the table (synchronises the device first).  Null is a no-op. */
 htl_status ht_destroy(htl_table* t);
 
-/* ht_clear -- mark every slot EMPTY again (rows, metadata are left as they are). */
+/* ht_clear -- mark every slot EMPTY again (rows, metadata are left as they
+ * are; a growable table also takes back every row handle). */
 htl_status ht_clear(htl_table* t, hipStream_t stream);
+
+/* ht_resize -- grow a growable table to 2^new_capacity_log2 slots ([MTGR]
+ * section 5: capacity expansion replicates the key storage, not the
+ * embeddings).  Maps row space for the new capacity, builds a new key index
+ * (every live key re-inserted with its row handle; tombstones are dropped),
+ * then frees the old index.  Rows, last_seen and Adam moments do not move,
+ * so every row handle stays valid.  new_capacity_log2 may equal the current
+ * one (a rehash that only drops tombstones).  Synchronises `stream` before it
+ * frees the old index; allocates device memory (hipMalloc / hipMemMap).
+ * Errors: INVALID if the table is not growable, or new_capacity_log2 is below
+ * the current one or above the reservation (2^min(30, created + 8) slots);
+ * NOMEM; DEVICE. */
+htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream);
 
 /* ht_find_or_insert -- look up keys, inserting the absent ones.
  * [MTGenRec] Abstract (real-time insertion), Theorem 1 (odd-step probing of a
@@ -107,12 +135,15 @@ htl_status ht_clear(htl_table* t, hipStream_t stream);
  *   n_dev    nullable device int64: the actual count n <= n_max (e.g. the
  *            unique count written by dedup_unique_inverse); null means n_max.
  *   step     stamped into last_seen of FOUND and INSERTED keys (if kept).
- *   slots    int32[n_max] out: slot of each key, -1 for FULL and RESERVED.
+ *   slots    int32[n_max] out: slot of each key (growable tables: its row
+ *            handle), -1 for FULL and RESERVED.
  *   status   uint8[n_max] out: HT_FOUND, HT_INSERTED (row set to the closed-
  *            form initial row, Adam moments zeroed), HT_FULL, or HT_RESERVED
  *            (key equals HT_EMPTY_KEY or HT_TOMBSTONE_KEY).
  * Entries at index >= n are not written.  Erased slots (tombstones) are
- * reused by inserts. */
+ * reused by inserts.  A growable table hands out row handles with a count,
+ * scan and assign pass (no shared counter) and keeps per-call temporaries
+ * of 8 bytes per key, allocated on first use and grown when n_max grows. */
 htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max,
                              const int64_t* n_dev, uint32_t step, int32_t* slots,
                              uint8_t* status, hipStream_t stream);
@@ -126,7 +157,8 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
 
 /* ht_scan -- compact listing of live slots ([MTGR] section 5, "compact key
  * scanning").  Writes, for each live slot in an unspecified order, its key,
- * its last_seen (if kept) and its slot index.
+ * its last_seen (if kept) and its slot index (growable tables: its row
+ * handle).
  *   keys       int64[M] out (nullable)    last_seen uint32[M] out (nullable)
  *   slots      int32[M] out (nullable)    n_live_dev int64 out: live count. */
 htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32_t* slots,
@@ -150,7 +182,10 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
 
 /* ht_view -- raw device views of the table's storage (read-only use intended).
  * Any output may be null.  rows is dtype[M][dim]; m, v are null unless the
- * table keeps Adam state; last_seen is null unless it keeps metadata. */
+ * table keeps Adam state; last_seen is null unless it keeps metadata.  In a
+ * growable table rows, last_seen, m and v are indexed by row handle, and
+ * row_of_slot (int32[M], valid at live slots) maps a slot to its handle;
+ * row_of_slot is null for other tables (handle = slot). */
 typedef struct {
     int64_t capacity;
     int32_t dim;
@@ -160,6 +195,7 @@ typedef struct {
     uint32_t* last_seen;
     float* adam_m;
     float* adam_v;
+    int32_t* row_of_slot;
 } htl_view;
 htl_status ht_view(const htl_table* t, htl_view* out);
 

@@ -61,6 +61,7 @@ def lib():
             "orc_table_create": (_P, [_I64, _I32, _I32, _U64, _I32]),
             "orc_table_destroy": (None, [_P]),
             "orc_table_size": (_I64, [_P]),
+            "orc_table_resize": (_I32, [_P, _I64]),
             "orc_find_or_insert": (None, [_P, _P, _I64, _U32, _P]),
             "orc_erase": (None, [_P, _P, _I64, _P]),
             "orc_lookup": (_I32, [_P, _I64, _P, _P, _P, _P]),
@@ -185,6 +186,12 @@ class Table:
 
     def __len__(self):
         return int(lib().orc_table_size(self._h))
+
+    def resize(self, capacity: int):
+        """Raise the capacity (live keys keep their rows and metadata)."""
+        if not lib().orc_table_resize(self._h, capacity):
+            raise ValueError("capacity below the live count")
+        self.capacity = capacity
 
     def find_or_insert(self, keys, step: int = 0) -> np.ndarray:
         keys = _c(keys, np.int64)

@@ -244,6 +244,17 @@ void orc_table_destroy(void* h) { delete (Table*)h; }
 
 int64_t orc_table_size(void* h) { return (int64_t)((Table*)h)->index.size(); }
 
+// Capacity expansion (MTGR section 5: capacity grows while keys keep their
+// vectors and metadata).  The map holds no slots, so growing is a change of
+// the bound that makes a table FULL; every live key keeps its row, last_seen
+// and Adam state.  Returns 0 if the new capacity is below the live count.
+int32_t orc_table_resize(void* h, int64_t capacity) {
+    Table* t = (Table*)h;
+    if (capacity < (int64_t)t->index.size()) return 0;
+    t->capacity = capacity;
+    return 1;
+}
+
 // Find-or-insert (MTGenRec abstract: real-time insertion into a dynamic hash
 // table; MTGR section 5: keys map to vectors and metadata).  Keys are taken
 // in call order: a reserved key is RESERVED; a present key is FOUND; with M

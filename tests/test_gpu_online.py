@@ -15,10 +15,13 @@ from conftest import to_np
 pytestmark = pytest.mark.gpu
 
 
-def _run_online(htl, orc, spec, steps):
-    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+def _run_online(htl, orc, spec, steps, growable=False, grow_at=()):
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=growable)
     otab = orc.Table(1 << spec.capacity_log2, spec.dim, orc.BF16)
     for s in range(steps):
+        if s in grow_at:
+            table.resize(table.capacity_log2 + 1)
+            otab.resize(table.capacity)
         keys_np = workloads.dynamic_online_step(spec, s)
         keys = torch.from_numpy(keys_np).cuda()
         out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=s)
@@ -52,6 +55,20 @@ def test_online_heavy_eviction(htl, orc):
     spec = workloads.DynamicOnlineSpec(window=1 << 12, n=1 << 11, capacity_log2=13, dim=8,
                                        evict_num=1, evict_den=3)
     _run_online(htl, orc, spec, steps=6)
+
+
+def test_online_growable_with_resizes(htl, orc):
+    """The same stream on a growable table (row handles, rows apart from the
+    key index), grown twice mid-stream: every status, gathered row, victim
+    set and live set still matches the oracle."""
+    spec = workloads.DynamicOnlineSpec(window=1 << 14, n=1 << 12, capacity_log2=14, dim=64)
+    _run_online(htl, orc, spec, steps=8, growable=True, grow_at=(3, 6))
+
+
+def test_online_growable_heavy_eviction(htl, orc):
+    spec = workloads.DynamicOnlineSpec(window=1 << 12, n=1 << 11, capacity_log2=12, dim=8,
+                                       evict_num=1, evict_den=3)
+    _run_online(htl, orc, spec, steps=6, growable=True, grow_at=(2,))
 
 
 def test_lru_edge_fractions(htl, orc):

@@ -98,3 +98,40 @@ def test_last_seen_follows_found_and_inserted(orc):
     t.find_or_insert([2, 4], step=7)
     got = {k: t.lookup(k)[1] for k in (1, 2, 3, 4)}
     assert got == {1: 1, 2: 7, 3: 1, 4: 7}
+
+
+@pytest.mark.parametrize("cap", [1, 2])
+def test_growth_sequences_against_set_model(orc, cap):
+    """Capacity growth (MTGR section 5) inside every sequence of length <= 5 of
+    insert / erase / double-the-capacity on 3 keys: statuses follow the set
+    model with the grown bound, and a live key's row and last_seen survive
+    each growth unchanged."""
+    keys = [11, -7, 1 << 50]
+    ops = [(o, k) for o in ("ins", "era") for k in keys] + [("grow", None)]
+    for length in range(1, 6):
+        for seq in itertools.product(ops, repeat=length):
+            t = orc.Table(cap, 4, orc.BF16)
+            live, c = set(), cap
+            for step, (op, k) in enumerate(seq):
+                if op == "grow":
+                    before = {q: t.lookup(q) for q in live}
+                    c *= 2
+                    t.resize(c)
+                    for q, (row, ls, _, _) in before.items():
+                        row2, ls2, _, _ = t.lookup(q)
+                        assert np.array_equal(row, row2) and ls == ls2
+                    continue
+                want = _model_apply(live, c, op, k)
+                got = (t.find_or_insert([k], step=step) if op == "ins" else t.erase([k]))[0]
+                assert got == want, (cap, seq)
+            lk, _ = t.live()
+            assert lk.tolist() == sorted(live)
+
+
+def test_resize_below_live_count_is_refused(orc):
+    t = orc.Table(4, 4)
+    t.find_or_insert([1, 2, 3])
+    with pytest.raises(ValueError):
+        t.resize(2)
+    t.resize(3)
+    assert t.find_or_insert([4])[0] == orc.FULL
