@@ -18,7 +18,9 @@ Other workloads (--workload), each its own hot-path rows:
                   (segment-sum, then Adam) is timed beside it
   dynamic_online  2^27-slot bf16 table (dim 64), steps of 2^22 IDs over a
                   drifting window: dedup -> find-or-insert -> gather, then
-                  LRU selection of 5% of the live keys and their erase
+                  LRU selection of 5% of the live keys and their erase;
+                  with --growable the table keeps rows apart from its key
+                  index and one capacity doubling (2^27 -> 2^28) is timed
 
 Timing: HIP events on the stream the library launches on bracket each step
 (and the dominant kernel inside it); table state that a step changes is
@@ -54,6 +56,8 @@ def _parse():
     ap.add_argument("--workload", default="single_large_table",
                     choices=["single_large_table", "tiny", "merged_tables", "backward", "dynamic_online"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--growable", action="store_true",
+                    help="dynamic_online: use a growable table and time one capacity doubling")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="IDs of the batch the CPU oracle processes (timed)")
     return ap.parse_args()
@@ -322,16 +326,18 @@ def run_backward(args, torch, htl, workloads, dev):
 def run_online(args, torch, htl, workloads, dev):
     spec = workloads.DynamicOnlineSpec()
     steps = args.warmup + args.steps
-    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=args.growable)
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.n, spec.dim), dtype=torch.bfloat16, device=dev)
     fwd, lru, ers = [], [], []
     U_last = 0
     gen = workloads.DynamicOnlineStream(spec, steps)
+    hold = _GpuHold(torch, stream)
     for s in range(steps):
         keys = torch.from_numpy(gen.keys(s)).to(dev)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         torch.cuda.synchronize()
+        hold(4.0)                       # the host enqueues forward + LRU behind it
         e[0].record(stream)
         uniq, inv, nu = htl.dedup_unique_inverse(keys)
         slots, status = table.find_or_insert(uniq, n_dev=nu, step=s)
@@ -340,18 +346,40 @@ def run_online(args, torch, htl, workloads, dev):
         victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
         e[2].record(stream)
         k = int(nv.item())                                # the host needs k to size the erase
-        table.erase(victims[:k])
+        hold(1.0)
         e[3].record(stream)
+        table.erase(victims[:k])
+        e[4].record(stream)
         torch.cuda.synchronize()
         if s >= args.warmup:
             fwd.append(e[0].elapsed_time(e[1]))
             lru.append(e[1].elapsed_time(e[2]))
-            ers.append(e[2].elapsed_time(e[3]))
+            ers.append(e[3].elapsed_time(e[4]))
             U_last = int(nu.item())
         print(f"online step {s} done", file=sys.stderr, flush=True)
     ms = float(np.mean(fwd))
     M = 1 << spec.capacity_log2
     row = spec.dim * 2
+    resize = None
+    if args.growable:
+        # one capacity doubling after the timed steps: rehash of the key index only
+        live = int(table.scan()[3].item())
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        table.resize(spec.capacity_log2 + 1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        M2 = 2 * M
+        rbytes = M * (8 + 4) + live * (8 + 4) + M2 * 8 + M * 4
+        resize = {"from_slots_log2": spec.capacity_log2, "to_slots_log2": spec.capacity_log2 + 1,
+                  "live_keys": live, "wall_ms": round(wall, 3),
+                  "algorithmic_bytes": rbytes,
+                  "rows_moved": 0,
+                  "what": "map row space for 2^28 handles, new index, rehash of the live keys with their handles, "
+                          "free of the old index (the call synchronises the stream)"}
     fwd_bytes = spec.n * (16 + row) + U_last * (33 + row)
     lru_bytes = M * 12
     config = {"workload": "dynamic_online", "ids_per_step": spec.n, "window": spec.window,
@@ -361,11 +389,35 @@ def run_online(args, torch, htl, workloads, dev):
     path = {"unique_last_step": U_last, "forward_ms": round(ms, 4),
             "lru_select_ms": round(float(np.mean(lru)), 4), "erase_ms": round(float(np.mean(ers)), 4),
             "forward_algorithmic_bytes": fwd_bytes,
+            "table": "growable (row handles, mapped row space)" if args.growable else "fixed",
+            "resize": resize,
             "implementation": "dedup + find_or_insert(step) + gather, then ht_lru_select + ht_erase",
             "timing": f"per-step HIP events over steps {args.warmup}..{steps - 1} of the drifting stream "
-                      "(the warm-up steps fill the table); value = forward IDs/s"}
+                      "(the warm-up steps fill the table); a GPU spin kernel (torch.cuda._sleep) holds the "
+                      "stream while the host enqueues each phase, so the events time GPU work, not launch "
+                      "overhead; value = forward IDs/s"}
     return _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
                    _roofline("ht_lru_select (full-table scan + radix select)", lru_bytes, float(np.mean(lru))))
+
+
+class _GpuHold:
+    """Keeps the stream busy for about `ms` milliseconds (torch.cuda._sleep,
+    calibrated once), so that work the host enqueues meanwhile then runs back
+    to back and events around it time the GPU, not the Python launches."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        cyc = 1 << 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        torch.cuda._sleep(cyc)
+        b.record(stream)
+        torch.cuda.synchronize()
+        self.cycles_per_ms = cyc / max(a.elapsed_time(b), 1e-3)
+
+    def __call__(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
 
 
 # -------------------------------------------------------------- references

@@ -95,7 +95,7 @@ struct htl_table {
     htl::TableDev dev;
     // growable tables only
     int max_capacity_log2;
-    htl::VmArray vm_rows, vm_last_seen, vm_m, vm_v;
+    htl::VmArray vm_rows, vm_m, vm_v;
     htl::RowAlloc alloc;
 };
 

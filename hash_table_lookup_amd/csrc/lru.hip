@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             if (live & (1u << j)) {
-                const uint32_t ls = T.last_seen[row_of(T, base + (int64_t)j * kThreads + tid)];
+                const uint32_t ls = T.last_seen[base + (int64_t)j * kThreads + tid];
                 my_max = ls > my_max ? ls : my_max;
                 cand_ls[base + pos] = ls;
                 cand_key[base + pos] = bias(k[j]);

@@ -13,11 +13,12 @@
 // moments float[M][dim].
 //
 // Growable tables (MTGR section 5: capacity grows by copying the key
-// storage, not the embeddings) add a row handle int32[M] per slot; rows,
-// last_seen and the moments are indexed by handle and live in a reserved
-// virtual range that grows by mapping physical memory at its end
-// (hipMemAddressReserve / hipMemCreate / hipMemMap), so a resize rehashes
-// only the 12-byte index entries and no row moves.  Handles come from a free
+// storage, not the embeddings) add a row handle int32[M] per slot; rows and
+// the moments are indexed by handle and live in a reserved virtual range
+// that grows by mapping physical memory at its end (hipMemAddressReserve /
+// hipMemCreate / hipMemMap), so a resize rehashes only the index entries
+// (key, handle and the 4-byte last_seen, which stays with the key) and no
+// row moves.  Handles come from a free
 // stack (handles of erased keys) and then a bump pointer; an insert pass
 // takes its handles with a count / prefix-sum / assign sequence, so no
 // counter is shared by the keys of a call.
@@ -147,12 +148,14 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
 constexpr int kChunkKeys = 64;    // keys per handle-allocation chunk
 constexpr int kAssignLanes = 4;   // lanes per key in the assign pass: 64 keys per 256-thread block
 
-// Pass 1 of an insert into a growable table: probe and claim slots; the
-// slot goes to slots[i] for pass 3, no row is written yet.
+// Pass 1 of an insert into a growable table: probe and claim slots, stamp
+// last_seen (kept per slot); the slot goes to slots[i] for pass 3, no row
+// is written yet.
 template <int G>
 __global__ __launch_bounds__(kProbeBlock) void k_foi_claim(TableDev T, const int64_t* __restrict__ keys,
                                                           int64_t n_max, const int64_t* __restrict__ n_dev,
-                                                          int32_t* __restrict__ slots, uint8_t* __restrict__ status) {
+                                                          uint32_t step, int32_t* __restrict__ slots,
+                                                          uint8_t* __restrict__ status) {
     const int64_t n = clamp_count(n_max, n_dev);
     const int lane = lane_id();
     const int gl = lane & (G - 1);
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(kProbeBlock) void k_foi_claim(TableDev T, const int
         int64_t slot;
         const int st = find_or_insert_key<G>(T, keys[i], gl, gshift, &slot);
         if (gl == 0) {
+            if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
             slots[i] = (int32_t)slot;
             status[i] = (uint8_t)st;
         }
@@ -192,11 +196,11 @@ __device__ __forceinline__ int32_t take_handle(int64_t r, int64_t bump, int64_t 
 }
 
 // Pass 3: INSERTED keys take handles in key order (rank within the chunk +
-// the chunk's prefix), record them at their slot, get their initial row and
-// last_seen; slots[i] becomes the handle.
+// the chunk's prefix), record them at their slot and get their initial row;
+// slots[i] becomes the handle.
 __global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const int64_t* __restrict__ keys,
                                                            int64_t n_max, const int64_t* __restrict__ n_dev,
-                                                           uint32_t step, const int32_t* __restrict__ chunk_off,
+                                                           const int32_t* __restrict__ chunk_off,
                                                            const int64_t* __restrict__ state,
                                                            const int32_t* __restrict__ free_stack,
                                                            int32_t* __restrict__ slots,
@@ -225,7 +229,6 @@ __global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const in
             write_initial_row<G>(T, row, keys[i], gl);
             if (gl == 0) {
                 T.rowid[slot] = (int32_t)row;
-                if (T.last_seen) T.last_seen[row] = step;
                 slots[i] = (int32_t)row;
             }
         }
@@ -233,17 +236,13 @@ __global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const in
 }
 
 // Pass 4: FOUND keys read their slot's handle (after pass 3, so a key that
-// another entry of the same call inserted reads the handle just recorded)
-// and stamp last_seen; slots[i] becomes the handle.
-__global__ void k_foi_found(const TableDev T, int64_t n_max, const int64_t* __restrict__ n_dev, uint32_t step,
+// another entry of the same call inserted reads the handle just recorded);
+// slots[i] becomes the handle.
+__global__ void k_foi_found(const TableDev T, int64_t n_max, const int64_t* __restrict__ n_dev,
                             int32_t* __restrict__ slots, const uint8_t* __restrict__ status) {
     const int64_t n = clamp_count(n_max, n_dev);
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        if (status[i] != HT_FOUND) continue;
-        const int32_t row = T.rowid[slots[i]];
-        if (T.last_seen) T.last_seen[row] = step;
-        slots[i] = row;
-    }
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        if (status[i] == HT_FOUND) slots[i] = T.rowid[slots[i]];
 }
 
 // Pass 5 (one thread): the handles taken leave the free stack / bump pointer.
@@ -274,22 +273,43 @@ __global__ void k_erase_finish(int64_t* __restrict__ state, const int32_t* __res
     state[1] += *total;
 }
 
-// Resize: one group of G lanes per old slot re-inserts its live key, with
-// its handle, into the new index (keys are distinct, so every one lands in
-// a free slot; the new index holds no tombstones).
+// Resize: each wavefront loads 64 consecutive old slots (one per lane),
+// ballots the live ones, and its 64/G groups of G lanes re-insert them,
+// with their handle and last_seen, into the new index (keys are distinct,
+// so each lands in a free slot; the new index holds no tombstones).
 template <int G>
 __global__ __launch_bounds__(kProbeBlock) void k_rehash(TableDev O, TableDev N) {
+    constexpr int GROUPS = 64 / G;
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
-    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
-    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
-    for (int64_t s = group0; s < O.capacity; s += ngroups) {
-        const int64_t k = O.keys[s];
-        if (k == kEmpty || k == kTomb) continue;
-        int64_t ns;
-        const int st = find_or_insert_key<G>(N, k, gl, gshift, &ns);
-        if (gl == 0 && st == HT_INSERTED) N.rowid[ns] = O.rowid[s];
+    const int grp = lane / G;
+    const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t s0 = wave * 64; s0 < O.capacity; s0 += nwaves * 64) {
+        const int64_t s = s0 + lane;
+        const int64_t k = s < O.capacity ? O.keys[s] : kEmpty;
+        const bool live = k != kEmpty && k != kTomb;
+        const int32_t rid = live ? O.rowid[s] : 0;
+        const uint32_t ls = (live && O.last_seen) ? O.last_seen[s] : 0u;
+        uint64_t mask = __ballot(live);
+        while (mask) {
+            // group g takes the g-th live lane of what is left
+            uint64_t m = mask;
+            for (int q = 0; q < grp && m; ++q) m &= m - 1;
+            const int src = m ? __builtin_ctzll(m) : -1;
+            const int64_t key = __shfl(k, src < 0 ? 0 : src);
+            const int32_t r = __shfl(rid, src < 0 ? 0 : src);
+            const uint32_t l = __shfl(ls, src < 0 ? 0 : src);
+            int64_t ns = -1;
+            int st = HT_FULL;
+            if (src >= 0) st = find_or_insert_key<G>(N, key, gl, gshift, &ns);
+            if (gl == 0 && src >= 0 && st == HT_INSERTED) {
+                N.rowid[ns] = r;
+                if (N.last_seen) N.last_seen[ns] = l;
+            }
+            for (int q = 0; q < GROUPS && mask; ++q) mask &= mask - 1;
+        }
     }
 }
 
@@ -345,9 +365,8 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_live(TableDev T, int64_t* _
             if (live & (1u << j)) {
                 const int64_t s = start + (int64_t)j * kScanBlock + tid;
                 if (out_keys) out_keys[pos] = k[j];
-                const int64_t row = row_of(T, s);
-                if (out_ls) out_ls[pos] = T.last_seen ? T.last_seen[row] : 0u;
-                if (out_slots) out_slots[pos] = (int32_t)row;
+                if (out_ls) out_ls[pos] = T.last_seen ? T.last_seen[s] : 0u;
+                if (out_slots) out_slots[pos] = (int32_t)row_of(T, s);
                 ++pos;
             }
         }
@@ -439,23 +458,14 @@ void vm_free(VmArray& a) {
     a = VmArray{};
 }
 
-// Maps the row space of a growable table for `rows` handles; new last_seen
-// entries start at 0.
-htl_status grow_row_space(htl_table* t, int64_t rows, hipStream_t stream) {
+// Maps the row space of a growable table for `rows` handles.
+htl_status grow_row_space(htl_table* t, int64_t rows) {
     TableDev& T = t->dev;
     const size_t rb = (size_t)t->dim * T.elem_bytes;
-    const int64_t old_rows = (int64_t)(t->vm_rows.mapped / rb);
     htl_status st = vm_map_to(t->vm_rows, (size_t)rows * rb, t->device);
-    if (st == HTL_OK && T.last_seen) st = vm_map_to(t->vm_last_seen, (size_t)rows * 4, t->device);
     if (st == HTL_OK && T.m) st = vm_map_to(t->vm_m, (size_t)rows * t->dim * 4, t->device);
     if (st == HTL_OK && T.v) st = vm_map_to(t->vm_v, (size_t)rows * t->dim * 4, t->device);
-    if (st != HTL_OK) return st;
-    if (T.last_seen && rows > old_rows) {
-        hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(rows - old_rows, 256 * 8, 1 << 16)), dim3(256), 0, stream,
-                           T.last_seen + old_rows, rows - old_rows, 0u);
-        return check_launch("clear last_seen");
-    }
-    return HTL_OK;
+    return st;
 }
 
 // Per-call temporaries of a growable table for up to n keys.
@@ -494,7 +504,6 @@ htl_status ensure_tmp(htl_table* t, int64_t n) {
 
 void free_growable(htl_table* t) {
     vm_free(t->vm_rows);
-    vm_free(t->vm_last_seen);
     vm_free(t->vm_m);
     vm_free(t->vm_v);
     RowAlloc& A = t->alloc;
@@ -550,6 +559,7 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
 
     auto cleanup = [&]() {
         if (T.keys) (void)hipFree(T.keys);
+        if (T.last_seen && growable) (void)hipFree(T.last_seen);
         if (growable) {
             free_growable(t);
         } else {
@@ -573,18 +583,18 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
         }
         const size_t R = (size_t)1 << t->max_capacity_log2;
         htl_status st = vm_reserve(t->vm_rows, R * (size_t)dim * T.elem_bytes, t->device);
-        if (st == HTL_OK && (flags & HT_META_LAST_SEEN)) st = vm_reserve(t->vm_last_seen, R * 4, t->device);
         if (st == HTL_OK && (flags & HT_ADAM_STATE)) st = vm_reserve(t->vm_m, R * dim * 4, t->device);
         if (st == HTL_OK && (flags & HT_ADAM_STATE)) st = vm_reserve(t->vm_v, R * dim * 4, t->device);
         if (st == HTL_OK) {
             T.rows = t->vm_rows.base;
-            T.last_seen = (uint32_t*)t->vm_last_seen.base;
             T.m = (float*)t->vm_m.base;
             T.v = (float*)t->vm_v.base;
-            st = grow_row_space(t, (int64_t)M, stream);
+            st = grow_row_space(t, (int64_t)M);
         }
         if (st == HTL_OK && (hipMalloc((void**)&T.keys, M * sizeof(int64_t)) != hipSuccess ||
                              hipMalloc((void**)&T.rowid, M * 4) != hipSuccess ||
+                             ((flags & HT_META_LAST_SEEN) &&
+                              hipMalloc((void**)&T.last_seen, M * 4) != hipSuccess) ||
                              hipMalloc((void**)&t->alloc.free_stack, M * 4) != hipSuccess ||
                              hipMalloc((void**)&t->alloc.state, 2 * sizeof(int64_t)) != hipSuccess)) {
             (void)hipGetLastError();
@@ -595,6 +605,11 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
             st = check_launch("ht_create: row allocator");
         }
         if (st == HTL_OK) st = fill_keys_empty(T, stream);
+        if (st == HTL_OK && T.last_seen) {
+            hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, stream,
+                               T.last_seen, T.capacity, 0u);
+            st = check_launch("clear last_seen");
+        }
         if (st != HTL_OK) {
             std::string msg = g_last_error;
             cleanup();
@@ -637,6 +652,7 @@ htl_status ht_destroy(htl_table* t) {
     TableDev& T = t->dev;
     (void)hipFree(T.keys);
     if (t->flags & HT_GROWABLE) {
+        if (T.last_seen) (void)hipFree(T.last_seen);
         free_growable(t);
     } else {
         (void)hipFree(T.rows);
@@ -674,15 +690,18 @@ htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream) {
     N.bucket_mask = (uint64_t)(N.capacity >> N.bucket_log2) - 1;
     N.keys = nullptr;
     N.rowid = nullptr;
+    N.last_seen = nullptr;
     int32_t* new_stack = nullptr;
     const size_t M2 = (size_t)N.capacity;
-    htl_status st = grow_row_space(t, N.capacity, stream);
+    htl_status st = grow_row_space(t, N.capacity);
     if (st != HTL_OK) return st;
     if (hipMalloc((void**)&N.keys, M2 * sizeof(int64_t)) != hipSuccess ||
-        hipMalloc((void**)&N.rowid, M2 * 4) != hipSuccess || hipMalloc((void**)&new_stack, M2 * 4) != hipSuccess) {
+        hipMalloc((void**)&N.rowid, M2 * 4) != hipSuccess || hipMalloc((void**)&new_stack, M2 * 4) != hipSuccess ||
+        (O.last_seen && hipMalloc((void**)&N.last_seen, M2 * 4) != hipSuccess)) {
         (void)hipGetLastError();
         if (N.keys) (void)hipFree(N.keys);
         if (N.rowid) (void)hipFree(N.rowid);
+        if (N.last_seen) (void)hipFree(N.last_seen);
         if (new_stack) (void)hipFree(new_stack);
         return fail(HTL_ERR_NOMEM, "ht_resize: device allocation failed");
     }
@@ -693,7 +712,7 @@ htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream) {
         st = fail(HTL_ERR_DEVICE, "ht_resize: copy of the free handles failed");
     }
     if (st == HTL_OK) {
-        hipLaunchKernelGGL(k_rehash<4>, dim3(grid_for(O.capacity, kProbeBlock / 4, 1 << 16)), dim3(kProbeBlock), 0,
+        hipLaunchKernelGGL(k_rehash<4>, dim3(grid_for(O.capacity, kProbeBlock, 1 << 16)), dim3(kProbeBlock), 0,
                            stream, O, N);
         st = check_launch("ht_resize: rehash");
     }
@@ -706,11 +725,13 @@ htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream) {
         (void)hipStreamSynchronize(stream);
         (void)hipFree(N.keys);
         (void)hipFree(N.rowid);
+        if (N.last_seen) (void)hipFree(N.last_seen);
         (void)hipFree(new_stack);
         return fail(st, msg);
     }
     (void)hipFree(O.keys);
     (void)hipFree(O.rowid);
+    if (O.last_seen) (void)hipFree(O.last_seen);
     (void)hipFree(t->alloc.free_stack);
     t->alloc.free_stack = new_stack;
     t->dev = N;
@@ -738,7 +759,7 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         const int64_t nchunks = ceil_div(n_max, kChunkKeys);
 #define HTL_CLAIM(GG)                                                                                        \
     hipLaunchKernelGGL(k_foi_claim<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev, \
-                       slots, status)
+                       step, slots, status)
         switch (G) {
             case 1: HTL_CLAIM(1); break;
             case 2: HTL_CLAIM(2); break;
@@ -752,9 +773,9 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
         if (st != HTL_OK) return st;
         hipLaunchKernelGGL(k_foi_assign, dim3(grid_for(nchunks, 1, 1 << 16)), dim3(kProbeBlock), 0, stream, t->dev,
-                           keys, n_max, n_dev, step, A.chunk_off, A.state, A.free_stack, slots, status);
+                           keys, n_max, n_dev, A.chunk_off, A.state, A.free_stack, slots, status);
         hipLaunchKernelGGL(k_foi_found, dim3(grid_for(n_max, 256 * 4)), dim3(256), 0, stream, t->dev, n_max, n_dev,
-                           step, slots, status);
+                           slots, status);
         hipLaunchKernelGGL(k_foi_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
         return check_launch("ht_find_or_insert");
     }

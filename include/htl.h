@@ -89,10 +89,11 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u };
  *
  * Growable tables ([MTGR] section 5: keys map to vectors and metadata, and
  * capacity grows by copying the key storage, not the embeddings): the key
- * index (keys int64[M] + a row handle int32[M] per slot) is separate from the
- * row space (rows, last_seen, m, v indexed by row handle).  The row space is
- * a reserved virtual range of up to 2^min(30, capacity_log2 + 8) rows, of
- * which M are mapped; ht_resize maps more and rehashes only the index.  In
+ * index (keys int64[M], a row handle int32[M] and last_seen uint32[M] per
+ * slot) is separate from the row space (rows, m, v indexed by row handle).
+ * The row space is a reserved virtual range of up to
+ * 2^min(30, capacity_log2 + 8) rows, of which M are mapped; ht_resize maps
+ * more and rehashes only the index.  In
  * such a table every "slot" that a call returns or takes (ht_find_or_insert,
  * ht_scan, emb_gather_pool, emb_rowwise_adam) is a row handle: stable for as
  * long as its key stays live, across resizes; the handle of an erased key is
@@ -114,8 +115,8 @@ htl_status ht_clear(htl_table* t, hipStream_t stream);
  * section 5: capacity expansion replicates the key storage, not the
  * embeddings).  Maps row space for the new capacity, builds a new key index
  * (every live key re-inserted with its row handle; tombstones are dropped),
- * then frees the old index.  Rows, last_seen and Adam moments do not move,
- * so every row handle stays valid.  new_capacity_log2 may equal the current
+ * then frees the old index.  Rows and Adam moments do not move, so every
+ * row handle stays valid; last_seen moves with its key.  new_capacity_log2 may equal the current
  * one (a rehash that only drops tombstones).  Synchronises `stream` before it
  * frees the old index; allocates device memory (hipMalloc / hipMemMap).
  * Errors: INVALID if the table is not growable, or new_capacity_log2 is below
@@ -182,9 +183,9 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
 
 /* ht_view -- raw device views of the table's storage (read-only use intended).
  * Any output may be null.  rows is dtype[M][dim]; m, v are null unless the
- * table keeps Adam state; last_seen is null unless it keeps metadata.  In a
- * growable table rows, last_seen, m and v are indexed by row handle, and
- * row_of_slot (int32[M], valid at live slots) maps a slot to its handle;
+ * table keeps Adam state; last_seen (per slot) is null unless it keeps
+ * metadata.  In a growable table rows, m and v are indexed by row handle,
+ * and row_of_slot (int32[M], valid at live slots) maps a slot to its handle;
  * row_of_slot is null for other tables (handle = slot). */
 typedef struct {
     int64_t capacity;

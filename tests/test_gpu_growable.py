@@ -60,8 +60,17 @@ def test_resize_keeps_handles_rows_and_state(htl, orc):
     otab.find_or_insert(live, step=9)
     g = torch.from_numpy(rng.standard_normal((live.size, dim)).astype(np.float32)).cuda()
     htl.rowwise_adam(table, h0, g, None, 1e-3, 0.9, 0.999, 1e-8, 1)
-    before = {n: to_np(htl.table_tensor(table, n))[to_np(h0)] for n in ("rows", "adam_m", "adam_v", "last_seen")}
+    before = {n: to_np(htl.table_tensor(table, n))[to_np(h0)] for n in ("rows", "adam_m", "adam_v")}
     assert np.count_nonzero(to_np(htl.table_keys(table)) == htl.TOMBSTONE_KEY) == gone.size
+
+    def live_state():
+        k, ls, h, n = table.scan()
+        L = int(n.item())
+        o = np.argsort(to_np(k)[:L])
+        return to_np(k)[:L][o], to_np(ls)[:L][o], to_np(h)[:L][o]
+
+    ks0, ls0, hs0 = live_state()
+    assert np.array_equal(ks0, live) and np.all(ls0 == 9)
 
     table.resize(12)
     otab.resize(1 << 12)
@@ -71,6 +80,8 @@ def test_resize_keeps_handles_rows_and_state(htl, orc):
     assert np.array_equal(np.sort(k_after[k_after >= 0]), live)
     for n, b in before.items():                                           # rows did not move
         assert np.array_equal(to_np(htl.table_tensor(table, n))[to_np(h0)], b), n
+    ks1, ls1, hs1 = live_state()                                          # last_seen moved with its key
+    assert np.array_equal(ks1, ks0) and np.array_equal(ls1, ls0) and np.array_equal(hs1, hs0)
     h1, st1 = table.find_or_insert(l_d, step=11)
     assert np.all(to_np(st1) == htl.FOUND)
     assert np.array_equal(to_np(h1), to_np(h0))                           # handles are stable
