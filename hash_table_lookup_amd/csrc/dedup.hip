@@ -29,6 +29,8 @@
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
 // more than 3n/2 slots it always ends at a free slot (load at most 2/3: the
 // set is cleared on every call, so its size is traded against that clear).
+// The set is capped at 2^30 slots (its slot numbers, and the extra entry of
+// key -1 at index 2^30, stay int32); with n < 2^30 a slot is always free.
 // Every int64 is a valid key: the value -1, which both sets use as their
 // empty marker, is carried out of band.
 #include "scan.h"
@@ -58,7 +60,7 @@ DedupWs layout(int64_t n, char* base) {
     DedupWs w{};
     const int64_t ntiles = ceil_div(n, kTile);
     uint64_t cap = 256;
-    while (cap <= (uint64_t)(n + n / 2)) cap <<= 1;
+    while (cap <= (uint64_t)(n + n / 2) && cap < ((uint64_t)1 << 30)) cap <<= 1;   // slot indices stay int32
     w.cap = cap;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -190,9 +192,12 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_count(const int32_t* _
 
 // Stage 2c: owned keys get dense ids in (tile, position in tile) order.  In
 // ordered mode that is the order of first occurrence in the whole batch.
+// An owner also leaves its id in its own survivor entry (tu_slot becomes
+// -(id + 1)), so that compose reads it there, in sequence, and only the
+// survivors that do not own their key read the id at the set slot.
 template <bool ORDERED>
 __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
-    const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, const int32_t* __restrict__ tu_slot,
+    const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count, int32_t* __restrict__ tu_slot,
     const uint8_t* __restrict__ tu_own, int64_t ntiles, const int32_t* __restrict__ set_owner,
     const int32_t* __restrict__ tile_off, int32_t* __restrict__ set_ids, int64_t* __restrict__ unique,
     int64_t* __restrict__ n_unique) {
@@ -214,6 +219,7 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
             if (own) {
                 set_ids[p] = run + r;
                 unique[run + r] = tu_keys[tile * kTile + j];
+                tu_slot[tile * kTile + j] = -(run + r) - 1;
             }
             run += tot;
         }
@@ -221,7 +227,8 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
 }
 
 // inverse[i] = id of the set slot of tile survivor local[i]: each block takes
-// one tile, fetches its survivors' ids once into LDS, then maps its IDs.
+// one tile, fetches its survivors' ids once into LDS (an owner's from its
+// own entry, the others' from the set), then maps its IDs.
 __global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* __restrict__ local, int64_t n,
                                                                const int32_t* __restrict__ tu_count,
                                                                const int32_t* __restrict__ tu_slot,
@@ -230,7 +237,10 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* 
     __shared__ int32_t s_gid[kTile];
     for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
         const int cnt = tu_count[tile];
-        for (int j = threadIdx.x; j < cnt; j += kTileThreads) s_gid[j] = set_ids[tu_slot[tile * kTile + j]];
+        for (int j = threadIdx.x; j < cnt; j += kTileThreads) {
+            const int32_t v = tu_slot[tile * kTile + j];
+            s_gid[j] = v < 0 ? -(v + 1) : set_ids[v];
+        }
         __syncthreads();
         const int64_t base = tile * kTile;
         for (int q = threadIdx.x; q < kTile; q += kTileThreads) {
