@@ -13,6 +13,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,8 @@ _SIGNATURES = {
     "ht_find_or_insert": [_P, _P, _I64, _P, _U32, _P, _P, _P],
     "ht_erase": [_P, _P, _I64, _P, _P],
     "ht_scan": [_P, _P, _P, _P, _P, _P],
+    "ht_export": [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P],
+    "ht_import": [_P, _P, _I64, _P, _P, _P, _P, _P, _P],
     "lru_workspace_bytes": [_P],
     "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
     "ht_view": [_P, ctypes.POINTER(_View)],
@@ -223,6 +226,72 @@ class Table:
         n = torch.empty(1, dtype=torch.int64, device=self.device)
         _check(lib().ht_scan(self._h, _ptr(keys), _ptr(ls), _ptr(slots), _ptr(n), _stream()))
         return keys, ls, slots, n
+
+    def export(self, begin: int = 0, end: Optional[int] = None):
+        """Live entries of slots [begin, end) in slot order: dict of tensors
+        (keys, rows, last_seen / adam_m / adam_v when kept) and n (device int64)."""
+        end = self.capacity if end is None else end
+        cap = max(end - begin, 1)
+        d = {"keys": torch.empty(cap, dtype=torch.int64, device=self.device),
+             "rows": torch.empty((cap, self.dim), dtype=self.row_dtype, device=self.device)}
+        v = self.view()
+        if v.last_seen:
+            d["last_seen"] = torch.empty(cap, dtype=torch.int32, device=self.device)
+        if v.adam_m:
+            d["adam_m"] = torch.empty((cap, self.dim), dtype=torch.float32, device=self.device)
+            d["adam_v"] = torch.empty((cap, self.dim), dtype=torch.float32, device=self.device)
+        n = torch.empty(1, dtype=torch.int64, device=self.device)
+        _check(lib().ht_export(self._h, begin, end, _ptr(d["keys"]), _ptr(d["rows"]), _ptr(d.get("last_seen")),
+                               _ptr(d.get("adam_m")), _ptr(d.get("adam_v")), _ptr(n), _stream()))
+        d["n"] = n
+        return d
+
+    def import_(self, keys: torch.Tensor, rows: torch.Tensor, last_seen=None, adam_m=None, adam_v=None):
+        """Insert keys with the given rows (and metadata); returns the status per key."""
+        keys = _dev(keys, torch.int64, "keys")
+        rows = _dev(rows, self.row_dtype, "rows")
+        if last_seen is not None:
+            last_seen = _dev(last_seen, torch.int32, "last_seen")
+        if adam_m is not None:
+            adam_m = _dev(adam_m, torch.float32, "adam_m")
+            adam_v = _dev(adam_v, torch.float32, "adam_v")
+        status = torch.empty(keys.numel(), dtype=torch.uint8, device=keys.device)
+        _check(lib().ht_import(self._h, _ptr(keys), keys.numel(), _ptr(rows), _ptr(last_seen), _ptr(adam_m),
+                               _ptr(adam_v), _ptr(status), _stream()))
+        return status
+
+    def checkpoint(self, chunk_slots: int = 1 << 24):
+        """The whole live state as host numpy arrays, exported range by range
+        (device buffers of chunk_slots entries)."""
+        parts = {}
+        for b in range(0, self.capacity, chunk_slots):
+            d = self.export(b, min(b + chunk_slots, self.capacity))
+            n = int(d.pop("n").item())
+            for name, t in d.items():
+                t = t[:n]
+                if t.dtype == torch.bfloat16:           # bf16 rows travel as their bits
+                    t = t.view(torch.int16)
+                parts.setdefault(name, []).append(t.cpu().numpy())
+        return {name: np.concatenate(v) for name, v in parts.items()}
+
+    def restore(self, ck, chunk: int = 1 << 24):
+        """Import a checkpoint() (in chunks of `chunk` keys); returns the statuses."""
+        out = []
+        n = ck["keys"].shape[0]
+
+        def part(name, b, e):
+            if name not in ck:
+                return None
+            return torch.from_numpy(np.ascontiguousarray(ck[name][b:e])).to(self.device)
+
+        for b in range(0, n, chunk):
+            e = min(b + chunk, n)
+            rows = part("rows", b, e)
+            if self.dtype == BF16:
+                rows = rows.view(torch.bfloat16)
+            out.append(self.import_(part("keys", b, e), rows, part("last_seen", b, e),
+                                    part("adam_m", b, e), part("adam_v", b, e)))
+        return torch.cat(out) if out else torch.empty(0, dtype=torch.uint8, device=self.device)
 
     def lru_select(self, num: int, den: int, victims_cap: Optional[int] = None):
         """(victims, n_victims): the floor(live*num/den) least recently used keys."""

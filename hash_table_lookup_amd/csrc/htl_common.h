@@ -69,7 +69,8 @@ struct VmArray {
     std::vector<size_t> sizes;
 };
 
-// Row-handle bookkeeping of a growable table (device memory).
+// Row-handle bookkeeping of a growable table, and per-call temporaries of
+// any table (device memory, allocated on first use).
 struct RowAlloc {
     int64_t* state = nullptr;      // [0] next never-used row, [1] handles on the free stack
     int32_t* free_stack = nullptr; // [rows]
@@ -80,6 +81,12 @@ struct RowAlloc {
     void* scan_tmp = nullptr;
     void* tmp_base = nullptr;      // one allocation holding the temporaries
     int64_t tmp_keys = 0;          // keys the temporaries are sized for
+    // export temporaries: per 4096-slot chunk counts and their prefix
+    int32_t* exp_cnt = nullptr;
+    int32_t* exp_off = nullptr;
+    void* exp_scan = nullptr;
+    void* exp_base = nullptr;
+    int64_t exp_chunks = 0;
 };
 
 }  // namespace htl
@@ -93,10 +100,9 @@ struct htl_table {
     uint32_t flags;
     uint32_t max_step;   // largest step any find-or-insert stamped since create/clear
     htl::TableDev dev;
-    // growable tables only
     int max_capacity_log2;
-    htl::VmArray vm_rows, vm_m, vm_v;
-    htl::RowAlloc alloc;
+    htl::VmArray vm_rows, vm_m, vm_v;   // growable tables only
+    htl::RowAlloc alloc;                // handles: growable only; temporaries: any table
 };
 
 namespace htl {

@@ -1,5 +1,5 @@
 // Bucket-walk helpers of the dynamic table, shared by the find-or-insert,
-// erase and fused lookup kernels (internal header).
+// erase, import and rehash kernels (internal header).
 //
 // MTGenRec (arXiv 2505.12663) Theorem 1: in a table of 2^n slots the walk
 // h_t = h_0 + t*S mod 2^n visits every slot iff S is odd.  Here the walk is
@@ -110,6 +110,30 @@ __device__ __forceinline__ void probe_bucket(const int64_t* bucket, int64_t k, i
         free_val = __shfl(fv, gshift + l);
     }
     has_empty = group_bits<G>(__ballot(emp), gshift) != 0;
+}
+
+// Walks the table for key k with the G lanes of this group, without
+// inserting: returns the slot holding k, or -1 (the walk ends at the first
+// bucket with an EMPTY slot, or after every bucket).
+template <int G>
+__device__ __forceinline__ int64_t find_key(const TableDev& T, int64_t k, int gl, int gshift) {
+    if (k == kEmpty || k == kTomb) return -1;
+    const int W = 1 << T.bucket_log2;
+    const uint64_t nb = T.bucket_mask + 1;
+    const uint64_t h = mix64((uint64_t)k ^ T.salt);
+    const uint64_t S = ((h >> 32) | 1ull) & T.bucket_mask;
+    uint64_t b = h & T.bucket_mask;
+    for (uint64_t t = 0; t < nb; ++t) {
+        const int64_t base = (int64_t)(b << T.bucket_log2);
+        int hit, fs;
+        int64_t fv;
+        bool has_empty;
+        probe_bucket<G>(T.keys + base, k, gl, gshift, 0, W, hit, fs, fv, has_empty);
+        if (hit >= 0) return base + hit;
+        if (has_empty) return -1;
+        b = (b + S) & T.bucket_mask;
+    }
+    return -1;
 }
 
 // Walks the table for key k with the G lanes of this group and returns its

@@ -313,6 +313,182 @@ __global__ __launch_bounds__(kProbeBlock) void k_rehash(TableDev O, TableDev N) 
     }
 }
 
+// ------------------------------------------------------- checkpoint --
+// Export of a slot range in chunks of kExpChunk slots, one block each: count
+// the live slots, prefix the counts, then write each chunk's live entries in
+// slot order (MTGR section 5: compact key scanning).
+constexpr int kExpChunk = 4096;
+constexpr int kExpThreads = 256;
+constexpr int kExpPerThread = kExpChunk / kExpThreads;   // consecutive slots per thread
+
+__device__ __forceinline__ bool is_live(int64_t k) { return k != kEmpty && k != kTomb; }
+
+__device__ __forceinline__ int block_sum_prefix(int& v, int* s_wave) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    int incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kExpThreads / 64; ++w) {
+        const int c = s_wave[w];
+        before += (w < wid) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    v = before + incl - v;
+    return tot;
+}
+
+__global__ __launch_bounds__(kExpThreads) void k_exp_count(TableDev T, int64_t begin, int64_t end, int64_t nchunks,
+                                                          int32_t* __restrict__ cnt) {
+    __shared__ int s_wave[kExpThreads / 64];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t s0 = begin + c * kExpChunk + (int64_t)threadIdx.x * kExpPerThread;
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < kExpPerThread; ++j) {
+            const int64_t s = s0 + j;
+            if (s < end && is_live(T.keys[s])) ++mine;
+        }
+        const int tot = block_sum_prefix(mine, s_wave);
+        if (threadIdx.x == 0) cnt[c] = tot;
+    }
+}
+
+__global__ __launch_bounds__(kExpThreads) void k_exp_write(TableDev T, int64_t begin, int64_t end, int64_t nchunks,
+                                                          const int32_t* __restrict__ off,
+                                                          int64_t* __restrict__ keys_out, void* __restrict__ rows_out,
+                                                          uint32_t* __restrict__ ls_out, float* __restrict__ m_out,
+                                                          float* __restrict__ v_out) {
+    __shared__ int s_wave[kExpThreads / 64];
+    __shared__ int32_t s_row[kExpChunk];     // row handle of the chunk's e-th live entry
+    const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t s0 = begin + c * kExpChunk + (int64_t)threadIdx.x * kExpPerThread;
+        int64_t k[kExpPerThread];
+        uint32_t live = 0;
+#pragma unroll
+        for (int j = 0; j < kExpPerThread; ++j) {
+            const int64_t s = s0 + j;
+            k[j] = s < end ? T.keys[s] : kEmpty;
+            if (is_live(k[j])) live |= 1u << j;
+        }
+        int pos = __popc(live);
+        const int total = block_sum_prefix(pos, s_wave);     // thread-major = slot order
+        const int64_t base = off[c];
+#pragma unroll
+        for (int j = 0; j < kExpPerThread; ++j) {
+            if (!(live & (1u << j))) continue;
+            if (keys_out) keys_out[base + pos] = k[j];
+            if (ls_out) ls_out[base + pos] = T.last_seen[s0 + j];
+            s_row[pos] = (int32_t)row_of(T, s0 + j);
+            ++pos;
+        }
+        __syncthreads();
+        if (rows_out) {
+            if ((row_bytes & 15) == 0) {
+                const int vpr = (int)(row_bytes >> 4);
+                const u32x4* src = reinterpret_cast<const u32x4*>(T.rows);
+                u32x4* dst = reinterpret_cast<u32x4*>(rows_out);
+                for (int64_t q = threadIdx.x; q < (int64_t)total * vpr; q += kExpThreads) {
+                    const int64_t e = q / vpr, v = q - e * vpr;
+                    dst[(base + e) * vpr + v] = src[(int64_t)s_row[e] * vpr + v];
+                }
+            } else if (T.elem_bytes == 4) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(T.rows);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(rows_out);
+                for (int64_t q = threadIdx.x; q < (int64_t)total * T.dim; q += kExpThreads) {
+                    const int64_t e = q / T.dim, j = q - e * T.dim;
+                    dst[(base + e) * T.dim + j] = src[(int64_t)s_row[e] * T.dim + j];
+                }
+            } else {
+                const uint16_t* src = reinterpret_cast<const uint16_t*>(T.rows);
+                uint16_t* dst = reinterpret_cast<uint16_t*>(rows_out);
+                for (int64_t q = threadIdx.x; q < (int64_t)total * T.dim; q += kExpThreads) {
+                    const int64_t e = q / T.dim, j = q - e * T.dim;
+                    dst[(base + e) * T.dim + j] = src[(int64_t)s_row[e] * T.dim + j];
+                }
+            }
+        }
+        if (m_out || v_out) {
+            for (int64_t q = threadIdx.x; q < (int64_t)total * T.dim; q += kExpThreads) {
+                const int64_t e = q / T.dim, j = q - e * T.dim;
+                const int64_t from = (int64_t)s_row[e] * T.dim + j;
+                if (m_out) m_out[(base + e) * T.dim + j] = T.m[from];
+                if (v_out) v_out[(base + e) * T.dim + j] = T.v[from];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_exp_total(const int32_t* __restrict__ total, int64_t* __restrict__ n_dev) { *n_dev = *total; }
+
+// Import: rows and Adam moments of the keys that are live after the
+// find-or-insert (FOUND or INSERTED) are written at their handle.
+__global__ void k_imp_rows(TableDev T, int64_t n, const int32_t* __restrict__ handles,
+                           const uint8_t* __restrict__ status, const void* __restrict__ rows_in,
+                           const float* __restrict__ m_in, const float* __restrict__ v_in) {
+    const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if ((row_bytes & 15) == 0) {
+        const int vpr = (int)(row_bytes >> 4);
+        const u32x4* src = reinterpret_cast<const u32x4*>(rows_in);
+        u32x4* dst = reinterpret_cast<u32x4*>(T.rows);
+        for (int64_t q = t0; q < n * vpr; q += stride) {
+            const int64_t i = q / vpr, v = q - i * vpr;
+            const int st = status[i];
+            if (st == HT_FOUND || st == HT_INSERTED) dst[(int64_t)handles[i] * vpr + v] = src[i * vpr + v];
+        }
+    } else {
+        for (int64_t q = t0; q < n * T.dim; q += stride) {
+            const int64_t i = q / T.dim, j = q - i * T.dim;
+            const int st = status[i];
+            if (st != HT_FOUND && st != HT_INSERTED) continue;
+            const int64_t to = (int64_t)handles[i] * T.dim + j;
+            if (T.elem_bytes == 4)
+                reinterpret_cast<uint32_t*>(T.rows)[to] = reinterpret_cast<const uint32_t*>(rows_in)[i * T.dim + j];
+            else
+                reinterpret_cast<uint16_t*>(T.rows)[to] = reinterpret_cast<const uint16_t*>(rows_in)[i * T.dim + j];
+        }
+    }
+    if (m_in) {
+        for (int64_t q = t0; q < n * T.dim; q += stride) {
+            const int64_t i = q / T.dim, j = q - i * T.dim;
+            const int st = status[i];
+            if (st != HT_FOUND && st != HT_INSERTED) continue;
+            const int64_t to = (int64_t)handles[i] * T.dim + j;
+            T.m[to] = m_in[i * T.dim + j];
+            T.v[to] = v_in[i * T.dim + j];
+        }
+    }
+}
+
+// Import: last_seen of the live keys, at their slot (found again by a walk:
+// in a growable table the handle is not the slot).
+template <int G>
+__global__ __launch_bounds__(kProbeBlock) void k_imp_ls(TableDev T, const int64_t* __restrict__ keys, int64_t n,
+                                                       const uint8_t* __restrict__ status,
+                                                       const uint32_t* __restrict__ ls_in) {
+    const int lane = lane_id();
+    const int gl = lane & (G - 1);
+    const int gshift = lane & ~(G - 1);
+    const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
+    const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
+    for (int64_t i = group0; i < n; i += ngroups) {
+        const int st = status[i];
+        if (st != HT_FOUND && st != HT_INSERTED) continue;
+        const int64_t slot = find_key<G>(T, keys[i], gl, gshift);
+        if (gl == 0 && slot >= 0) T.last_seen[slot] = ls_in[i];
+    }
+}
+
 // Compact scan of live slots.  Each block owns a contiguous range of
 // kScanPerBlock slots, counts its live slots, reserves an output range with
 // one atomic, and writes them there (thread-major order within the block).
@@ -502,17 +678,56 @@ htl_status ensure_tmp(htl_table* t, int64_t n) {
     return HTL_OK;
 }
 
+void free_temporaries(htl_table* t) {
+    RowAlloc& A = t->alloc;
+    if (A.tmp_base) (void)hipFree(A.tmp_base);
+    if (A.exp_base) (void)hipFree(A.exp_base);
+    A.tmp_base = A.exp_base = nullptr;
+    A.tmp_keys = A.exp_chunks = 0;
+}
+
 void free_growable(htl_table* t) {
     vm_free(t->vm_rows);
     vm_free(t->vm_m);
     vm_free(t->vm_v);
+    free_temporaries(t);
     RowAlloc& A = t->alloc;
     if (A.state) (void)hipFree(A.state);
     if (A.free_stack) (void)hipFree(A.free_stack);
-    if (A.tmp_base) (void)hipFree(A.tmp_base);
     A = RowAlloc{};
     if (t->dev.rowid) (void)hipFree(t->dev.rowid);
     t->dev.rowid = nullptr;
+}
+
+// Export temporaries for ranges of up to nchunks chunks.
+htl_status ensure_exp(htl_table* t, int64_t nchunks) {
+    RowAlloc& A = t->alloc;
+    if (nchunks <= A.exp_chunks) return HTL_OK;
+    if (A.exp_base) {
+        HTL_HIP(hipDeviceSynchronize());
+        (void)hipFree(A.exp_base);
+        A.exp_base = nullptr;
+        A.exp_chunks = 0;
+    }
+    size_t off = 0;
+    auto take = [&](size_t b) {
+        const size_t o = off;
+        off = align_up(off + b, 256);
+        return o;
+    };
+    const size_t o_cnt = take((size_t)nchunks * 4), o_off = take((size_t)(nchunks + 1) * 4);
+    const size_t o_scan = take(scan_temp_bytes(nchunks));
+    if (hipMalloc(&A.exp_base, off) != hipSuccess) {
+        (void)hipGetLastError();
+        A.exp_base = nullptr;
+        return fail(HTL_ERR_NOMEM, "ht_export: temporaries allocation failed");
+    }
+    char* b = (char*)A.exp_base;
+    A.exp_cnt = (int32_t*)(b + o_cnt);
+    A.exp_off = (int32_t*)(b + o_off);
+    A.exp_scan = b + o_scan;
+    A.exp_chunks = nchunks;
+    return HTL_OK;
 }
 
 }  // namespace htl
@@ -655,6 +870,7 @@ htl_status ht_destroy(htl_table* t) {
         if (T.last_seen) (void)hipFree(T.last_seen);
         free_growable(t);
     } else {
+        free_temporaries(t);
         (void)hipFree(T.rows);
         if (T.last_seen) (void)hipFree(T.last_seen);
         if (T.m) (void)hipFree(T.m);
@@ -833,6 +1049,72 @@ htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32
                        dim3(kScanBlock), 0, stream, t->dev, keys, last_seen, slots,
                        (unsigned long long*)n_live_dev);
     return check_launch("ht_scan");
+}
+
+htl_status ht_export(const htl_table* tc, int64_t slot_begin, int64_t slot_end, int64_t* keys, void* rows,
+                     uint32_t* last_seen, float* adam_m, float* adam_v, int64_t* n_dev, hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(tc != nullptr, "ht_export: null table");
+    htl_table* t = const_cast<htl_table*>(tc);     // only its call temporaries change
+    const TableDev& T = t->dev;
+    HTL_REQUIRE(slot_begin >= 0 && slot_begin <= slot_end && slot_end <= T.capacity,
+                "ht_export: need 0 <= slot_begin <= slot_end <= capacity");
+    HTL_REQUIRE(n_dev && aligned(n_dev, 8), "ht_export: null or misaligned n_dev");
+    HTL_REQUIRE(!keys || aligned(keys, 8), "ht_export: misaligned keys");
+    HTL_REQUIRE(!rows || aligned(rows, ((int64_t)T.dim * T.elem_bytes) % 16 == 0 ? 16 : T.elem_bytes),
+                "ht_export: misaligned rows");
+    HTL_REQUIRE(!last_seen || T.last_seen, "ht_export: the table keeps no last_seen");
+    HTL_REQUIRE((!adam_m && !adam_v) || T.m, "ht_export: the table keeps no Adam state");
+    const int64_t nchunks = ceil_div(slot_end - slot_begin, kExpChunk);
+    if (nchunks == 0) {
+        hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, stream, n_dev);
+        return check_launch("ht_export");
+    }
+    htl_status st = ensure_exp(t, ceil_div(T.capacity, kExpChunk));
+    if (st != HTL_OK) return st;
+    RowAlloc& A = t->alloc;
+    const unsigned grid = grid_for(nchunks, 1, 1 << 16);
+    hipLaunchKernelGGL(k_exp_count, dim3(grid), dim3(kExpThreads), 0, stream, T, slot_begin, slot_end, nchunks,
+                       A.exp_cnt);
+    st = scan_exclusive_i32(A.exp_cnt, A.exp_off, nchunks, nullptr, kScanIdentity, 1, A.exp_scan, stream);
+    if (st != HTL_OK) return st;
+    hipLaunchKernelGGL(k_exp_write, dim3(grid), dim3(kExpThreads), 0, stream, T, slot_begin, slot_end, nchunks,
+                       A.exp_off, keys, rows, last_seen, adam_m, adam_v);
+    hipLaunchKernelGGL(k_exp_total, dim3(1), dim3(1), 0, stream, A.exp_off + nchunks, n_dev);
+    return check_launch("ht_export");
+}
+
+htl_status ht_import(htl_table* t, const int64_t* keys, int64_t n, const void* rows, const uint32_t* last_seen,
+                     const float* adam_m, const float* adam_v, uint8_t* status, hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(t != nullptr, "ht_import: null table");
+    HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "ht_import: n out of range");
+    if (n == 0) return HTL_OK;
+    const TableDev& T0 = t->dev;
+    HTL_REQUIRE(keys && rows && status && aligned(keys, 8), "ht_import: null or misaligned keys/rows/status");
+    HTL_REQUIRE(aligned(rows, ((int64_t)T0.dim * T0.elem_bytes) % 16 == 0 ? 16 : T0.elem_bytes),
+                "ht_import: misaligned rows");
+    HTL_REQUIRE(!last_seen || T0.last_seen, "ht_import: the table keeps no last_seen");
+    HTL_REQUIRE((!adam_m && !adam_v) || (adam_m && adam_v && T0.m), "ht_import: Adam state needs both m and v "
+                                                                    "and a table that keeps it");
+    htl_status st = ensure_tmp(t, n);
+    if (st != HTL_OK) return st;
+    int32_t* handles = t->alloc.row_tmp;
+    const uint32_t keep_step = t->max_step;
+    st = ht_find_or_insert(t, keys, n, nullptr, 0u, handles, status, stream);
+    if (st != HTL_OK) return st;
+    t->max_step = keep_step;
+    const TableDev& T = t->dev;
+    const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
+    const int64_t items = (row_bytes % 16 == 0) ? n * (row_bytes / 16) : n * T.dim;
+    hipLaunchKernelGGL(k_imp_rows, dim3(grid_for(items > n * T.dim ? items : n * T.dim, 256 * 4)), dim3(256), 0,
+                       stream, T, n, handles, status, rows, adam_m, adam_v);
+    if (last_seen) {
+        hipLaunchKernelGGL(k_imp_ls<4>, dim3(grid_for(n, kProbeBlock / 4)), dim3(kProbeBlock), 0, stream, T, keys, n,
+                           status, last_seen);
+        t->max_step = 0xFFFFFFFFu;       // values unknown on the host: selections check all four digits
+    }
+    return check_launch("ht_import");
 }
 
 htl_status ht_view(const htl_table* t, htl_view* out) {

@@ -165,6 +165,34 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
 htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32_t* slots,
                    int64_t* n_live_dev, hipStream_t stream);
 
+/* ht_export -- checkpoint: the live entries of slots [slot_begin, slot_end),
+ * written compactly in slot order ([MTGR] section 5, "compact key
+ * scanning"), so that a table is saved range by range with bounded buffers.
+ *   keys       int64[slot_end - slot_begin] out (nullable)
+ *   rows       dtype[slot_end - slot_begin][dim] out (nullable; 16-byte
+ *              aligned when a row is a multiple of 16 bytes)
+ *   last_seen  uint32[...] out (nullable; the table must keep it)
+ *   adam_m, adam_v  float[...][dim] out (nullable; the table must keep them)
+ *   n_dev      int64 out: number of entries written.
+ * Keeps per-call temporaries with the table (allocated on first use). */
+htl_status ht_export(const htl_table* t, int64_t slot_begin, int64_t slot_end, int64_t* keys,
+                     void* rows, uint32_t* last_seen, float* adam_m, float* adam_v,
+                     int64_t* n_dev, hipStream_t stream);
+
+/* ht_import -- restore: find-or-insert each key (as ht_find_or_insert with
+ * step 0), then set the live ones' row, and where given their last_seen and
+ * Adam moments, to the values passed (keys are distinct, as for
+ * ht_find_or_insert).  An export followed by an import into an empty table
+ * of the same dim and dtype reproduces every live key's state.
+ *   keys int64[n]; rows dtype[n][dim]; last_seen uint32[n] (nullable);
+ *   adam_m, adam_v float[n][dim] (both or neither);
+ *   status uint8[n] out: as ht_find_or_insert (FULL / RESERVED keys are not
+ *   written).  After an import with last_seen, eviction selections examine
+ *   all four bytes of last_seen (the values are not known on the host). */
+htl_status ht_import(htl_table* t, const int64_t* keys, int64_t n, const void* rows,
+                     const uint32_t* last_seen, const float* adam_m, const float* adam_v,
+                     uint8_t* status, hipStream_t stream);
+
 /* ht_lru_select -- choose eviction victims for an online table: the
  * floor(live * num / den) live keys smallest by (last_seen, key), last_seen
  * compared as uint32 and keys as int64.  [MTGenRec] Abstract (deletions in
