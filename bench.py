@@ -56,6 +56,10 @@ def _parse():
     ap.add_argument("--workload", default="single_large_table",
                     choices=["single_large_table", "tiny", "merged_tables", "backward", "dynamic_online"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pcie", action="store_true",
+                    help="skip the host-to-device overlap measurement of the large-table workload")
+    ap.add_argument("--checkpoint", action="store_true",
+                    help="dynamic_online: time a full export / host copy / import of the table")
     ap.add_argument("--growable", action="store_true",
                     help="dynamic_online: use a growable table and time one capacity doubling")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
@@ -199,6 +203,8 @@ def run_lookup(args, torch, htl, workloads, dev):
             "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool",
             "timing": "HIP events around dedup+find_or_insert+gather per step on the launch stream; table keys "
                       "restored by a D2D copy between steps, outside the events"}
+    if w.name == "single_large_table" and not args.no_pcie:
+        path["pcie_inclusive"] = _pcie_inclusive(torch, htl, table, w, dev, out, restore)
     traffic = _measured_traffic() if w.name == "single_large_table" else None
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config,
                   "int64 keys, " + ("fp32" if w.dtype == "f32" else "bf16") + " rows", path,
@@ -386,11 +392,15 @@ def run_online(args, torch, htl, workloads, dev):
               "new_ids_per_step": spec.delta, "zipf_a": spec.zipf_a, "table_slots_log2": spec.capacity_log2,
               "dim": spec.dim, "row_dtype": "bf16", "evict_fraction": f"{spec.evict_num}/{spec.evict_den}",
               "parallelism": "single GPU"}
+    ckpt = None
+    if args.checkpoint:
+        ckpt = _time_checkpoint(torch, htl, table, spec, stream)
     path = {"unique_last_step": U_last, "forward_ms": round(ms, 4),
             "lru_select_ms": round(float(np.mean(lru)), 4), "erase_ms": round(float(np.mean(ers)), 4),
             "forward_algorithmic_bytes": fwd_bytes,
             "table": "growable (row handles, mapped row space)" if args.growable else "fixed",
             "resize": resize,
+            "checkpoint": ckpt,
             "implementation": "dedup + find_or_insert(step) + gather, then ht_lru_select + ht_erase",
             "timing": f"per-step HIP events over steps {args.warmup}..{steps - 1} of the drifting stream "
                       "(the warm-up steps fill the table); a GPU spin kernel (torch.cuda._sleep) holds the "
@@ -398,6 +408,133 @@ def run_online(args, torch, htl, workloads, dev):
                       "overhead; value = forward IDs/s"}
     return _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
                    _roofline("ht_lru_select (full-table scan + radix select)", lru_bytes, float(np.mean(lru))))
+
+
+def _pcie_inclusive(torch, htl, table, w, dev, out, restore, steps=12):
+    """Keys arriving in pinned host memory each step: one stream (H2D copy,
+    then the lookup) against two (the next batch's copy on a second stream
+    while the current batch is looked up).  Wall time over `steps` steps;
+    the table-key restore between steps runs in both."""
+    n = w.keys.size
+    host = torch.from_numpy(w.keys).pin_memory()
+    bufs = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(2)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def lookup(k):
+        uniq, inv, nu = htl.dedup_unique_inverse(k)
+        slots, _ = table.find_or_insert(uniq, n_dev=nu)
+        htl.gather(table, slots, inv, out=out)
+
+    # the H2D rate alone
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(main)
+    for _ in range(4):
+        bufs[0].copy_(host, non_blocking=True)
+    b.record(main)
+    torch.cuda.synchronize()
+    h2d_gbs = 4 * n * 8 / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    def one_stream(k):
+        for _ in range(k):
+            bufs[0].copy_(host, non_blocking=True)
+            lookup(bufs[0])
+            restore()
+
+    def two_streams(k):
+        E = lambda: torch.cuda.Event()  # noqa: E731
+        copied, used = [E(), E()], [None, None]
+        with torch.cuda.stream(side):
+            bufs[0].copy_(host, non_blocking=True)
+            copied[0].record(side)
+        for i in range(k):
+            cur, nxt = i % 2, 1 - i % 2
+            if i + 1 < k:
+                with torch.cuda.stream(side):
+                    if used[nxt] is not None:
+                        side.wait_event(used[nxt])
+                    bufs[nxt].copy_(host, non_blocking=True)
+                    copied[nxt].record(side)
+            main.wait_event(copied[cur])
+            lookup(bufs[cur])
+            used[cur] = E()
+            used[cur].record(main)
+            restore()
+
+    def wall(f):
+        f(2)                                   # warm-up: streams, events, workspaces
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        f(steps)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    seq = wall(one_stream)
+    ovl = wall(two_streams)
+    return {"h2d_gbs": round(h2d_gbs, 1),
+            "one_stream_mkeys_s": round(steps * n / seq / 1e6, 1),
+            "two_streams_mkeys_s": round(steps * n / ovl / 1e6, 1),
+            "what": "keys copied from pinned host memory every step (32 MiB); wall time over "
+                    f"{steps} steps including the table-key restore; not the headline value"}
+
+
+def _time_checkpoint(torch, htl, table, spec, stream, chunk=1 << 24):
+    """Export the whole table range by range into reused device buffers
+    (events, stream held while each call is enqueued), copy the live entries
+    into pinned host memory, and import them into a fresh table of the same
+    shape (events)."""
+    M = table.capacity
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    hold = _GpuHold(torch, stream)
+    bufs = table.export_buffers(chunk)
+    host_parts, exp_ms, d2h_ms = [], 0.0, 0.0
+    for b in range(0, M, chunk):
+        a, c = E(), E()
+        torch.cuda.synchronize()
+        hold(1.0)
+        a.record(stream)
+        d = table.export(b, min(b + chunk, M), bufs=bufs)
+        c.record(stream)
+        n = int(d.pop("n").item())
+        exp_ms += a.elapsed_time(c)
+        part = {}
+        a2, c2 = E(), E()
+        a2.record(stream)
+        for k, v in d.items():
+            v = v[:n].view(torch.int16) if v.dtype == torch.bfloat16 else v[:n]
+            h = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+            h.copy_(v, non_blocking=True)
+            part[k] = h
+        c2.record(stream)
+        torch.cuda.synchronize()
+        d2h_ms += a2.elapsed_time(c2)
+        host_parts.append(part)
+    live = sum(int(p["keys"].shape[0]) for p in host_parts)
+    del bufs
+    fresh = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+    keys = torch.cat([p["keys"] for p in host_parts]).to(stream.device)
+    rows = torch.cat([p["rows"] for p in host_parts]).to(stream.device).view(torch.bfloat16)
+    ls = torch.cat([p["last_seen"] for p in host_parts]).to(stream.device)
+    a, c = E(), E()
+    torch.cuda.synchronize()
+    hold(1.0)
+    a.record(stream)
+    st = fresh.import_(keys, rows, ls)
+    c.record(stream)
+    torch.cuda.synchronize()
+    imp_ms = a.elapsed_time(c)
+    ok = bool((st == htl.INSERTED).all().item())
+    fresh.close()
+    entry = 8 + spec.dim * 2 + 4
+    return {"live_entries": live, "entry_bytes": entry,
+            "export_ms": round(exp_ms, 3), "export_calls": M // chunk,
+            "export_gbs": round((M * 8 + live * (entry + 4)) / (exp_ms * 1e-3) / 1e9, 1),
+            "d2h_ms": round(d2h_ms, 3), "d2h_gbs": round(live * entry / (d2h_ms * 1e-3) / 1e9, 1),
+            "import_ms": round(imp_ms, 3), "import_all_inserted": ok,
+            "what": "ht_export over 2^24-slot ranges of the 2^27-slot table (the key array scanned, live "
+                    "entries written), copy of the live entries to pinned host memory, ht_import into an "
+                    "empty table"}
 
 
 class _GpuHold:

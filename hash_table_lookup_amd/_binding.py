@@ -227,11 +227,9 @@ class Table:
         _check(lib().ht_scan(self._h, _ptr(keys), _ptr(ls), _ptr(slots), _ptr(n), _stream()))
         return keys, ls, slots, n
 
-    def export(self, begin: int = 0, end: Optional[int] = None):
-        """Live entries of slots [begin, end) in slot order: dict of tensors
-        (keys, rows, last_seen / adam_m / adam_v when kept) and n (device int64)."""
-        end = self.capacity if end is None else end
-        cap = max(end - begin, 1)
+    def export_buffers(self, entries: int):
+        """Device buffers for an export of up to `entries` live entries."""
+        cap = max(entries, 1)
         d = {"keys": torch.empty(cap, dtype=torch.int64, device=self.device),
              "rows": torch.empty((cap, self.dim), dtype=self.row_dtype, device=self.device)}
         v = self.view()
@@ -240,7 +238,18 @@ class Table:
         if v.adam_m:
             d["adam_m"] = torch.empty((cap, self.dim), dtype=torch.float32, device=self.device)
             d["adam_v"] = torch.empty((cap, self.dim), dtype=torch.float32, device=self.device)
-        n = torch.empty(1, dtype=torch.int64, device=self.device)
+        d["n"] = torch.empty(1, dtype=torch.int64, device=self.device)
+        return d
+
+    def export(self, begin: int = 0, end: Optional[int] = None, bufs=None):
+        """Live entries of slots [begin, end) in slot order: dict of tensors
+        (keys, rows, last_seen / adam_m / adam_v when kept) and n (device int64).
+        bufs: buffers from export_buffers(>= end - begin) to reuse."""
+        end = self.capacity if end is None else end
+        d = dict(bufs) if bufs is not None else self.export_buffers(end - begin)
+        if d["keys"].numel() < end - begin:
+            raise ValueError("export buffers are smaller than the slot range")
+        n = d["n"]
         _check(lib().ht_export(self._h, begin, end, _ptr(d["keys"]), _ptr(d["rows"]), _ptr(d.get("last_seen")),
                                _ptr(d.get("adam_m")), _ptr(d.get("adam_v")), _ptr(n), _stream()))
         d["n"] = n
