@@ -25,6 +25,11 @@
 //   compose (k_dedup_compose): inverse[i] = id(set slot of tile survivor
 //     local[i]), one workgroup per tile with the survivors' ids in LDS.
 //
+// Adaptive choice (the TensorFlow article, section 3.6: a heuristic picks the
+// Unique implementation): a batch of at most one tile (2048 keys, e.g. a
+// serving request) is deduplicated by the LDS stage alone in one launch; the
+// device set and its clear, the claim, the scan and the compose are skipped.
+//
 // Both sets probe with an odd step over a power-of-two capacity, so by
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
 // more than 3n/2 slots it always ends at a free slot (load at most 2/3: the
@@ -279,6 +284,14 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
                 std::string(who) + ": misaligned pointer");
     DedupWs w = layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
+    if (n <= kTile) {
+        // A batch of one tile: the LDS stage alone is the answer (one
+        // launch, no device set to clear), in first-occurrence order, which
+        // both modes accept.
+        hipLaunchKernelGGL(k_dedup_tile<true>, dim3(1), dim3(kTileThreads), 0, stream, keys, n, unique,
+                           (int32_t*)nullptr, (uint16_t*)nullptr, inverse, n_unique_dev);
+        return check_launch(who);
+    }
     const int64_t ntiles = ceil_div(n, kTile);
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
     const unsigned gclear = grid_for((int64_t)w.cap + 1, 256 * 8, 1 << 14);
@@ -289,8 +302,8 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     else
         hipLaunchKernelGGL(k_dedup_clear<false>, dim3(gclear), dim3(256), 0, stream, w.set_keys, w.set_owner, w.cap,
                            w.misc);
-    hipLaunchKernelGGL(k_dedup_tile, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
-                       w.local);
+    hipLaunchKernelGGL(k_dedup_tile<false>, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
+                       w.local, (int32_t*)nullptr, (int64_t*)nullptr);
     if (ordered) {
         hipLaunchKernelGGL(k_dedup_claim<true>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
                            ntiles, w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot, w.tu_own, w.tile_win,

@@ -46,10 +46,16 @@ __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
 // Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
 // occurrence inside the tile (LDS atomicMin of the position, then a block
 // scan over positions), so the result does not depend on scheduling.
+// FINAL (a batch of at most one tile, one workgroup): the tile's result is
+// the whole answer, written straight to unique / inverse / the unique count
+// (tu_keys, local, tu_count stand for them), in first-occurrence order.
+template <bool FINAL>
 __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __restrict__ keys, int64_t n,
                                                             int64_t* __restrict__ tu_keys,
                                                             int32_t* __restrict__ tu_count,
-                                                            uint16_t* __restrict__ local) {
+                                                            uint16_t* __restrict__ local,
+                                                            int32_t* __restrict__ inverse,
+                                                            int64_t* __restrict__ n_unique) {
     __shared__ unsigned long long s_key[kLdsCap];
     __shared__ int32_t s_tag[kLdsCap + 1];   // first position of the key, then its tile-local id
     __shared__ int s_wave[kTileThreads / 64];
@@ -115,9 +121,13 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
             if (!(valid & (1u << j))) continue;
-            local[base + j * kTileThreads + tid] = (uint16_t)s_tag[pos[j]];
+            if (FINAL) inverse[base + j * kTileThreads + tid] = s_tag[pos[j]];
+            else local[base + j * kTileThreads + tid] = (uint16_t)s_tag[pos[j]];
         }
-        if (tid == 0) tu_count[tile] = run;
+        if (tid == 0) {
+            if (FINAL) *n_unique = run;
+            else tu_count[tile] = run;
+        }
         __syncthreads();
     }
 }

@@ -238,7 +238,9 @@ htl_status ht_view(const htl_table* t, htl_view* out);
  * stage 2 dedups the tile survivors device-wide.
  *   keys          int64[n]; every 64-bit value is a valid key.
  *   unique        int64[n] out: the U distinct keys.  Order: unspecified
- *                 (it depends on which tile's insert wins a race).
+ *                 (it depends on which tile's insert wins a race); a batch
+ *                 of at most 2048 keys is deduplicated in one launch and
+ *                 comes out in first-occurrence order.
  *   inverse       int32[n] out: unique[inverse[i]] == keys[i].
  *   n_unique_dev  int64 out: U.
  *   ws, ws_bytes  workspace of at least dedup_workspace_bytes(n) bytes,

@@ -65,6 +65,8 @@ def test_dedup_special_values(htl, orc, ordered):
     keys = np.concatenate([base, rng.choice(base, 5000), rng.integers(-50, 50, 5000)])
     rng.shuffle(keys)
     _dedup_check(htl, orc, keys, ordered)
+    _dedup_check(htl, orc, base, ordered)                               # one-tile batches (single launch)
+    _dedup_check(htl, orc, rng.choice(base, 2048), ordered)
     _dedup_check(htl, orc, np.full(70000, -1, np.int64), ordered)     # only the out-of-band key
     _dedup_check(htl, orc, np.full(70000, 12345, np.int64), ordered)  # all equal
     _dedup_check(htl, orc, rng.permutation(150000).astype(np.int64), ordered)   # all distinct
