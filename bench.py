@@ -44,7 +44,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
-TRAFFIC_SOURCES = [os.path.join(CSRC, f) for f in ("gather.hip", "htl_common.h")]
+TRAFFIC_SOURCES = [os.path.join(CSRC, "gather.hip")]     # the source of k_gather
 METRIC = "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X"
 
 
