@@ -551,12 +551,14 @@ int team_for(int vpr) {
 template <int TEAM, int QMAX, bool ADAM>
 void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, const int64_t* n_dev, float* out,
                    const AdamArgs& A, hipStream_t s) {
-    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM)),
+    // Persistent grids: u_max bounds the segments from above (often by far:
+    // 753K segments for u_max = 8.4M), and idle workgroups cost launch time.
+    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM, 1 << 15)),
                        dim3(kRBlock), 0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, (u32x4*)out, A,
                        w.large, w.n_large);
     hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off,
                        w.part_off);
-    hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX, ADAM>), dim3(grid_for(w.max_chunks, 1, 1 << 16)), dim3(kRBlock),
+    hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX, ADAM>), dim3(grid_for(w.max_chunks, 1, 1 << 14)), dim3(kRBlock),
                        0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off, w.part_off,
                        w.max_chunks, u_max, n_dev, (u32x4*)w.partial, (u32x4*)out, A);
     int lanes = 1;

@@ -44,6 +44,7 @@ namespace htl {
 namespace {
 thread_local std::string g_last_error;
 constexpr uint64_t kProbeSalt = 0x2545F4914F6CDD1Dull;
+constexpr int64_t kProbeGridMax = 1 << 15;   // workgroups of the find-or-insert kernels
 }  // namespace
 
 int probe_lanes() {
@@ -966,7 +967,9 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
                 "ht_find_or_insert: misaligned pointer");
     if (step > t->max_step) t->max_step = step;
     const int G = probe_lanes();
-    const unsigned grid = grid_for(n_max, kProbeBlock / G);
+    // n_max is an upper bound (the dedup output's size: N, with U < N keys
+    // real); a persistent grid keeps the blocks past U from costing launches.
+    const unsigned grid = grid_for(n_max, kProbeBlock / G, kProbeGridMax);
     if (t->flags & HT_GROWABLE) {
         // claim slots, count the inserts per chunk, prefix them, hand out rows
         htl_status st = ensure_tmp(t, n_max);
