@@ -991,7 +991,7 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
                            n_dev, (int)HT_INSERTED, A.chunk_cnt, nchunks);
         st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
         if (st != HTL_OK) return st;
-        hipLaunchKernelGGL(k_foi_assign, dim3(grid_for(nchunks, 1, 1 << 16)), dim3(kProbeBlock), 0, stream, t->dev,
+        hipLaunchKernelGGL(k_foi_assign, dim3(grid_for(nchunks, 1, 1 << 14)), dim3(kProbeBlock), 0, stream, t->dev,
                            keys, n_max, n_dev, A.chunk_off, A.state, A.free_stack, slots, status);
         hipLaunchKernelGGL(k_foi_found, dim3(grid_for(n_max, 256 * 4)), dim3(256), 0, stream, t->dev, n_max, n_dev,
                            slots, status);
