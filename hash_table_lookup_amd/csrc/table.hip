@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kExpThreads) void k_exp_write(TableDev T, int64_t b
                                                           const int32_t* __restrict__ off,
                                                           int64_t* __restrict__ keys_out, void* __restrict__ rows_out,
                                                           uint32_t* __restrict__ ls_out, float* __restrict__ m_out,
-                                                          float* __restrict__ v_out) {
+                                                          float* __restrict__ v_out, int32_t* __restrict__ slots_out) {
     __shared__ int s_wave[kExpThreads / 64];
     __shared__ int32_t s_row[kExpChunk];     // row handle of the chunk's e-th live entry
     const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
@@ -386,8 +386,9 @@ __global__ __launch_bounds__(kExpThreads) void k_exp_write(TableDev T, int64_t b
         for (int j = 0; j < kExpPerThread; ++j) {
             if (!(live & (1u << j))) continue;
             if (keys_out) keys_out[base + pos] = k[j];
-            if (ls_out) ls_out[base + pos] = T.last_seen[s0 + j];
+            if (ls_out) ls_out[base + pos] = T.last_seen ? T.last_seen[s0 + j] : 0u;
             s_row[pos] = (int32_t)row_of(T, s0 + j);
+            if (slots_out) slots_out[base + pos] = s_row[pos];
             ++pos;
         }
         __syncthreads();
@@ -429,6 +430,8 @@ __global__ __launch_bounds__(kExpThreads) void k_exp_write(TableDev T, int64_t b
 }
 
 __global__ void k_exp_total(const int32_t* __restrict__ total, int64_t* __restrict__ n_dev) { *n_dev = *total; }
+
+__global__ void k_zero_i64(int64_t* p) { *p = 0; }
 
 // Import: rows and Adam moments of the keys that are live after the
 // find-or-insert (FOUND or INSERTED) are written at their handle.
@@ -487,67 +490,6 @@ __global__ __launch_bounds__(kProbeBlock) void k_imp_ls(TableDev T, const int64_
         if (st != HT_FOUND && st != HT_INSERTED) continue;
         const int64_t slot = find_key<G>(T, keys[i], gl, gshift);
         if (gl == 0 && slot >= 0) T.last_seen[slot] = ls_in[i];
-    }
-}
-
-// Compact scan of live slots.  Each block owns a contiguous range of
-// kScanPerBlock slots, counts its live slots, reserves an output range with
-// one atomic, and writes them there (thread-major order within the block).
-constexpr int kScanBlock = 256;
-constexpr int kScanPerThread = 16;
-constexpr int kScanPerBlock = kScanBlock * kScanPerThread;
-
-__global__ void k_zero_i64(int64_t* p) { *p = 0; }
-
-__global__ __launch_bounds__(kScanBlock) void k_scan_live(TableDev T, int64_t* __restrict__ out_keys,
-                                                         uint32_t* __restrict__ out_ls,
-                                                         int32_t* __restrict__ out_slots,
-                                                         unsigned long long* __restrict__ counter) {
-    __shared__ int s_warp[kScanBlock / 64];
-    __shared__ unsigned long long s_base;
-    const int tid = threadIdx.x;
-    const int wid = tid >> 6;
-    for (int64_t blk = blockIdx.x; blk * kScanPerBlock < T.capacity; blk += gridDim.x) {
-        const int64_t start = blk * kScanPerBlock;
-        int64_t k[kScanPerThread];
-        uint32_t live = 0;
-#pragma unroll
-        for (int j = 0; j < kScanPerThread; ++j) {
-            const int64_t s = start + (int64_t)j * kScanBlock + tid;
-            k[j] = s < T.capacity ? T.keys[s] : kEmpty;
-            if (k[j] != kEmpty && k[j] != kTomb) live |= 1u << j;
-        }
-        // per-wave counts of each round j, then a block-wide exclusive prefix
-        int my_total = __popc(live);
-        int incl = my_total;
-        for (int off = 1; off < 64; off <<= 1) {
-            int y = __shfl_up(incl, off);
-            if (lane_id() >= off) incl += y;
-        }
-        if (lane_id() == 63) s_warp[wid] = incl;
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int w = 0; w < kScanBlock / 64; ++w) {
-                int c = s_warp[w];
-                s_warp[w] = run;
-                run += c;
-            }
-            s_base = run ? atomicAdd(counter, (unsigned long long)run) : 0ull;
-        }
-        __syncthreads();
-        int64_t pos = (int64_t)s_base + s_warp[wid] + (incl - my_total);
-#pragma unroll
-        for (int j = 0; j < kScanPerThread; ++j) {
-            if (live & (1u << j)) {
-                const int64_t s = start + (int64_t)j * kScanBlock + tid;
-                if (out_keys) out_keys[pos] = k[j];
-                if (out_ls) out_ls[pos] = T.last_seen ? T.last_seen[s] : 0u;
-                if (out_slots) out_slots[pos] = (int32_t)row_of(T, s);
-                ++pos;
-            }
-        }
-        __syncthreads();
     }
 }
 
@@ -1041,16 +983,28 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
     return check_launch("ht_erase");
 }
 
-htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32_t* slots,
+htl_status ht_scan(const htl_table* tc, int64_t* keys, uint32_t* last_seen, int32_t* slots,
                    int64_t* n_live_dev, hipStream_t stream) {
     clear_error();
-    HTL_REQUIRE(t != nullptr, "ht_scan: null table");
+    HTL_REQUIRE(tc != nullptr, "ht_scan: null table");
     HTL_REQUIRE(n_live_dev && aligned(n_live_dev, 8), "ht_scan: null or misaligned n_live_dev");
     HTL_REQUIRE(!keys || aligned(keys, 8), "ht_scan: misaligned keys");
-    hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, stream, n_live_dev);
-    hipLaunchKernelGGL(k_scan_live, dim3(grid_for(t->dev.capacity, kScanPerBlock, 1 << 16)),
-                       dim3(kScanBlock), 0, stream, t->dev, keys, last_seen, slots,
-                       (unsigned long long*)n_live_dev);
+    // the export's count / prefix / write passes over every slot: slot
+    // order, no shared counter
+    htl_table* t = const_cast<htl_table*>(tc);     // only its call temporaries change
+    const TableDev& T = t->dev;
+    const int64_t nchunks = ceil_div(T.capacity, kExpChunk);
+    htl_status st = ensure_exp(t, nchunks);
+    if (st != HTL_OK) return st;
+    RowAlloc& A = t->alloc;
+    const unsigned grid = grid_for(nchunks, 1, 1 << 16);
+    hipLaunchKernelGGL(k_exp_count, dim3(grid), dim3(kExpThreads), 0, stream, T, (int64_t)0, T.capacity, nchunks,
+                       A.exp_cnt);
+    st = scan_exclusive_i32(A.exp_cnt, A.exp_off, nchunks, nullptr, kScanIdentity, 1, A.exp_scan, stream);
+    if (st != HTL_OK) return st;
+    hipLaunchKernelGGL(k_exp_write, dim3(grid), dim3(kExpThreads), 0, stream, T, (int64_t)0, T.capacity, nchunks,
+                       A.exp_off, keys, (void*)nullptr, last_seen, (float*)nullptr, (float*)nullptr, slots);
+    hipLaunchKernelGGL(k_exp_total, dim3(1), dim3(1), 0, stream, A.exp_off + nchunks, n_live_dev);
     return check_launch("ht_scan");
 }
 
@@ -1082,7 +1036,7 @@ htl_status ht_export(const htl_table* tc, int64_t slot_begin, int64_t slot_end, 
     st = scan_exclusive_i32(A.exp_cnt, A.exp_off, nchunks, nullptr, kScanIdentity, 1, A.exp_scan, stream);
     if (st != HTL_OK) return st;
     hipLaunchKernelGGL(k_exp_write, dim3(grid), dim3(kExpThreads), 0, stream, T, slot_begin, slot_end, nchunks,
-                       A.exp_off, keys, rows, last_seen, adam_m, adam_v);
+                       A.exp_off, keys, rows, last_seen, adam_m, adam_v, (int32_t*)nullptr);
     hipLaunchKernelGGL(k_exp_total, dim3(1), dim3(1), 0, stream, A.exp_off + nchunks, n_dev);
     return check_launch("ht_export");
 }

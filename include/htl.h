@@ -157,9 +157,9 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
                     hipStream_t stream);
 
 /* ht_scan -- compact listing of live slots ([MTGR] section 5, "compact key
- * scanning").  Writes, for each live slot in an unspecified order, its key,
- * its last_seen (if kept) and its slot index (growable tables: its row
- * handle).
+ * scanning").  Writes, for each live slot in slot order, its key, its
+ * last_seen (if kept) and its slot index (growable tables: its row handle).
+ * Keeps per-call temporaries with the table (allocated on first use).
  *   keys       int64[M] out (nullable)    last_seen uint32[M] out (nullable)
  *   slots      int32[M] out (nullable)    n_live_dev int64 out: live count. */
 htl_status ht_scan(const htl_table* t, int64_t* keys, uint32_t* last_seen, int32_t* slots,

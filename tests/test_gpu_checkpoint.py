@@ -113,3 +113,21 @@ def test_export_errors_and_empty_ranges(htl):
         table.export(0, 2048)                              # beyond capacity
     with pytest.raises(htl.HTLError):
         table.export(5, 3)
+
+
+@pytest.mark.parametrize("growable", [False, True])
+def test_scan_lists_live_slots_in_slot_order(htl, growable):
+    rng = np.random.default_rng(11)
+    table = htl.Table(13, 4, "f32", last_seen=True, growable=growable)
+    keys = np.unique(rng.integers(0, 1 << 40, 6000)).astype(np.int64)
+    table.find_or_insert(torch.from_numpy(keys).cuda(), step=4)
+    table.erase(torch.from_numpy(keys[::5]).cuda())
+    k, ls, h, n = table.scan()
+    L = int(n.item())
+    slots = to_np(htl.table_keys(table))
+    live_slots = np.flatnonzero((slots != htl.EMPTY_KEY) & (slots != htl.TOMBSTONE_KEY))
+    assert L == live_slots.size
+    assert np.array_equal(to_np(k)[:L], slots[live_slots])
+    assert np.all(to_np(ls)[:L] == 4)
+    want_h = to_np(htl.table_tensor(table, "row_of_slot"))[live_slots] if growable else live_slots
+    assert np.array_equal(to_np(h)[:L], want_h)
