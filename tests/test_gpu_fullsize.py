@@ -1,0 +1,85 @@
+"""Full-size runs of the pooled and online workloads, in the launch shapes
+bench.py times, checked on what the oracle computes one by one (closed-form
+rows of sampled keys, brute-force sums of sampled bags) and on properties
+that hold at any size (unique set, inverse, LRU order, erase statuses).
+
+Merged tables: 65,536 samples x 26 bags of Poisson(20) IDs (34.08M IDs), one
+2^26-slot bf16 table of dim 128 warmed by an earlier batch.  Online: the
+2^27-slot bf16 table of dim 64 over the first steps of the drifting stream.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from conftest import to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def test_merged_tables_full_size(htl, orc):
+    w = workloads.merged_tables()
+    warm = workloads.merged_tables(seed=1)
+    table = htl.Table(w.capacity_log2, w.dim, w.dtype)
+    wk = torch.from_numpy(warm.keys).cuda()
+    u0, _, n0 = htl.dedup_unique_inverse(wk)
+    table.find_or_insert(u0, n_dev=n0)
+    del wk, u0
+    keys = torch.from_numpy(w.keys).cuda()
+    offsets = torch.from_numpy(w.offsets).cuda()
+    out, uniq, inv, nu, slots, status = htl.lookup(table, keys, offsets=offsets, out_dtype="bf16")
+    U = int(nu.item())
+    u = to_np(uniq)[:U]
+    assert np.array_equal(np.sort(u), np.unique(w.keys))
+    sample = np.random.default_rng(3).integers(0, w.keys.size, 1 << 16)
+    assert np.array_equal(u[to_np(inv)[sample]], w.keys[sample])
+    st = to_np(status)[:U]
+    assert np.array_equal(st == htl.FOUND, np.isin(u, warm.keys))
+    # sampled bags: brute-force fp64 sums of closed-form bf16 rows, rounded
+    # to bf16 (exact in fp32 in any order, so bit-equal)
+    rng = np.random.default_rng(4)
+    bags = np.concatenate([rng.integers(0, w.nbags, 3000), [0, w.nbags - 1]])
+    got = to_np(out[torch.from_numpy(bags).cuda()])
+    for b, row in zip(bags, got):
+        ks = w.keys[w.offsets[b]:w.offsets[b + 1]]
+        if ks.size == 0:
+            assert np.all(row == 0)
+            continue
+        rows = orc.bf16_bits_to_f32(orc.init_rows(ks, w.dim, orc.BF16)).astype(np.float64)
+        s = rows.sum(axis=0).astype(np.float32)
+        want = (s.view(np.uint32) + 0x7FFF + ((s.view(np.uint32) >> 16) & 1)) >> 16
+        assert np.array_equal(row, want.astype(np.uint16)), b
+
+
+def test_online_full_size_steps(htl, orc):
+    spec = workloads.DynamicOnlineSpec()
+    steps = 3
+    gen = workloads.DynamicOnlineStream(spec, steps)
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
+    live_before = 0
+    for s in range(steps):
+        keys_np = gen.keys(s)
+        keys = torch.from_numpy(keys_np).cuda()
+        out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=s)
+        U = int(nu.item())
+        u = to_np(uniq)[:U]
+        st = to_np(status)[:U]
+        assert np.array_equal(np.sort(u), np.unique(keys_np))
+        ins = st == htl.INSERTED
+        assert np.all((st == htl.FOUND) | ins)
+        idx = np.random.default_rng(s).integers(0, keys_np.size, 2048)
+        assert np.array_equal(to_np(out[torch.from_numpy(idx).cuda()]),
+                              orc.init_rows(keys_np[idx], spec.dim, orc.BF16))
+        k_all, ls_all, _, n_all = table.scan()
+        L = int(n_all.item())
+        assert L == live_before + int(ins.sum())
+        victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
+        k = int(nv.item())
+        assert k == L * spec.evict_num // spec.evict_den
+        vk = to_np(victims)[:k]
+        lk, lls = to_np(k_all)[:L], to_np(ls_all)[:L].astype(np.uint32)
+        order = np.lexsort((lk, lls))                      # by (last_seen, key)
+        assert np.array_equal(np.sort(vk), np.sort(lk[order[:k]]))
+        est = to_np(table.erase(victims[:k]))
+        assert np.all(est == htl.ERASED)
+        live_before = L - k
