@@ -83,3 +83,35 @@ def test_online_full_size_steps(htl, orc):
         est = to_np(table.erase(victims[:k]))
         assert np.all(est == htl.ERASED)
         live_before = L - k
+
+
+def test_backward_fused_full_size_matches_two_calls(htl):
+    """2^23 IDs Zipf(1.2), dim 128, at full size: the fused segment-sum + Adam
+    gives bit-for-bit the rows, m and v of segment-sum then Adam, with
+    gradients that are multiples of 2^-6 in [-1/8, 1/8] (every segment sum,
+    up to the hottest key's 1.5M rows, is exact in fp32, so the order of
+    summation cannot matter)."""
+    w = workloads.backward(with_grad=False)
+    n, dim = w.keys.size, w.dim
+    keys = torch.from_numpy(w.keys).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    grad = torch.randint(-8, 9, (n, dim), generator=gen, device="cuda").to(torch.float32) * 2.0 ** -6
+    uniq, inv, nu = htl.dedup_unique_inverse(keys, ordered=True)
+    U = int(nu.item())
+    res = []
+    for fused in (True, False):
+        t = htl.Table(w.capacity_log2, dim, "f32", adam=True)
+        slots, _ = t.find_or_insert(uniq, n_dev=nu)
+        if fused:
+            htl.segment_sum_adam(t, slots, grad, inv, nu, n)
+        else:
+            g = htl.segment_sum(grad, inv, nu, u_max=n)
+            htl.rowwise_adam(t, slots, g, nu, 1e-3, 0.9, 0.999, 1e-8, 1)
+            del g
+        sl = slots[:U].long()
+        res.append([htl.table_tensor(t, name)[sl].cpu() for name in ("rows", "adam_m", "adam_v")])
+        del t
+        torch.cuda.empty_cache()
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
