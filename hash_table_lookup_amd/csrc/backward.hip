@@ -23,8 +23,11 @@
 //   small  -- one team of lanes per segment of <= kSmallMax IDs sums its rows;
 //   large  -- longer segments (Zipf's head: the hottest key of a 2^23-ID
 //             Zipf(1.2) batch owns ~18% of all rows) are cut into kChunk-row
-//             chunks, one workgroup each, and the chunk partials are then
-//             added in chunk order.
+//             chunks, one workgroup each; a one-chunk segment is finished in
+//             its workgroup, the partials of longer ones are added by a
+//             1024-thread workgroup per segment.
+// emb_grad_segment_sum_adam runs the same passes but hands each finished
+// summed row straight to Adam on the unique key's table row.
 // Accumulation is fp32.  The order of IDs inside a segment depends on atomic
 // order, so sums are reproducible only up to fp32 rounding.
 #include <cmath>
@@ -45,7 +48,7 @@ constexpr int kRBlock = 256;
 constexpr int kSpread = 1024;              // S of the spread segment order
 
 // Spread order: q(u) = (u mod S) * C + u / S with C = ceil(U / S), a
-// bijection from [0, U) into [0, S * C); qinv inverts it on that range.
+// bijection from [0, U) into [0, S * C); spread_u inverts it on that range.
 __device__ __forceinline__ int64_t spread_c(int64_t U) { return (U + kSpread - 1) / kSpread; }
 __device__ __forceinline__ int64_t spread_q(int64_t u, int64_t C) { return (u % kSpread) * C + u / kSpread; }
 __device__ __forceinline__ int64_t spread_u(int64_t q, int64_t C) { return (q % C) * kSpread + q / C; }
@@ -243,8 +246,8 @@ __device__ __forceinline__ void emit4(u32x4* __restrict__ out, int vpr, int64_t 
     A.v[st.o] = st.v;
 }
 
-// Sums rows perm[beg..end) of `grad` into acc, TEAM lanes per row, the
-// TEAMS teams of `nthreads` lanes taking every TEAMS-th row.
+// Sums rows perm[beg..end) of `grad` into acc, TEAM lanes per row: team
+// `team` of `teams` takes rows beg + team, beg + team + teams, ...
 template <int TEAM, int QMAX>
 __device__ __forceinline__ void sum_rows(const u32x4* __restrict__ grad, int vpr, const int32_t* __restrict__ perm,
                                          int32_t beg, int32_t end, int team, int teams, int tl,

@@ -1,5 +1,5 @@
-// Dynamic open-addressing embedding table: create/clear/destroy,
-// find-or-insert, erase, compact scan.
+// Dynamic open-addressing embedding table: create/clear/destroy/resize,
+// find-or-insert, erase, compact scan, export / import (checkpoint).
 //
 // MTGenRec (arXiv 2505.12663): Abstract and Figure 5 (a hash-based dynamic
 // embedding table replaces static tables so embeddings can be inserted and
@@ -18,10 +18,10 @@
 // that grows by mapping physical memory at its end (hipMemAddressReserve /
 // hipMemCreate / hipMemMap), so a resize rehashes only the index entries
 // (key, handle and the 4-byte last_seen, which stays with the key) and no
-// row moves.  Handles come from a free
-// stack (handles of erased keys) and then a bump pointer; an insert pass
-// takes its handles with a count / prefix-sum / assign sequence, so no
-// counter is shared by the keys of a call.
+// row moves.  Handles come from a free stack (handles of erased keys) and
+// then a bump pointer; an insert pass takes its handles with a count /
+// prefix-sum / assign sequence, so no counter is shared by the keys of a
+// call.
 //
 // Probing (this library's layout, not the pages'): the M slots form
 // min(16, M)-slot buckets, one 128-byte line of keys each.  A key's walk
@@ -29,8 +29,8 @@
 // buckets every bucket -- hence every slot -- is on the walk.  Within a bucket
 // the slots are taken in order.  A group of G lanes (1, 2, 4, 8 or 16) works
 // on one key, each lane holding 16/G consecutive slots of the bucket, so a
-// wavefront keeps 64/G keys in flight; the group loads the bucket's 128-byte line together and
-// ballots decide found / first free slot / EMPTY seen.  An insert claims the
+// wavefront keeps 64/G keys in flight; the group loads the bucket's 128-byte
+// line together and ballots decide found / first free slot / EMPTY seen.  An insert claims the
 // first free (EMPTY or TOMBSTONE) slot of the walk with a 64-bit CAS; if the
 // CAS loses, the returned key is either the key itself (FOUND) or another
 // key, and the walk resumes right after that slot.

@@ -1,5 +1,5 @@
 // Stage 1 of the feature-ID dedup: one workgroup dedups one tile of keys in
-// LDS (internal header, shared by the dedup and fused lookup entry points).
+// LDS (internal header of the dedup).
 //
 // MTGenRec (arXiv 2505.12663) TL;DR: two-stage ID deduplication; MTGR (arXiv
 // 2505.18654) section 5, "Embedding Lookup": IDs are unique before the
