@@ -83,6 +83,9 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.emb_grad_segment_sum_adam(None, None, None, None, 10, None, 5, 1e-3, 0.9, 0.999, 1e-8, 1,
                                        None, 0, None) == INVALID
     assert L.ht_lru_select(None, 1, 20, None, 0, None, None, 0, None) == INVALID
+    assert L.ht_resize(None, 10, None) == INVALID
+    assert L.ht_export(None, 0, 1, None, None, None, None, None, None, None) == INVALID
+    assert L.ht_import(None, None, 1, None, None, None, None, None, None) == INVALID
     assert L.ht_view(None, None) == INVALID
     assert L.ht_destroy(None) == 0
 
