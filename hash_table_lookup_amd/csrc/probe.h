@@ -54,6 +54,53 @@ __device__ void write_initial_row(const TableDev& T, int64_t slot, int64_t key, 
     }
 }
 
+// Writes the initial rows (and zeroed Adam moments) of every key that the
+// groups of this wave have just inserted, with all 64 lanes: each 16-byte
+// vector of those rows is one lane's store, so the stores of a row leave
+// together and no lane of a group that found its key sits idle.  Must be
+// called by the whole wave; `ins` marks a group that inserted key `k` at
+// `slot` (every lane of the group passes the same values).  Needs 16-byte
+// rows (dim*elem_bytes % 16 == 0).
+template <int G>
+__device__ void write_initial_rows_wave(const TableDev& T, bool ins, int64_t slot, int64_t k) {
+    const int lane = lane_id();
+    const bool lead = ins && (lane & (G - 1)) == 0;
+    const uint64_t lm = __ballot(lead);
+    const int cnt = __popcll(lm);
+    if (cnt == 0) return;
+    // Forward-permute the leaders' (slot, row seed) to lanes 0..cnt-1 (the
+    // other lanes fill lanes cnt..63, so every destination is written once).
+    const uint64_t below = lanemask_lt();
+    const int dst = lead ? __popcll(lm & below) : cnt + __popcll(~lm & below);
+    const uint64_t seed = row_base(k, T.init_base);
+    const int s_c = __builtin_amdgcn_ds_permute(dst * 4, (int)slot);
+    const int lo_c = __builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)seed);
+    const int hi_c = __builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)(seed >> 32));
+    const int vpr = (T.dim * T.elem_bytes) >> 4;
+    const int mvv = T.m ? (T.dim >> 2) : 0;       // 16-byte vectors per moment row
+    const int per = vpr + 2 * mvv;
+    const int total = cnt * per;
+    u32x4* rows = reinterpret_cast<u32x4*>(T.rows);
+    for (int b0 = 0; b0 < total; b0 += 64) {
+        const int w = b0 + lane;
+        int r = w / per;
+        if (r >= cnt) r = cnt - 1;
+        const int64_t s = (int64_t)(uint32_t)__shfl(s_c, r);
+        const uint64_t base = ((uint64_t)(uint32_t)__shfl(hi_c, r) << 32) | (uint32_t)__shfl(lo_c, r);
+        if (w < total) {
+            const int u = w - r * per;
+            if (u < vpr) {
+                rows[s * vpr + u] = init_vec(base, u, T.dtype);
+            } else {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                float* mv = (u < vpr + mvv) ? T.m : T.v;
+                const int q = (u < vpr + mvv) ? u - vpr : u - vpr - mvv;
+                reinterpret_cast<u32x4*>(mv)[s * mvv + q] = z;
+            }
+        }
+    }
+}
+
 // One bucket as seen by a group of G lanes: lane gl holds the SPL = 16/G
 // consecutive slots [gl*SPL, gl*SPL + SPL), read with 16-byte loads when the
 // bucket is a full 16 slots.  Slots outside [from, W) are not examined.

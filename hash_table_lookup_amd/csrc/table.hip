@@ -81,7 +81,10 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) 
         p[i] = value;
 }
 
-template <int G>
+// WAVE_ROWS (rows of a multiple of 16 bytes): the whole wave writes the new
+// rows of its groups together, after the probes; else each group writes its
+// own key's row.
+template <int G, bool WAVE_ROWS>
 __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
     TableDev T, const int64_t* __restrict__ keys, int64_t n_max, const int64_t* __restrict__ n_dev,
     uint32_t step, int32_t* __restrict__ slots, uint8_t* __restrict__ status) {
@@ -91,17 +94,25 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
     const int gshift = lane & ~(G - 1);
     const int64_t group0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / G;
     const int64_t ngroups = (int64_t)gridDim.x * blockDim.x / G;
+    // The loop runs the same number of times on every lane of a wave (its
+    // bound is the wave's first group), so the whole wave can write rows.
+    const int64_t wave0 = group0 - lane / G;
 
-    for (int64_t i = group0; i < n; i += ngroups) {
-        const int64_t k = keys[i];
-        int64_t slot;
-        const int st = find_or_insert_key<G>(T, k, gl, gshift, &slot);
-        if (st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
-        if (gl == 0) {
-            if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
-            slots[i] = (int32_t)slot;
-            status[i] = (uint8_t)st;
+    for (int64_t iw = wave0; iw < n; iw += ngroups) {
+        const int64_t i = iw + lane / G;
+        int st = HT_NOT_FOUND;
+        int64_t slot = -1, k = 0;
+        if (i < n) {
+            k = keys[i];
+            st = find_or_insert_key<G>(T, k, gl, gshift, &slot);
+            if (!WAVE_ROWS && st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
+            if (gl == 0) {
+                if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
+                slots[i] = (int32_t)slot;
+                status[i] = (uint8_t)st;
+            }
         }
+        if (WAVE_ROWS) write_initial_rows_wave<G>(T, st == HT_INSERTED, slot, k);
     }
 }
 
@@ -197,8 +208,9 @@ __device__ __forceinline__ int32_t take_handle(int64_t r, int64_t bump, int64_t 
 }
 
 // Pass 3: INSERTED keys take handles in key order (rank within the chunk +
-// the chunk's prefix), record them at their slot and get their initial row;
-// slots[i] becomes the handle.
+// the chunk's prefix), record them at their slot and get their initial row
+// (written by the whole wave when WAVE_ROWS); slots[i] becomes the handle.
+template <bool WAVE_ROWS>
 __global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const int64_t* __restrict__ keys,
                                                            int64_t n_max, const int64_t* __restrict__ n_dev,
                                                            const int32_t* __restrict__ chunk_off,
@@ -223,16 +235,19 @@ __global__ __launch_bounds__(kProbeBlock) void k_foi_assign(TableDev T, const in
         int before = 0;
         for (int w = 0; w < wid; ++w) before += s_wave[w];
         __syncthreads();
+        int64_t row = 0, key = 0;
         if (ins) {
             const int64_t slot = slots[i];
             const int64_t r = chunk_off[c] + before + __popcll(m & ((1ull << gshift) - 1ull));
-            const int64_t row = take_handle(r, bump, nfree, free_stack);
-            write_initial_row<G>(T, row, keys[i], gl);
+            row = take_handle(r, bump, nfree, free_stack);
+            key = keys[i];
+            if (!WAVE_ROWS) write_initial_row<G>(T, row, key, gl);
             if (gl == 0) {
                 T.rowid[slot] = (int32_t)row;
                 slots[i] = (int32_t)row;
             }
         }
+        if (WAVE_ROWS) write_initial_rows_wave<G>(T, ins, row, key);
     }
 }
 
@@ -933,16 +948,25 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
                            n_dev, (int)HT_INSERTED, A.chunk_cnt, nchunks);
         st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
         if (st != HTL_OK) return st;
-        hipLaunchKernelGGL(k_foi_assign, dim3(grid_for(nchunks, 1, 1 << 14)), dim3(kProbeBlock), 0, stream, t->dev,
-                           keys, n_max, n_dev, A.chunk_off, A.state, A.free_stack, slots, status);
+        if (((t->dev.dim * t->dev.elem_bytes) & 15) == 0)
+            hipLaunchKernelGGL(k_foi_assign<true>, dim3(grid_for(nchunks, 1, 1 << 14)), dim3(kProbeBlock), 0, stream,
+                               t->dev, keys, n_max, n_dev, A.chunk_off, A.state, A.free_stack, slots, status);
+        else
+            hipLaunchKernelGGL(k_foi_assign<false>, dim3(grid_for(nchunks, 1, 1 << 14)), dim3(kProbeBlock), 0, stream,
+                               t->dev, keys, n_max, n_dev, A.chunk_off, A.state, A.free_stack, slots, status);
         hipLaunchKernelGGL(k_foi_found, dim3(grid_for(n_max, 256 * 4)), dim3(256), 0, stream, t->dev, n_max, n_dev,
                            slots, status);
         hipLaunchKernelGGL(k_foi_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
         return check_launch("ht_find_or_insert");
     }
-#define HTL_FOI(GG)                                                                                        \
-    hipLaunchKernelGGL(k_find_or_insert<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, \
-                       n_dev, step, slots, status)
+#define HTL_FOI(GG)                                                                                      \
+    if (wave_rows)                                                                                       \
+        hipLaunchKernelGGL((k_find_or_insert<GG, true>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, \
+                           keys, n_max, n_dev, step, slots, status);                                       \
+    else                                                                                                 \
+        hipLaunchKernelGGL((k_find_or_insert<GG, false>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, \
+                           keys, n_max, n_dev, step, slots, status)
+    const bool wave_rows = ((t->dev.dim * t->dev.elem_bytes) & 15) == 0;
     switch (G) {
         case 1: HTL_FOI(1); break;
         case 2: HTL_FOI(2); break;
