@@ -34,6 +34,10 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // -------------------------------------------------------------- table ----
 constexpr int64_t kEmpty = -1;       // HT_EMPTY_KEY
 constexpr int64_t kTomb = -2;        // HT_TOMBSTONE_KEY
+// last_seen of every slot that holds no live key (EMPTY, TOMBSTONE), so a
+// pass over last_seen alone tells the live slots apart; steps stamped into
+// last_seen are below it.
+constexpr uint32_t kLsDead = 0xFFFFFFFFu;
 constexpr int kBucketLog2 = 4;       // 16 slots = 128 bytes of keys per bucket
 
 // Everything a kernel needs to know about a table, passed by value.

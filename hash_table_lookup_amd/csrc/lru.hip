@@ -10,9 +10,12 @@
 // All on the device, no host synchronisation and no counter atomics (a
 // counter that every block bumps serialises on MI355X):
 //   collect -- the table is cut into chunks of kChunk slots; each chunk
-//              compacts its live slots' (last_seen, key) into its own fixed
+//              compacts its live slots' (last_seen, slot) into its own fixed
 //              region of the candidate arrays and records its count and its
-//              largest last_seen;
+//              largest last_seen.  Only last_seen is read (dead slots hold
+//              kLsDead there), so the pass moves 4 bytes per slot, not 12;
+//              keys are read later, through the slot, for the candidates
+//              that tie on the selected last_seen and for the victims;
 //   init    -- one block sums the counts (live L), takes the maximum
 //              last_seen and sets k = floor(L * num / den);
 //   select  -- radix select with 8-bit digits: per digit, LDS histograms of
@@ -57,8 +60,8 @@ struct LruState {
 
 struct LruWs {
     LruState* st;
-    uint32_t* cand_ls;     // [nchunks * kChunk]: per chunk, its live slots first
-    uint64_t* cand_key;    // [nchunks * kChunk], biased keys
+    uint32_t* cand_ls;     // [nchunks * kChunk]: per chunk, its live slots' last_seen first
+    uint32_t* cand_slot;   // [nchunks * kChunk]: those slots
     uint64_t* ties;        // [nchunks * kChunk]: per chunk, candidates tying on last_seen
     int32_t* chunk_cnt;    // [nchunks]
     uint32_t* chunk_max;   // [nchunks]
@@ -82,7 +85,7 @@ LruWs lru_layout(int64_t M, char* base) {
     };
     w.st = (LruState*)take(sizeof(LruState));
     w.cand_ls = (uint32_t*)take(cap * 4);
-    w.cand_key = (uint64_t*)take(cap * 8);
+    w.cand_slot = (uint32_t*)take(cap * 4);
     w.ties = (uint64_t*)take(cap * 8);
     w.chunk_cnt = (int32_t*)take((size_t)w.nchunks * 4);
     w.chunk_max = (uint32_t*)take((size_t)w.nchunks * 4);
@@ -118,37 +121,57 @@ __device__ __forceinline__ int block_prefix(int& v, int* s_wave) {
     return tot;
 }
 
-// Each chunk compacts its live slots into its own region (order within the
-// region: by thread, then by the thread's slots).  Loads are coalesced: slot
-// j * kThreads + tid of the chunk belongs to thread tid.
+// Each chunk compacts its live slots (last_seen, slot) into its own region
+// (order within the region: by thread, then by the thread's slots).  Only
+// last_seen is read: a slot without a live key holds kLsDead there.  Loads
+// are 16 bytes per lane: slot quad j * kThreads + tid of the chunk belongs to
+// thread tid.
+typedef uint32_t u32x4l __attribute__((ext_vector_type(4)));
+constexpr int kQuads = kPerThread / 4;
+
 __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nchunks,
                                                          uint32_t* __restrict__ cand_ls,
-                                                         uint64_t* __restrict__ cand_key,
+                                                         uint32_t* __restrict__ cand_slot,
                                                          int32_t* __restrict__ chunk_cnt,
                                                          uint32_t* __restrict__ chunk_max) {
     __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_max[kThreads / 64];
     const int tid = threadIdx.x;
+    const u32x4l* ls4 = reinterpret_cast<const u32x4l*>(T.last_seen);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const int64_t base = c * kChunk;
-        int64_t k[kPerThread];
-        uint32_t live = 0;
+        const int64_t qbase = c * (kChunk / 4);           // first slot quad of the chunk
+        uint32_t ls[kPerThread];
+        uint32_t live = 0;                                // bit 4j+e: slot 4*(quad j)+e
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            const int64_t s = base + (int64_t)j * kThreads + tid;
-            k[j] = s < T.capacity ? T.keys[s] : kEmpty;
-            if (k[j] != kEmpty && k[j] != kTomb) live |= 1u << j;
+        for (int j = 0; j < kQuads; ++j) {
+            const int64_t q = qbase + (int64_t)j * kThreads + tid;
+            u32x4l x;
+            x.x = x.y = x.z = x.w = kLsDead;
+            // capacity is a multiple of 4 or below 4 slots
+            if (4 * q + 3 < T.capacity) {
+                x = ls4[q];
+            } else if (4 * q < T.capacity) {
+                x.x = T.last_seen[4 * q];
+                if (4 * q + 1 < T.capacity) x.y = T.last_seen[4 * q + 1];
+            }
+            ls[4 * j] = x.x;
+            ls[4 * j + 1] = x.y;
+            ls[4 * j + 2] = x.z;
+            ls[4 * j + 3] = x.w;
         }
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e)
+            if (ls[e] != kLsDead) live |= 1u << e;
         int pos = __popc(live);
         const int total = block_prefix(pos, s_wave);
         uint32_t my_max = 0;
+        const int64_t base = 4 * qbase;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            if (live & (1u << j)) {
-                const uint32_t ls = T.last_seen[base + (int64_t)j * kThreads + tid];
-                my_max = ls > my_max ? ls : my_max;
-                cand_ls[base + pos] = ls;
-                cand_key[base + pos] = bias(k[j]);
+        for (int e = 0; e < kPerThread; ++e) {
+            if (live & (1u << e)) {
+                my_max = ls[e] > my_max ? ls[e] : my_max;
+                cand_ls[base + pos] = ls[e];
+                cand_slot[base + pos] = (uint32_t)(4 * (qbase + (int64_t)(e >> 2) * kThreads + tid) + (e & 3));
                 ++pos;
             }
         }
@@ -308,7 +331,8 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_ls(LruState* __restrict__
 // (digits where the two agree are the same in every tie and need no pass).
 __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st,
                                                       const uint32_t* __restrict__ cand_ls,
-                                                      const uint64_t* __restrict__ cand_key,
+                                                      const uint32_t* __restrict__ cand_slot,
+                                                      const int64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
                                                       uint64_t* __restrict__ ties, int32_t* __restrict__ tie_cnt) {
     __shared__ int s_wave[kThreads / 64];
@@ -330,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st
             const bool tie = j < cnt && cand_ls[c * kChunk + j] == thr;
             uint64_t key = 0;
             if (tie) {
-                key = cand_key[c * kChunk + j];
+                key = bias(keys[cand_slot[c * kChunk + j]]);
                 atomicAdd(&s_h[(uint32_t)(key >> 56)], 1u);
                 k_and &= key;
                 k_or |= key;
@@ -408,13 +432,17 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict_
     commit_hist(st, s_h);
 }
 
-__device__ __forceinline__ bool is_victim(uint32_t ls, uint64_t key, uint32_t thr, uint64_t kthr) {
-    return ls < thr || (ls == thr && key <= kthr);
+// Victim test of a candidate; its key is read (through its slot) only when
+// its last_seen equals the selected one.
+__device__ __forceinline__ bool is_victim(uint32_t ls, uint32_t slot, const int64_t* __restrict__ keys,
+                                          uint32_t thr, uint64_t kthr) {
+    return ls < thr || (ls == thr && bias(keys[slot]) <= kthr);
 }
 
 __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* __restrict__ st,
                                                                const uint32_t* __restrict__ cand_ls,
-                                                               const uint64_t* __restrict__ cand_key,
+                                                               const uint32_t* __restrict__ cand_slot,
+                                                               const int64_t* __restrict__ keys,
                                                                const int32_t* __restrict__ chunk_cnt,
                                                                int64_t nchunks, int32_t* __restrict__ vic_cnt) {
     __shared__ int s_wave[kThreads / 64];
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* 
         const int cnt = any ? chunk_cnt[c] : 0;
         int mine = 0;
         for (int j = threadIdx.x; j < cnt; j += kThreads)
-            mine += is_victim(cand_ls[c * kChunk + j], cand_key[c * kChunk + j], thr, kthr);
+            mine += is_victim(cand_ls[c * kChunk + j], cand_slot[c * kChunk + j], keys, thr, kthr);
         const int tot = block_prefix(mine, s_wave);
         if (threadIdx.x == 0) vic_cnt[c] = tot;
     }
@@ -433,7 +461,8 @@ __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* 
 
 __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restrict__ st,
                                                       const uint32_t* __restrict__ cand_ls,
-                                                      const uint64_t* __restrict__ cand_key,
+                                                      const uint32_t* __restrict__ cand_slot,
+                                                      const int64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
                                                       const int32_t* __restrict__ vic_off, int64_t* __restrict__ victims,
                                                       int64_t cap, int64_t* __restrict__ n_victims) {
@@ -447,15 +476,18 @@ __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restric
         int64_t run = vic_off[c];
         for (int j0 = 0; j0 < cnt; j0 += kThreads) {
             const int j = j0 + threadIdx.x;
-            uint64_t key = 0;
+            int64_t key = 0;
             bool v = false;
             if (j < cnt) {
-                key = cand_key[c * kChunk + j];
-                v = is_victim(cand_ls[c * kChunk + j], key, thr, kthr);
+                const uint32_t ls = cand_ls[c * kChunk + j];
+                if (ls <= thr) {
+                    key = keys[cand_slot[c * kChunk + j]];
+                    v = ls < thr || bias(key) <= kthr;
+                }
             }
             int pos = v ? 1 : 0;
             const int tot = block_prefix(pos, s_wave);
-            if (v && run + pos < cap) victims[run + pos] = (int64_t)(key ^ 0x8000000000000000ull);
+            if (v && run + pos < cap) victims[run + pos] = key;
             run += tot;
         }
     }
@@ -490,7 +522,7 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     const TableDev& T = t->dev;
     const unsigned gchunk = grid_for(w.nchunks, 1, 1 << 16);
     const unsigned ghist = grid_for(w.nchunks, 1, kHistBlocks);
-    hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_key,
+    hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_slot,
                        w.chunk_cnt, w.chunk_max);
     hipLaunchKernelGGL(k_lru_init, dim3(1), dim3(1024), 0, stream, w.st, w.chunk_cnt, w.chunk_max, w.nchunks, num,
                        den);
@@ -503,7 +535,7 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
                            w.nchunks, d);
         hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 0);
     }
-    hipLaunchKernelGGL(k_lru_ties, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key,
+    hipLaunchKernelGGL(k_lru_ties, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
                        w.chunk_cnt, w.nchunks, w.ties, w.tie_cnt);
     hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, 7, 1);
     for (int d = 6; d >= 0; --d) {
@@ -511,13 +543,13 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
                            w.nchunks, d);
         hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 1);
     }
-    hipLaunchKernelGGL(k_lru_count_victims, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key,
-                       w.chunk_cnt, w.nchunks, w.vic_cnt);
+    hipLaunchKernelGGL(k_lru_count_victims, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot,
+                       T.keys, w.chunk_cnt, w.nchunks, w.vic_cnt);
     htl_status st = scan_exclusive_i32(w.vic_cnt, w.vic_off, w.nchunks, nullptr, kScanIdentity, 1, w.scan_tmp,
                                        stream);
     if (st != HTL_OK) return st;
-    hipLaunchKernelGGL(k_lru_emit, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_key, w.chunk_cnt,
-                       w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev);
+    hipLaunchKernelGGL(k_lru_emit, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
+                       w.chunk_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev);
     return check_launch("ht_lru_select");
 }
 

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
                     old = __shfl(old, gshift);
                     st = (old == k) ? HT_ERASED : HT_NOT_FOUND;
                     if (gl == 0 && st == HT_ERASED && row_tmp) row_tmp[i] = T.rowid[base + hit];
+                    if (gl == 0 && st == HT_ERASED && T.last_seen) T.last_seen[base + hit] = kLsDead;
                     break;
                 }
                 if (has_empty) break;
@@ -504,14 +505,19 @@ __global__ __launch_bounds__(kProbeBlock) void k_imp_ls(TableDev T, const int64_
         const int st = status[i];
         if (st != HT_FOUND && st != HT_INSERTED) continue;
         const int64_t slot = find_key<G>(T, keys[i], gl, gshift);
-        if (gl == 0 && slot >= 0) T.last_seen[slot] = ls_in[i];
+        // kLsDead marks dead slots: an imported stamp takes at most the step below it
+        if (gl == 0 && slot >= 0) T.last_seen[slot] = ls_in[i] < kLsDead ? ls_in[i] : kLsDead - 1u;
     }
 }
 
 // ------------------------------------------------------------ host side --
+// Every slot EMPTY; where last_seen is kept, every slot's last_seen dead.
 htl_status fill_keys_empty(const TableDev& T, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_i64, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, s,
                        T.keys, T.capacity, kEmpty);
+    if (T.last_seen)
+        hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, s,
+                           T.last_seen, T.capacity, kLsDead);
     return check_launch("clear table keys");
 }
 
@@ -778,11 +784,6 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
             st = check_launch("ht_create: row allocator");
         }
         if (st == HTL_OK) st = fill_keys_empty(T, stream);
-        if (st == HTL_OK && T.last_seen) {
-            hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0, stream,
-                               T.last_seen, T.capacity, 0u);
-            st = check_launch("clear last_seen");
-        }
         if (st != HTL_OK) {
             std::string msg = g_last_error;
             cleanup();
@@ -801,11 +802,6 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
         return fail(HTL_ERR_NOMEM, "ht_create: device allocation failed");
     }
     htl_status st = fill_keys_empty(T, stream);
-    if (st == HTL_OK && T.last_seen) {
-        hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(T.capacity, 256 * 8, 1 << 16)), dim3(256), 0,
-                           stream, T.last_seen, T.capacity, 0u);
-        st = check_launch("clear last_seen");
-    }
     if (st != HTL_OK) {
         std::string msg = g_last_error;
         cleanup();
@@ -918,6 +914,8 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
     clear_error();
     HTL_REQUIRE(t != nullptr, "ht_find_or_insert: null table");
     HTL_REQUIRE(n_max >= 0 && n_max < ((int64_t)1 << 31), "ht_find_or_insert: n_max out of range");
+    HTL_REQUIRE(!t->dev.last_seen || step != kLsDead,
+                "ht_find_or_insert: step 0xFFFFFFFF is reserved on a table that keeps last_seen");
     if (n_max == 0) return HTL_OK;
     HTL_REQUIRE(keys && slots && status, "ht_find_or_insert: null keys/slots/status");
     HTL_REQUIRE(aligned(keys, 8) && aligned(slots, 4) && (!n_dev || aligned(n_dev, 8)),

@@ -135,7 +135,9 @@ htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream);
  *   n_max    host upper bound on the number of keys (sizes the launch).
  *   n_dev    nullable device int64: the actual count n <= n_max (e.g. the
  *            unique count written by dedup_unique_inverse); null means n_max.
- *   step     stamped into last_seen of FOUND and INSERTED keys (if kept).
+ *   step     stamped into last_seen of FOUND and INSERTED keys (if kept);
+ *            on a table that keeps last_seen, 0xFFFFFFFF is reserved (it
+ *            marks slots with no live key) and is refused (HTL_ERR_INVALID).
  *   slots    int32[n_max] out: slot of each key (growable tables: its row
  *            handle), -1 for FULL and RESERVED.
  *   status   uint8[n_max] out: HT_FOUND, HT_INSERTED (row set to the closed-
@@ -187,8 +189,10 @@ htl_status ht_export(const htl_table* t, int64_t slot_begin, int64_t slot_end, i
  *   keys int64[n]; rows dtype[n][dim]; last_seen uint32[n] (nullable);
  *   adam_m, adam_v float[n][dim] (both or neither);
  *   status uint8[n] out: as ht_find_or_insert (FULL / RESERVED keys are not
- *   written).  After an import with last_seen, eviction selections examine
- *   all four bytes of last_seen (the values are not known on the host). */
+ *   written).  A last_seen of 0xFFFFFFFF (reserved, see ht_find_or_insert)
+ *   is stored as 0xFFFFFFFE.  After an import with last_seen, eviction
+ *   selections examine all four bytes of last_seen (the values are not
+ *   known on the host). */
 htl_status ht_import(htl_table* t, const int64_t* keys, int64_t n, const void* rows,
                      const uint32_t* last_seen, const float* adam_m, const float* adam_v,
                      uint8_t* status, hipStream_t stream);

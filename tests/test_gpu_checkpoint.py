@@ -131,3 +131,25 @@ def test_scan_lists_live_slots_in_slot_order(htl, growable):
     assert np.all(to_np(ls)[:L] == 4)
     want_h = to_np(htl.table_tensor(table, "row_of_slot"))[live_slots] if growable else live_slots
     assert np.array_equal(to_np(h)[:L], want_h)
+
+
+def test_import_of_reserved_last_seen(htl):
+    # 0xFFFFFFFF marks slots without a live key, so an imported stamp of that
+    # value is stored as 0xFFFFFFFE and the key stays an eviction candidate
+    table = htl.Table(8, 4, "f32", last_seen=True)
+    keys = torch.tensor([11, 12, 13], dtype=torch.int64).cuda()
+    rows = torch.zeros((3, 4), dtype=torch.float32).cuda()
+    ls = torch.tensor([5, -1, -2], dtype=torch.int32).cuda()        # 5, 0xFFFFFFFF, 0xFFFFFFFE
+    st = table.import_(keys, rows, last_seen=ls)
+    assert (st.cpu().numpy() == htl.INSERTED).all()
+    d = table.export()
+    n = int(d["n"].item())
+    got = dict(zip(d["keys"][:n].cpu().tolist(), (d["last_seen"][:n].cpu().numpy().astype(np.uint32)).tolist()))
+    assert got == {11: 5, 12: 0xFFFFFFFE, 13: 0xFFFFFFFE}
+    victims, nv = table.lru_select(1, 1)
+    assert int(nv.item()) == 3
+    victims, nv = table.lru_select(1, 3)
+    assert int(nv.item()) == 1 and int(victims[0].item()) == 11
+    # ties on 0xFFFFFFFE: the smaller key goes first
+    victims, nv = table.lru_select(2, 3)
+    assert sorted(victims[:2].cpu().tolist()) == [11, 12]

@@ -120,3 +120,43 @@ def test_lru_many_ties(htl, orc):
         ref = otab.lru_victims(num, den)
         assert k == ref.size
         assert np.array_equal(np.sort(to_np(victims)[:k]), np.sort(ref))
+
+
+@pytest.mark.parametrize("growable", [False, True])
+def test_lru_sees_only_live_slots(htl, orc, growable):
+    # erased, cleared and rehashed slots must not be eviction candidates:
+    # selecting every live key returns exactly the live set
+    table = htl.Table(12, 8, "f32", last_seen=True, growable=growable)
+    rng = np.random.default_rng(21)
+    keys = np.unique(rng.integers(-(1 << 62), 1 << 62, 1500).astype(np.int64))
+    table.find_or_insert(torch.from_numpy(keys).cuda(), step=7)
+    gone = keys[::3]
+    st = to_np(table.erase(torch.from_numpy(gone).cuda()))
+    assert (st == htl.ERASED).all()
+    live = np.setdiff1d(keys, gone)
+
+    def all_victims():
+        victims, nv = table.lru_select(1, 1)
+        k = int(nv.item())
+        return np.sort(to_np(victims)[:k])
+
+    assert np.array_equal(all_victims(), live)
+    if growable:
+        table.resize(13)
+        assert np.array_equal(all_victims(), live)
+    # re-inserting an erased key makes it a candidate again, with its new step
+    table.find_or_insert(torch.from_numpy(gone[:10]).cuda(), step=2)
+    victims, nv = table.lru_select(10, live.size + 10)
+    assert int(nv.item()) == 10
+    assert np.array_equal(np.sort(to_np(victims)[:10]), np.sort(gone[:10]))
+    table.clear()
+    victims, nv = table.lru_select(1, 1)
+    assert int(nv.item()) == 0
+
+
+def test_reserved_step(htl):
+    keys = torch.arange(5, dtype=torch.int64).cuda()
+    with pytest.raises(htl.HTLError):
+        htl.Table(6, 4, "f32", last_seen=True).find_or_insert(keys, step=0xFFFFFFFF)
+    _, st = htl.Table(6, 4, "f32").find_or_insert(keys, step=0xFFFFFFFF)   # no last_seen kept: any step
+    assert (to_np(st) == htl.INSERTED).all()
