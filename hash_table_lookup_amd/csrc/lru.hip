@@ -122,7 +122,8 @@ __device__ __forceinline__ int block_prefix(int& v, int* s_wave) {
 }
 
 // Each chunk compacts its live slots (last_seen, slot) into its own region
-// (order within the region: by thread, then by the thread's slots).  Only
+// (order within the region: by thread, then by the thread's slots), staged
+// in LDS.  Only
 // last_seen is read: a slot without a live key holds kLsDead there.  Loads
 // are 16 bytes per lane: slot quad j * kThreads + tid of the chunk belongs to
 // thread tid.
@@ -136,6 +137,8 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
                                                          uint32_t* __restrict__ chunk_max) {
     __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_max[kThreads / 64];
+    __shared__ uint32_t s_ls[kChunk];
+    __shared__ uint16_t s_off[kChunk];
     const int tid = threadIdx.x;
     const u32x4l* ls4 = reinterpret_cast<const u32x4l*>(T.last_seen);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
@@ -166,12 +169,14 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
         const int total = block_prefix(pos, s_wave);
         uint32_t my_max = 0;
         const int64_t base = 4 * qbase;
+        // compacted in LDS first: the global stores then go out dense, a
+        // few per block, instead of many sparse partial-line stores
 #pragma unroll
         for (int e = 0; e < kPerThread; ++e) {
             if (live & (1u << e)) {
                 my_max = ls[e] > my_max ? ls[e] : my_max;
-                cand_ls[base + pos] = ls[e];
-                cand_slot[base + pos] = (uint32_t)(4 * (qbase + (int64_t)(e >> 2) * kThreads + tid) + (e & 3));
+                s_ls[pos] = ls[e];
+                s_off[pos] = (uint16_t)(4 * ((e >> 2) * kThreads + tid) + (e & 3));
                 ++pos;
             }
         }
@@ -181,6 +186,10 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
         }
         if (lane_id() == 0) s_max[tid >> 6] = my_max;
         __syncthreads();
+        for (int j = tid; j < total; j += kThreads) {
+            cand_ls[base + j] = s_ls[j];
+            cand_slot[base + j] = (uint32_t)(base + s_off[j]);
+        }
         if (tid == 0) {
             uint32_t m = 0;
             for (int w = 0; w < kThreads / 64; ++w) m = s_max[w] > m ? s_max[w] : m;
@@ -275,32 +284,33 @@ __global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d, int is_ke
     }
 }
 
-// Calls f(c, cnt) for each chunk c = blockIdx.x + i * gridDim.x whose count
-// is nonzero.  The block's counts are loaded kThreads at a time in one round
-// (a chain of one dependent load per chunk costs microseconds per block once
-// the lists are sparse).  When zero_out is given, zero_out[c] = 0 is stored
-// for the chunks skipped.  f may use block barriers: cnt is block-uniform.
+// Calls f(c, cnt) for each chunk c = w + i * W whose count is nonzero, where
+// w is this wave's index in the grid and W the number of waves: each wave
+// works through its own chunks, so the per-chunk work needs no block
+// barrier.  The wave's counts are loaded 64 at a time in one round (a chain
+// of one dependent load per chunk costs microseconds once the lists are
+// sparse).  When zero_out is given, zero_out[c] = 0 is stored for the
+// chunks skipped.  f may use wave-wide operations: cnt is wave-uniform.
 template <class F>
-__device__ __forceinline__ void for_my_chunks(const int32_t* __restrict__ cnts, int64_t nchunks,
-                                              int32_t* __restrict__ zero_out, F&& f) {
-    __shared__ int32_t s_cnt[kThreads];
-    const int64_t G = gridDim.x;
-    const int64_t mine = nchunks > (int64_t)blockIdx.x ? (nchunks - blockIdx.x + G - 1) / G : 0;
-    for (int64_t i0 = 0; i0 < mine; i0 += kThreads) {
-        const int64_t i = i0 + threadIdx.x;
+__device__ __forceinline__ void for_wave_chunks(const int32_t* __restrict__ cnts, int64_t nchunks,
+                                                int32_t* __restrict__ zero_out, F&& f) {
+    constexpr int kWaves = kThreads / 64;
+    const int lane = lane_id();
+    const int64_t W = (int64_t)gridDim.x * kWaves;
+    const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t mine = nchunks > w ? (nchunks - w + W - 1) / W : 0;
+    for (int64_t i0 = 0; i0 < mine; i0 += 64) {
+        const int64_t i = i0 + lane;
         int32_t cnt = 0;
         if (i < mine) {
-            cnt = cnts[blockIdx.x + i * G];
-            if (cnt <= 0 && zero_out) zero_out[blockIdx.x + i * G] = 0;
+            cnt = cnts[w + i * W];
+            if (cnt <= 0 && zero_out) zero_out[w + i * W] = 0;
         }
-        s_cnt[threadIdx.x] = cnt;
-        __syncthreads();
-        const int nb = (int)(mine - i0 < kThreads ? mine - i0 : kThreads);
+        const int nb = (int)(mine - i0 < 64 ? mine - i0 : 64);
         for (int j = 0; j < nb; ++j) {
-            const int c = s_cnt[j];
-            if (c > 0) f(blockIdx.x + (i0 + j) * G, c);
+            const int c = __shfl(cnt, j);
+            if (c > 0) f(w + (i0 + j) * W, c);
         }
-        __syncthreads();
     }
 }
 
@@ -315,8 +325,9 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_ls(LruState* __restrict__
     __syncthreads();
     const uint32_t hi_shift = 8u * (uint32_t)(d + 1);
     const uint32_t want = hi_shift >= 32 ? 0u : (st->ls_prefix >> hi_shift);
-    for_my_chunks(chunk_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
-        for (int j = threadIdx.x; j < cnt; j += kThreads) {
+    const int lane = lane_id();
+    for_wave_chunks(chunk_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
+        for (int j = lane; j < cnt; j += 64) {
             const uint32_t x = cand_ls[c * kChunk + j];
             const uint32_t hi = hi_shift >= 32 ? 0u : (x >> hi_shift);
             if (hi == want) atomicAdd(&s_h[(x >> (8 * d)) & 255u], 1u);
@@ -326,16 +337,16 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_ls(LruState* __restrict__
     commit_hist(st, s_h);
 }
 
-// Candidates tying on the selected last_seen, compacted per chunk; the
-// histogram of their top key digit (7); and the AND and OR of all their keys
-// (digits where the two agree are the same in every tie and need no pass).
+// Candidates tying on the selected last_seen, compacted per chunk, with
+// their keys (read through the slot); the histogram of their top key digit
+// (7); and the AND and OR of all their keys (digits where the two agree are
+// the same in every tie and need no pass).
 __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st,
                                                       const uint32_t* __restrict__ cand_ls,
                                                       const uint32_t* __restrict__ cand_slot,
                                                       const int64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
                                                       uint64_t* __restrict__ ties, int32_t* __restrict__ tie_cnt) {
-    __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_h[256];
     __shared__ unsigned long long s_and[kThreads / 64], s_or[kThreads / 64];
     if (st->k <= 0) {
@@ -344,33 +355,38 @@ __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st
         return;
     }
     const uint32_t thr = st->ls_prefix;
+    const int lane = lane_id();
     s_h[threadIdx.x] = 0u;
     unsigned long long k_and = ~0ull, k_or = 0ull;
     __syncthreads();
-    for_my_chunks(chunk_cnt, nchunks, tie_cnt, [&](int64_t c, int cnt) {
+    for_wave_chunks(chunk_cnt, nchunks, tie_cnt, [&](int64_t c, int cnt) {
         int run = 0;
-        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
-            const int j = j0 + threadIdx.x;
-            const bool tie = j < cnt && cand_ls[c * kChunk + j] == thr;
+        for (int j0 = 0; j0 < cnt; j0 += 64) {
+            const int j = j0 + lane;
+            uint32_t ls = 0, slot = 0;
+            if (j < cnt) {
+                ls = cand_ls[c * kChunk + j];
+                slot = cand_slot[c * kChunk + j];
+            }
+            const bool tie = j < cnt && ls == thr;
             uint64_t key = 0;
             if (tie) {
-                key = bias(keys[cand_slot[c * kChunk + j]]);
+                key = bias(keys[slot]);
                 atomicAdd(&s_h[(uint32_t)(key >> 56)], 1u);
                 k_and &= key;
                 k_or |= key;
             }
-            int pos = tie ? 1 : 0;
-            const int tot = block_prefix(pos, s_wave);
-            if (tie) ties[c * kChunk + run + pos] = key;
-            run += tot;
+            const uint64_t m = __ballot(tie);
+            if (tie) ties[c * kChunk + run + __popcll(m & lanemask_lt())] = key;
+            run += __popcll(m);
         }
-        if (threadIdx.x == 0) tie_cnt[c] = run;
+        if (lane == 0) tie_cnt[c] = run;
     });
     for (int off = 32; off > 0; off >>= 1) {
         k_and &= __shfl_xor(k_and, off);
         k_or |= __shfl_xor(k_or, off);
     }
-    if (lane_id() == 0) {
+    if (lane == 0) {
         s_and[threadIdx.x >> 6] = k_and;
         s_or[threadIdx.x >> 6] = k_or;
     }
@@ -396,24 +412,24 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict_
     const uint64_t diff = st->key_or ^ st->key_and;
     if (((diff >> (8 * d)) & 255u) == 0) return;
     const bool compact = (diff >> (8 * (d + 1))) != 0;     // d < 7 here: digit 7 is counted by k_lru_ties
-    __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_h[256];
     s_h[threadIdx.x] = 0u;
     __syncthreads();
     const uint64_t want = st->key_prefix >> (8 * (d + 1));
-    for_my_chunks(tie_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
+    const int lane = lane_id();
+    for_wave_chunks(tie_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
         if (!compact) {
-            for (int j = threadIdx.x; j < cnt; j += kThreads) {
+            for (int j = lane; j < cnt; j += 64) {
                 const uint64_t x = ties[c * kChunk + j];
                 atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
             }
             return;
         }
-        // in place: the writes of a round land below the round's reads,
-        // and block_prefix's barriers order every read before them
+        // in place, one wave per chunk: a round's writes land below the
+        // next round's reads, and each store waits for its own round's load
         int run = 0;
-        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
-            const int j = j0 + threadIdx.x;
+        for (int j0 = 0; j0 < cnt; j0 += 64) {
+            const int j = j0 + lane;
             uint64_t x = 0;
             bool keep = false;
             if (j < cnt) {
@@ -421,12 +437,11 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict_
                 keep = (x >> (8 * (d + 1))) == want;
                 if (keep) atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
             }
-            int pos = keep ? 1 : 0;
-            const int tot = block_prefix(pos, s_wave);
-            if (keep) ties[c * kChunk + run + pos] = x;
-            run += tot;
+            const uint64_t m = __ballot(keep);
+            if (keep) ties[c * kChunk + run + __popcll(m & lanemask_lt())] = x;
+            run += __popcll(m);
         }
-        if (threadIdx.x == 0) tie_cnt[c] = run;
+        if (lane == 0) tie_cnt[c] = run;
     });
     __syncthreads();
     commit_hist(st, s_h);
@@ -439,23 +454,28 @@ __device__ __forceinline__ bool is_victim(uint32_t ls, uint32_t slot, const int6
     return ls < thr || (ls == thr && bias(keys[slot]) <= kthr);
 }
 
+// The victim passes take one chunk per wave (c = w + i * W over the grid's
+// waves), with wave-wide prefixes.
 __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* __restrict__ st,
                                                                const uint32_t* __restrict__ cand_ls,
                                                                const uint32_t* __restrict__ cand_slot,
                                                                const int64_t* __restrict__ keys,
                                                                const int32_t* __restrict__ chunk_cnt,
                                                                int64_t nchunks, int32_t* __restrict__ vic_cnt) {
-    __shared__ int s_wave[kThreads / 64];
     const bool any = st->k > 0;
     const uint32_t thr = st->ls_prefix;
     const uint64_t kthr = st->key_prefix;
-    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int lane = lane_id();
+    const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); c < nchunks; c += W) {
         const int cnt = any ? chunk_cnt[c] : 0;
-        int mine = 0;
-        for (int j = threadIdx.x; j < cnt; j += kThreads)
-            mine += is_victim(cand_ls[c * kChunk + j], cand_slot[c * kChunk + j], keys, thr, kthr);
-        const int tot = block_prefix(mine, s_wave);
-        if (threadIdx.x == 0) vic_cnt[c] = tot;
+        int tot = 0;
+        for (int j0 = 0; j0 < cnt; j0 += 64) {
+            const int j = j0 + lane;
+            const bool v = j < cnt && is_victim(cand_ls[c * kChunk + j], cand_slot[c * kChunk + j], keys, thr, kthr);
+            tot += __popcll(__ballot(v));
+        }
+        if (lane == 0) vic_cnt[c] = tot;
     }
 }
 
@@ -466,16 +486,17 @@ __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restric
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
                                                       const int32_t* __restrict__ vic_off, int64_t* __restrict__ victims,
                                                       int64_t cap, int64_t* __restrict__ n_victims) {
-    __shared__ int s_wave[kThreads / 64];
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_victims = st->k;
     const bool any = st->k > 0;
     const uint32_t thr = st->ls_prefix;
     const uint64_t kthr = st->key_prefix;
-    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int lane = lane_id();
+    const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); c < nchunks; c += W) {
         const int cnt = any ? chunk_cnt[c] : 0;
         int64_t run = vic_off[c];
-        for (int j0 = 0; j0 < cnt; j0 += kThreads) {
-            const int j = j0 + threadIdx.x;
+        for (int j0 = 0; j0 < cnt; j0 += 64) {
+            const int j = j0 + lane;
             int64_t key = 0;
             bool v = false;
             if (j < cnt) {
@@ -485,10 +506,10 @@ __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restric
                     v = ls < thr || bias(key) <= kthr;
                 }
             }
-            int pos = v ? 1 : 0;
-            const int tot = block_prefix(pos, s_wave);
-            if (v && run + pos < cap) victims[run + pos] = key;
-            run += tot;
+            const uint64_t m = __ballot(v);
+            const int64_t at = run + __popcll(m & lanemask_lt());
+            if (v && at < cap) victims[at] = key;
+            run += __popcll(m);
         }
     }
 }
@@ -521,6 +542,7 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     HTL_REQUIRE(ws_bytes >= w.bytes, "ht_lru_select: workspace too small");
     const TableDev& T = t->dev;
     const unsigned gchunk = grid_for(w.nchunks, 1, 1 << 16);
+    const unsigned gwave = grid_for(w.nchunks, kThreads / 64, 1 << 16);   // a chunk per wave
     const unsigned ghist = grid_for(w.nchunks, 1, kHistBlocks);
     hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_slot,
                        w.chunk_cnt, w.chunk_max);
@@ -543,12 +565,12 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
                            w.nchunks, d);
         hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 1);
     }
-    hipLaunchKernelGGL(k_lru_count_victims, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot,
+    hipLaunchKernelGGL(k_lru_count_victims, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot,
                        T.keys, w.chunk_cnt, w.nchunks, w.vic_cnt);
     htl_status st = scan_exclusive_i32(w.vic_cnt, w.vic_off, w.nchunks, nullptr, kScanIdentity, 1, w.scan_tmp,
                                        stream);
     if (st != HTL_OK) return st;
-    hipLaunchKernelGGL(k_lru_emit, dim3(gchunk), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
+    hipLaunchKernelGGL(k_lru_emit, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
                        w.chunk_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev);
     return check_launch("ht_lru_select");
 }
