@@ -335,18 +335,19 @@ def run_online(args, torch, htl, workloads, dev):
     table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=args.growable)
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.n, spec.dim), dtype=torch.bfloat16, device=dev)
-    fwd, lru, ers = [], [], []
+    fwd, lru, ers, gat = [], [], [], []
     U_last = 0
     gen = workloads.DynamicOnlineStream(spec, steps)
     hold = _GpuHold(torch, stream)
     for s in range(steps):
         keys = torch.from_numpy(gen.keys(s)).to(dev)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         torch.cuda.synchronize()
         hold(4.0)                       # the host enqueues forward + LRU behind it
         e[0].record(stream)
         uniq, inv, nu = htl.dedup_unique_inverse(keys)
         slots, status = table.find_or_insert(uniq, n_dev=nu, step=s)
+        e[5].record(stream)
         htl.gather(table, slots, inv, out=out)
         e[1].record(stream)
         victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
@@ -361,6 +362,7 @@ def run_online(args, torch, htl, workloads, dev):
             fwd.append(e[0].elapsed_time(e[1]))
             lru.append(e[1].elapsed_time(e[2]))
             ers.append(e[3].elapsed_time(e[4]))
+            gat.append(e[5].elapsed_time(e[1]))
             U_last = int(nu.item())
         print(f"online step {s} done", file=sys.stderr, flush=True)
     ms = float(np.mean(fwd))
@@ -387,7 +389,11 @@ def run_online(args, torch, htl, workloads, dev):
                   "what": "map row space for 2^28 handles, new index, rehash of the live keys with their handles, "
                           "free of the old index (the call synchronises the stream)"}
     fwd_bytes = spec.n * (16 + row) + U_last * (33 + row)
-    lru_bytes = M * 12
+    gather_bytes = spec.n * (4 + row) + U_last * (4 + row)
+    live_now = int(table.scan()[3].item())
+    # the selection reads last_seen of every slot (dead slots are marked
+    # there) and writes then reads back each live slot's (last_seen, slot)
+    lru_bytes = M * 4 + live_now * 8 * 2
     config = {"workload": "dynamic_online", "ids_per_step": spec.n, "window": spec.window,
               "new_ids_per_step": spec.delta, "zipf_a": spec.zipf_a, "table_slots_log2": spec.capacity_log2,
               "dim": spec.dim, "row_dtype": "bf16", "evict_fraction": f"{spec.evict_num}/{spec.evict_den}",
@@ -397,6 +403,9 @@ def run_online(args, torch, htl, workloads, dev):
         ckpt = _time_checkpoint(torch, htl, table, spec, stream)
     path = {"unique_last_step": U_last, "forward_ms": round(ms, 4),
             "lru_select_ms": round(float(np.mean(lru)), 4), "erase_ms": round(float(np.mean(ers)), 4),
+            "live_keys": live_now,
+            "lru_select_roofline": _roofline("ht_lru_select (last_seen scan + radix select, all its kernels)",
+                                             lru_bytes, float(np.mean(lru))),
             "forward_algorithmic_bytes": fwd_bytes,
             "table": "growable (row handles, mapped row space)" if args.growable else "fixed",
             "resize": resize,
@@ -407,7 +416,7 @@ def run_online(args, torch, htl, workloads, dev):
                       "stream while the host enqueues each phase, so the events time GPU work, not launch "
                       "overhead; value = forward IDs/s"}
     return _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
-                   _roofline("ht_lru_select (full-table scan + radix select)", lru_bytes, float(np.mean(lru))))
+                   _roofline("k_gather (forward per-ID rows, bf16)", gather_bytes, float(np.mean(gat))))
 
 
 def _pcie_inclusive(torch, htl, table, w, dev, out, restore, steps=12):

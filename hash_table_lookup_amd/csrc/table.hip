@@ -333,47 +333,37 @@ __global__ __launch_bounds__(kProbeBlock) void k_rehash(TableDev O, TableDev N) 
 // ------------------------------------------------------- checkpoint --
 // Export of a slot range in chunks of kExpChunk slots, one block each: count
 // the live slots, prefix the counts, then write each chunk's live entries in
-// slot order (MTGR section 5: compact key scanning).
+// slot order (MTGR section 5: compact key scanning).  Keys are loaded
+// coalesced: slot j * kExpThreads + tid of the chunk belongs to thread tid
+// (load round j), so slot order is (round, wave, lane) order and a chunk's
+// prefix is taken over its kExpRounds x (kExpThreads / 64) wave counts.
 constexpr int kExpChunk = 4096;
 constexpr int kExpThreads = 256;
-constexpr int kExpPerThread = kExpChunk / kExpThreads;   // consecutive slots per thread
+constexpr int kExpRounds = kExpChunk / kExpThreads;
+constexpr int kExpWaves = kExpThreads / 64;
 
 __device__ __forceinline__ bool is_live(int64_t k) { return k != kEmpty && k != kTomb; }
 
-__device__ __forceinline__ int block_sum_prefix(int& v, int* s_wave) {
-    const int lane = lane_id(), wid = threadIdx.x >> 6;
-    int incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    if (lane == 63) s_wave[wid] = incl;
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kExpThreads / 64; ++w) {
-        const int c = s_wave[w];
-        before += (w < wid) ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    v = before + incl - v;
-    return tot;
-}
-
 __global__ __launch_bounds__(kExpThreads) void k_exp_count(TableDev T, int64_t begin, int64_t end, int64_t nchunks,
                                                           int32_t* __restrict__ cnt) {
-    __shared__ int s_wave[kExpThreads / 64];
+    __shared__ int s_wave[kExpWaves];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const int64_t s0 = begin + c * kExpChunk + (int64_t)threadIdx.x * kExpPerThread;
+        const int64_t s0 = begin + c * kExpChunk + threadIdx.x;
         int mine = 0;
 #pragma unroll
-        for (int j = 0; j < kExpPerThread; ++j) {
-            const int64_t s = s0 + j;
+        for (int j = 0; j < kExpRounds; ++j) {
+            const int64_t s = s0 + (int64_t)j * kExpThreads;
             if (s < end && is_live(T.keys[s])) ++mine;
         }
-        const int tot = block_sum_prefix(mine, s_wave);
-        if (threadIdx.x == 0) cnt[c] = tot;
+        for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
+        if (lane_id() == 0) s_wave[threadIdx.x >> 6] = mine;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int tot = 0;
+            for (int w = 0; w < kExpWaves; ++w) tot += s_wave[w];
+            cnt[c] = tot;
+        }
+        __syncthreads();
     }
 }
 
@@ -382,32 +372,56 @@ __global__ __launch_bounds__(kExpThreads) void k_exp_write(TableDev T, int64_t b
                                                           int64_t* __restrict__ keys_out, void* __restrict__ rows_out,
                                                           uint32_t* __restrict__ ls_out, float* __restrict__ m_out,
                                                           float* __restrict__ v_out, int32_t* __restrict__ slots_out) {
-    __shared__ int s_wave[kExpThreads / 64];
-    __shared__ int32_t s_row[kExpChunk];     // row handle of the chunk's e-th live entry
+    __shared__ int s_pre[kExpRounds * kExpWaves];   // per (round, wave): live entries before it in the chunk
+    __shared__ int s_total;
+    __shared__ int32_t s_row[kExpChunk];            // row handle of the chunk's e-th live entry
+    __shared__ int32_t s_slot[kExpChunk];           // its slot
     const int64_t row_bytes = (int64_t)T.dim * T.elem_bytes;
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const int64_t s0 = begin + c * kExpChunk + (int64_t)threadIdx.x * kExpPerThread;
-        int64_t k[kExpPerThread];
-        uint32_t live = 0;
+        const int64_t s0 = begin + c * kExpChunk + threadIdx.x;
+        int64_t k[kExpRounds];
 #pragma unroll
-        for (int j = 0; j < kExpPerThread; ++j) {
-            const int64_t s = s0 + j;
+        for (int j = 0; j < kExpRounds; ++j) {
+            const int64_t s = s0 + (int64_t)j * kExpThreads;
             k[j] = s < end ? T.keys[s] : kEmpty;
-            if (is_live(k[j])) live |= 1u << j;
         }
-        int pos = __popc(live);
-        const int total = block_sum_prefix(pos, s_wave);     // thread-major = slot order
-        const int64_t base = off[c];
+        uint64_t m[kExpRounds];
 #pragma unroll
-        for (int j = 0; j < kExpPerThread; ++j) {
-            if (!(live & (1u << j))) continue;
-            if (keys_out) keys_out[base + pos] = k[j];
-            if (ls_out) ls_out[base + pos] = T.last_seen ? T.last_seen[s0 + j] : 0u;
-            s_row[pos] = (int32_t)row_of(T, s0 + j);
-            if (slots_out) slots_out[base + pos] = s_row[pos];
-            ++pos;
+        for (int j = 0; j < kExpRounds; ++j) {
+            m[j] = __ballot(is_live(k[j]));
+            if (lane == 0) s_pre[j * kExpWaves + wid] = __popcll(m[j]);
         }
         __syncthreads();
+        if (threadIdx.x < 64) {                       // exclusive scan of the 64 counts
+            const int v = threadIdx.x < kExpRounds * kExpWaves ? s_pre[threadIdx.x] : 0;
+            int incl = v;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            if (threadIdx.x < kExpRounds * kExpWaves) s_pre[threadIdx.x] = incl - v;
+            if (threadIdx.x == 63) s_total = incl;
+        }
+        __syncthreads();
+        const int total = s_total;
+        const int64_t base = off[c];
+        const uint64_t below = lanemask_lt();
+#pragma unroll
+        for (int j = 0; j < kExpRounds; ++j) {
+            if (m[j] & (1ull << lane)) {
+                const int pos = s_pre[j * kExpWaves + wid] + __popcll(m[j] & below);
+                const int64_t s = s0 + (int64_t)j * kExpThreads;
+                if (keys_out) keys_out[base + pos] = k[j];
+                s_slot[pos] = (int32_t)s;
+                s_row[pos] = (int32_t)row_of(T, s);
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < total; e += kExpThreads) {
+            if (ls_out) ls_out[base + e] = T.last_seen ? T.last_seen[s_slot[e]] : 0u;
+            if (slots_out) slots_out[base + e] = s_row[e];
+        }
         if (rows_out) {
             if ((row_bytes & 15) == 0) {
                 const int vpr = (int)(row_bytes >> 4);
