@@ -13,7 +13,7 @@ namespace htl {
 
 constexpr int kProbeBlock = 256;
 
-// Lanes per key in the probe kernels (1, 2, 4, 8 or 16; default 4); the
+// Lanes per key in the probe kernels (1, 2, 4, 8 or 16; default 2); the
 // environment variable HTL_PROBE_LANES overrides it.
 int probe_lanes();
 

@@ -50,8 +50,8 @@ constexpr int64_t kProbeGridMax = 1 << 15;   // workgroups of the find-or-insert
 int probe_lanes() {
     static int lanes = [] {
         const char* e = getenv("HTL_PROBE_LANES");
-        int v = e ? atoi(e) : 4;
-        return (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 4;
+        int v = e ? atoi(e) : 2;
+        return (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 2;
     }();
     return lanes;
 }
