@@ -37,11 +37,10 @@
 namespace htl {
 namespace {
 
-constexpr int kCTile = 2048;               // IDs per counting tile
-constexpr int kCThreads = 256;
-constexpr int kCPerThread = kCTile / kCThreads;
-constexpr int kCCap = 2 * kCTile;          // LDS hash slots
-constexpr int kCCapLog2 = 12;
+constexpr int kCThreads = 256;             // threads of a counting block
+// IDs per counting tile (on the backward workload: 2048 -> 235 us, 4096 ->
+// 196 us, 8192 -> 245 us, where its 128 KB of LDS leaves one block per CU)
+constexpr int kCTile = 4096;
 constexpr int kSmallMax = 32;              // longest segment summed by one team
 constexpr int kChunk = 1024;               // rows per workgroup in long segments
 constexpr int kRBlock = 256;
@@ -113,25 +112,34 @@ __global__ void k_seg_zero(int32_t* __restrict__ counts, int64_t u_max, const in
     }
 }
 
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
+
+// Counting tile of TILE IDs: an LDS hash of the tile's distinct uniques
+// (2*TILE slots) counts each one's IDs and ranks them in tile order; then
+// one atomic per (tile, unique) on the unique's counter returns the tile's
+// base in the segment.  Every tile that holds a hot unique adds to that one
+// counter, and those same-address atomics serialise: bigger tiles mean fewer
+// of them.
+template <int TILE>
 __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restrict__ inverse, int64_t n,
                                                         int64_t u_max, const int64_t* __restrict__ n_dev,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ rel) {
-    __shared__ int32_t s_u[kCCap];
-    __shared__ int32_t s_cnt[kCCap];
-    __shared__ int32_t s_base[kCCap];
+    constexpr int CAP = 2 * TILE, CAP_LOG2 = ilog2(CAP), PER = TILE / kCThreads;
+    __shared__ int32_t s_u[CAP];
+    __shared__ int32_t s_cnt[CAP];          // count of each key in the tile, then its base
     const int tid = threadIdx.x;
     const int64_t U = dev_count(u_max, n_dev);
     const int64_t C = spread_c(U);
-    for (int64_t tile = blockIdx.x; tile * kCTile < n; tile += gridDim.x) {
-        const int64_t base = tile * kCTile;
-        for (int i = tid; i < kCCap; i += kCThreads) {
+    for (int64_t tile = blockIdx.x; tile * TILE < n; tile += gridDim.x) {
+        const int64_t base = tile * TILE;
+        for (int i = tid; i < CAP; i += kCThreads) {
             s_u[i] = -1;
             s_cnt[i] = 0;
         }
         __syncthreads();
-        int pos[kCPerThread], rank[kCPerThread];
+        int pos[PER], rank[PER];
 #pragma unroll
-        for (int j = 0; j < kCPerThread; ++j) {
+        for (int j = 0; j < PER; ++j) {
             const int64_t idx = base + j * kCThreads + tid;
             pos[j] = -1;
             rank[j] = 0;
@@ -139,26 +147,26 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
             const int32_t u = inverse[idx];
             if (u < 0 || u >= U) continue;       // outside [0, U): contributes nowhere
             const uint32_t h = (uint32_t)u * 0x9E3779B1u;
-            uint32_t p = h >> (32 - kCCapLog2);
-            const uint32_t stp = ((h >> 7) | 1u) & (kCCap - 1);
-            for (int probe = 0; probe < kCCap; ++probe) {
+            uint32_t p = h >> (32 - CAP_LOG2);
+            const uint32_t stp = ((h >> 7) | 1u) & (CAP - 1);
+            for (int probe = 0; probe < CAP; ++probe) {
                 const int32_t old = atomicCAS(&s_u[p], -1, u);
                 if (old == -1 || old == u) break;
-                p = (p + stp) & (kCCap - 1);
+                p = (p + stp) & (CAP - 1);
             }
             pos[j] = (int)p;
             rank[j] = atomicAdd(&s_cnt[p], 1);
         }
         __syncthreads();
-        for (int i = tid; i < kCCap; i += kCThreads) {
+        for (int i = tid; i < CAP; i += kCThreads) {
             const int32_t u = s_u[i];
-            if (u >= 0) s_base[i] = atomicAdd(&counts[spread_q(u, C)], s_cnt[i]);
+            if (u >= 0) s_cnt[i] = atomicAdd(&counts[spread_q(u, C)], s_cnt[i]);
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kCPerThread; ++j) {
+        for (int j = 0; j < PER; ++j) {
             const int64_t idx = base + j * kCThreads + tid;
-            if (pos[j] >= 0) rel[idx] = s_base[pos[j]] + rank[j];
+            if (pos[j] >= 0) rel[idx] = s_cnt[pos[j]] + rank[j];
         }
         __syncthreads();
     }
@@ -662,8 +670,8 @@ htl_status build_csr(const int32_t* inverse, int64_t n, const int64_t* n_dev, in
                      hipStream_t stream) {
     hipLaunchKernelGGL(k_seg_zero, dim3(grid_for(u_max + kSpread, 256 * 4, 1 << 14)), dim3(256), 0, stream, w.counts,
                        u_max, n_dev, w.n_large, w.n_seg);
-    hipLaunchKernelGGL(k_seg_count, dim3(grid_for(ceil_div(n, kCTile), 1, 1 << 16)), dim3(kCThreads), 0, stream,
-                       inverse, n, u_max, n_dev, w.counts, w.rel);
+    hipLaunchKernelGGL(k_seg_count<kCTile>, dim3(grid_for(ceil_div(n, kCTile), 1, 1 << 16)), dim3(kCThreads), 0,
+                       stream, inverse, n, u_max, n_dev, w.counts, w.rel);
     htl_status st = scan_exclusive_i32(w.counts, w.seg_off, u_max + kSpread, w.n_seg, kScanIdentity, 1, w.scan_tmp,
                                        stream);
     if (st != HTL_OK) return st;
