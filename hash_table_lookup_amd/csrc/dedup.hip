@@ -12,7 +12,9 @@
 //     and a 16-bit local index per key.  One copy of each key leaves the tile,
 //     as one copy per sender would leave a device before the exchange; under
 //     Zipf traffic this also turns the hottest key's thousands of global
-//     atomics into at most one per tile.
+//     atomics into at most one per tile.  The same grid first clears the
+//     stage-2 set (no launch of its own; its stores stream out while the
+//     tiles work in LDS).
 //   stage 2 (k_dedup_claim, [k_dedup_count], k_dedup_assign): every tile
 //     survivor is inserted into a device-wide open-addressing set
 //     (next_pow2(3n/2 + 1) slots, 64-bit CAS).  One survivor per key owns
@@ -87,17 +89,6 @@ DedupWs layout(int64_t n, char* base) {
     w.local = (uint16_t*)take((size_t)n * 2);
     w.bytes = off;
     return w;
-}
-
-template <bool ORDERED>
-__global__ void k_dedup_clear(unsigned long long* __restrict__ set_keys, int32_t* __restrict__ set_owner,
-                              uint64_t cap, int32_t* __restrict__ misc) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i <= (int64_t)cap; i += stride) {
-        if (i < (int64_t)cap) set_keys[i] = kFree;
-        if (ORDERED) set_owner[i] = kNoOwner;
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0) misc[0] = 0;
 }
 
 constexpr int kGlobalThreads = kTileThreads;
@@ -289,21 +280,15 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
         // launch, no device set to clear), in first-occurrence order, which
         // both modes accept.
         hipLaunchKernelGGL(k_dedup_tile<true>, dim3(1), dim3(kTileThreads), 0, stream, keys, n, unique,
-                           (int32_t*)nullptr, (uint16_t*)nullptr, inverse, n_unique_dev);
+                           (int32_t*)nullptr, (uint16_t*)nullptr, inverse, n_unique_dev, SetClear{});
         return check_launch(who);
     }
     const int64_t ntiles = ceil_div(n, kTile);
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
-    const unsigned gclear = grid_for((int64_t)w.cap + 1, 256 * 8, 1 << 14);
-
-    if (ordered)
-        hipLaunchKernelGGL(k_dedup_clear<true>, dim3(gclear), dim3(256), 0, stream, w.set_keys, w.set_owner, w.cap,
-                           w.misc);
-    else
-        hipLaunchKernelGGL(k_dedup_clear<false>, dim3(gclear), dim3(256), 0, stream, w.set_keys, w.set_owner, w.cap,
-                           w.misc);
+    // the stage-1 grid also clears the device set (owners only in ordered mode)
+    const SetClear clr{w.set_keys, ordered ? w.set_owner : nullptr, w.cap, w.misc};
     hipLaunchKernelGGL(k_dedup_tile<false>, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
-                       w.local, (int32_t*)nullptr, (int64_t*)nullptr);
+                       w.local, (int32_t*)nullptr, (int64_t*)nullptr, clr);
     if (ordered) {
         hipLaunchKernelGGL(k_dedup_claim<true>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
                            ntiles, w.set_keys, w.set_owner, (uint64_t)(w.cap - 1), w.tu_slot, w.tu_own, w.tile_win,

@@ -43,6 +43,29 @@ __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
     return before + __popcll(m & lanemask_lt());
 }
 
+// The device set of stage 2, cleared by the stage-1 grid before its tiles
+// (the stores stream out while the tiles work in LDS; stage 2 starts after
+// the whole grid).  keys == nullptr: nothing to clear.
+struct SetClear {
+    unsigned long long* keys;   // [cap] -> kFree
+    int32_t* owner;             // [cap + 1] -> kNoOwner, or nullptr
+    uint64_t cap;               // a power of two >= 256
+    int32_t* misc;              // misc[0] -> 0
+};
+
+__device__ __forceinline__ void clear_set(const SetClear& c) {
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    u64x2 f;
+    f.x = f.y = kFree;
+    u64x2* k2 = reinterpret_cast<u64x2*>(c.keys);
+    for (int64_t i = t0; i < (int64_t)(c.cap / 2); i += stride) k2[i] = f;
+    if (c.owner)
+        for (int64_t i = t0; i <= (int64_t)c.cap; i += stride) c.owner[i] = kNoOwner;
+    if (t0 == 0) c.misc[0] = 0;
+}
+
 // Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
 // occurrence inside the tile (LDS atomicMin of the position, then a block
 // scan over positions), so the result does not depend on scheduling.
@@ -55,11 +78,12 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
                                                             int32_t* __restrict__ tu_count,
                                                             uint16_t* __restrict__ local,
                                                             int32_t* __restrict__ inverse,
-                                                            int64_t* __restrict__ n_unique) {
+                                                            int64_t* __restrict__ n_unique, SetClear clr) {
     __shared__ unsigned long long s_key[kLdsCap];
     __shared__ int32_t s_tag[kLdsCap + 1];   // first position of the key, then its tile-local id
     __shared__ int s_wave[kTileThreads / 64];
     const int tid = threadIdx.x;
+    if (!FINAL && clr.keys) clear_set(clr);
 
     for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
         const int64_t base = tile * kTile;
