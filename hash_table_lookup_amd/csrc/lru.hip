@@ -208,9 +208,22 @@ __global__ __launch_bounds__(1024) void k_lru_init(LruState* st, const int32_t* 
     __shared__ uint32_t s_max[1024 / 64];
     unsigned long long sum = 0;
     uint32_t mx = 0;
-    for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
-        sum += (unsigned long long)chunk_cnt[c];
-        mx = chunk_max[c] > mx ? chunk_max[c] : mx;
+    // kInitUnroll independent loads of each array in flight per thread
+    constexpr int kInitUnroll = 8;
+    for (int64_t c0 = threadIdx.x; c0 < nchunks; c0 += (int64_t)blockDim.x * kInitUnroll) {
+        int32_t cv[kInitUnroll];
+        uint32_t mv[kInitUnroll];
+#pragma unroll
+        for (int u = 0; u < kInitUnroll; ++u) {
+            const int64_t c = c0 + (int64_t)u * blockDim.x;
+            cv[u] = c < nchunks ? chunk_cnt[c] : 0;
+            mv[u] = c < nchunks ? chunk_max[c] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kInitUnroll; ++u) {
+            sum += (unsigned long long)cv[u];
+            mx = mv[u] > mx ? mv[u] : mx;
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
         sum += __shfl_xor(sum, off);

@@ -12,7 +12,7 @@ namespace htl {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kPoolUnroll = 4;             // IDs per team in flight in the pooling loop
+constexpr int kPoolUnroll = 8;             // IDs per team in flight (merged-tables step: 4 -> 1.40 ms, 8 -> 1.29, 16 -> 1.89)
 constexpr int64_t kPoolBlocks = 1 << 14;   // workgroups of the pooling kernel (persistent grid)
 
 __device__ __forceinline__ u32x4 zero4() {
