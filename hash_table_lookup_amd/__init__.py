@@ -19,12 +19,12 @@ import torch
 from ._binding import (  # noqa: F401
     ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, GROWABLE, HTLError, INSERTED, LIB_PATH,
     META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
-    gather_pool, lib, rowwise_adam, segment_sum, segment_sum_adam, table_keys, table_tensor,
+    gather_pool, lib, release_workspaces, rowwise_adam, segment_sum, segment_sum_adam, table_keys, table_tensor,
 )
 
 __all__ = [
     "Table", "dedup_unique_inverse", "gather", "gather_pool", "segment_sum", "rowwise_adam",
-    "segment_sum_adam", "lookup", "lib", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
+    "segment_sum_adam", "lookup", "lib", "release_workspaces", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
 ]
 
 

@@ -136,6 +136,11 @@ def _workspace(tag: str, nbytes: int, device) -> torch.Tensor:
     return buf
 
 
+def release_workspaces() -> None:
+    """Drop the cached workspaces (the next call on each path allocates anew)."""
+    _ws_cache.clear()
+
+
 def _dtype_code(dtype) -> int:
     if dtype in ("f32", "fp32", "float32", torch.float32, F32):
         return F32
