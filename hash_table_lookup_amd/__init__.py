@@ -18,6 +18,7 @@ import torch
 
 from ._binding import (  # noqa: F401
     ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, GROWABLE, HTLError, INSERTED, LIB_PATH,
+    copy_probe,
     META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
     gather_pool, lib, release_workspaces, rowwise_adam, segment_sum, segment_sum_adam, table_keys, table_tensor,
 )

@@ -71,6 +71,7 @@ _SIGNATURES = {
     "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
     "segsum_adam_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum_adam": [_P, _P, _P, _P, _I64, _P, _I64, _F, _F, _F, _F, _I64, _P, _SZ, _P],
+    "htl_copy_probe": [_P, _P, _I64, _P],
     "htl_last_error": [],
 }
 _SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes",
@@ -134,6 +135,17 @@ def _workspace(tag: str, nbytes: int, device) -> torch.Tensor:
         buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
+
+
+def copy_probe(src: torch.Tensor, dst: torch.Tensor):
+    """dst <- src with the library's streaming-copy probe kernel (a bandwidth
+    reference; both contiguous, same byte size, a multiple of 16 bytes)."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("copy_probe needs contiguous GPU tensors")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("copy_probe: src and dst differ in size")
+    _check(lib().htl_copy_probe(_ptr(src), _ptr(dst), nb, _stream()))
 
 
 def release_workspaces() -> None:

@@ -334,6 +334,14 @@ htl_status emb_grad_segment_sum_adam(htl_table* t, const int32_t* slots, const f
                                      int64_t u_max, float lr, float b1, float b2, float eps,
                                      int64_t step, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* htl_copy_probe -- a plain streaming device-to-device copy (one 16-byte
+ * vector per thread, full grid), the achievable-bandwidth reference against
+ * which the lookup kernels' HBM rates are read.  A measurement aid, not a
+ * step of the lookup path (the pages define no such operation).
+ *   src, dst  device, 16-byte aligned, not overlapping; bytes a multiple of
+ *             16 (HTL_ERR_INVALID otherwise).  Enqueued on `stream`. */
+htl_status htl_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 /* htl_last_error -- message of the last failed call on this thread ("" if none). */
 const char* htl_last_error(void);
 

@@ -297,3 +297,12 @@ def test_single_large_table_full_size(htl, orc):
     idx = np.concatenate([rng.integers(0, w.keys.size, 4096), [0, w.keys.size - 1]])
     got = to_np(out[torch.from_numpy(idx).cuda()])
     assert np.array_equal(got, orc.init_rows(w.keys[idx], w.dim, orc.F32))
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 48, (1 << 24) + 16])
+def test_copy_probe(htl, nbytes):
+    # the bandwidth reference kernel copies exactly
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    htl.copy_probe(src, dst)
+    assert torch.equal(src, dst)

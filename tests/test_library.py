@@ -88,6 +88,10 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.ht_import(None, None, 1, None, None, None, None, None, None) == INVALID
     assert L.ht_view(None, None) == INVALID
     assert L.ht_destroy(None) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert L.htl_copy_probe(fake, fake, 24, None) == INVALID            # not a multiple of 16
+    assert L.htl_copy_probe(fake, ctypes.c_void_p(0x1008), 32, None) == INVALID   # misaligned
+    assert L.htl_copy_probe(None, None, 0, None) == 0                   # nothing to copy
 
 
 def test_misaligned_workspace_rejected(L):
