@@ -34,6 +34,8 @@
 //   emit    -- victims (candidates at or below the selected (last_seen,
 //              key)) are counted per chunk, the counts prefix-summed, and
 //              written densely.
+// Every pass after the collect takes one chunk per wave, with wave-wide
+// prefixes: no block barrier per chunk.
 #include "scan.h"
 
 namespace htl {
