@@ -215,8 +215,8 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
 
 /* ht_view -- raw device views of the table's storage (read-only use intended).
  * Any output may be null.  rows is dtype[M][dim]; m, v are null unless the
- * table keeps Adam state; last_seen (per slot) is null unless it keeps
- * metadata.  In a growable table rows, m and v are indexed by row handle,
+ * table keeps Adam state; last_seen (per slot; 0xFFFFFFFF at slots with no
+ * live key) is null unless it keeps metadata.  In a growable table rows, m and v are indexed by row handle,
  * and row_of_slot (int32[M], valid at live slots) maps a slot to its handle;
  * row_of_slot is null for other tables (handle = slot). */
 typedef struct {
