@@ -160,3 +160,25 @@ def test_reserved_step(htl):
         htl.Table(6, 4, "f32", last_seen=True).find_or_insert(keys, step=0xFFFFFFFF)
     _, st = htl.Table(6, 4, "f32").find_or_insert(keys, step=0xFFFFFFFF)   # no last_seen kept: any step
     assert (to_np(st) == htl.INSERTED).all()
+
+
+def test_lru_select_extremes(htl, orc):
+    # k = 0 (num = 0) selects nothing; num = den selects every live key, in
+    # any order; victims_cap below k keeps a subset of the victims
+    table = htl.Table(10, 4, "f32", last_seen=True)
+    otab = orc.Table(1 << 10, 4, orc.F32)
+    rng = np.random.default_rng(5)
+    for s in range(4):
+        ks = np.unique(rng.integers(-(1 << 40), 1 << 40, 100)).astype(np.int64)
+        table.find_or_insert(torch.from_numpy(ks).cuda(), step=s)
+        otab.find_or_insert(ks, step=s)
+    _, nv = table.lru_select(0, 5)
+    assert int(nv.item()) == 0
+    victims, nv = table.lru_select(7, 7)
+    k = int(nv.item())
+    ref = otab.lru_victims(7, 7)
+    assert k == ref.size and np.array_equal(np.sort(to_np(victims)[:k]), np.sort(ref))
+    victims, nv = table.lru_select(1, 2, victims_cap=10)
+    k = int(nv.item())
+    assert k == otab.lru_victims(1, 2).size and k > 10
+    assert np.isin(to_np(victims)[:10], otab.lru_victims(1, 2)).all()
