@@ -44,7 +44,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 4096;               // table slots per chunk (one block pass)
 constexpr int kPerThread = kChunk / kThreads;
-constexpr int kHistBlocks = 1024;          // persistent grid of the histogram passes
+// persistent grid of the histogram passes (selection on the online
+// workload: 512 blocks 0.383 ms, 1024 0.364 ms, 4096 0.452 ms)
+constexpr int kHistBlocks = 1024;
 constexpr int kBinStride = 32;             // words between global histogram bins
 
 struct LruState {
