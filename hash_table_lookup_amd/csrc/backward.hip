@@ -261,6 +261,9 @@ __device__ __forceinline__ void sum_rows(const u32x4* __restrict__ grad, int vpr
                                          int32_t beg, int32_t end, int team, int teams, int tl,
                                          float (&acc)[QMAX][4]) {
     constexpr int U = 4;
+    // i0 + teams * U must not pass INT32_MAX: n < 2^31 - 1024 leaves room
+    // for teams * U <= 1024 (teams <= kRBlock)
+    static_assert(kRBlock * U <= 1024, "int32 row index could overflow near n = 2^31");
     for (int32_t i0 = beg + team; i0 < end; i0 += teams * U) {
         int32_t r[U];
 #pragma unroll
