@@ -52,13 +52,14 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
         for (int a = 0; a < QMAX; ++a)
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[a][e] = 0.0f;
-        const int32_t beg = offsets[bag], end = offsets[bag + 1];
-        for (int32_t i0 = beg + q; i0 < end; i0 += TEAMS * kPoolUnroll) {
+        // 64-bit positions: end may lie within TEAMS * kPoolUnroll of 2^31
+        const int64_t beg = offsets[bag], end = offsets[bag + 1];
+        for (int64_t i0 = beg + q; i0 < end; i0 += TEAMS * kPoolUnroll) {
             // kPoolUnroll IDs per team in flight: inverse, then slots, then rows
             int32_t s[kPoolUnroll];
 #pragma unroll
             for (int u = 0; u < kPoolUnroll; ++u) {
-                const int32_t i = i0 + u * TEAMS;
+                const int64_t i = i0 + u * TEAMS;
                 s[u] = i < end ? (inverse ? inverse[i] : i) : -1;
             }
 #pragma unroll

@@ -1,11 +1,12 @@
 """GPU tests at the largest sizes the C ABI accepts.
 
 Slot numbers at the top of int32, row offsets past 2^32 bytes, a dedup batch
-of 2^30 - 1 keys and a segment-sum of 2^31 - 1025 IDs: the oracle cannot run
-these, so each test checks what holds at any size -- the closed-form initial
-rows of sampled keys (oracle), the unique set against torch.unique, the
-identity unique[inverse[i]] == keys[i] for every i, and segment sums whose
-exact values follow from how the inputs were built.  Tens of GB of device
+of 2^30 - 1 keys, a segment-sum of 2^31 - 1025 IDs and a pooled gather of
+2^31 - 1 IDs: the oracle cannot run these, so each test checks what holds at
+any size -- the closed-form initial rows of sampled keys (oracle), the unique
+set against torch.unique, the identity unique[inverse[i]] == keys[i] for
+every i, and segment and bag sums whose exact values follow from how the
+inputs were built.  Tens of GB of device
 memory each; the workspaces are released afterwards.
 """
 import numpy as np
@@ -93,4 +94,36 @@ def test_segment_sum_at_max_n(htl):
         S += np.where(K % 7 > r, (u + r * U) % 7, 0)
     want = S[:, None].astype(np.float64) + np.arange(dim)[None, :] * K[:, None]
     assert np.array_equal(g.astype(np.float64), want)
+    _release(htl)
+
+
+def test_pooling_at_max_n(htl, orc):
+    # 2^31 - 1 IDs in 2^16 bags, the last ending at the top of int32: each
+    # ID i reads the row of key i mod 64 of a bf16 table, so a bag's sum is
+    # a count-weighted sum of 64 rows, exact in fp32 (bag lengths <= 2^16)
+    n, nbags, U, dim = (1 << 31) - 1, 1 << 16, 64, 8
+    table = htl.Table(10, dim, "bf16")
+    keys_np = np.arange(U, dtype=np.int64) * 7919 + 3
+    slots, st = table.find_or_insert(torch.from_numpy(keys_np).cuda())
+    assert (to_np(st) == htl.INSERTED).all()
+    inv = torch.empty(n, dtype=torch.int32, device="cuda")
+    step = 1 << 28
+    for b in range(0, n, step):
+        e = min(n, b + step)
+        inv[b:e] = (torch.arange(b, e, dtype=torch.int64, device="cuda") % U).to(torch.int32)
+    rng = np.random.default_rng(7)
+    offsets_np = np.linspace(0, n, nbags + 1).round().astype(np.int64)   # bags of ~32768 IDs
+    offsets_np[1:-1] += rng.integers(-2000, 2001, nbags - 1)
+    assert offsets_np[-1] == n and np.diff(offsets_np).min() > 0 and np.diff(offsets_np).max() <= 1 << 16
+    offsets = torch.from_numpy(offsets_np.astype(np.int32)).cuda()
+    out = to_np(htl.gather_pool(table, slots, inv, offsets, out_dtype="f32"))
+    del inv
+    # count of i in [a, e) with i mod U == r, for every bag and r
+    r = np.arange(U, dtype=np.int64)[None, :]
+    a, e = offsets_np[:-1, None], offsets_np[1:, None]
+    cnt = (e - 1 - r) // U - (a - 1 - r) // U
+    rows = orc.bf16_bits_to_f32(orc.init_rows(keys_np, dim, orc.BF16)).astype(np.float64)
+    want = cnt.astype(np.float64) @ rows
+    assert np.array_equal(out.astype(np.float64), want)
+    table.close()
     _release(htl)
