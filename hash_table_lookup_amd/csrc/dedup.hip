@@ -27,10 +27,31 @@
 //   compose (k_dedup_compose): inverse[i] = id(set slot of tile survivor
 //     local[i]), one workgroup per tile with the survivors' ids in LDS.
 //
+// Stage 2 has a second form, hash-partitioned, that needs no global atomics
+// (a device-scope CAS costs as much as three or four random loads on this
+// part, whatever the working set):
+//   k_part_count counts the survivors of each row of tiles per hash bin (P
+//     bins, the top bits of a salted mix);
+//   k_col_sums / scan / k_col_apply turn the row x bin counts into the place
+//     of each (row, bin) run in a bin-major survivor array;
+//   k_part_scatter moves every survivor (key, tile position) there; rows are
+//     spread over the XCDs in contiguous runs, so each XCD writes contiguous
+//     pieces of every bin and its L2 merges them into whole lines;
+//   k_part_dedup: one workgroup per bin dedups the bin's survivors in an LDS
+//     set (ids in order of first arrival, by chunk), writes the bin's distinct
+//     keys and, at each survivor's tile position, its id inside the bin; a
+//     bin with more distinct keys than its LDS set holds is redone in a
+//     region of device memory of its own;
+//   k_part_finish: the bins' distinct keys are packed by the prefix of their
+//     counts (unique = bin-major), and the inverse is composed per tile from
+//     (bin offset + id in bin) -- no random reads.
+//
 // Adaptive choice (the TensorFlow article, section 3.6: a heuristic picks the
 // Unique implementation): a batch of at most one tile (2048 keys, e.g. a
 // serving request) is deduplicated by the LDS stage alone in one launch; the
 // device set and its clear, the claim, the scan and the compose are skipped.
+// Larger batches of up to 2^26 keys take the partitioned stage 2 in the
+// unordered mode; the ordered mode, and larger batches, take the set.
 //
 // Both sets probe with an odd step over a power-of-two capacity, so by
 // MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
@@ -249,6 +270,437 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* 
 
 __global__ void k_write_zero(int64_t* p) { *p = 0; }
 
+// ------------------------------------------------ partitioned stage 2 ----
+constexpr int kPartMinLog2 = 8;               // bins: 2^8 .. 2^12
+constexpr int kPartMaxLog2 = 12;
+constexpr int kPartRowsMax = 1024;            // rows of tiles (count-matrix height)
+constexpr int kColChunk = 32;                 // rows per partial column sum
+constexpr int kChunksMax = kPartRowsMax / kColChunk;   // 32
+constexpr int64_t kPartMaxN = (int64_t)1 << 23;   // larger batches: the device set (see run_dedup)
+constexpr int kRowThreads = 1024;             // count and scatter passes
+constexpr int kRowVec = 4;                    // survivor slots per thread in flight
+constexpr int kBinThreads = 512;
+constexpr int kBinVec = 4;                    // survivors per thread per round of a bin
+constexpr int kBinSet = 4096;                 // LDS set slots of one bin
+constexpr int kBinMax = kBinSet * 7 / 10;     // distinct keys a bin may hold in LDS
+
+struct PartWs {
+    int64_t* tu_keys;      // [ntiles * kTile]: per-tile distinct keys
+    int32_t* tu_count;     // [ntiles]
+    int32_t* tu_l;         // [ntiles * kTile]: id of the survivor's key inside its bin
+    uint16_t* local;       // [n]
+    int32_t* cnt;          // [rows << plog2]: counts, then run offsets
+    int32_t* cpre;         // [bins * 32]: per bin, its rows in the chunks before each chunk
+    int32_t* btotal;       // [bins]: survivors per bin
+    int32_t* base;         // [bins + 1]: start of each bin in the bin-major array
+    u32x4* ent;            // [n]: bin-major survivors (key lo, key hi, tile slot, 0)
+    int64_t* ustage;       // [n]: each bin's distinct keys at the bin's start
+    int32_t* ucount;       // [bins]
+    int32_t* uoff;         // [bins + 1]: exclusive prefix of ucount
+    unsigned long long* fb_keys;   // [2n + bins]: sets of bins past the LDS set
+    int32_t* fb_ids;       // [2n + bins]
+    int plog2, rows, tpr, chunks;
+    size_t bytes;
+};
+
+PartWs part_layout(int64_t n, char* base) {
+    PartWs w{};
+    const int64_t ntiles = ceil_div(n, kTile);
+    int plog2 = kPartMinLog2;
+    while (plog2 < kPartMaxLog2 && ((int64_t)1 << plog2) < ntiles) ++plog2;
+    const int64_t P = (int64_t)1 << plog2;
+    w.plog2 = plog2;
+    w.tpr = (int)ceil_div(ntiles, kPartRowsMax);
+    w.rows = (int)ceil_div(ntiles, w.tpr);
+    w.chunks = (int)ceil_div(w.rows, kColChunk);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off = align_up(off + bytes, 256);
+        return p;
+    };
+    w.tu_keys = (int64_t*)take((size_t)ntiles * kTile * 8);
+    w.tu_count = (int32_t*)take((size_t)ntiles * 4);
+    w.tu_l = (int32_t*)take((size_t)ntiles * kTile * 4);
+    w.local = (uint16_t*)take((size_t)n * 2);
+    w.cnt = (int32_t*)take((size_t)w.rows * P * 4);
+    w.cpre = (int32_t*)take((size_t)P * kChunksMax * 4);
+    w.btotal = (int32_t*)take((size_t)P * 4);
+    w.base = (int32_t*)take((size_t)(P + 1) * 4);
+    w.ent = (u32x4*)take((size_t)n * 16);
+    w.ustage = (int64_t*)take((size_t)n * 8);
+    w.ucount = (int32_t*)take((size_t)P * 4);
+    w.uoff = (int32_t*)take((size_t)(P + 1) * 4);
+    w.fb_keys = (unsigned long long*)take((size_t)(2 * n + P) * 8);
+    w.fb_ids = (int32_t*)take((size_t)(2 * n + P) * 4);
+    w.bytes = off;
+    return w;
+}
+
+// Row of the count matrix that block `bid` of a rows-wide grid takes: the
+// rows are dealt to the 8 XCDs (workgroups go round-robin over them) in
+// contiguous runs, so one XCD's concurrent rows write adjacent pieces of
+// each bin.  A bijection of [0, rows) onto itself.
+__device__ __forceinline__ int xcd_row(int bid, int rows) {
+    const int q = rows >> 3, rem = rows & 7;
+    const int x = bid & 7, i = bid >> 3;
+    return x < rem ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+}
+
+// The survivor slots of row r are [t0 * kTile, t1 * kTile) of the tile-major
+// arrays; slot s holds a survivor iff s mod kTile < tu_count[s / kTile].
+// Loads kRowVec slots per thread at once; returns a bit per live slot.
+__device__ __forceinline__ uint32_t load_row_slots(const int64_t* __restrict__ tu_keys,
+                                                   const int32_t* __restrict__ tu_count, int64_t s0, int64_t s1,
+                                                   uint64_t* k, int64_t* slot) {
+    uint32_t live = 0;
+#pragma unroll
+    for (int u = 0; u < kRowVec; ++u) {
+        const int64_t s = s0 + u * kRowThreads + threadIdx.x;
+        slot[u] = s;
+        k[u] = 0;
+        if (s < s1 && (int)(s & (kTile - 1)) < tu_count[s >> kTileLog2]) {
+            k[u] = (uint64_t)tu_keys[s];
+            live |= 1u << u;
+        }
+    }
+    return live;
+}
+
+// cnt[r][b] = survivors of row r's tiles in bin b.
+__global__ __launch_bounds__(kRowThreads) void k_part_count(const int64_t* __restrict__ tu_keys,
+                                                           const int32_t* __restrict__ tu_count, int64_t ntiles,
+                                                           int tpr, int plog2, int32_t* __restrict__ cnt) {
+    extern __shared__ int32_t s_hist[];   // [1 << plog2]
+    const int r = blockIdx.x;
+    for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) s_hist[b] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)r * tpr;
+    const int64_t t1 = t0 + tpr < ntiles ? t0 + tpr : ntiles;
+    for (int64_t s0 = t0 * kTile; s0 < t1 * kTile; s0 += kRowThreads * kRowVec) {
+        uint64_t k[kRowVec];
+        int64_t slot[kRowVec];
+        const uint32_t live = load_row_slots(tu_keys, tu_count, s0, t1 * kTile, k, slot);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u)
+            if (live & (1u << u)) atomicAdd(&s_hist[part_bin(k[u], plog2)], 1);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) cnt[((int64_t)r << plog2) + b] = s_hist[b];
+}
+
+// Column pass 1 over the row-major count matrix.  A workgroup takes 32 bins
+// and every chunk of kColChunk rows (thread = (chunk, bin)); it sums each
+// chunk's rows, then per bin the chunk sums in LDS: cpre[b][c] = rows of bin
+// b in chunks before c, total[b] = all rows of bin b.
+constexpr int kColBins = 1024 / kChunksMax;            // bins per workgroup
+
+__global__ __launch_bounds__(1024) void k_col_sums(const int32_t* __restrict__ cnt, int rows, int plog2,
+                                                  int32_t* __restrict__ cpre, int32_t* __restrict__ total) {
+    __shared__ int32_t s_c[kChunksMax][kColBins];
+    const int bl = threadIdx.x % kColBins;
+    const int c = threadIdx.x / kColBins;
+    const int b = blockIdx.x * kColBins + bl;
+    const int r0 = c * kColChunk;
+    int32_t v[kColChunk];
+#pragma unroll
+    for (int j = 0; j < kColChunk; ++j) v[j] = r0 + j < rows ? cnt[((int64_t)(r0 + j) << plog2) + b] : 0;
+    int32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kColChunk; ++j) sum += v[j];
+    s_c[c][bl] = sum;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int c2 = 0; c2 < kChunksMax; ++c2) {
+        const int32_t x = s_c[c2][bl];
+        before += c2 < c ? x : 0;
+        all += x;
+    }
+    cpre[(int64_t)b * kChunksMax + c] = before;
+    if (c == 0) total[b] = all;
+}
+
+constexpr int kBaseThreads = 1024;
+
+// One workgroup: out[b] = sum of in[b'] for b' < b, out[P] = total (P <= 4096).
+__global__ __launch_bounds__(kBaseThreads) void k_prefix_bins(const int32_t* __restrict__ in, int P,
+                                                             int32_t* __restrict__ out) {
+    __shared__ int s_w[kBaseThreads / 64];
+    int t[4];
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = threadIdx.x * 4 + u;
+        t[u] = b < P ? in[b] : 0;
+        sum += t[u];
+    }
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_w[wid] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBaseThreads / 64; ++w) {
+        before += (w < wid) ? s_w[w] : 0;
+        tot += s_w[w];
+    }
+    int run = before + incl - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = threadIdx.x * 4 + u;
+        if (b < P) out[b] = run;
+        run += t[u];
+    }
+    if (threadIdx.x == 0) out[P] = tot;
+}
+
+// cnt[r][b] <- place of row r's run of bin b in the bin-major array:
+// base[b] + the bin's rows in earlier chunks + the rows before r.
+__global__ __launch_bounds__(256) void k_col_apply(int32_t* __restrict__ cnt, int rows, int plog2, int chunks,
+                                                  const int32_t* __restrict__ cpre,
+                                                  const int32_t* __restrict__ base) {
+    const int64_t total = (int64_t)chunks << plog2;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int c = (int)(i >> plog2);
+        const int b = (int)(i & ((1 << plog2) - 1));
+        const int r0 = c * kColChunk;
+        const int nr = rows - r0 < kColChunk ? rows - r0 : kColChunk;
+        int32_t v[kColChunk];
+#pragma unroll
+        for (int j = 0; j < kColChunk; ++j) v[j] = j < nr ? cnt[((int64_t)(r0 + j) << plog2) + b] : 0;
+        int32_t run = base[b] + cpre[(int64_t)b * kChunksMax + c];
+#pragma unroll
+        for (int j = 0; j < kColChunk; ++j) {
+            if (j < nr) cnt[((int64_t)(r0 + j) << plog2) + b] = run;
+            run += v[j];
+        }
+    }
+}
+
+// Every survivor of a row's tiles goes to its bin's run: (key, tile slot).
+__global__ __launch_bounds__(kRowThreads) void k_part_scatter(const int64_t* __restrict__ tu_keys,
+                                                             const int32_t* __restrict__ tu_count, int64_t ntiles,
+                                                             const int32_t* __restrict__ cnt, int rows, int tpr,
+                                                             int plog2, u32x4* __restrict__ ent) {
+    extern __shared__ int32_t s_cur[];   // [1 << plog2]
+    const int r = xcd_row(blockIdx.x, rows);
+    for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) s_cur[b] = cnt[((int64_t)r << plog2) + b];
+    __syncthreads();
+    const int64_t t0 = (int64_t)r * tpr;
+    const int64_t t1 = t0 + tpr < ntiles ? t0 + tpr : ntiles;
+    for (int64_t s0 = t0 * kTile; s0 < t1 * kTile; s0 += kRowThreads * kRowVec) {
+        uint64_t k[kRowVec];
+        int64_t slot[kRowVec];
+        const uint32_t live = load_row_slots(tu_keys, tu_count, s0, t1 * kTile, k, slot);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u) {
+            if (!(live & (1u << u))) continue;
+            const int pos = atomicAdd(&s_cur[part_bin(k[u], plog2)], 1);
+            u32x4 e;
+            e.x = (uint32_t)k[u];
+            e.y = (uint32_t)(k[u] >> 32);
+            e.z = (uint32_t)slot[u];
+            e.w = 0u;
+            ent[pos] = e;
+        }
+    }
+}
+
+// Block-wide exclusive scan of one small count per thread (kBinThreads
+// threads); returns the block total.  Uses s_wave[kBinThreads / 64].
+__device__ __forceinline__ int bin_block_scan(int v, int* s_wave, int* total) {
+    const int lane = lane_id();
+    const int wid = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBinThreads / 64; ++w) {
+        const int c = s_wave[w];
+        before += (w < wid) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + incl - v;
+}
+
+// One pass of a bin's dedup over its survivors ent[start, start + cnt), in
+// rounds of kBinVec survivors per thread, into a set of `size` slots: LDS
+// (GLOBAL false; size a power of two, odd-step walk) or device memory (GLOBAL
+// true; any size, walk of step 1, every slot on it).  Per round, the
+// survivors whose CAS inserted a key take the next ids (thread order).
+// Writes the bin's distinct keys to ustage[start + id] and each survivor's
+// id to tu_l[its tile slot].  Returns false (the LDS pass only) once the bin
+// has more than `max_keys` distinct keys; the caller then redoes the bin.
+// A key that finds the LDS set full can only do so past that limit.  Key -1,
+// the empty marker, is carried in s_neg.
+template <bool GLOBAL>
+__device__ bool bin_pass(const u32x4* __restrict__ ent, int64_t start, int cnt, unsigned long long* skeys,
+                         int32_t* sids, uint32_t size, int max_keys, int32_t* __restrict__ tu_l,
+                         int64_t* __restrict__ ustage, int* s_wave, int* s_neg, int* nd_out) {
+    const int tid = threadIdx.x;
+    int nd = 0;
+    if (tid == 0) {
+        s_neg[0] = 0;    // key -1 claimed
+        s_neg[1] = -1;   // its id
+    }
+    __syncthreads();
+    for (int r0 = 0; r0 < cnt; r0 += kBinThreads * kBinVec) {
+        uint64_t k[kBinVec];
+        int32_t org[kBinVec];
+        uint32_t q[kBinVec];
+        uint32_t valid = 0, won = 0;
+#pragma unroll
+        for (int u = 0; u < kBinVec; ++u) {
+            const int e = r0 + u * kBinThreads + tid;
+            k[u] = 0;
+            org[u] = 0;
+            q[u] = 0;
+            if (e < cnt) {
+                const u32x4 v = ent[start + e];
+                k[u] = ((uint64_t)v.y << 32) | v.x;
+                org[u] = (int32_t)v.z;
+                valid |= 1u << u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBinVec; ++u) {
+            if (!(valid & (1u << u))) continue;
+            if (k[u] == kFree) {
+                if (atomicCAS(&s_neg[0], 0, 1) == 0) won |= 1u << u;
+                continue;
+            }
+            const uint64_t h = mix64(k[u] ^ kSalt1);
+            uint32_t p, stp;
+            if (GLOBAL) {
+                p = (uint32_t)(h % size);
+                stp = 1;
+            } else {
+                p = (uint32_t)h & (size - 1);
+                stp = ((uint32_t)(h >> 32) | 1u) & (size - 1);
+            }
+            for (uint32_t probe = 0; probe < size; ++probe) {
+                const unsigned long long old = atomicCAS(&skeys[p], kFree, (unsigned long long)k[u]);
+                if (old == kFree) {
+                    won |= 1u << u;
+                    break;
+                }
+                if (old == k[u]) break;
+                p += stp;
+                if (GLOBAL) p = p >= size ? p - size : p;
+                else p &= size - 1;
+            }
+            q[u] = p;
+        }
+        int tot;
+        int id = nd + bin_block_scan(__popc(won), s_wave, &tot);
+        if (!GLOBAL && nd + tot > max_keys) return false;   // tot is the same in every thread
+#pragma unroll
+        for (int u = 0; u < kBinVec; ++u) {
+            if (!(won & (1u << u))) continue;
+            if (k[u] == kFree) s_neg[1] = id;
+            else sids[q[u]] = id;
+            ustage[start + id] = (int64_t)k[u];
+            ++id;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kBinVec; ++u) {
+            if (!(valid & (1u << u))) continue;
+            int32_t v;
+            if (k[u] == kFree) v = s_neg[1];
+            else if (GLOBAL) v = __hip_atomic_load(&sids[q[u]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else v = sids[q[u]];
+            tu_l[org[u]] = v;
+        }
+        nd += tot;
+    }
+    *nd_out = nd;
+    return true;
+}
+
+// One workgroup per bin: the LDS set first; a bin that outgrows it is redone
+// in its own region of fb_keys / fb_ids (2*cnt + 1 slots from 2*start + bin,
+// so the regions of the bins do not overlap).
+__global__ __launch_bounds__(kBinThreads) void k_part_dedup(const u32x4* __restrict__ ent,
+                                                           const int32_t* __restrict__ base, int max_keys, int32_t* __restrict__ tu_l,
+                                                           int64_t* __restrict__ ustage,
+                                                           int32_t* __restrict__ ucount,
+                                                           unsigned long long* __restrict__ fb_keys,
+                                                           int32_t* __restrict__ fb_ids) {
+    __shared__ unsigned long long s_key[kBinSet];
+    __shared__ int32_t s_id[kBinSet];
+    __shared__ int s_wave[kBinThreads / 64];
+    __shared__ int s_neg[2];
+    const int b = blockIdx.x;
+    const int64_t start = base[b];
+    const int cnt = (int)(base[b + 1] - start);
+    for (int i = threadIdx.x; i < kBinSet; i += kBinThreads) s_key[i] = kFree;
+    __syncthreads();
+    int nd = 0;
+    if (!bin_pass<false>(ent, start, cnt, s_key, s_id, kBinSet, max_keys, tu_l, ustage, s_wave, s_neg, &nd)) {
+        const int64_t fb0 = 2 * start + b;
+        const uint32_t size = 2u * (uint32_t)cnt + 1u;
+        for (uint32_t i = threadIdx.x; i < size; i += kBinThreads) fb_keys[fb0 + i] = kFree;
+        __syncthreads();
+        bin_pass<true>(ent, start, cnt, fb_keys + fb0, fb_ids + fb0, size, cnt, tu_l, ustage, s_wave, s_neg,
+                       &nd);
+    }
+    if (threadIdx.x == 0) ucount[b] = nd;
+}
+
+// Blocks [0, bins): pack bin b's distinct keys at uoff[b]; the other blocks:
+// compose the inverse tile by tile, id = uoff[bin] + id inside the bin.
+__global__ __launch_bounds__(kTileThreads) void k_part_finish(
+    const int64_t* __restrict__ ustage, const int32_t* __restrict__ base, int plog2,
+    const int32_t* __restrict__ ucount, const int32_t* __restrict__ uoff, int64_t* __restrict__ unique,
+    int64_t* __restrict__ n_unique, const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count,
+    const int32_t* __restrict__ tu_l, const uint16_t* __restrict__ local, int64_t n,
+    int32_t* __restrict__ inverse) {
+    const int P = 1 << plog2;
+    if ((int)blockIdx.x < P) {
+        const int b = blockIdx.x;
+        const int64_t src = base[b];
+        const int64_t dst = uoff[b];
+        const int c = ucount[b];
+        for (int l = threadIdx.x; l < c; l += kTileThreads) unique[dst + l] = ustage[src + l];
+        if (b == 0 && threadIdx.x == 0) *n_unique = uoff[P];
+        return;
+    }
+    __shared__ int32_t s_gid[kTile];
+    __shared__ int32_t s_uoff[1 << kPartMaxLog2];
+    for (int b = threadIdx.x; b < P; b += kTileThreads) s_uoff[b] = uoff[b];
+    __syncthreads();
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    for (int64_t tile = (int64_t)blockIdx.x - P; tile < ntiles; tile += (int64_t)gridDim.x - P) {
+        const int cnt = tu_count[tile];
+        for (int j = threadIdx.x; j < cnt; j += kTileThreads) {
+            const uint64_t k = (uint64_t)tu_keys[tile * kTile + j];
+            s_gid[j] = s_uoff[part_bin(k, plog2)] + tu_l[tile * kTile + j];
+        }
+        __syncthreads();
+        const int64_t b0 = tile * kTile;
+        for (int q = threadIdx.x; q < kTile; q += kTileThreads) {
+            const int64_t i = b0 + q;
+            if (i < n) inverse[i] = s_gid[local[i]];
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 }  // namespace htl
 
@@ -258,7 +710,57 @@ extern "C" {
 
 size_t dedup_workspace_bytes(int64_t n) {
     if (n < 0) n = 0;
-    return layout(n, nullptr).bytes;
+    size_t b = layout(n, nullptr).bytes;
+    if (n > kTile && n <= kPartMaxN) {
+        const size_t bp = part_layout(n, nullptr).bytes;
+        if (bp > b) b = bp;
+    }
+    return b;
+}
+
+// Stage 2 path: HTL_DEDUP_PATH=set forces the device set for every size;
+// HTL_DEDUP_BIN_MAX lowers the distinct keys a bin may hold in LDS (to test
+// the device-memory redo).
+static bool use_part_path(bool ordered, int64_t n) {
+    if (ordered || n <= kTile || n > kPartMaxN) return false;
+    const char* e = getenv("HTL_DEDUP_PATH");
+    return !(e && std::string(e) == "set");
+}
+static int bin_max_keys() {
+    const char* e = getenv("HTL_DEDUP_BIN_MAX");
+    if (!e) return kBinMax;
+    const int v = atoi(e);
+    return v < 0 ? 0 : (v > kBinMax ? kBinMax : v);
+}
+
+static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
+                           int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    PartWs w = part_layout(n, (char*)ws);
+    HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
+    const int64_t ntiles = ceil_div(n, kTile);
+    const int P = 1 << w.plog2;
+    const size_t bin_lds = (size_t)P * 4;
+    const unsigned gt = grid_for(ntiles, 1, 1 << 16);
+    static_assert((1 << kPartMaxLog2) <= 4 * kBaseThreads, "one-workgroup bin prefix");
+    hipLaunchKernelGGL(k_dedup_tile<false>, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
+                       w.local, (int32_t*)nullptr, (int64_t*)nullptr, SetClear{});
+    hipLaunchKernelGGL(k_part_count, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count, ntiles,
+                       w.tpr, w.plog2, w.cnt);
+    const int64_t cells = (int64_t)w.chunks * P;
+    const unsigned cg = grid_for(cells, 256, 4096);
+    hipLaunchKernelGGL(k_col_sums, dim3(P / kColBins), dim3(1024), 0, stream, w.cnt, w.rows, w.plog2, w.cpre,
+                       w.btotal);
+    hipLaunchKernelGGL(k_prefix_bins, dim3(1), dim3(kBaseThreads), 0, stream, w.btotal, P, w.base);
+    hipLaunchKernelGGL(k_col_apply, dim3(cg), dim3(256), 0, stream, w.cnt, w.rows, w.plog2, w.chunks, w.cpre,
+                       w.base);
+    hipLaunchKernelGGL(k_part_scatter, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count,
+                       ntiles, w.cnt, w.rows, w.tpr, w.plog2, w.ent);
+    hipLaunchKernelGGL(k_part_dedup, dim3(P), dim3(kBinThreads), 0, stream, w.ent, w.base, bin_max_keys(), w.tu_l,
+                       w.ustage, w.ucount, w.fb_keys, w.fb_ids);
+    hipLaunchKernelGGL(k_prefix_bins, dim3(1), dim3(kBaseThreads), 0, stream, w.ucount, P, w.uoff);
+    hipLaunchKernelGGL(k_part_finish, dim3(P + gt), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
+                       w.ucount, w.uoff, unique, n_unique_dev, w.tu_keys, w.tu_count, w.tu_l, w.local, n, inverse);
+    return check_launch(who);
 }
 
 static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, int64_t n, int64_t* unique,
@@ -273,6 +775,7 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     HTL_REQUIRE(keys && unique && inverse && ws, std::string(who) + ": null pointer");
     HTL_REQUIRE(aligned(keys, 8) && aligned(unique, 8) && aligned(inverse, 4) && aligned(ws, 256),
                 std::string(who) + ": misaligned pointer");
+    if (use_part_path(ordered, n)) return run_part(who, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream);
     DedupWs w = layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
     if (n <= kTile) {

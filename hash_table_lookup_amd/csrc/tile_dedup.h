@@ -66,6 +66,12 @@ __device__ __forceinline__ void clear_set(const SetClear& c) {
     if (t0 == 0) c.misc[0] = 0;
 }
 
+// Hash bin of a key in the partitioned stage 2: the top plog2 bits of a
+// salted mix (the LDS sets inside a bin hash with the other salt).
+__device__ __forceinline__ uint32_t part_bin(uint64_t k, int plog2) {
+    return (uint32_t)(mix64(k ^ kSalt2) >> (64 - plog2));
+}
+
 // Stage 1: dedup one tile in LDS.  Tile-local ids follow the order of first
 // occurrence inside the tile (LDS atomicMin of the position, then a block
 // scan over positions), so the result does not depend on scheduling.
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
                                                             int64_t* __restrict__ n_unique, SetClear clr) {
     __shared__ unsigned long long s_key[kLdsCap];
     __shared__ int32_t s_tag[kLdsCap + 1];   // first position of the key, then its tile-local id
-    __shared__ int s_wave[kTileThreads / 64];
+    __shared__ int s_jcnt[kKeysPerThread][kTileThreads / 64];
     const int tid = threadIdx.x;
     if (!FINAL && clr.keys) clear_set(clr);
 
@@ -128,16 +134,29 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
         for (int j = 0; j < kKeysPerThread; ++j)
             if ((valid & (1u << j)) && s_tag[pos[j]] == j * kTileThreads + tid) first |= 1u << j;
         __syncthreads();
-        // ids in position order: positions j*256 + tid run j-major
+        // ids in position order: positions j*256 + tid run j-major.  One
+        // ballot per j; the per-wave counts of every j go through LDS at once.
+        uint64_t bal[kKeysPerThread];
+#pragma unroll
+        for (int j = 0; j < kKeysPerThread; ++j) {
+            bal[j] = __ballot((first >> j) & 1u);
+            if (lane_id() == 0) s_jcnt[j][tid >> 6] = __popcll(bal[j]);
+        }
+        __syncthreads();
         int run = 0;
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
-            const bool f = (first >> j) & 1u;
-            int tot;
-            const int r = block_rank(f, s_wave, &tot);
-            if (f) {
-                s_tag[pos[j]] = run + r;
-                tu_keys[base + run + r] = (int64_t)k[j];
+            int before = 0, tot = 0;
+#pragma unroll
+            for (int w = 0; w < kTileThreads / 64; ++w) {
+                const int c = s_jcnt[j][w];
+                before += (w < (tid >> 6)) ? c : 0;
+                tot += c;
+            }
+            if ((first >> j) & 1u) {
+                const int id = run + before + __popcll(bal[j] & lanemask_lt());
+                s_tag[pos[j]] = id;
+                tu_keys[base + id] = (int64_t)k[j];
             }
             run += tot;
         }

@@ -72,6 +72,34 @@ def test_dedup_special_values(htl, orc, ordered):
     _dedup_check(htl, orc, rng.permutation(150000).astype(np.int64), ordered)   # all distinct
 
 
+def _dedup_cases(rng):
+    i64 = np.iinfo(np.int64)
+    base = np.array([-1, -2, i64.min, i64.max, 0, 1], dtype=np.int64)
+    return [
+        rng.integers(0, 30_000, 100_003).astype(np.int64) * 977 - 5,
+        np.concatenate([rng.choice(base, 9000), rng.integers(-300, 300, 9000)]),
+        rng.permutation(150_000).astype(np.int64),                      # all distinct
+        np.full(70_000, -1, np.int64),                                  # only the out-of-band key
+    ]
+
+
+@pytest.mark.parametrize("bin_max", ["0", "3", "200"])
+def test_dedup_bins_redone_in_device_memory(htl, orc, monkeypatch, bin_max):
+    # Bins whose distinct keys outgrow the LDS set are redone in device
+    # memory; lowering the LDS limit sends some or all bins that way.
+    monkeypatch.setenv("HTL_DEDUP_BIN_MAX", bin_max)
+    for keys in _dedup_cases(np.random.default_rng(int(bin_max))):
+        _dedup_check(htl, orc, keys)
+
+
+def test_dedup_set_path(htl, orc, monkeypatch):
+    # The device-set stage 2 (the ordered mode's, and very large batches')
+    # also serves the unordered mode when asked.
+    monkeypatch.setenv("HTL_DEDUP_PATH", "set")
+    for keys in _dedup_cases(np.random.default_rng(7)):
+        _dedup_check(htl, orc, keys)
+
+
 def test_dedup_tiny_workload(htl, orc):
     w = workloads.tiny()
     _, _, U = _dedup_check(htl, orc, w.keys)
