@@ -32,8 +32,9 @@
 // part, whatever the working set):
 //   k_part_count counts the survivors of each row of tiles per hash bin (P
 //     bins, the top bits of a salted mix);
-//   k_col_sums / scan / k_col_apply turn the row x bin counts into the place
-//     of each (row, bin) run in a bin-major survivor array;
+//   k_col_scan turns the row x bin counts into the place of each (row, bin)
+//     run inside its bin and the bins' totals; the bins' bases in the
+//     bin-major survivor array are the prefix of the totals;
 //   k_part_scatter moves every survivor (key, tile position) there; rows are
 //     spread over the XCDs in contiguous runs, so each XCD writes contiguous
 //     pieces of every bin and its L2 merges them into whole lines;
@@ -290,7 +291,6 @@ struct PartWs {
     int32_t* tu_l;         // [ntiles * kTile]: id of the survivor's key inside its bin
     uint16_t* local;       // [n]
     int32_t* cnt;          // [rows << plog2]: counts, then run offsets
-    int32_t* cpre;         // [bins * 32]: per bin, its rows in the chunks before each chunk
     int32_t* btotal;       // [bins]: survivors per bin
     int32_t* base;         // [bins + 1]: start of each bin in the bin-major array
     u32x4* ent;            // [n]: bin-major survivors (key lo, key hi, tile slot, 0)
@@ -324,7 +324,6 @@ PartWs part_layout(int64_t n, char* base) {
     w.tu_l = (int32_t*)take((size_t)ntiles * kTile * 4);
     w.local = (uint16_t*)take((size_t)n * 2);
     w.cnt = (int32_t*)take((size_t)w.rows * P * 4);
-    w.cpre = (int32_t*)take((size_t)P * kChunksMax * 4);
     w.btotal = (int32_t*)take((size_t)P * 4);
     w.base = (int32_t*)take((size_t)(P + 1) * 4);
     w.ent = (u32x4*)take((size_t)n * 16);
@@ -389,14 +388,16 @@ __global__ __launch_bounds__(kRowThreads) void k_part_count(const int64_t* __res
     for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) cnt[((int64_t)r << plog2) + b] = s_hist[b];
 }
 
-// Column pass 1 over the row-major count matrix.  A workgroup takes 32 bins
-// and every chunk of kColChunk rows (thread = (chunk, bin)); it sums each
-// chunk's rows, then per bin the chunk sums in LDS: cpre[b][c] = rows of bin
-// b in chunks before c, total[b] = all rows of bin b.
+// The column pass over the row-major count matrix.  A workgroup takes 32
+// bins and every chunk of kColChunk rows (thread = (chunk, bin)): it sums
+// each chunk's rows, takes per bin the prefix of the chunk sums in LDS, and
+// rewrites cnt[r][b] in place as the rows of bin b before row r; total[b] =
+// all rows of bin b.  The bins' own bases (prefix of total) are taken by the
+// kernels that need them.
 constexpr int kColBins = 1024 / kChunksMax;            // bins per workgroup
 
-__global__ __launch_bounds__(1024) void k_col_sums(const int32_t* __restrict__ cnt, int rows, int plog2,
-                                                  int32_t* __restrict__ cpre, int32_t* __restrict__ total) {
+__global__ __launch_bounds__(1024) void k_col_scan(int32_t* __restrict__ cnt, int rows, int plog2,
+                                                  int32_t* __restrict__ total) {
     __shared__ int32_t s_c[kChunksMax][kColBins];
     const int bl = threadIdx.x % kColBins;
     const int c = threadIdx.x / kColBins;
@@ -410,15 +411,51 @@ __global__ __launch_bounds__(1024) void k_col_sums(const int32_t* __restrict__ c
     for (int j = 0; j < kColChunk; ++j) sum += v[j];
     s_c[c][bl] = sum;
     __syncthreads();
-    int32_t before = 0, all = 0;
+    int32_t run = 0, all = 0;
 #pragma unroll
     for (int c2 = 0; c2 < kChunksMax; ++c2) {
         const int32_t x = s_c[c2][bl];
-        before += c2 < c ? x : 0;
+        run += c2 < c ? x : 0;
         all += x;
     }
-    cpre[(int64_t)b * kChunksMax + c] = before;
+#pragma unroll
+    for (int j = 0; j < kColChunk; ++j) {
+        if (r0 + j < rows) cnt[((int64_t)(r0 + j) << plog2) + b] = run;
+        run += v[j];
+    }
     if (c == 0) total[b] = all;
+}
+
+// Exclusive prefix of the P <= 4096 bin totals in LDS by one workgroup of
+// kRowThreads threads (4 bins per thread); s_w holds kRowThreads / 64 ints.
+__device__ __forceinline__ void bin_bases(const int32_t* __restrict__ total, int P, int32_t* s_base, int* s_w) {
+    int t[4];
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = threadIdx.x * 4 + u;
+        t[u] = b < P ? total[b] : 0;
+        sum += t[u];
+    }
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_w[wid] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wid; ++w) before += s_w[w];
+    int run = before + incl - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = threadIdx.x * 4 + u;
+        if (b < P) s_base[b] = run;
+        run += t[u];
+    }
+    __syncthreads();
 }
 
 constexpr int kBaseThreads = 1024;
@@ -460,37 +497,18 @@ __global__ __launch_bounds__(kBaseThreads) void k_prefix_bins(const int32_t* __r
     if (threadIdx.x == 0) out[P] = tot;
 }
 
-// cnt[r][b] <- place of row r's run of bin b in the bin-major array:
-// base[b] + the bin's rows in earlier chunks + the rows before r.
-__global__ __launch_bounds__(256) void k_col_apply(int32_t* __restrict__ cnt, int rows, int plog2, int chunks,
-                                                  const int32_t* __restrict__ cpre,
-                                                  const int32_t* __restrict__ base) {
-    const int64_t total = (int64_t)chunks << plog2;
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        const int c = (int)(i >> plog2);
-        const int b = (int)(i & ((1 << plog2) - 1));
-        const int r0 = c * kColChunk;
-        const int nr = rows - r0 < kColChunk ? rows - r0 : kColChunk;
-        int32_t v[kColChunk];
-#pragma unroll
-        for (int j = 0; j < kColChunk; ++j) v[j] = j < nr ? cnt[((int64_t)(r0 + j) << plog2) + b] : 0;
-        int32_t run = base[b] + cpre[(int64_t)b * kChunksMax + c];
-#pragma unroll
-        for (int j = 0; j < kColChunk; ++j) {
-            if (j < nr) cnt[((int64_t)(r0 + j) << plog2) + b] = run;
-            run += v[j];
-        }
-    }
-}
-
 // Every survivor of a row's tiles goes to its bin's run: (key, tile slot).
 __global__ __launch_bounds__(kRowThreads) void k_part_scatter(const int64_t* __restrict__ tu_keys,
                                                              const int32_t* __restrict__ tu_count, int64_t ntiles,
-                                                             const int32_t* __restrict__ cnt, int rows, int tpr,
+                                                             const int32_t* __restrict__ cnt,
+                                                             const int32_t* __restrict__ total, int rows, int tpr,
                                                              int plog2, u32x4* __restrict__ ent) {
     extern __shared__ int32_t s_cur[];   // [1 << plog2]
+    __shared__ int s_w[kRowThreads / 64];
     const int r = xcd_row(blockIdx.x, rows);
-    for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) s_cur[b] = cnt[((int64_t)r << plog2) + b];
+    static_assert((1 << kPartMaxLog2) <= 4 * kRowThreads, "four bins per thread");
+    bin_bases(total, 1 << plog2, s_cur, s_w);
+    for (int b = threadIdx.x; b < (1 << plog2); b += kRowThreads) s_cur[b] += cnt[((int64_t)r << plog2) + b];
     __syncthreads();
     const int64_t t0 = (int64_t)r * tpr;
     const int64_t t1 = t0 + tpr < ntiles ? t0 + tpr : ntiles;
@@ -636,7 +654,9 @@ __device__ bool bin_pass(const u32x4* __restrict__ ent, int64_t start, int cnt, 
 // in its own region of fb_keys / fb_ids (2*cnt + 1 slots from 2*start + bin,
 // so the regions of the bins do not overlap).
 __global__ __launch_bounds__(kBinThreads) void k_part_dedup(const u32x4* __restrict__ ent,
-                                                           const int32_t* __restrict__ base, int max_keys, int32_t* __restrict__ tu_l,
+                                                           const int32_t* __restrict__ total,
+                                                           int32_t* __restrict__ base, int max_keys,
+                                                           int32_t* __restrict__ tu_l,
                                                            int64_t* __restrict__ ustage,
                                                            int32_t* __restrict__ ucount,
                                                            unsigned long long* __restrict__ fb_keys,
@@ -646,10 +666,20 @@ __global__ __launch_bounds__(kBinThreads) void k_part_dedup(const u32x4* __restr
     __shared__ int s_wave[kBinThreads / 64];
     __shared__ int s_neg[2];
     const int b = blockIdx.x;
-    const int64_t start = base[b];
-    const int cnt = (int)(base[b + 1] - start);
+    // the bin's start: survivors of the bins before it
+    constexpr int kPer = (1 << kPartMaxLog2) / kBinThreads;
+    int part = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = threadIdx.x * kPer + u;
+        part += i < b ? total[i] : 0;
+    }
     for (int i = threadIdx.x; i < kBinSet; i += kBinThreads) s_key[i] = kFree;
-    __syncthreads();
+    int start32;
+    bin_block_scan(part, s_wave, &start32);   // its barriers also order the set clear
+    const int64_t start = start32;
+    const int cnt = total[b];
+    if (threadIdx.x == 0) base[b] = start32;
     int nd = 0;
     if (!bin_pass<false>(ent, start, cnt, s_key, s_id, kBinSet, max_keys, tu_l, ustage, s_wave, s_neg, &nd)) {
         const int64_t fb0 = 2 * start + b;
@@ -746,17 +776,11 @@ static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int6
                        w.local, (int32_t*)nullptr, (int64_t*)nullptr, SetClear{});
     hipLaunchKernelGGL(k_part_count, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count, ntiles,
                        w.tpr, w.plog2, w.cnt);
-    const int64_t cells = (int64_t)w.chunks * P;
-    const unsigned cg = grid_for(cells, 256, 4096);
-    hipLaunchKernelGGL(k_col_sums, dim3(P / kColBins), dim3(1024), 0, stream, w.cnt, w.rows, w.plog2, w.cpre,
-                       w.btotal);
-    hipLaunchKernelGGL(k_prefix_bins, dim3(1), dim3(kBaseThreads), 0, stream, w.btotal, P, w.base);
-    hipLaunchKernelGGL(k_col_apply, dim3(cg), dim3(256), 0, stream, w.cnt, w.rows, w.plog2, w.chunks, w.cpre,
-                       w.base);
+    hipLaunchKernelGGL(k_col_scan, dim3(P / kColBins), dim3(1024), 0, stream, w.cnt, w.rows, w.plog2, w.btotal);
     hipLaunchKernelGGL(k_part_scatter, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count,
-                       ntiles, w.cnt, w.rows, w.tpr, w.plog2, w.ent);
-    hipLaunchKernelGGL(k_part_dedup, dim3(P), dim3(kBinThreads), 0, stream, w.ent, w.base, bin_max_keys(), w.tu_l,
-                       w.ustage, w.ucount, w.fb_keys, w.fb_ids);
+                       ntiles, w.cnt, w.btotal, w.rows, w.tpr, w.plog2, w.ent);
+    hipLaunchKernelGGL(k_part_dedup, dim3(P), dim3(kBinThreads), 0, stream, w.ent, w.btotal, w.base, bin_max_keys(),
+                       w.tu_l, w.ustage, w.ucount, w.fb_keys, w.fb_ids);
     hipLaunchKernelGGL(k_prefix_bins, dim3(1), dim3(kBaseThreads), 0, stream, w.ucount, P, w.uoff);
     hipLaunchKernelGGL(k_part_finish, dim3(P + gt), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
                        w.ucount, w.uoff, unique, n_unique_dev, w.tu_keys, w.tu_count, w.tu_l, w.local, n, inverse);
