@@ -44,7 +44,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
-TRAFFIC_SOURCES = [os.path.join(CSRC, "gather.hip")]     # the source of k_gather
+# k_gather's source, and the dedup's: the order of unique ids it produces
+# decides how the gather's slot reads fall on cache lines
+TRAFFIC_SOURCES = [os.path.join(CSRC, f) for f in ("gather.hip", "dedup.hip", "tile_dedup.h")]
 METRIC = "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X"
 
 
@@ -69,7 +71,8 @@ def _parse():
 
 def _measured_traffic():
     """Counter-measured HBM bytes per gather launch, or None if the gather's
-    source changed since the counters were taken (or no record exists)."""
+    or the dedup's source changed since the counters were taken (or no
+    record exists)."""
     import hashlib
     try:
         rec = {}
