@@ -93,10 +93,8 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
 
     for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
         const int64_t base = tile * kTile;
-        for (int i = tid; i < kLdsCap; i += kTileThreads) s_key[i] = kFree;
-        for (int i = tid; i <= kLdsCap; i += kTileThreads) s_tag[i] = kTile;
-        __syncthreads();
-
+        // the tile's keys are requested first, so that they arrive while the
+        // LDS set is being cleared
         uint64_t k[kKeysPerThread];
         int pos[kKeysPerThread];
         uint32_t valid = 0;
@@ -110,6 +108,9 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
                 k[j] = (uint64_t)keys[idx];
             }
         }
+        for (int i = tid; i < kLdsCap; i += kTileThreads) s_key[i] = kFree;
+        for (int i = tid; i <= kLdsCap; i += kTileThreads) s_tag[i] = kTile;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < kKeysPerThread; ++j) {
             if (!(valid & (1u << j))) continue;
