@@ -115,3 +115,22 @@ def test_backward_fused_full_size_matches_two_calls(htl):
         torch.cuda.empty_cache()
     for a, b in zip(*res):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("path", ["bins", "bins_in_device_memory", "set"])
+def test_large_table_batch_dedup_paths(htl, orc, monkeypatch, path):
+    # the large-table batch (2^22 Zipf IDs) through each form of the second
+    # dedup stage: LDS bins (the default), every bin redone in device memory,
+    # and the device-wide set -- the same unique set and a correct inverse
+    if path == "bins_in_device_memory":
+        monkeypatch.setenv("HTL_DEDUP_BIN_MAX", "0")
+    if path == "set":
+        monkeypatch.setenv("HTL_DEDUP_PATH", "set")
+    w = workloads.single_large_table()
+    keys = torch.from_numpy(w.keys).cuda()
+    uniq, inv, nu = htl.dedup_unique_inverse(keys)
+    U = int(nu.item())
+    u = to_np(uniq)[:U]
+    ref = np.unique(w.keys)
+    assert U == ref.size and np.array_equal(np.sort(u), ref)
+    assert np.array_equal(u[to_np(inv)], w.keys)
