@@ -134,3 +134,19 @@ def test_large_table_batch_dedup_paths(htl, orc, monkeypatch, path):
     ref = np.unique(w.keys)
     assert U == ref.size and np.array_equal(np.sort(u), ref)
     assert np.array_equal(u[to_np(inv)], w.keys)
+
+
+@pytest.mark.parametrize("n", [1 << 23, (1 << 23) + 1])
+def test_dedup_at_the_partitioned_limit(htl, n):
+    # 2^23 keys is the largest batch the hash-binned second stage takes
+    # (all distinct: ~2048 distinct keys per bin, the most its LDS sets see
+    # for random keys); one key more goes to the device set
+    rng = np.random.default_rng(n)
+    distinct = rng.choice(1 << 40, size=n, replace=False).astype(np.int64) * 7 + 3
+    for keys in (distinct, distinct[rng.integers(0, n // 3, n)]):
+        uniq, inv, nu = htl.dedup_unique_inverse(torch.from_numpy(keys).cuda())
+        U = int(nu.item())
+        u = to_np(uniq)[:U]
+        ref = np.unique(keys)
+        assert U == ref.size and np.array_equal(np.sort(u), ref)
+        assert np.array_equal(u[to_np(inv)], keys)
