@@ -39,10 +39,11 @@
 //     spread over the XCDs in contiguous runs, so each XCD writes contiguous
 //     pieces of every bin and its L2 merges them into whole lines;
 //   k_part_dedup: one workgroup per bin dedups the bin's survivors in an LDS
-//     set (ids in order of first arrival, by chunk), writes the bin's distinct
-//     keys and, at each survivor's tile position, its id inside the bin; a
-//     bin with more distinct keys than its LDS set holds is redone in a
-//     region of device memory of its own;
+//     set (ids in order of arrival: per round of survivors, the inserting
+//     ones in thread order), writes the bin's distinct keys and, at each
+//     survivor's tile position, its id inside the bin; a bin with more
+//     distinct keys than its LDS set holds is redone in a region of device
+//     memory of its own;
 //   k_part_finish: the bins' distinct keys are packed by the prefix of their
 //     counts (unique = bin-major), and the inverse is composed per tile from
 //     (bin offset + id in bin) -- no random reads.
@@ -51,13 +52,18 @@
 // Unique implementation): a batch of at most one tile (2048 keys, e.g. a
 // serving request) is deduplicated by the LDS stage alone in one launch; the
 // device set and its clear, the claim, the scan and the compose are skipped.
-// Larger batches of up to 2^26 keys take the partitioned stage 2 in the
-// unordered mode; the ordered mode, and larger batches, take the set.
+// Larger batches of up to 2^23 keys take the partitioned stage 2 in the
+// unordered mode; the ordered mode, and larger batches, take the set (above
+// 2^23 keys each row's run per bin shrinks below a cache line and the
+// scatter falls behind).
 //
-// Both sets probe with an odd step over a power-of-two capacity, so by
-// MTGenRec's Theorem 1 a probe walk reaches every slot; with at most n keys in
-// more than 3n/2 slots it always ends at a free slot (load at most 2/3: the
-// set is cleared on every call, so its size is traded against that clear).
+// The LDS sets and the device set probe with an odd step over a power-of-two
+// capacity, so by MTGenRec's Theorem 1 a probe walk reaches every slot; with
+// at most n keys in more than 3n/2 slots the device set's walk always ends
+// at a free slot (load at most 2/3: the set is cleared on every call, so its
+// size is traded against that clear).  A bin redone in device memory walks
+// with step 1 over 2*cnt + 1 slots, so it too reaches every slot and never
+// fills.
 // The set is capped at 2^30 slots (its slot numbers, and the extra entry of
 // key -1 at index 2^30, stay int32); with n < 2^30 a slot is always free.
 // Every int64 is a valid key: the value -1, which both sets use as their
@@ -299,7 +305,7 @@ struct PartWs {
     int32_t* uoff;         // [bins + 1]: exclusive prefix of ucount
     unsigned long long* fb_keys;   // [2n + bins]: sets of bins past the LDS set
     int32_t* fb_ids;       // [2n + bins]
-    int plog2, rows, tpr, chunks;
+    int plog2, rows, tpr;
     size_t bytes;
 };
 
@@ -312,7 +318,6 @@ PartWs part_layout(int64_t n, char* base) {
     w.plog2 = plog2;
     w.tpr = (int)ceil_div(ntiles, kPartRowsMax);
     w.rows = (int)ceil_div(ntiles, w.tpr);
-    w.chunks = (int)ceil_div(w.rows, kColChunk);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char* p = base ? base + off : nullptr;
