@@ -239,12 +239,16 @@ htl_status ht_view(const htl_table* t, htl_view* out);
  * Lookup": IDs are unique before and after the all-to-all.  On one device,
  * stage 1 dedups each tile of keys in on-chip memory (one copy per tile
  * leaves it, as one copy per sender leaves a device before the exchange), and
- * stage 2 dedups the tile survivors device-wide.
+ * stage 2 dedups the tile survivors device-wide: for 2048 < n <= 2^23 by hash
+ * bins, each deduplicated in on-chip memory by one workgroup (no device
+ * atomics), for larger n through one device-wide set.
  *   keys          int64[n]; every 64-bit value is a valid key.
  *   unique        int64[n] out: the U distinct keys.  Order: unspecified
- *                 (it depends on which tile's insert wins a race); a batch
- *                 of at most 2048 keys is deduplicated in one launch and
- *                 comes out in first-occurrence order.
+ *                 (hash-bin order for the binned stage 2, and within a bin
+ *                 the order in which survivors arrive; with the set, the
+ *                 tile order of the survivor whose insert won); a batch of
+ *                 at most 2048 keys is deduplicated in one launch and comes
+ *                 out in first-occurrence order.
  *   inverse       int32[n] out: unique[inverse[i]] == keys[i].
  *   n_unique_dev  int64 out: U.
  *   ws, ws_bytes  workspace of at least dedup_workspace_bytes(n) bytes,
