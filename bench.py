@@ -262,8 +262,11 @@ def run_pooled(args, torch, htl, workloads, dev):
             "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
             "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool (pooled)",
             "timing": "HIP events per step; table keys restored between steps outside the events"}
-    return _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
-                   _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms))
+    res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
+                  _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline_pooled(w, warm)
+    return res
 
 
 # ----------------------------------------------------------------- backward
@@ -327,8 +330,11 @@ def run_backward(args, torch, htl, workloads, dev):
             "grad": "torch.randn on the GPU, seeded generator (1000003)",
             "timing": "HIP events per step; the forward's dedup and find-or-insert run once, untimed; "
                       "Adam's step counter advances"}
-    return _result(args, n / (ms * 1e-3) / 1e6, ms, config, "fp32 gradients and rows", path,
-                   _roofline("emb_grad_segment_sum_adam (fused backward)", fused_bytes, ms))
+    res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "fp32 gradients and rows", path,
+                  _roofline("emb_grad_segment_sum_adam (fused backward)", fused_bytes, ms))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline_backward(w, grad[:1 << 22].cpu().numpy())
+    return res
 
 
 # ------------------------------------------------------------------- online
@@ -418,8 +424,11 @@ def run_online(args, torch, htl, workloads, dev):
                       "(the warm-up steps fill the table); a GPU spin kernel (torch.cuda._sleep) holds the "
                       "stream while the host enqueues each phase, so the events time GPU work, not launch "
                       "overhead; value = forward IDs/s"}
-    return _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
-                   _roofline("k_gather (forward per-ID rows, bf16)", gather_bytes, float(np.mean(gat))))
+    res = _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
+                  _roofline("k_gather (forward per-ID rows, bf16)", gather_bytes, float(np.mean(gat))))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline_online(workloads, spec)
+    return res
 
 
 def _pcie_inclusive(torch, htl, table, w, dev, out, restore, steps=12):
@@ -620,6 +629,86 @@ def _cpu_baseline_lookup(w, sample, reps=6):
             "sample": f"first {m} IDs of the same batch, dedup+find_or_insert+gather, median of {reps} passes "
                       f"({sum(times):.1f} s timed in all); the table is pre-filled untimed and the keys a pass "
                       "inserts are erased untimed before the next", "host_cpus": os.cpu_count()}
+
+
+def _cpu_baseline_pooled(w, warm, samples=16384, reps=3):
+    """The oracle on the bags of the first `samples` samples (sample-major, so
+    a prefix of the batch): dedup + find-or-insert + sum-pooling, `reps`
+    passes on a table warmed (untimed) by the same samples of the earlier
+    batch; the keys a pass inserts are erased untimed before the next."""
+    import oracle
+    nb = min(samples * w.meta["n_tables"], w.nbags)
+    keys = np.ascontiguousarray(w.keys[:w.offsets[nb]])
+    offsets = np.ascontiguousarray(w.offsets[:nb + 1])
+    wb = min(nb, warm.nbags)
+    tab = oracle.Table(1 << w.capacity_log2, w.dim, oracle.BF16)
+    tab.find_or_insert(np.unique(warm.keys[:warm.offsets[wb]]))
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        uniq, _ = oracle.dedup(keys)
+        st = tab.find_or_insert(uniq)
+        tab.gather_pool(keys, offsets, oracle.BF16)
+        times.append(time.perf_counter() - t0)
+        tab.erase(uniq[st == oracle.INSERTED])
+    dt = float(np.median(times))
+    return {"value": round(keys.size / dt / 1e6, 3), "unit": "Mkeys/s", "cores": 1, "kind": "oracle",
+            "sample": f"the {nb} bags of the first {nb // w.meta['n_tables']} samples ({keys.size} IDs), "
+                      f"dedup+find_or_insert+sum-pool, median of {reps} passes ({sum(times):.1f} s timed in all); "
+                      "the table is warmed untimed by the same samples of the earlier batch",
+            "host_cpus": os.cpu_count()}
+
+
+def _cpu_baseline_backward(w, grad_host, reps=6):
+    """The oracle on the first len(grad_host) IDs: segment-sum (fp64) and the
+    row-wise Adam step on the rows hit, `reps` passes; the dedup and the
+    inserts of the keys run untimed, as the forward does on the GPU."""
+    import oracle
+    m = grad_host.shape[0]
+    keys = np.ascontiguousarray(w.keys[:m])
+    uniq, inv = oracle.dedup(keys)
+    tab = oracle.Table(1 << w.capacity_log2, w.dim, oracle.F32, adam=True)
+    tab.find_or_insert(uniq)
+    times = []
+    for t in range(1, reps + 1):
+        t0 = time.perf_counter()
+        s, _ = oracle.segment_sum(grad_host, inv, uniq.size, want_abs=False)
+        tab.adam(uniq, s.astype(np.float32), step=t)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": round(m / dt / 1e6, 3), "unit": "Mkeys/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {m} IDs and their gradient rows ({uniq.size} unique keys), segment-sum (fp64) + "
+                      f"row-wise Adam, median of {reps} passes ({sum(times):.1f} s timed in all)",
+            "host_cpus": os.cpu_count()}
+
+
+def _cpu_baseline_online(workloads, spec, steps=6, m=1 << 22):
+    """The oracle on the first `m` IDs of each of the first `steps` steps of
+    the drifting stream: per step, dedup + find-or-insert + gather (timed as
+    the forward), then the least-recently-used choice and its erase (timed
+    apart); the median over the steps after the first."""
+    import oracle
+    gen = workloads.DynamicOnlineStream(spec, steps)
+    tab = oracle.Table(1 << spec.capacity_log2, spec.dim, oracle.BF16)
+    fwd, lru = [], []
+    for s in range(steps):
+        keys = np.ascontiguousarray(gen.keys(s)[:m])
+        t0 = time.perf_counter()
+        uniq, _ = oracle.dedup(keys)
+        tab.find_or_insert(uniq, step=s)
+        tab.gather(keys)
+        t1 = time.perf_counter()
+        tab.erase(tab.lru_victims(spec.evict_num, spec.evict_den))
+        t2 = time.perf_counter()
+        fwd.append(t1 - t0)
+        lru.append(t2 - t1)
+    dt = float(np.median(fwd[1:]))
+    return {"value": round(m / dt / 1e6, 3), "unit": "Mkeys/s", "cores": 1, "kind": "oracle",
+            "lru_choice_and_erase_ms": round(float(np.median(lru[1:])) * 1e3, 1),
+            "sample": f"first {m} IDs of each of the first {steps} steps: forward (dedup+find_or_insert+gather) "
+                      f"and, timed apart, the LRU choice of 5% of the live keys and their erase; median over "
+                      f"steps 1..{steps - 1} ({sum(fwd) + sum(lru):.1f} s timed in all)",
+            "host_cpus": os.cpu_count()}
 
 
 def main():
