@@ -43,10 +43,17 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gather_single_large_table_traffic.txt")
-# k_gather's source, and the dedup's: the order of unique ids it produces
-# decides how the gather's slot reads fall on cache lines
-TRAFFIC_SOURCES = [os.path.join(CSRC, f) for f in ("gather.hip", "dedup.hip", "tile_dedup.h")]
+# Counter-measured HBM bytes of each workload's roofline kernel, per record
+# under profiles/, with the sources that decide them: the kernel's own, and
+# the dedup's (the order of unique ids it produces decides how the kernel's
+# slot and row reads fall on cache lines).
+_DEDUP_SRC = ("dedup.hip", "tile_dedup.h")
+TRAFFIC_RECORDS = {
+    "single_large_table": ("gather_single_large_table_traffic.txt", ("gather.hip",) + _DEDUP_SRC),
+    "merged_tables": ("pool_merged_tables_traffic.txt", ("pool.hip",) + _DEDUP_SRC),
+    "backward": ("backward_fused_traffic.txt", ("backward.hip", "scan.hip") + _DEDUP_SRC),
+    "dynamic_online": ("gather_dynamic_online_traffic.txt", ("gather.hip",) + _DEDUP_SRC),
+}
 METRIC = "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X"
 
 
@@ -69,20 +76,21 @@ def _parse():
     return ap.parse_args()
 
 
-def _measured_traffic():
-    """Counter-measured HBM bytes per gather launch, or None if the gather's
-    or the dedup's source changed since the counters were taken (or no
-    record exists)."""
+def _measured_traffic(workload):
+    """Counter-measured HBM bytes per launch of the workload's roofline
+    kernel, or None if its sources or the dedup's changed since the counters
+    were taken (or no record exists)."""
     import hashlib
     try:
+        name, sources = TRAFFIC_RECORDS[workload]
         rec = {}
-        for line in open(TRAFFIC_RECORD):
+        for line in open(os.path.join(ROOT, "profiles", name)):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 rec[k.strip()] = v.strip()
         h = hashlib.sha256()
-        for f in TRAFFIC_SOURCES:
-            h.update(open(f, "rb").read())
+        for f in sources:
+            h.update(open(os.path.join(CSRC, f), "rb").read())
         if h.hexdigest() != rec.get("source_sha256"):
             return None
         return int(rec["traffic_bytes_per_launch"])
@@ -208,7 +216,7 @@ def run_lookup(args, torch, htl, workloads, dev):
                       "restored by a D2D copy between steps, outside the events"}
     if w.name == "single_large_table" and not args.no_pcie:
         path["pcie_inclusive"] = _pcie_inclusive(torch, htl, table, w, dev, out, restore)
-    traffic = _measured_traffic() if w.name == "single_large_table" else None
+    traffic = _measured_traffic(w.name) if w.name == "single_large_table" else None
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config,
                   "int64 keys, " + ("fp32" if w.dtype == "f32" else "bf16") + " rows", path,
                   _roofline("k_gather (emb_gather_pool: per-ID rows)", gather_bytes, g_ms, traffic))
@@ -263,7 +271,8 @@ def run_pooled(args, torch, htl, workloads, dev):
             "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool (pooled)",
             "timing": "HIP events per step; table keys restored between steps outside the events"}
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
-                  _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms))
+                  _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms,
+                            _measured_traffic("merged_tables")))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline_pooled(w, warm)
     return res
@@ -331,7 +340,8 @@ def run_backward(args, torch, htl, workloads, dev):
             "timing": "HIP events per step; the forward's dedup and find-or-insert run once, untimed; "
                       "Adam's step counter advances"}
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "fp32 gradients and rows", path,
-                  _roofline("emb_grad_segment_sum_adam (fused backward)", fused_bytes, ms))
+                  _roofline("emb_grad_segment_sum_adam (fused backward)", fused_bytes, ms,
+                            _measured_traffic("backward")))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline_backward(w, grad[:1 << 22].cpu().numpy())
     return res
@@ -425,7 +435,8 @@ def run_online(args, torch, htl, workloads, dev):
                       "stream while the host enqueues each phase, so the events time GPU work, not launch "
                       "overhead; value = forward IDs/s"}
     res = _result(args, spec.n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows", path,
-                  _roofline("k_gather (forward per-ID rows, bf16)", gather_bytes, float(np.mean(gat))))
+                  _roofline("k_gather (forward per-ID rows, bf16)", gather_bytes, float(np.mean(gat)),
+                            None if args.growable else _measured_traffic("dynamic_online")))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline_online(workloads, spec)
     return res
