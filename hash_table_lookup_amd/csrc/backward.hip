@@ -45,6 +45,7 @@ constexpr int kSmallMax = 32;              // longest segment summed by one team
 constexpr int kChunk = 1024;               // rows per workgroup in long segments
 constexpr int kRBlock = 256;
 constexpr int kSpread = 1024;              // S of the spread segment order
+constexpr int kFillUnroll = 4;             // IDs per thread and pass of the fill
 
 // Spread order: q(u) = (u mod S) * C + u / S with C = ceil(U / S), a
 // bijection from [0, U) into [0, S * C); spread_u inverts it on that range.
@@ -137,6 +138,15 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
             s_cnt[i] = 0;
         }
         __syncthreads();
+        // all of the thread's inverse values are loaded before any is hashed
+        // (a load in each guarded branch would wait for the one before it);
+        // past the end the last ID is loaded again and ignored
+        int32_t uv[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int64_t idx = base + j * kCThreads + tid;
+            uv[j] = inverse[idx < n ? idx : n - 1];
+        }
         int pos[PER], rank[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
             pos[j] = -1;
             rank[j] = 0;
             if (idx >= n) continue;
-            const int32_t u = inverse[idx];
+            const int32_t u = uv[j];
             if (u < 0 || u >= U) continue;       // outside [0, U): contributes nowhere
             const uint32_t h = (uint32_t)u * 0x9E3779B1u;
             uint32_t p = h >> (32 - CAP_LOG2);
@@ -158,9 +168,22 @@ __global__ __launch_bounds__(kCThreads) void k_seg_count(const int32_t* __restri
             rank[j] = atomicAdd(&s_cnt[p], 1);
         }
         __syncthreads();
-        for (int i = tid; i < CAP; i += kCThreads) {
-            const int32_t u = s_u[i];
-            if (u >= 0) s_cnt[i] = atomicAdd(&counts[spread_q(u, C)], s_cnt[i]);
+        {
+            // the thread's atomics are all issued before their results are
+            // stored, so they are in flight together
+            constexpr int SLOTS = CAP / kCThreads;
+            int32_t got[SLOTS];
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) {
+                const int i = k * kCThreads + tid;
+                const int32_t u = s_u[i];
+                got[k] = u >= 0 ? atomicAdd(&counts[spread_q(u, C)], s_cnt[i]) : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) {
+                const int i = k * kCThreads + tid;
+                if (s_u[i] >= 0) s_cnt[i] = got[k];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -178,9 +201,27 @@ __global__ void k_seg_fill(const int32_t* __restrict__ inverse, const int32_t* _
     const int64_t U = dev_count(u_max, n_dev);
     const int64_t C = spread_c(U);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int32_t u = inverse[i];
-        if (u >= 0 && u < U) perm[seg_off[spread_q(u, C)] + rel[i]] = (int32_t)i;
+    // kFillUnroll IDs per thread, each level's loads issued together (past
+    // the end the last ID is loaded again and not stored)
+    for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < n; i0 += kFillUnroll * stride) {
+        int32_t u[kFillUnroll], r[kFillUnroll], off[kFillUnroll];
+#pragma unroll
+        for (int k = 0; k < kFillUnroll; ++k) {
+            const int64_t i = i0 + k * stride;
+            const int64_t ic = i < n ? i : n - 1;
+            u[k] = inverse[ic];
+            r[k] = rel[ic];
+        }
+#pragma unroll
+        for (int k = 0; k < kFillUnroll; ++k) {
+            const bool ok = u[k] >= 0 && u[k] < U;
+            off[k] = seg_off[spread_q(ok ? u[k] : 0, C)];
+        }
+#pragma unroll
+        for (int k = 0; k < kFillUnroll; ++k) {
+            const int64_t i = i0 + k * stride;
+            if (i < n && u[k] >= 0 && u[k] < U) perm[off[k] + r[k]] = (int32_t)i;
+        }
     }
 }
 
