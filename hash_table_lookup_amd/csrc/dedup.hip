@@ -586,6 +586,15 @@ __device__ bool bin_pass(const u32x4* __restrict__ ent, int64_t start, int cnt, 
         int32_t org[kBinVec];
         uint32_t q[kBinVec];
         uint32_t valid = 0, won = 0;
+        // the round's entries are loaded without a branch each (past the
+        // bin's end its last entry is loaded again and ignored), so the
+        // loads are in flight together
+        u32x4 v[kBinVec];
+#pragma unroll
+        for (int u = 0; u < kBinVec; ++u) {
+            const int e = r0 + u * kBinThreads + tid;
+            v[u] = ent[start + (e < cnt ? e : cnt - 1)];
+        }
 #pragma unroll
         for (int u = 0; u < kBinVec; ++u) {
             const int e = r0 + u * kBinThreads + tid;
@@ -593,9 +602,8 @@ __device__ bool bin_pass(const u32x4* __restrict__ ent, int64_t start, int cnt, 
             org[u] = 0;
             q[u] = 0;
             if (e < cnt) {
-                const u32x4 v = ent[start + e];
-                k[u] = ((uint64_t)v.y << 32) | v.x;
-                org[u] = (int32_t)v.z;
+                k[u] = ((uint64_t)v[u].y << 32) | v[u].x;
+                org[u] = (int32_t)v[u].z;
                 valid |= 1u << u;
             }
         }
@@ -721,16 +729,40 @@ __global__ __launch_bounds__(kTileThreads) void k_part_finish(
     __syncthreads();
     const int64_t ntiles = (n + kTile - 1) / kTile;
     for (int64_t tile = (int64_t)blockIdx.x - P; tile < ntiles; tile += (int64_t)gridDim.x - P) {
+        // loads without a branch per element (past the end the last
+        // element is loaded again and dropped), so each pass's loads are in
+        // flight together
+        constexpr int kV = 4;
         const int cnt = tu_count[tile];
-        for (int j = threadIdx.x; j < cnt; j += kTileThreads) {
-            const uint64_t k = (uint64_t)tu_keys[tile * kTile + j];
-            s_gid[j] = s_uoff[part_bin(k, plog2)] + tu_l[tile * kTile + j];
+        for (int j0 = threadIdx.x; j0 < cnt; j0 += kV * kTileThreads) {
+            uint64_t k[kV];
+            int32_t l[kV];
+#pragma unroll
+            for (int u = 0; u < kV; ++u) {
+                const int j = j0 + u * kTileThreads;
+                const int64_t at = tile * kTile + (j < cnt ? j : cnt - 1);
+                k[u] = (uint64_t)tu_keys[at];
+                l[u] = tu_l[at];
+            }
+#pragma unroll
+            for (int u = 0; u < kV; ++u) {
+                const int j = j0 + u * kTileThreads;
+                if (j < cnt) s_gid[j] = s_uoff[part_bin(k[u], plog2)] + l[u];
+            }
         }
         __syncthreads();
         const int64_t b0 = tile * kTile;
-        for (int q = threadIdx.x; q < kTile; q += kTileThreads) {
-            const int64_t i = b0 + q;
-            if (i < n) inverse[i] = s_gid[local[i]];
+        constexpr int kPerT = kTile / kTileThreads;
+        uint16_t lo[kPerT];
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) {
+            const int64_t i = b0 + u * kTileThreads + threadIdx.x;
+            lo[u] = local[i < n ? i : n - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) {
+            const int64_t i = b0 + u * kTileThreads + threadIdx.x;
+            if (i < n) inverse[i] = s_gid[lo[u]];
         }
         __syncthreads();
     }
