@@ -47,3 +47,19 @@ def test_online_leg():
     res = bench._cpu_baseline_online(workloads, spec, steps=3, m=1 << 9)
     _check(res)
     assert res["lru_choice_and_erase_ms"] >= 0
+
+
+def test_traffic_records_follow_their_sources(tmp_path, monkeypatch):
+    """Each workload's counter record is reported while the sources it names
+    hash to the recorded value, and not once any of them changes."""
+    import shutil
+    for name, (_, sources) in bench.TRAFFIC_RECORDS.items():
+        assert isinstance(bench._measured_traffic(name), int), name
+        for changed in sources:
+            for f in sources:
+                shutil.copy(os.path.join(bench.CSRC, f), tmp_path / f)
+            with open(tmp_path / changed, "a") as fh:
+                fh.write("\n")
+            monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+            assert bench._measured_traffic(name) is None, (name, changed)
+            monkeypatch.undo()
