@@ -50,16 +50,28 @@ def test_online_leg():
 
 
 def test_traffic_records_follow_their_sources(tmp_path, monkeypatch):
-    """Each workload's counter record is reported while the sources it names
-    hash to the recorded value, and not once any of them changes."""
+    """A workload's counter record is reported while the sources it names
+    hash to the recorded value, and not once any of them changes (checked on
+    a temporary record over copies of the sources)."""
+    import hashlib
     import shutil
-    for name, (_, sources) in bench.TRAFFIC_RECORDS.items():
-        assert isinstance(bench._measured_traffic(name), int), name
-        for changed in sources:
-            for f in sources:
-                shutil.copy(os.path.join(bench.CSRC, f), tmp_path / f)
-            with open(tmp_path / changed, "a") as fh:
-                fh.write("\n")
-            monkeypatch.setattr(bench, "CSRC", str(tmp_path))
-            assert bench._measured_traffic(name) is None, (name, changed)
-            monkeypatch.undo()
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "csrc"
+    src.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for name, (record, sources) in bench.TRAFFIC_RECORDS.items():
+        for f in sources:
+            shutil.copy(os.path.join(bench.CSRC, f), src / f)
+        h = hashlib.sha256()
+        for f in sources:
+            h.update((src / f).read_bytes())
+        (tmp_path / "profiles" / record).write_text(
+            f"# test record\nsource_sha256 = {h.hexdigest()}\ntraffic_bytes_per_launch = 12345\n")
+        with monkeypatch.context() as m:
+            m.setattr(bench, "CSRC", str(src))
+            assert bench._measured_traffic(name) == 12345, name
+            for changed in sources:
+                keep = (src / changed).read_bytes()
+                (src / changed).write_bytes(keep + b"\n")
+                assert bench._measured_traffic(name) is None, (name, changed)
+                (src / changed).write_bytes(keep)
