@@ -127,6 +127,16 @@ def _result(args, value, ms, config, dtype, path, roofline, unit="Mkeys/s"):
             "config": config, "path": path, "roofline": roofline}
 
 
+def _lookup_bufs(torch, n, dev):
+    """Output buffers of emb_lookup_slots, allocated once outside the timed steps."""
+    return {"unique": torch.empty(n, dtype=torch.int64, device=dev),
+            "inverse": torch.empty(n, dtype=torch.int32, device=dev),
+            "n_unique": torch.empty(1, dtype=torch.int64, device=dev),
+            "slots": torch.empty(n, dtype=torch.int32, device=dev),
+            "status": torch.empty(n, dtype=torch.uint8, device=dev),
+            "id_slots": torch.empty(n, dtype=torch.int32, device=dev)}
+
+
 def _lookup_bytes(n, U, hits, misses, row):
     """Minimum HBM bytes of the forward path and of its gather kernel.
 
@@ -134,11 +144,11 @@ def _lookup_bytes(n, U, hits, misses, row):
     row (output); per unique key 8 (unique write) + 8 (unique read) + 4 + 4
     (slot write/read) + 1 (status) + 8 (table key probe); per hit one row
     read; per miss one key claim (8) and one initial-row write.
-    Gather kernel (k_gather): per ID 4 (inverse) + row (output); per unique
-    4 (slot) + row (read).
+    Gather kernel (k_gather over the per-ID slots): per ID 4 (its slot) + row
+    (output); per unique key one row read.
     """
     path = n * (8 + 4 + 4 + row) + U * (8 + 8 + 4 + 4 + 1 + 8) + hits * row + misses * (8 + row)
-    gather = n * (4 + row) + U * (4 + row)
+    gather = n * (4 + row) + U * row
     return path, gather
 
 
@@ -180,12 +190,25 @@ def run_lookup(args, torch, htl, workloads, dev):
     saved_keys = htl.table_keys(table).clone()
     view = table.view()
     stream = torch.cuda.current_stream()
-    out = torch.empty((n, w.dim), dtype=table.row_dtype, device=dev)   # the timed region allocates nothing
+    # the outputs of the timed step are allocated once, here (the three-call
+    # reference takes its unique, inverse, slots and status from torch's
+    # caching allocator every step: no device allocation once it holds them)
+    out = torch.empty((n, w.dim), dtype=table.row_dtype, device=dev)
+    bufs = _lookup_bufs(torch, n, dev)
 
     def restore():
         htl._binding.copy_to_device_ptr(view.keys, saved_keys)
 
     def step(mark):
+        # emb_lookup_slots (dedup, find-or-insert, each ID's slot), then the
+        # gather over the per-ID slots -- the two halves of emb_lookup
+        uniq, inv, nu, slots, status, ids = htl.lookup_slots(table, keys, bufs=bufs)
+        if mark is not None:
+            mark.record(stream)
+        htl.gather(table, ids, None, out=out)
+        return uniq, inv, nu, slots, status
+
+    def three_calls(mark):
         uniq, inv, nu = htl.dedup_unique_inverse(keys)
         slots, status = table.find_or_insert(uniq, n_dev=nu)
         if mark is not None:
@@ -193,6 +216,7 @@ def run_lookup(args, torch, htl, workloads, dev):
         htl.gather(table, slots, inv, out=out)
         return uniq, inv, nu, slots, status
 
+    T3, _, _ = _timed(torch, args, three_calls, restore)
     T, wall, (uniq, inv, nu, slots, status) = _timed(torch, args, step, restore)
     ms = float(T.step_ms().mean())
     g_ms = float(T.kernel_ms().mean())
@@ -200,6 +224,7 @@ def run_lookup(args, torch, htl, workloads, dev):
     hits, misses = _statuses(htl, status, U)
     row = w.dim * (4 if w.dtype == "f32" else 2)
     path_bytes, gather_bytes = _lookup_bytes(n, U, hits, misses, row)
+    ms3, g3 = float(T3.step_ms().mean()), float(T3.kernel_ms().mean())
     found = (status[:U] == htl.FOUND)[inv.long()].float().mean().item()
     config = {"workload": w.name, "ids_per_step": n, "zipf_a": w.meta.get("zipf_a"),
               "key_universe_log2": w.meta.get("universe_log2"), "table_slots_log2": w.capacity_log2,
@@ -211,8 +236,13 @@ def run_lookup(args, torch, htl, workloads, dev):
             "frac_of_hbm_peak": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "ms_median": round(float(np.median(T.step_ms())), 4),
             "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
-            "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool",
-            "timing": "HIP events around dedup+find_or_insert+gather per step on the launch stream; table keys "
+            "implementation": "emb_lookup_slots (dedup_unique_inverse + ht_find_or_insert, each ID's slot "
+                              "composed per tile after the insert) + emb_gather_pool over the per-ID slots",
+            "three_calls": {"ms_per_step": round(ms3, 4), "gather_ms": round(g3, 4),
+                            "mkeys_s": round(n / (ms3 * 1e-3) / 1e6, 1),
+                            "implementation": "dedup_unique_inverse + ht_find_or_insert + "
+                                              "emb_gather_pool(slots, inverse)"},
+            "timing": "HIP events around the whole step on the launch stream; table keys "
                       "restored by a D2D copy between steps, outside the events"}
     if w.name == "single_large_table" and not args.no_pcie:
         path["pcie_inclusive"] = _pcie_inclusive(torch, htl, table, w, dev, out, restore)
@@ -244,7 +274,17 @@ def run_pooled(args, torch, htl, workloads, dev):
     def restore():
         htl._binding.copy_to_device_ptr(view.keys, saved_keys)
 
+    bufs = _lookup_bufs(torch, n, dev)
+
     def step(mark):
+        # emb_lookup_slots, then bag sums over the per-ID slots
+        uniq, inv, nu, slots, status, ids = htl.lookup_slots(table, keys, bufs=bufs)
+        if mark is not None:
+            mark.record(stream)
+        htl.gather_pool(table, ids, None, offsets, out_dtype="bf16", out=out)
+        return uniq, inv, nu, slots, status
+
+    def three_calls(mark):
         uniq, inv, nu = htl.dedup_unique_inverse(keys)
         slots, status = table.find_or_insert(uniq, n_dev=nu)
         if mark is not None:
@@ -252,15 +292,18 @@ def run_pooled(args, torch, htl, workloads, dev):
         htl.gather_pool(table, slots, inv, offsets, out_dtype="bf16", out=out)
         return uniq, inv, nu, slots, status
 
+    T3, _, _ = _timed(torch, args, three_calls, restore)
     T, wall, (uniq, inv, nu, slots, status) = _timed(torch, args, step, restore)
     ms, p_ms = float(T.step_ms().mean()), float(T.kernel_ms().mean())
+    ms3, p3 = float(T3.step_ms().mean()), float(T3.kernel_ms().mean())
     U = int(nu.item())
     hits, misses = _statuses(htl, status, U)
     row = w.dim * 2
     # per ID: key 8 + inverse 4 + 4; per bag: offsets 4 + pooled row; per unique: 33 + a row read
     # (hits) or a key claim and a row write (misses)
     path_bytes = n * 16 + nb * (4 + row) + U * 33 + hits * row + misses * (8 + row)
-    pool_bytes = n * 4 + nb * (4 + row) + U * (4 + row)
+    # pooling over the per-ID slots: per ID its slot, per bag offsets and the pooled row, each unique row once
+    pool_bytes = n * 4 + nb * (4 + row) + U * row
     config = {"workload": w.name, "ids_per_step": n, "bags": nb, "tables": w.meta["n_tables"],
               "zipf_a": w.meta["zipf_a"], "mean_bag": w.meta["mean_bag"], "table_slots_log2": w.capacity_log2,
               "dim": w.dim, "row_dtype": "bf16", "pooled_dtype": "bf16", "parallelism": "single GPU"}
@@ -268,7 +311,12 @@ def run_pooled(args, torch, htl, workloads, dev):
             "achieved_gbs": round(path_bytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "wall_ms_per_step_incl_restore": round(wall / args.steps * 1e3, 4),
-            "implementation": "dedup_unique_inverse + ht_find_or_insert + emb_gather_pool (pooled)",
+            "implementation": "emb_lookup_slots (dedup + find-or-insert + each ID's slot) + emb_gather_pool "
+                              "(bags over the per-ID slots)",
+            "three_calls": {"ms_per_step": round(ms3, 4), "pool_ms": round(p3, 4),
+                            "mkeys_s": round(n / (ms3 * 1e-3) / 1e6, 1),
+                            "implementation": "dedup_unique_inverse + ht_find_or_insert + "
+                                              "emb_gather_pool(slots, inverse, offsets)"},
             "timing": "HIP events per step; table keys restored between steps outside the events"}
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
                   _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms,
@@ -354,6 +402,7 @@ def run_online(args, torch, htl, workloads, dev):
     table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=args.growable)
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.n, spec.dim), dtype=torch.bfloat16, device=dev)
+    bufs = _lookup_bufs(torch, spec.n, dev)
     fwd, lru, ers, gat = [], [], [], []
     U_last = 0
     gen = workloads.DynamicOnlineStream(spec, steps)
@@ -364,10 +413,9 @@ def run_online(args, torch, htl, workloads, dev):
         torch.cuda.synchronize()
         hold(4.0)                       # the host enqueues forward + LRU behind it
         e[0].record(stream)
-        uniq, inv, nu = htl.dedup_unique_inverse(keys)
-        slots, status = table.find_or_insert(uniq, n_dev=nu, step=s)
+        uniq, inv, nu, slots, status, ids = htl.lookup_slots(table, keys, step=s, bufs=bufs)
         e[5].record(stream)
-        htl.gather(table, slots, inv, out=out)
+        htl.gather(table, ids, None, out=out)
         e[1].record(stream)
         victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
         e[2].record(stream)
@@ -408,7 +456,7 @@ def run_online(args, torch, htl, workloads, dev):
                   "what": "map row space for 2^28 handles, new index, rehash of the live keys with their handles, "
                           "free of the old index (the call synchronises the stream)"}
     fwd_bytes = spec.n * (16 + row) + U_last * (33 + row)
-    gather_bytes = spec.n * (4 + row) + U_last * (4 + row)
+    gather_bytes = spec.n * (4 + row) + U_last * row
     live_now = int(table.scan()[3].item())
     # the selection reads last_seen of every slot (dead slots are marked
     # there) and writes then reads back each live slot's (last_seen, slot)
@@ -429,7 +477,8 @@ def run_online(args, torch, htl, workloads, dev):
             "table": "growable (row handles, mapped row space)" if args.growable else "fixed",
             "resize": resize,
             "checkpoint": ckpt,
-            "implementation": "dedup + find_or_insert(step) + gather, then ht_lru_select + ht_erase",
+            "implementation": "emb_lookup_slots(step) + gather over the per-ID slots, then ht_lru_select + "
+                              "ht_erase",
             "timing": f"per-step HIP events over steps {args.warmup}..{steps - 1} of the drifting stream "
                       "(the warm-up steps fill the table); a GPU spin kernel (torch.cuda._sleep) holds the "
                       "stream while the host enqueues each phase, so the events time GPU work, not launch "
@@ -453,10 +502,11 @@ def _pcie_inclusive(torch, htl, table, w, dev, out, restore, steps=12):
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
 
+    lbufs = _lookup_bufs(torch, n, dev)
+
     def lookup(k):
-        uniq, inv, nu = htl.dedup_unique_inverse(k)
-        slots, _ = table.find_or_insert(uniq, n_dev=nu)
-        htl.gather(table, slots, inv, out=out)
+        _, _, _, _, _, ids = htl.lookup_slots(table, k, bufs=lbufs)
+        htl.gather(table, ids, None, out=out)
 
     # the H2D rate alone
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

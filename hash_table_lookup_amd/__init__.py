@@ -20,23 +20,30 @@ from ._binding import (  # noqa: F401
     ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, GROWABLE, HTLError, INSERTED, LIB_PATH,
     copy_probe,
     META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
-    gather_pool, lib, release_workspaces, rowwise_adam, segment_sum, segment_sum_adam, table_keys, table_tensor,
+    gather_pool, lib, lookup_fused, lookup_slots, release_workspaces, rowwise_adam, segment_sum, segment_sum_adam, table_keys,
+    table_tensor,
 )
 
 __all__ = [
     "Table", "dedup_unique_inverse", "gather", "gather_pool", "segment_sum", "rowwise_adam",
-    "segment_sum_adam", "lookup", "lib", "release_workspaces", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
+    "segment_sum_adam", "lookup", "lookup_fused", "lookup_slots", "lib", "release_workspaces", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
 ]
 
 
 def lookup(table: Table, keys: torch.Tensor, step: int = 0,
-           offsets: Optional[torch.Tensor] = None, out_dtype=None):
+           offsets: Optional[torch.Tensor] = None, out_dtype=None, fused: bool = True):
     """The forward hot path on one batch of feature IDs.
 
     dedup_unique_inverse -> ht_find_or_insert (absent keys inserted) ->
     emb_gather_pool.  Returns (out, unique, inverse, n_unique, slots, status);
     out is per-ID rows, or per-bag sums when CSR ``offsets`` are given.
+    fused=True makes the one emb_lookup call, False the three calls.
     """
+    if fused:
+        od = out_dtype
+        if offsets is not None and od is None:
+            od = table.dtype
+        return lookup_fused(table, keys, step, offsets, od)
     unique, inverse, n_unique = dedup_unique_inverse(keys)
     slots, status = table.find_or_insert(unique, n_dev=n_unique, step=step)
     if offsets is None:

@@ -61,11 +61,15 @@ _SIGNATURES = {
     "ht_import": [_P, _P, _I64, _P, _P, _P, _P, _P, _P],
     "lru_workspace_bytes": [_P],
     "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
+    "ht_rows": [_P, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
     "ht_view": [_P, ctypes.POINTER(_View)],
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
+    "emb_lookup_slots": [_P, _P, _I64, _U32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "emb_lookup_workspace_bytes": [_I64],
+    "emb_lookup": [_P, _P, _I64, _U32, _P, _P, _P, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P],
     "segsum_workspace_bytes": [_I64, _I64, _I32],
     "emb_grad_segment_sum": [_P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P],
     "emb_rowwise_adam": [_P, _P, _P, _I64, _P, _F, _F, _F, _F, _I64, _P],
@@ -75,7 +79,7 @@ _SIGNATURES = {
     "htl_last_error": [],
 }
 _SIZE_FUNCS = {"lru_workspace_bytes", "dedup_workspace_bytes", "segsum_workspace_bytes",
-               "segsum_adam_workspace_bytes"}
+               "segsum_adam_workspace_bytes", "emb_lookup_workspace_bytes"}
 EXPORTED = tuple(_SIGNATURES)
 
 _lib = None
@@ -128,8 +132,14 @@ _ws_cache = {}
 
 
 def _workspace(tag: str, nbytes: int, device) -> torch.Tensor:
-    """A cached uint8 device buffer of at least nbytes (256-byte aligned by torch)."""
-    key = (tag, str(device))
+    """A cached uint8 device buffer of at least nbytes (256-byte aligned by torch).
+
+    One buffer per (path, device, stream): calls enqueued on one stream run in
+    order, so they may share it; calls on two streams get two buffers and do
+    not race.  A buffer that has to grow is replaced on the stream that uses
+    it -- torch's allocator hands freed memory out again only in that
+    stream's order -- so no work still queued reads a freed buffer."""
+    key = (tag, str(device), _stream())
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -330,6 +340,13 @@ class Table:
                                    _stream()))
         return victims, n
 
+    def rows_view(self):
+        """(device address of the rows, bytes per row): the read-only row view
+        of ht_rows (rows indexed by slot, or by row handle when growable)."""
+        p, rb = _P(), _I64()
+        _check(lib().ht_rows(self._h, ctypes.byref(p), ctypes.byref(rb)))
+        return p.value, rb.value
+
     def view(self) -> _View:
         v = _View()
         _check(lib().ht_view(self._h, ctypes.byref(v)))
@@ -350,6 +367,71 @@ def dedup_unique_inverse(keys: torch.Tensor, ordered: bool = False):
     fn = lib().dedup_unique_inverse_ordered if ordered else lib().dedup_unique_inverse
     _check(fn(_ptr(keys), n, _ptr(unique), _ptr(inverse), _ptr(n_unique), _ptr(ws), nb, _stream()))
     return unique, inverse, n_unique
+
+
+def lookup_fused(table: Table, keys: torch.Tensor, step: int = 0, offsets: Optional[torch.Tensor] = None,
+                 out_dtype=None, out: Optional[torch.Tensor] = None, bufs: Optional[dict] = None):
+    """The forward path in one call (emb_lookup): dedup -> find-or-insert ->
+    gather, or bag sums with CSR ``offsets``.  Returns (out, unique, inverse,
+    n_unique, slots, status) as the three calls do.  ``bufs`` may hold
+    preallocated unique / inverse / n_unique / slots / status tensors."""
+    keys = _dev(keys, torch.int64, "keys")
+    n = keys.numel()
+    d = keys.device
+    b = bufs or {}
+    unique = b.get("unique")
+    unique = unique if unique is not None else torch.empty(max(n, 1), dtype=torch.int64, device=d)
+    inverse = b.get("inverse")
+    inverse = inverse if inverse is not None else torch.empty(n, dtype=torch.int32, device=d)
+    n_unique = b.get("n_unique")
+    n_unique = n_unique if n_unique is not None else torch.empty(1, dtype=torch.int64, device=d)
+    slots = b.get("slots")
+    slots = slots if slots is not None else torch.empty(max(n, 1), dtype=torch.int32, device=d)
+    status = b.get("status")
+    status = status if status is not None else torch.empty(max(n, 1), dtype=torch.uint8, device=d)
+    if offsets is None:
+        od = table.dtype if out_dtype is None else _dtype_code(out_dtype)
+        nb = 0
+        shape = (n, table.dim)
+    else:
+        offsets = _dev(offsets, torch.int32, "offsets")
+        od = table.dtype if out_dtype is None else _dtype_code(out_dtype)
+        nb = offsets.numel() - 1
+        shape = (nb, table.dim)
+    if out is None:
+        out = torch.empty(shape, dtype=_TORCH_DTYPE[od], device=d)
+    nbytes = lib().emb_lookup_workspace_bytes(n)
+    ws = _workspace("lookup", nbytes, d)
+    _check(lib().emb_lookup(table.handle, _ptr(keys), n, step, _ptr(unique), _ptr(inverse), _ptr(n_unique),
+                            _ptr(slots), _ptr(status), _ptr(offsets), nb, od, _ptr(out), _ptr(ws), nbytes,
+                            _stream()))
+    return out, unique, inverse, n_unique, slots, status
+
+
+def lookup_slots(table: Table, keys: torch.Tensor, step: int = 0, bufs: Optional[dict] = None):
+    """dedup -> find-or-insert, and each ID's slot (emb_lookup_slots).
+    Returns (unique, inverse, n_unique, slots, status, id_slots); a gather of
+    id_slots with no inverse gives the batch's rows."""
+    keys = _dev(keys, torch.int64, "keys")
+    n = keys.numel()
+    d = keys.device
+    b = bufs or {}
+
+    def buf(name, size, dtype):
+        t = b.get(name)
+        return t if t is not None else torch.empty(size, dtype=dtype, device=d)
+
+    unique = buf("unique", max(n, 1), torch.int64)
+    inverse = buf("inverse", n, torch.int32)
+    n_unique = buf("n_unique", 1, torch.int64)
+    slots = buf("slots", max(n, 1), torch.int32)
+    status = buf("status", max(n, 1), torch.uint8)
+    id_slots = buf("id_slots", max(n, 1), torch.int32)
+    nbytes = lib().dedup_workspace_bytes(n)
+    ws = _workspace("dedup", nbytes, d)
+    _check(lib().emb_lookup_slots(table.handle, _ptr(keys), n, step, _ptr(unique), _ptr(inverse), _ptr(n_unique),
+                                  _ptr(slots), _ptr(status), _ptr(id_slots), _ptr(ws), nbytes, _stream()))
+    return unique, inverse, n_unique, slots, status, id_slots
 
 
 def gather(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor] = None,

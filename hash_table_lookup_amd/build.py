@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libhtl.so")
 ARCH = os.environ.get("HTL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["table.hip", "dedup.hip", "gather.hip", "pool.hip", "scan.hip", "backward.hip", "lru.hip", "copy.hip"]
+SOURCES = ["table.hip", "dedup.hip", "lookup.hip", "gather.hip", "pool.hip", "scan.hip", "backward.hip", "lru.hip",
+           "copy.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

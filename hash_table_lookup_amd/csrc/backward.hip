@@ -297,19 +297,20 @@ __device__ __forceinline__ void emit4(u32x4* __restrict__ out, int vpr, int64_t 
 
 // Sums rows perm[beg..end) of `grad` into acc, TEAM lanes per row: team
 // `team` of `teams` takes rows beg + team, beg + team + teams, ...
+// Positions are 64-bit: with 32-bit ones, i0 + u * teams and the loop step
+// i0 + teams * U reach end - 1 + teams * U, which passes 2^31 - 1 whenever
+// end is within teams * U of it (end may be n, up to 2^31 - 1025); in 64
+// bits that sum stays below 2^32.
 template <int TEAM, int QMAX>
 __device__ __forceinline__ void sum_rows(const u32x4* __restrict__ grad, int vpr, const int32_t* __restrict__ perm,
-                                         int32_t beg, int32_t end, int team, int teams, int tl,
+                                         int64_t beg, int64_t end, int team, int teams, int tl,
                                          float (&acc)[QMAX][4]) {
     constexpr int U = 4;
-    // i0 + teams * U must not pass INT32_MAX: n < 2^31 - 1024 leaves room
-    // for teams * U <= 1024 (teams <= kRBlock)
-    static_assert(kRBlock * U <= 1024, "int32 row index could overflow near n = 2^31");
-    for (int32_t i0 = beg + team; i0 < end; i0 += teams * U) {
+    for (int64_t i0 = beg + team; i0 < end; i0 += (int64_t)teams * U) {
         int32_t r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t i = i0 + u * teams;
+            const int64_t i = i0 + (int64_t)u * teams;
             r[u] = i < end ? perm[i] : -1;
         }
 #pragma unroll
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
     for (int64_t q = team; q < kSpread * C; q += nteams) {
         const int64_t u = spread_u(q, C);
         if (u >= U) continue;                    // a hole of the spread order
-        const int32_t beg = seg_off[q], end = seg_off[q + 1];
+        const int64_t beg = seg_off[q], end = seg_off[q + 1];
         if (end - beg > kSmallMax) {
             if (tl == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
             continue;
@@ -467,8 +468,8 @@ __global__ __launch_bounds__(kRBlock) void k_large_reduce(const u32x4* __restric
         }
         const int32_t q = large[lo];
         const int32_t part = (int32_t)(c - large_off[lo]);
-        const int32_t beg = seg_off[q] + part * kChunk;
-        const int32_t end = min(seg_off[q + 1], beg + kChunk);
+        const int64_t beg = (int64_t)seg_off[q] + (int64_t)part * kChunk;
+        const int64_t end = min((int64_t)seg_off[q + 1], beg + kChunk);
         const bool single = large_off[lo + 1] - large_off[lo] == 1;
         const int64_t u = spread_u(q, C);
         AdamVec st;

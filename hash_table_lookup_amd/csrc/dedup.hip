@@ -68,6 +68,7 @@
 // key -1 at index 2^30, stay int32); with n < 2^30 a slot is always free.
 // Every int64 is a valid key: the value -1, which both sets use as their
 // empty marker, is carried out of band.
+#include "lookup.h"
 #include "scan.h"
 #include "tile_dedup.h"
 
@@ -252,24 +253,36 @@ __global__ __launch_bounds__(kGlobalThreads) void k_dedup_assign(
 
 // inverse[i] = id of the set slot of tile survivor local[i]: each block takes
 // one tile, fetches its survivors' ids once into LDS (an owner's from its
-// own entry, the others' from the set), then maps its IDs.
+// own entry, the others' from the set), then maps its IDs.  With `slots`
+// (the find-or-insert result of `unique`), each survivor also fetches its
+// key's slot once, and sid[i] = slots[inverse[i]] is written beside the
+// inverse, so that a later gather reads one index per ID, in sequence.
 __global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* __restrict__ local, int64_t n,
                                                                const int32_t* __restrict__ tu_count,
                                                                const int32_t* __restrict__ tu_slot,
                                                                const int32_t* __restrict__ set_ids,
-                                                               int32_t* __restrict__ inverse) {
+                                                               int32_t* __restrict__ inverse,
+                                                               const int32_t* __restrict__ slots,
+                                                               int32_t* __restrict__ sid) {
     __shared__ int32_t s_gid[kTile];
+    __shared__ int32_t s_sl[kTile];
     for (int64_t tile = blockIdx.x; tile * kTile < n; tile += gridDim.x) {
         const int cnt = tu_count[tile];
         for (int j = threadIdx.x; j < cnt; j += kTileThreads) {
             const int32_t v = tu_slot[tile * kTile + j];
-            s_gid[j] = v < 0 ? -(v + 1) : set_ids[v];
+            const int32_t g = v < 0 ? -(v + 1) : set_ids[v];
+            s_gid[j] = g;
+            if (slots) s_sl[j] = slots[g];
         }
         __syncthreads();
         const int64_t base = tile * kTile;
         for (int q = threadIdx.x; q < kTile; q += kTileThreads) {
             const int64_t i = base + q;
-            if (i < n) inverse[i] = s_gid[local[i]];
+            if (i < n) {
+                const int l = local[i];
+                inverse[i] = s_gid[l];
+                if (slots) sid[i] = s_sl[l];
+            }
         }
         __syncthreads();
     }
@@ -705,16 +718,21 @@ __global__ __launch_bounds__(kBinThreads) void k_part_dedup(const u32x4* __restr
     if (threadIdx.x == 0) ucount[b] = nd;
 }
 
-// Blocks [0, bins): pack bin b's distinct keys at uoff[b]; the other blocks:
-// compose the inverse tile by tile, id = uoff[bin] + id inside the bin.
+// Blocks [0, pack_blocks) (pack_blocks is 0 or the number of bins): pack bin
+// b's distinct keys at uoff[b]; the other blocks: compose the inverse tile
+// by tile, id = uoff[bin] + id inside the bin.  With `slots` (the
+// find-or-insert result of `unique`), each survivor also fetches its key's
+// slot once into LDS and sid[i] = slots[inverse[i]] is written beside the
+// inverse (one index per ID, in sequence, for a later gather).
 __global__ __launch_bounds__(kTileThreads) void k_part_finish(
     const int64_t* __restrict__ ustage, const int32_t* __restrict__ base, int plog2,
     const int32_t* __restrict__ ucount, const int32_t* __restrict__ uoff, int64_t* __restrict__ unique,
     int64_t* __restrict__ n_unique, const int64_t* __restrict__ tu_keys, const int32_t* __restrict__ tu_count,
     const int32_t* __restrict__ tu_l, const uint16_t* __restrict__ local, int64_t n,
-    int32_t* __restrict__ inverse) {
+    int32_t* __restrict__ inverse, int pack_blocks, const int32_t* __restrict__ slots,
+    int32_t* __restrict__ sid) {
     const int P = 1 << plog2;
-    if ((int)blockIdx.x < P) {
+    if ((int)blockIdx.x < pack_blocks) {
         const int b = blockIdx.x;
         const int64_t src = base[b];
         const int64_t dst = uoff[b];
@@ -724,11 +742,12 @@ __global__ __launch_bounds__(kTileThreads) void k_part_finish(
         return;
     }
     __shared__ int32_t s_gid[kTile];
+    __shared__ int32_t s_sl[kTile];
     __shared__ int32_t s_uoff[1 << kPartMaxLog2];
     for (int b = threadIdx.x; b < P; b += kTileThreads) s_uoff[b] = uoff[b];
     __syncthreads();
     const int64_t ntiles = (n + kTile - 1) / kTile;
-    for (int64_t tile = (int64_t)blockIdx.x - P; tile < ntiles; tile += (int64_t)gridDim.x - P) {
+    for (int64_t tile = (int64_t)blockIdx.x - pack_blocks; tile < ntiles; tile += (int64_t)gridDim.x - pack_blocks) {
         // loads without a branch per element (past the end the last
         // element is loaded again and dropped), so each pass's loads are in
         // flight together
@@ -744,10 +763,23 @@ __global__ __launch_bounds__(kTileThreads) void k_part_finish(
                 k[u] = (uint64_t)tu_keys[at];
                 l[u] = tu_l[at];
             }
+            int32_t g[kV];
+#pragma unroll
+            for (int u = 0; u < kV; ++u) g[u] = s_uoff[part_bin(k[u], plog2)] + l[u];
+            if (slots) {
+                int32_t sl[kV];
+#pragma unroll
+                for (int u = 0; u < kV; ++u) sl[u] = slots[g[u]];
+#pragma unroll
+                for (int u = 0; u < kV; ++u) {
+                    const int j = j0 + u * kTileThreads;
+                    if (j < cnt) s_sl[j] = sl[u];
+                }
+            }
 #pragma unroll
             for (int u = 0; u < kV; ++u) {
                 const int j = j0 + u * kTileThreads;
-                if (j < cnt) s_gid[j] = s_uoff[part_bin(k[u], plog2)] + l[u];
+                if (j < cnt) s_gid[j] = g[u];
             }
         }
         __syncthreads();
@@ -762,7 +794,10 @@ __global__ __launch_bounds__(kTileThreads) void k_part_finish(
 #pragma unroll
         for (int u = 0; u < kPerT; ++u) {
             const int64_t i = b0 + u * kTileThreads + threadIdx.x;
-            if (i < n) inverse[i] = s_gid[lo[u]];
+            if (i < n) {
+                inverse[i] = s_gid[lo[u]];
+                if (slots) sid[i] = s_sl[lo[u]];
+            }
         }
         __syncthreads();
     }
@@ -785,6 +820,8 @@ size_t dedup_workspace_bytes(int64_t n) {
     return b;
 }
 
+}  // extern "C"
+
 // Stage 2 path: HTL_DEDUP_PATH=set forces the device set for every size;
 // HTL_DEDUP_BIN_MAX lowers the distinct keys a bin may hold in LDS (to test
 // the device-memory redo).
@@ -801,7 +838,7 @@ static int bin_max_keys() {
 }
 
 static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
-                           int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream, DedupRun* split) {
     PartWs w = part_layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
@@ -819,16 +856,23 @@ static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int6
     hipLaunchKernelGGL(k_part_dedup, dim3(P), dim3(kBinThreads), 0, stream, w.ent, w.btotal, w.base, bin_max_keys(),
                        w.tu_l, w.ustage, w.ucount, w.fb_keys, w.fb_ids);
     hipLaunchKernelGGL(k_prefix_bins, dim3(1), dim3(kBaseThreads), 0, stream, w.ucount, P, w.uoff);
-    hipLaunchKernelGGL(k_part_finish, dim3(P + gt), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
-                       w.ucount, w.uoff, unique, n_unique_dev, w.tu_keys, w.tu_count, w.tu_l, w.local, n, inverse);
+    // packing the bins' keys and composing the inverse share one launch;
+    // split: the packing only (the compose runs after find-or-insert)
+    const unsigned grid = split ? P : P + gt;
+    hipLaunchKernelGGL(k_part_finish, dim3(grid), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
+                       w.ucount, w.uoff, unique, n_unique_dev, w.tu_keys, w.tu_count, w.tu_l, w.local, n, inverse, P,
+                       (const int32_t*)nullptr, (int32_t*)nullptr);
+    if (split) *split = DedupRun{kRunPart, n, ws};
     return check_launch(who);
 }
 
 static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, int64_t n, int64_t* unique,
-                            int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream,
+                            DedupRun* split = nullptr) {
     clear_error();
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 30), std::string(who) + ": n must be in [0, 2^30)");
     HTL_REQUIRE(n_unique_dev && aligned(n_unique_dev, 8), std::string(who) + ": null or misaligned n_unique_dev");
+    if (split) *split = DedupRun{kRunDone, n, ws};
     if (n == 0) {
         hipLaunchKernelGGL(k_write_zero, dim3(1), dim3(1), 0, stream, n_unique_dev);
         return check_launch(who);
@@ -836,13 +880,14 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     HTL_REQUIRE(keys && unique && inverse && ws, std::string(who) + ": null pointer");
     HTL_REQUIRE(aligned(keys, 8) && aligned(unique, 8) && aligned(inverse, 4) && aligned(ws, 256),
                 std::string(who) + ": misaligned pointer");
-    if (use_part_path(ordered, n)) return run_part(who, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream);
+    if (use_part_path(ordered, n))
+        return run_part(who, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream, split);
     DedupWs w = layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
     if (n <= kTile) {
         // A batch of one tile: the LDS stage alone is the answer (one
         // launch, no device set to clear), in first-occurrence order, which
-        // both modes accept.
+        // both modes accept.  Nothing is left for a split's second half.
         hipLaunchKernelGGL(k_dedup_tile<true>, dim3(1), dim3(kTileThreads), 0, stream, keys, n, unique,
                            (int32_t*)nullptr, (uint16_t*)nullptr, inverse, n_unique_dev, SetClear{});
         return check_launch(who);
@@ -872,10 +917,44 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     else
         hipLaunchKernelGGL(k_dedup_assign<false>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
                            w.tu_slot, w.tu_own, ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
+    if (split) {
+        *split = DedupRun{kRunSet, n, ws};
+        return check_launch(who);
+    }
     hipLaunchKernelGGL(k_dedup_compose, dim3(gt), dim3(kTileThreads), 0, stream, w.local, n, w.tu_count, w.tu_slot,
-                       w.set_ids, inverse);
+                       w.set_ids, inverse, (const int32_t*)nullptr, (int32_t*)nullptr);
     return check_launch(who);
 }
+
+namespace htl {
+
+htl_status dedup_until_unique(const char* who, const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
+                              int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream, DedupRun* run) {
+    return run_dedup(who, false, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream, run);
+}
+
+htl_status dedup_compose(const char* who, const DedupRun& run, const int32_t* slots, int32_t* inverse, int32_t* sid,
+                         hipStream_t stream) {
+    if (run.path == kRunDone) return HTL_OK;
+    const int64_t n = run.n;
+    const int64_t ntiles = ceil_div(n, kTile);
+    const unsigned gt = grid_for(ntiles, 1, 1 << 16);
+    if (run.path == kRunPart) {
+        PartWs w = part_layout(n, (char*)run.ws);
+        hipLaunchKernelGGL(k_part_finish, dim3(gt), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
+                           w.ucount, w.uoff, (int64_t*)nullptr, (int64_t*)nullptr, w.tu_keys, w.tu_count, w.tu_l,
+                           w.local, n, inverse, 0, slots, sid);
+    } else {
+        DedupWs w = layout(n, (char*)run.ws);
+        hipLaunchKernelGGL(k_dedup_compose, dim3(gt), dim3(kTileThreads), 0, stream, w.local, n, w.tu_count,
+                           w.tu_slot, w.set_ids, inverse, slots, sid);
+    }
+    return check_launch(who);
+}
+
+}  // namespace htl
+
+extern "C" {
 
 htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
                                 int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {

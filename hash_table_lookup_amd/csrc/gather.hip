@@ -191,7 +191,7 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
     HTL_REQUIRE(aligned(offsets, 4) && (!slots || aligned(slots, 4)) && (!inverse || aligned(inverse, 4)) &&
                     aligned(out, 16),
                 "emb_gather_pool: misaligned pointer (out needs 16 bytes)");
-    return launch_pooling(t->dev, t->dtype, vec, vpr, slots, inverse, offsets, nbags, out_dtype == HTL_BF16, out,
+    return launch_pooling(t->dev, t->dtype, vec, vpr, slots, inverse, n, offsets, nbags, out_dtype == HTL_BF16, out,
                           stream);
 }
 

@@ -21,6 +21,11 @@ __device__ __forceinline__ u32x4 zero4() {
     return z;
 }
 
+// A CSR position clamped to [0, n].
+__device__ __forceinline__ int64_t clamp_pos(int32_t p, int64_t n) {
+    return p < 0 ? 0 : (p > n ? n : (int64_t)p);
+}
+
 int team_for(int vpr) {
     int t = 1;
     while (t < vpr && t < 64) t <<= 1;
@@ -36,7 +41,7 @@ int team_for(int vpr) {
 template <int TEAM, int QMAX, bool IN_BF16>
 __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows, int vpr, int64_t M,
                                                 const int32_t* __restrict__ slots,
-                                                const int32_t* __restrict__ inverse,
+                                                const int32_t* __restrict__ inverse, int64_t n,
                                                 const int32_t* __restrict__ offsets, int64_t nbags,
                                                 bool out_bf16, void* __restrict__ out) {
     constexpr int E = IN_BF16 ? 8 : 4;            // elements per 16-byte vector
@@ -52,8 +57,10 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
         for (int a = 0; a < QMAX; ++a)
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[a][e] = 0.0f;
-        // 64-bit positions: end may lie within TEAMS * kPoolUnroll of 2^31
-        const int64_t beg = offsets[bag], end = offsets[bag + 1];
+        // 64-bit positions: end may lie within TEAMS * kPoolUnroll of 2^31.
+        // A bag is clamped to [0, n): offsets that break the CSR rules read
+        // no ID outside the batch.
+        const int64_t beg = clamp_pos(offsets[bag], n), end = clamp_pos(offsets[bag + 1], n);
         for (int64_t i0 = beg + q; i0 < end; i0 += TEAMS * kPoolUnroll) {
             // kPoolUnroll IDs per team in flight: inverse, then slots, then rows
             int32_t s[kPoolUnroll];
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void k_pool(const u32x4* __restrict__ rows,
 // Element-wise pooling fallback: one thread per (bag, element), fp32 sums.
 template <typename TIn>
 __global__ void k_pool_elem(const TIn* __restrict__ rows, int dim, int64_t M, const int32_t* __restrict__ slots,
-                            const int32_t* __restrict__ inverse, const int32_t* __restrict__ offsets,
+                            const int32_t* __restrict__ inverse, int64_t n, const int32_t* __restrict__ offsets,
                             int64_t nbags, bool in_bf16, bool out_bf16, void* __restrict__ out) {
     const int64_t total = nbags * dim;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -145,7 +152,8 @@ __global__ void k_pool_elem(const TIn* __restrict__ rows, int dim, int64_t M, co
         const int64_t bag = e / dim;
         const int j = (int)(e - bag * dim);
         float acc = 0.0f;
-        for (int32_t i = offsets[bag]; i < offsets[bag + 1]; ++i) {
+        const int64_t end = clamp_pos(offsets[bag + 1], n);
+        for (int64_t i = clamp_pos(offsets[bag], n); i < end; ++i) {
             const int32_t s = slots[inverse ? inverse[i] : i];
             if (s < 0 || s >= M) continue;
             const TIn x = rows[(int64_t)s * dim + j];
@@ -157,7 +165,7 @@ __global__ void k_pool_elem(const TIn* __restrict__ rows, int dim, int64_t M, co
 }
 
 template <int TEAM, int QMAX>
-void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t* inverse,
+void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t* inverse, int64_t n,
                  const int32_t* offsets, int64_t nbags, bool out_bf16, void* out, hipStream_t s) {
     // A persistent grid (each wavefront strides over bags): on the 1.7M-bag
     // pooled workload, 16K workgroups ran 10% faster than one wavefront per
@@ -165,43 +173,43 @@ void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t
     const unsigned grid = grid_for(nbags, kBlock / 64, kPoolBlocks);
     if (T.dtype == HTL_BF16)
         hipLaunchKernelGGL((k_pool<TEAM, QMAX, true>), dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
-                           vpr, T.capacity, slots, inverse, offsets, nbags, out_bf16, out);
+                           vpr, T.capacity, slots, inverse, n, offsets, nbags, out_bf16, out);
     else
         hipLaunchKernelGGL((k_pool<TEAM, QMAX, false>), dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
-                           vpr, T.capacity, slots, inverse, offsets, nbags, out_bf16, out);
+                           vpr, T.capacity, slots, inverse, n, offsets, nbags, out_bf16, out);
 }
 
 }  // namespace
 
 htl_status launch_pooling(const TableDev& T, int dtype, bool vec, int vpr, const int32_t* slots,
-                          const int32_t* inverse, const int32_t* offsets, int64_t nbags, bool out_bf16, void* out,
-                          hipStream_t stream) {
+                          const int32_t* inverse, int64_t n, const int32_t* offsets, int64_t nbags, bool out_bf16,
+                          void* out, hipStream_t stream) {
     if (vec && vpr <= 256) {
         // One 16-byte vector per lane.  (Narrower teams with two vectors
         // per lane, which keep a whole 20-ID bag in flight in one round,
         // measured 3% slower on the 26-table bf16 workload: the pooled rows
         // come from cache and the loop is not latency-bound.)
         switch (team_for(vpr)) {
-            case 1: launch_pool<1, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
-            case 2: launch_pool<2, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
-            case 4: launch_pool<4, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
-            case 8: launch_pool<8, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
-            case 16: launch_pool<16, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
-            case 32: launch_pool<32, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream); break;
+            case 1: launch_pool<1, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
+            case 2: launch_pool<2, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
+            case 4: launch_pool<4, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
+            case 8: launch_pool<8, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
+            case 16: launch_pool<16, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
+            case 32: launch_pool<32, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
             default:
-                if (vpr <= 64) launch_pool<64, 1>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
-                else if (vpr <= 128) launch_pool<64, 2>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
-                else launch_pool<64, 4>(T, vpr, slots, inverse, offsets, nbags, out_bf16, out, stream);
+                if (vpr <= 64) launch_pool<64, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream);
+                else if (vpr <= 128) launch_pool<64, 2>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream);
+                else launch_pool<64, 4>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream);
                 break;
         }
     } else {
         const unsigned grid = grid_for(nbags * T.dim, 256 * 4);
         if (dtype == HTL_F32)
             hipLaunchKernelGGL((k_pool_elem<uint32_t>), dim3(grid), dim3(256), 0, stream, (const uint32_t*)T.rows,
-                               T.dim, T.capacity, slots, inverse, offsets, nbags, false, out_bf16, out);
+                               T.dim, T.capacity, slots, inverse, n, offsets, nbags, false, out_bf16, out);
         else
             hipLaunchKernelGGL((k_pool_elem<uint16_t>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)T.rows,
-                               T.dim, T.capacity, slots, inverse, offsets, nbags, true, out_bf16, out);
+                               T.dim, T.capacity, slots, inverse, n, offsets, nbags, true, out_bf16, out);
     }
     return check_launch("emb_gather_pool (pool)");
 }

@@ -1110,6 +1110,14 @@ htl_status ht_import(htl_table* t, const int64_t* keys, int64_t n, const void* r
     return check_launch("ht_import");
 }
 
+htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes) {
+    clear_error();
+    HTL_REQUIRE(t, "ht_rows: null table");
+    if (rows) *rows = t->dev.rows;
+    if (row_bytes) *row_bytes = (int64_t)t->dim * t->dev.elem_bytes;
+    return HTL_OK;
+}
+
 htl_status ht_view(const htl_table* t, htl_view* out) {
     clear_error();
     HTL_REQUIRE(t && out, "ht_view: null argument");

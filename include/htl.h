@@ -213,12 +213,29 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
                          int64_t victims_cap, int64_t* n_victims_dev, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
-/* ht_view -- raw device views of the table's storage (read-only use intended).
- * Any output may be null.  rows is dtype[M][dim]; m, v are null unless the
- * table keeps Adam state; last_seen (per slot; 0xFFFFFFFF at slots with no
- * live key) is null unless it keeps metadata.  In a growable table rows, m and v are indexed by row handle,
- * and row_of_slot (int32[M], valid at live slots) maps a slot to its handle;
- * row_of_slot is null for other tables (handle = slot). */
+/* ht_rows -- read-only view of the table's embedding rows ([MTGR] section 5,
+ * "Embedding Management": the table keeps, per key, an embedding vector and
+ * metadata).  *rows receives the device address of dtype[R][dim], where R is
+ * the capacity (rows indexed by slot) or, for a growable table, the rows
+ * mapped so far (indexed by row handle); *row_bytes receives dim times the
+ * element size.  The caller reads the rows of the slots / handles that
+ * ht_find_or_insert or ht_scan returned; it must not write through the
+ * pointer.  The pointer stays valid until ht_destroy (a growable table's row
+ * space never moves: ht_resize maps more rows behind it).  Either output may
+ * be null.  Errors: INVALID for a null table. */
+htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes);
+
+/* ht_view -- every storage array of the table, for checkpoint tooling,
+ * tests and measurement.  Any output may be null.  rows is dtype[M][dim]; m,
+ * v are null unless the table keeps Adam state; last_seen (per slot;
+ * 0xFFFFFFFF at slots with no live key) is null unless it keeps metadata.  In
+ * a growable table rows, m and v are indexed by row handle, and row_of_slot
+ * (int32[M], valid at live slots) maps a slot to its handle; row_of_slot is
+ * null for other tables (handle = slot).  The pointers are the table's own
+ * storage: reading them is always safe; a caller that writes through them
+ * (a benchmark restoring the key array between timed steps, say) takes over
+ * the table's invariants -- keys distinct, EMPTY / TOMBSTONE markers, the
+ * last_seen marker of dead slots -- and must keep them. */
 typedef struct {
     int64_t capacity;
     int32_t dim;
@@ -234,9 +251,10 @@ htl_status ht_view(const htl_table* t, htl_view* out);
 
 /* ------------------------------------------------------------------ dedup --
  * dedup_unique_inverse -- feature-ID deduplication in two stages.
- * [MTGenRec] TL;DR and table of contents section 6: two-stage ID
- * deduplication for faster embedding lookups; [MTGR] section 5 "Embedding
- * Lookup": IDs are unique before and after the all-to-all.  On one device,
+ * [MTGenRec] TL;DR (one of its four components: IDs are deduplicated in two
+ * stages to speed up the embedding lookup) and table of contents section 6,
+ * "Embedding Table Lookup Acceleration"; [MTGR] section 5 "Embedding Lookup":
+ * the IDs stay unique both before and after the cross-device exchange.  On one device,
  * stage 1 dedups each tile of keys in on-chip memory (one copy per tile
  * leaves it, as one copy per sender leaves a device before the exchange), and
  * stage 2 dedups the tile survivors device-wide: for 2048 < n <= 2^23 by hash
@@ -269,7 +287,9 @@ htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t*
 
 /* ----------------------------------------------------------------- gather --
  * emb_gather_pool -- embedding row gather with optional bag sum-pooling.
- * [MTGenRec] TL;DR: faster embedding lookups; pooling over multi-hot bags is
+ * [MTGenRec] TL;DR: the embedding lookup that the dynamic table and the
+ * deduplication serve; [MTGR] section 5 "Other Optimizations" names table
+ * lookup as the work of its dispatch stream.  Pooling over multi-hot bags is
  * this library's reading for bag-shaped features (the pages describe none).
  *   slots     int32[U]: table slot per unique key (from ht_find_or_insert);
  *             a negative slot stands for a zero row.
@@ -278,6 +298,9 @@ htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t*
  *   n         number of IDs.
  *   offsets   nullable int32[nbags + 1], non-decreasing, offsets[0] = 0,
  *             offsets[nbags] = n: CSR bags over the IDs.  Null = no pooling.
+ *             The kernels clamp every bag to [0, n), so offsets that break
+ *             this rule read no ID outside the n given (such a bag sums the
+ *             IDs it keeps inside [0, n), possibly none).
  *   out_dtype HTL_F32 or HTL_BF16.  Without pooling it must equal the table's
  *             dtype, or be HTL_F32 for a bf16 table (exact widening).  With
  *             pooling, sums accumulate in fp32 and are rounded to bf16 to
@@ -288,10 +311,57 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
                            int64_t n, const int32_t* offsets, int64_t nbags,
                            htl_dtype out_dtype, void* out, hipStream_t stream);
 
+/* ------------------------------------------------------------ one call --
+ * emb_lookup_slots -- dedup_unique_inverse(keys), then
+ * ht_find_or_insert(t, unique, n, n_unique_dev, step), and the slot of every
+ * ID: id_slots[i] = slots[inverse[i]].  [MTGenRec] TL;DR and Figure 5 (IDs
+ * deduplicated in two stages, then looked up in the dynamic hash table);
+ * [MTGR] section 5 "Embedding Lookup".  unique, inverse, U, slots and status
+ * are what the two calls write (unique in the same unspecified order), with
+ * the same preconditions.  The dedup's last pass (the inverse, composed per
+ * tile of IDs from the tile's distinct keys) runs after find-or-insert, so it
+ * writes id_slots in the same pass, with one slot load per distinct key of a
+ * tile instead of one per ID; a gather then reads one index per ID in
+ * sequence: emb_gather_pool(t, id_slots, NULL, n, ...).
+ *   keys, n        int64[n], 0 <= n < 2^30.
+ *   step           as ht_find_or_insert.
+ *   unique, inverse, n_unique_dev   as dedup_unique_inverse (unique int64[n]).
+ *   slots, status  int32[n], uint8[n] out: as ht_find_or_insert on unique
+ *                  (entries at index >= U are not written).
+ *   id_slots       int32[n] out: the slot (growable tables: row handle) of
+ *                  each ID's key, -1 for a RESERVED key.
+ *   ws, ws_bytes   at least dedup_workspace_bytes(n) bytes, 256-byte
+ *                  aligned; contents on entry are ignored.
+ * Errors: every argument is checked before anything is enqueued
+ * (HTL_ERR_INVALID); a growable table may allocate, as in ht_find_or_insert. */
+htl_status emb_lookup_slots(htl_table* t, const int64_t* keys, int64_t n, uint32_t step, int64_t* unique,
+                            int32_t* inverse, int64_t* n_unique_dev, int32_t* slots, uint8_t* status,
+                            int32_t* id_slots, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* emb_lookup -- the whole forward lookup in one call: emb_lookup_slots, then
+ * emb_gather_pool(t, id_slots, NULL, n, offsets, nbags, out_dtype, out)
+ * with id_slots kept in the workspace.  Every output equals what
+ * dedup_unique_inverse, ht_find_or_insert and emb_gather_pool(t, slots,
+ * inverse, ...) write.
+ *   offsets, nbags, out_dtype, out  as emb_gather_pool.
+ *   ws, ws_bytes   at least emb_lookup_workspace_bytes(n) bytes, 256-byte
+ *                  aligned.
+ * Other arguments and errors as emb_lookup_slots; the gather's arguments are
+ * checked before anything is enqueued as well. */
+size_t emb_lookup_workspace_bytes(int64_t n);
+htl_status emb_lookup(htl_table* t, const int64_t* keys, int64_t n, uint32_t step, int64_t* unique,
+                      int32_t* inverse, int64_t* n_unique_dev, int32_t* slots, uint8_t* status,
+                      const int32_t* offsets, int64_t nbags, htl_dtype out_dtype, void* out, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------- backward --
  * emb_grad_segment_sum -- backward gradient dedup: out[u] = sum of grad[i]
- * over the IDs with inverse[i] == u, accumulated in fp32 (the backward of the
- * deduplicated lookup; summation order is unspecified).
+ * over the IDs with inverse[i] == u, accumulated in fp32; summation order is
+ * unspecified.  It is the backward of the deduplicated lookup: [MTGR]
+ * section 5 "Embedding Lookup" keeps IDs unique around the exchange, and
+ * [MTGenRec] TL;DR deduplicates IDs before the lookup, so every ID that
+ * shares a unique key sends its gradient to that key's one row; the pages
+ * describe no backward, and summing per unique key is the plain reading.
  *   grad          float[n][dim]; inverse int32[n] with values < U; entries
  *                 outside [0, U) contribute nowhere.  n < 2^31 - 1024,
  *                 1 <= dim <= 65536, 0 <= u_max <= n (HTL_ERR_INVALID
@@ -299,7 +369,9 @@ htl_status emb_gather_pool(const htl_table* t, const int32_t* slots, const int32
  *   n_unique_dev  device int64 U (nullable: then U = u_max); u_max host bound.
  *   out           float[u_max][dim]: rows 0..U-1 written, the rest untouched.
  *   ws, ws_bytes  at least segsum_workspace_bytes(n, u_max, dim) bytes,
- *                 256-byte aligned. */
+ *                 256-byte aligned.  The size takes dim because segments
+ *                 longer than one chunk of IDs leave a partial sum row
+ *                 (dim floats) per chunk in the workspace. */
 size_t segsum_workspace_bytes(int64_t n, int64_t u_max, int dim);
 htl_status emb_grad_segment_sum(const float* grad, const int32_t* inverse, int64_t n,
                                 const int64_t* n_unique_dev, int64_t u_max, int dim,

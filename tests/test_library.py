@@ -27,11 +27,44 @@ def L():
     return h.lib()
 
 
+# The C ABI proposed for the lookup path: every one of these calls must be
+# declared and exported under its name.
+BOUNDARY_CALLS = ("ht_create", "ht_destroy", "ht_find_or_insert", "ht_erase", "dedup_workspace_bytes",
+                  "dedup_unique_inverse", "emb_gather_pool", "segsum_workspace_bytes", "emb_grad_segment_sum",
+                  "emb_rowwise_adam", "ht_scan", "ht_rows", "htl_last_error")
+
+
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("ht_create", "ht_destroy", "ht_find_or_insert", "ht_erase", "dedup_unique_inverse",
-                     "emb_gather_pool", "emb_grad_segment_sum"):
-        assert required in names
+    missing = [c for c in BOUNDARY_CALLS if c not in names]
+    assert not missing, missing
+
+
+def test_boundary_signatures():
+    # argument lists of the boundary calls as the header declares them
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+
+    def args(name):
+        m = re.search(r"\b" + name + r"\s*\(([^;]*?)\)\s*;", src, flags=re.S)
+        assert m, name
+        return [" ".join(a.split()) for a in m.group(1).split(",")]
+
+    assert args("ht_rows") == ["const htl_table* t", "const void** rows", "int64_t* row_bytes"]
+    assert args("ht_scan") == ["const htl_table* t", "int64_t* keys", "uint32_t* last_seen", "int32_t* slots",
+                               "int64_t* n_live_dev", "hipStream_t stream"]
+    assert args("dedup_unique_inverse")[:5] == ["const int64_t* keys", "int64_t n", "int64_t* unique",
+                                                "int32_t* inverse", "int64_t* n_unique_dev"]
+    assert args("emb_gather_pool") == ["const htl_table* t", "const int32_t* slots", "const int32_t* inverse",
+                                       "int64_t n", "const int32_t* offsets", "int64_t nbags",
+                                       "htl_dtype out_dtype", "void* out", "hipStream_t stream"]
+    assert args("segsum_workspace_bytes") == ["int64_t n", "int64_t u_max", "int dim"]
+
+
+def test_rows_view_rejects_a_null_table(L):
+    import ctypes as C
+    p, rb = C.c_void_p(), C.c_int64(-1)
+    assert L.ht_rows(None, C.byref(p), C.byref(rb)) == 1
+    assert b"null table" in L.htl_last_error()
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -87,6 +120,9 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.ht_export(None, 0, 1, None, None, None, None, None, None, None) == INVALID
     assert L.ht_import(None, None, 1, None, None, None, None, None, None) == INVALID
     assert L.ht_view(None, None) == INVALID
+    assert L.emb_lookup_slots(None, None, 4, 0, None, None, None, None, None, None, None, 0, None) == INVALID
+    assert L.emb_lookup(None, None, 4, 0, None, None, None, None, None, None, 0, 0, None, None, 0, None) == INVALID
+    assert L.emb_lookup_workspace_bytes(1 << 20) >= L.dedup_workspace_bytes(1 << 20) + 4 * (1 << 20)
     assert L.ht_destroy(None) == 0
     fake = ctypes.c_void_p(0x1000)
     assert L.htl_copy_probe(fake, fake, 24, None) == INVALID            # not a multiple of 16
