@@ -66,6 +66,8 @@ _SIGNATURES = {
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
+    "dedup_noalloc_max_keys": [],
+    "dedup_unique_inverse_noalloc": [_P, _I64, _P, _P, _P, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
     "emb_lookup_slots": [_P, _P, _I64, _U32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "emb_lookup_workspace_bytes": [_I64],
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
             f.argtypes = args
             if name in _SIZE_FUNCS:
                 f.restype = _SZ
+            elif name == "dedup_noalloc_max_keys":
+                f.restype = _I64
             elif name == "htl_last_error":
                 f.restype = ctypes.c_char_p
             else:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libhtl.so")
 ARCH = os.environ.get("HTL_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["table.hip", "dedup.hip", "lookup.hip", "gather.hip", "pool.hip", "scan.hip", "backward.hip", "lru.hip",
-           "copy.hip"]
+           "copy.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -285,6 +285,25 @@ htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t*
                                         int32_t* inverse, int64_t* n_unique_dev, void* ws,
                                         size_t ws_bytes, hipStream_t stream);
 
+/* dedup_unique_inverse_noalloc -- dedup_unique_inverse with no workspace
+ * argument and no allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same kernels, arguments and results as dedup_unique_inverse;
+ * the workspace is a fixed 64 MiB array in device memory that the library
+ * carries (one per device, held from the library's first use on that
+ * device until the process ends), so n is limited to
+ * dedup_noalloc_max_keys() = 2^20 keys (HTL_ERR_INVALID beyond it, before
+ * anything is enqueued).  The call allocates nothing: the array's device
+ * address is looked up once per device, on the first call with that device
+ * current (keys and outputs must live on the current device).  Every call on
+ * one device shares that device's array, so calls that overlap on one
+ * device -- on two streams, or from two threads without ordering -- race;
+ * order them on one stream.  The array keeps the last call's contents; the
+ * dedup reads nothing from it that it has not written in the same call. */
+int64_t dedup_noalloc_max_keys(void);
+htl_status dedup_unique_inverse_noalloc(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
+                                        int64_t* n_unique_dev, hipStream_t stream);
+
 /* ----------------------------------------------------------------- gather --
  * emb_gather_pool -- embedding row gather with optional bag sum-pooling.
  * [MTGenRec] TL;DR: the embedding lookup that the dynamic table and the

@@ -139,3 +139,12 @@ def test_misaligned_workspace_rejected(L):
     assert L.dedup_unique_inverse(fake, 10, fake, fake, n_dev, odd, 1 << 20, None) == INVALID
     assert L.dedup_unique_inverse(fake, 10, fake, fake, n_dev, fake, 16, None) == INVALID
     assert b"workspace" in L.htl_last_error()
+
+
+def test_noalloc_dedup_limit_checked_on_the_host(L):
+    # beyond 2^20 keys the allocation-free dedup refuses before touching a device
+    assert L.dedup_noalloc_max_keys() == 1 << 20
+    fake = ctypes.c_void_p(0x1000)
+    assert L.dedup_unique_inverse_noalloc(fake, (1 << 20) + 1, fake, fake, fake, None) == 1
+    assert b"2^20" in L.htl_last_error()
+    assert L.dedup_unique_inverse_noalloc(fake, -1, fake, fake, fake, None) == 1
