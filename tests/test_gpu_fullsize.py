@@ -1,11 +1,12 @@
-"""Full-size runs of the pooled and online workloads, in the launch shapes
-bench.py times, checked on what the oracle computes one by one (closed-form
-rows of sampled keys, brute-force sums of sampled bags) and on properties
-that hold at any size (unique set, inverse, LRU order, erase statuses).
+"""Full-size runs of the pooled, online and backward workloads, in the launch
+shapes bench.py times, checked against the oracle value by value: every
+pooled bag, every key's status, the live set with its last_seen stamps and
+the eviction victims of every step.
 
 Merged tables: 65,536 samples x 26 bags of Poisson(20) IDs (34.08M IDs), one
 2^26-slot bf16 table of dim 128 warmed by an earlier batch.  Online: the
-2^27-slot bf16 table of dim 64 over the first steps of the drifting stream.
+2^27-slot bf16 table of dim 64 over all 50 steps of the drifting stream,
+the oracle table stepped beside it.
 """
 import numpy as np
 import pytest
@@ -17,72 +18,113 @@ from conftest import to_np
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def test_merged_tables_full_size(htl, orc):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fused", [True, False])
+def test_merged_tables_full_size(htl, orc, fused):
     w = workloads.merged_tables()
     warm = workloads.merged_tables(seed=1)
     table = htl.Table(w.capacity_log2, w.dim, w.dtype)
     wk = torch.from_numpy(warm.keys).cuda()
     u0, _, n0 = htl.dedup_unique_inverse(wk)
     table.find_or_insert(u0, n_dev=n0)
+    warm_u = to_np(u0)[:int(n0.item())]
     del wk, u0
     keys = torch.from_numpy(w.keys).cuda()
     offsets = torch.from_numpy(w.offsets).cuda()
-    out, uniq, inv, nu, slots, status = htl.lookup(table, keys, offsets=offsets, out_dtype="bf16")
+    out, uniq, inv, nu, slots, status = htl.lookup(table, keys, offsets=offsets, out_dtype="bf16", fused=fused)
     U = int(nu.item())
     u = to_np(uniq)[:U]
     assert np.array_equal(np.sort(u), np.unique(w.keys))
-    sample = np.random.default_rng(3).integers(0, w.keys.size, 1 << 16)
-    assert np.array_equal(u[to_np(inv)[sample]], w.keys[sample])
-    st = to_np(status)[:U]
-    assert np.array_equal(st == htl.FOUND, np.isin(u, warm.keys))
-    # sampled bags: brute-force fp64 sums of closed-form bf16 rows, rounded
-    # to bf16 (exact in fp32 in any order, so bit-equal)
-    rng = np.random.default_rng(4)
-    bags = np.concatenate([rng.integers(0, w.nbags, 3000), [0, w.nbags - 1]])
-    got = to_np(out[torch.from_numpy(bags).cuda()])
-    for b, row in zip(bags, got):
-        ks = w.keys[w.offsets[b]:w.offsets[b + 1]]
-        if ks.size == 0:
-            assert np.all(row == 0)
-            continue
-        rows = orc.bf16_bits_to_f32(orc.init_rows(ks, w.dim, orc.BF16)).astype(np.float64)
-        s = rows.sum(axis=0).astype(np.float32)
-        want = (s.view(np.uint32) + 0x7FFF + ((s.view(np.uint32) >> 16) & 1)) >> 16
-        assert np.array_equal(row, want.astype(np.uint16)), b
+    assert np.array_equal(u[to_np(inv)], w.keys)
+    otab = orc.Table(1 << w.capacity_log2, w.dim, orc.BF16)
+    assert np.all(otab.find_or_insert(warm_u) == orc.INSERTED)
+    assert np.array_equal(to_np(status)[:U], otab.find_or_insert(u))
+    got = to_np(out)
+    del out
+    want = otab.gather_pool(w.keys, w.offsets, orc.BF16)
+    assert got.shape == want.shape and np.array_equal(got, want)
 
 
-def test_online_full_size_steps(htl, orc):
-    spec = workloads.DynamicOnlineSpec()
-    steps = 3
-    gen = workloads.DynamicOnlineStream(spec, steps)
-    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True)
-    live_before = 0
-    for s in range(steps):
-        keys_np = gen.keys(s)
+class _OnlineRun:
+    """The online stream stepped on the GPU table and the oracle table side by
+    side; advance(s_end) runs every step below s_end not yet run and checks,
+    per step: each unique key's status, the live keys with their last_seen
+    stamps, the victims and the erase statuses; the gathered rows in full
+    every tenth step and on a fixed sample of 2^16 IDs at the others."""
+
+    FULL_ROWS = (0, 10, 20, 30, 40, 49)
+
+    def __init__(self, htl, orc):
+        import concurrent.futures as cf
+        self.htl, self.orc = htl, orc
+        self.spec = workloads.DynamicOnlineSpec()
+        self.gen = workloads.DynamicOnlineStream(self.spec, self.spec.steps)
+        # the host draws the key batches ahead on a few threads
+        self.pool = cf.ThreadPoolExecutor(max_workers=4)
+        self.batches = {s: self.pool.submit(self.gen.keys, s) for s in range(self.spec.steps)}
+        self.table = htl.Table(self.spec.capacity_log2, self.spec.dim, "bf16", last_seen=True)
+        self.otab = orc.Table(1 << self.spec.capacity_log2, self.spec.dim, orc.BF16)
+        self.sample = np.random.default_rng(17).integers(0, self.spec.n, 1 << 16)
+        self.next = 0
+
+    def step(self, s):
+        htl, orc, spec = self.htl, self.orc, self.spec
+        keys_np = self.batches.pop(s).result()
         keys = torch.from_numpy(keys_np).cuda()
-        out, uniq, inv, nu, slots, status = htl.lookup(table, keys, step=s)
+        # even steps through the one-call forward, odd steps through the three calls
+        out, uniq, inv, nu, slots, status = htl.lookup(self.table, keys, step=s, fused=(s % 2 == 0))
         U = int(nu.item())
         u = to_np(uniq)[:U]
-        st = to_np(status)[:U]
-        assert np.array_equal(np.sort(u), np.unique(keys_np))
-        ins = st == htl.INSERTED
-        assert np.all((st == htl.FOUND) | ins)
-        idx = np.random.default_rng(s).integers(0, keys_np.size, 2048)
-        assert np.array_equal(to_np(out[torch.from_numpy(idx).cuda()]),
-                              orc.init_rows(keys_np[idx], spec.dim, orc.BF16))
-        k_all, ls_all, _, n_all = table.scan()
+        assert np.array_equal(u[to_np(inv)], keys_np), s          # also: u holds every key of the batch
+        assert np.unique(u).size == U, s                           # ... once
+        assert np.array_equal(to_np(status)[:U], self.otab.find_or_insert(u, step=s)), s
+        if s in self.FULL_ROWS:
+            got = to_np(out)
+            assert np.array_equal(got, self.otab.gather(keys_np)), s
+            del got
+        else:
+            idx = self.sample
+            assert np.array_equal(to_np(out[torch.from_numpy(idx).cuda()]), self.otab.gather(keys_np[idx])), s
+        del out
+        k_all, ls_all, _, n_all = self.table.scan()
         L = int(n_all.item())
-        assert L == live_before + int(ins.sum())
-        victims, nv = table.lru_select(spec.evict_num, spec.evict_den)
+        lk, order = torch.sort(k_all[:L])                           # key order, on the device
+        lls = ls_all[:L][order]
+        ok, ols = self.otab.live()
+        assert np.array_equal(to_np(lk), ok), s
+        assert np.array_equal(to_np(lls).astype(np.uint32), ols), s
+        del k_all, ls_all, lk, lls, order
+        victims, nv = self.table.lru_select(spec.evict_num, spec.evict_den)
         k = int(nv.item())
-        assert k == L * spec.evict_num // spec.evict_den
-        vk = to_np(victims)[:k]
-        lk, lls = to_np(k_all)[:L], to_np(ls_all)[:L].astype(np.uint32)
-        order = np.lexsort((lk, lls))                      # by (last_seen, key)
-        assert np.array_equal(np.sort(vk), np.sort(lk[order[:k]]))
-        est = to_np(table.erase(victims[:k]))
-        assert np.all(est == htl.ERASED)
-        live_before = L - k
+        want_v = self.otab.lru_victims(spec.evict_num, spec.evict_den)
+        assert k == want_v.size, s
+        assert np.array_equal(to_np(torch.sort(victims[:k])[0]), np.sort(want_v)), s
+        est = to_np(self.table.erase(victims[:k]))
+        assert np.all(est == htl.ERASED), s
+        assert np.all(self.otab.erase(want_v) == orc.ERASED), s
+
+    def advance(self, s_end):
+        while self.next < s_end:
+            self.step(self.next)
+            self.next += 1
+
+    def close(self):
+        self.pool.shutdown(wait=True, cancel_futures=True)
+
+
+@pytest.fixture(scope="module")
+def online_run(htl, orc):
+    run = _OnlineRun(htl, orc)
+    yield run
+    run.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("s_end", [10, 20, 30, 40, 50])
+def test_online_full_size_steps(online_run, s_end):
+    # all 50 steps of the online stream in five parts (each part runs the
+    # steps the parts before it left, so a part run alone checks from step 0)
+    online_run.advance(s_end)
 
 
 def test_backward_fused_full_size_matches_two_calls(htl):

@@ -224,13 +224,17 @@ class DynamicOnlineStream:
         self.steps = steps
         span = (steps - 1) * spec.delta + spec.window
         ids = np.arange(span, dtype=np.uint64)
-        self._order = ids[np.argsort(scramble(ids, 64), kind="stable")]
+        # scramble is a bijection, so the sort keys are distinct and any sort
+        # gives the one order (no stable sort needed)
+        self._order = ids[np.argsort(scramble(ids, 64))]
 
     def keys(self, step: int) -> np.ndarray:
         assert 0 <= step < self.steps
         spec = self.spec
         lo = np.uint64(step * spec.delta)
-        in_window = (self._order >= lo) & (self._order < lo + np.uint64(spec.window))
+        # ids below lo wrap to huge values, so one unsigned compare tests the window
+        with np.errstate(over="ignore"):
+            in_window = (self._order - lo) < np.uint64(spec.window)
         ordered = self._order[in_window]
         rng = np.random.Generator(np.random.PCG64(step))
         r = zipf_ranks(rng, spec.zipf_a, spec.window, spec.n)
