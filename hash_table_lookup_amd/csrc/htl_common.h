@@ -151,20 +151,25 @@ __device__ __forceinline__ uint32_t init_bf16_bits(uint32_t w) {
 }
 // 16-byte vector v of the initial row (elements [v*E, v*E + E) with E = 4
 // fp32 or 8 bf16).
+// Consecutive outputs of the stream are seeded base + (c+1)*gamma, so the
+// states of one vector's outputs differ by gamma and follow by addition
+// (mod 2^64: the same values as one multiply each).
 __device__ __forceinline__ u32x4 init_vec(uint64_t base, int v, int dtype) {
     u32x4 out;
     if (dtype == HTL_F32) {
-        uint64_t r0 = row_word_pair(base, 2 * v);
-        uint64_t r1 = row_word_pair(base, 2 * v + 1);
+        const uint64_t z0 = base + (uint64_t)(2 * v + 1) * kGamma;
+        const uint64_t r0 = mix64(z0);
+        const uint64_t r1 = mix64(z0 + kGamma);
         out.x = __float_as_uint(init_f32((uint32_t)(r0 >> 32)));
         out.y = __float_as_uint(init_f32((uint32_t)r0));
         out.z = __float_as_uint(init_f32((uint32_t)(r1 >> 32)));
         out.w = __float_as_uint(init_f32((uint32_t)r1));
     } else {
         uint32_t o[4];
+        uint64_t z = base + (uint64_t)(4 * v + 1) * kGamma;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint64_t r = row_word_pair(base, 4 * v + q);
+        for (int q = 0; q < 4; ++q, z += kGamma) {
+            const uint64_t r = mix64(z);
             o[q] = init_bf16_bits((uint32_t)(r >> 32)) | (init_bf16_bits((uint32_t)r) << 16);
         }
         out.x = o[0]; out.y = o[1]; out.z = o[2]; out.w = o[3];

@@ -35,9 +35,25 @@ def _check_forward(htl, orc, table, otab, keys_np, res, offsets_np=None, out_dty
         if table.dtype == htl.BF16 and out_dtype == "f32":
             want = orc.bf16_bits_to_f32(want)
         assert np.array_equal(got, want)
-    else:
+    elif table.dtype == htl.BF16:
+        # bf16 rows: every fp32 partial sum is exact, so the sums are bit-exact
         od = orc.BF16 if out_dtype == "bf16" else orc.F32
         assert np.array_equal(to_np(out), otab.gather_pool(keys_np, offsets_np, od))
+    else:
+        _check_f32_pool(orc, otab, keys_np, offsets_np, to_np(out))
+
+
+def _check_f32_pool(orc, otab, keys_np, offsets_np, got):
+    # fp32 rows summed in fp32 in an unspecified order: within 1e-5 of the
+    # bag's sum of |row| (the summation-error scale), against fp64 sums
+    ref = otab.gather_pool(keys_np, offsets_np, orc.F32).astype(np.float64)
+    rows = np.abs(otab.gather(keys_np).astype(np.float64))
+    nz = np.diff(offsets_np) > 0
+    absum = np.zeros_like(ref)
+    absum[nz] = np.add.reduceat(rows, offsets_np[:-1][nz], axis=0)
+    got = got.astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-5 * absum)
+    assert not got[~nz].any()
 
 
 @pytest.mark.parametrize("n", [0, 1, 2047, 2048, 2049, 6144 + 5, 100_003, 1 << 20])
@@ -138,3 +154,35 @@ def test_fused_lookup_reserved_keys(htl, orc):
     o = to_np(out)
     assert np.all(o[keys_np < 0] == 0)
     assert np.array_equal(o[keys_np == 5], orc.init_rows(keys_np[keys_np == 5], 8, orc.F32))
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "adam", "dim6", "growable"])
+@pytest.mark.parametrize("pooled", [False, True])
+def test_fused_lookup_leaves_initial_rows_in_the_table(htl, orc, kind, pooled):
+    # after the call, every unique key's row in the table (read back at the
+    # slot the call returned) is the oracle's row, for tables of each kind
+    dtype = "bf16" if kind == "bf16" else "f32"
+    dim = 6 if kind == "dim6" else 32
+    table = htl.Table(17, dim, dtype, adam=(kind == "adam"), growable=(kind == "growable"))
+    otab = orc.Table(1 << 17, dim, orc.BF16 if dtype == "bf16" else orc.F32)
+    rng = np.random.default_rng(3)
+    pre = rng.integers(0, 1 << 40, 20_000).astype(np.int64)
+    table.find_or_insert(torch.from_numpy(np.unique(pre)).cuda())
+    otab.find_or_insert(np.unique(pre))
+    keys_np = np.concatenate([pre[:10_000], rng.integers(0, 1 << 40, 60_000)]).astype(np.int64)
+    keys_np = keys_np[rng.permutation(keys_np.size)]
+    offsets_np = None
+    offsets = None
+    if pooled:
+        lens = rng.integers(0, 9, 12_000)
+        offsets_np = np.zeros(lens.size + 1, dtype=np.int32)
+        np.cumsum(lens, out=offsets_np[1:])
+        keys_np = keys_np[:int(offsets_np[-1])]
+        offsets = torch.from_numpy(offsets_np).cuda()
+    res = htl.lookup(table, torch.from_numpy(keys_np).cuda(), step=1, offsets=offsets, fused=True)
+    _check_forward(htl, orc, table, otab, keys_np, res, offsets_np=offsets_np,
+                   out_dtype=dtype if pooled else None, step=1)
+    _, uniq, _, nu, slots, _ = res
+    U = int(nu.item())
+    rows = htl.gather(table, slots[:U].contiguous())
+    assert np.array_equal(to_np(rows), otab.gather(to_np(uniq)[:U]))
