@@ -17,6 +17,7 @@ from typing import Optional
 import torch
 
 from ._binding import (  # noqa: F401
+    DEDUP_BINS_ONLY, DEDUP_DEVICE_SET, DEDUP_ONE_TILE, DEDUP_TWO_STAGE_BINS, DedupPlan,
     ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, GROWABLE, HTLError, INSERTED, LIB_PATH,
     copy_probe,
     META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
@@ -24,8 +25,10 @@ from ._binding import (  # noqa: F401
     table_tensor,
 )
 
+from .pipeline import LookupPipeline, PipelineBatch  # noqa: F401
+
 __all__ = [
-    "Table", "dedup_unique_inverse", "gather", "gather_pool", "segment_sum", "rowwise_adam",
+    "Table", "DedupPlan", "LookupPipeline", "PipelineBatch", "dedup_unique_inverse", "gather", "gather_pool", "segment_sum", "rowwise_adam",
     "segment_sum_adam", "lookup", "lookup_fused", "lookup_slots", "lib", "release_workspaces", "HTLError", "FOUND", "INSERTED", "FULL", "RESERVED", "NOT_FOUND", "ERASED",
 ]
 

@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhtl.so")
+# HTL_LIB names another build of the library (the sanitizer build, say)
+LIB_PATH = os.environ.get("HTL_LIB") or os.path.join(_HERE, "libhtl.so")
 
 HTL_OK, HTL_ERR_INVALID, HTL_ERR_NOMEM, HTL_ERR_DEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
@@ -66,6 +67,11 @@ _SIGNATURES = {
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_unique_inverse_ordered": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
+    "dedup_plan_create": [ctypes.POINTER(_P)],
+    "dedup_plan_destroy": [_P],
+    "dedup_plan_stats": [_P, _P],
+    "dedup_plan_choose": [_P, _I64],
+    "dedup_unique_inverse_adaptive": [_P, _P, _I64, _P, _P, _P, _P, _SZ, _P],
     "dedup_noalloc_max_keys": [],
     "dedup_unique_inverse_noalloc": [_P, _I64, _P, _P, _P, _P],
     "emb_gather_pool": [_P, _P, _P, _I64, _P, _I64, _I32, _P, _P],
@@ -102,6 +108,8 @@ def lib() -> ctypes.CDLL:
                 f.restype = _SZ
             elif name == "dedup_noalloc_max_keys":
                 f.restype = _I64
+            elif name == "dedup_plan_choose":
+                f.restype = ctypes.c_int32
             elif name == "htl_last_error":
                 f.restype = ctypes.c_char_p
             else:
@@ -355,6 +363,55 @@ class Table:
         v = _View()
         _check(lib().ht_view(self._h, ctypes.byref(v)))
         return v
+
+
+DEDUP_ONE_TILE, DEDUP_TWO_STAGE_BINS, DEDUP_BINS_ONLY, DEDUP_DEVICE_SET = 0, 1, 2, 3
+
+
+class _DedupStats(ctypes.Structure):
+    _fields_ = [("calls", _I64), ("n", _I64), ("survivors", _I64), ("n_unique", _I64), ("path", ctypes.c_int32)]
+
+
+class DedupPlan:
+    """State of the adaptive dedup (dedup_plan_*): the statistics of its
+    previous calls, which pick the second-stage form of the next."""
+
+    def __init__(self):
+        h = _P()
+        _check(lib().dedup_plan_create(ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(lib().dedup_plan_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stats(self) -> dict:
+        v = _DedupStats()
+        _check(lib().dedup_plan_stats(self._h, ctypes.byref(v)))
+        return {"calls": v.calls, "n": v.n, "survivors": v.survivors, "n_unique": v.n_unique, "path": v.path}
+
+    def choose(self, n: int) -> int:
+        return int(lib().dedup_plan_choose(self._h, n))
+
+    def dedup(self, keys: torch.Tensor):
+        """(unique, inverse, n_unique) as dedup_unique_inverse, adaptively."""
+        keys = _dev(keys, torch.int64, "keys")
+        n = keys.numel()
+        unique = torch.empty(max(n, 1), dtype=torch.int64, device=keys.device)
+        inverse = torch.empty(n, dtype=torch.int32, device=keys.device)
+        n_unique = torch.empty(1, dtype=torch.int64, device=keys.device)
+        nb = lib().dedup_workspace_bytes(n)
+        ws = _workspace("dedup", nb, keys.device)
+        _check(lib().dedup_unique_inverse_adaptive(self._h, _ptr(keys), n, _ptr(unique), _ptr(inverse),
+                                                   _ptr(n_unique), _ptr(ws), nb, _stream()))
+        return unique, inverse, n_unique
 
 
 def dedup_unique_inverse(keys: torch.Tensor, ordered: bool = False):

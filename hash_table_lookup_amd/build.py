@@ -38,30 +38,47 @@ def _hipcc() -> str:
     return p
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is built as usual): a library for checking the host side --
+# argument checks, workspace layouts, table bookkeeping -- under the
+# sanitizers, loaded in place of libhtl.so through HTL_LIB with the clang
+# ASan runtime preloaded.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_BUILD_DIR = os.path.join(HERE, "_build_san")
+SAN_LIB_PATH = os.path.join(HERE, "libhtl_san.so")
+
+
+def _compile(src: str, san: bool = False) -> str:
+    obj = os.path.join(SAN_BUILD_DIR if san else BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    flags = [f for f in HIPCC_FLAGS if not (san and f == "-O3")] + (["-O1", "-g"] + SAN_FLAGS if san else [])
+    cmd = [_hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    """Compile every HIP source and link libhtl.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = True, sanitize: bool = False) -> str:
+    """Compile every HIP source and link libhtl.so (sanitize: libhtl_san.so,
+    host code under ASan + UBSan); returns its path."""
+    out_dir, lib = (SAN_BUILD_DIR, SAN_LIB_PATH) if sanitize else (BUILD_DIR, LIB_PATH)
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if sanitize:
+        cmd[3:3] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(jobs=int(sys.argv[1]) if len(sys.argv) > 1 else 8)
+    args = [a for a in sys.argv[1:] if a != "--sanitize"]
+    build(jobs=int(args[0]) if args else 8, sanitize="--sanitize" in sys.argv)

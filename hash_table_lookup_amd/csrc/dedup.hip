@@ -68,6 +68,10 @@
 // key -1 at index 2^30, stay int32); with n < 2^30 a slot is always free.
 // Every int64 is a valid key: the value -1, which both sets use as their
 // empty marker, is carried out of band.
+#include <atomic>
+#include <cstring>
+#include <new>
+
 #include "lookup.h"
 #include "scan.h"
 #include "tile_dedup.h"
@@ -289,6 +293,13 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_compose(const uint16_t* 
 }
 
 __global__ void k_write_zero(int64_t* p) { *p = 0; }
+
+// Stage 2 without stage 1: every tile's "survivors" are its keys, as many
+// as the tile holds.
+__global__ void k_tile_lengths(int32_t* __restrict__ tu_count, int64_t n, int64_t ntiles) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * blockDim.x)
+        tu_count[t] = (int32_t)(n - t * kTile < kTile ? n - t * kTile : kTile);
+}
 
 // ------------------------------------------------ partitioned stage 2 ----
 constexpr int kPartMinLog2 = 8;               // bins: 2^8 .. 2^12
@@ -789,7 +800,8 @@ __global__ __launch_bounds__(kTileThreads) void k_part_finish(
 #pragma unroll
         for (int u = 0; u < kPerT; ++u) {
             const int64_t i = b0 + u * kTileThreads + threadIdx.x;
-            lo[u] = local[i < n ? i : n - 1];
+            const int64_t ic = i < n ? i : n - 1;
+            lo[u] = local ? local[ic] : (uint16_t)(ic - b0);   // no stage 1: every ID is its own survivor
         }
 #pragma unroll
         for (int u = 0; u < kPerT; ++u) {
@@ -822,14 +834,33 @@ size_t dedup_workspace_bytes(int64_t n) {
 
 }  // extern "C"
 
-// Stage 2 path: HTL_DEDUP_PATH=set forces the device set for every size;
-// HTL_DEDUP_BIN_MAX lowers the distinct keys a bin may hold in LDS (to test
-// the device-memory redo).
-static bool use_part_path(bool ordered, int64_t n) {
-    if (ordered || n <= kTile || n > kPartMaxN) return false;
-    const char* e = getenv("HTL_DEDUP_PATH");
-    return !(e && std::string(e) == "set");
+// Stage-2 forms.  The default for a batch (N-based, and what the adaptive
+// call starts from): one tile -> kOneTile; unordered 2^11 < n <= 2^23 ->
+// kBins; the ordered mode and larger batches -> kSet.  HTL_DEDUP_PATH
+// forces a form where it applies: "set" (any size), "bins" / "bins_only"
+// (unordered 2^11 < n <= 2^23).  HTL_DEDUP_BIN_MAX lowers the distinct keys
+// a bin may hold in LDS (to test the device-memory redo).
+enum DedupPath { kOneTile = HTL_DEDUP_ONE_TILE, kBins = HTL_DEDUP_TWO_STAGE_BINS, kBinsOnly = HTL_DEDUP_BINS_ONLY,
+                 kSet = HTL_DEDUP_DEVICE_SET };
+
+static bool bins_allowed(bool ordered, int64_t n) { return !ordered && n > kTile && n <= kPartMaxN; }
+
+static int default_path(bool ordered, int64_t n) {
+    if (n <= kTile) return kOneTile;
+    return bins_allowed(ordered, n) ? kBins : kSet;
 }
+
+static int forced_path(bool ordered, int64_t n, int chosen) {
+    if (n <= kTile) return kOneTile;
+    const char* e = getenv("HTL_DEDUP_PATH");
+    if (!e) return chosen;
+    const std::string v(e);
+    if (v == "set") return kSet;
+    if (bins_allowed(ordered, n) && v == "bins") return kBins;
+    if (bins_allowed(ordered, n) && v == "bins_only") return kBinsOnly;
+    return chosen;
+}
+
 static int bin_max_keys() {
     const char* e = getenv("HTL_DEDUP_BIN_MAX");
     if (!e) return kBinMax;
@@ -837,8 +868,51 @@ static int bin_max_keys() {
     return v < 0 ? 0 : (v > kBinMax ? kBinMax : v);
 }
 
+// Statistics of one call, for the adaptive choice of the next: written by
+// one workgroup at the end of the call into pinned host memory (seqlock:
+// seq odd while the fields are being written).
+struct DedupStatsDev {
+    volatile int64_t seq;
+    volatile int64_t n;
+    volatile int64_t survivors;
+    volatile int64_t n_unique;
+    volatile int64_t path;
+};
+
+// survivors: the sum of per-tile counts (stage 1), or n (no stage 1).
+__global__ __launch_bounds__(1024) void k_dedup_stats(DedupStatsDev* st, int64_t call, int64_t n, int path,
+                                                      const int32_t* __restrict__ tu_count, int64_t ntiles,
+                                                      const int64_t* __restrict__ n_unique) {
+    __shared__ int64_t s_part[1024 / 64];
+    int64_t sum = 0;
+    if (tu_count)
+        for (int64_t t = threadIdx.x; t < ntiles; t += 1024) sum += tu_count[t];
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane_id() == 0) s_part[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t tot = 0;
+        for (int w = 0; w < 1024 / 64; ++w) tot += s_part[w];
+        const int64_t u = *n_unique;
+        st->seq = 2 * call - 1;
+        __threadfence_system();
+        st->n = n;
+        st->survivors = tu_count ? tot : (path == kOneTile ? u : n);
+        st->n_unique = u;
+        st->path = path;
+        __threadfence_system();
+        st->seq = 2 * call;
+    }
+}
+
+struct StatsSink {
+    DedupStatsDev* dev = nullptr;
+    int64_t call = 0;
+};
+
 static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
-                           int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream, DedupRun* split) {
+                           int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream, DedupRun* split,
+                           bool raw, const StatsSink& sink) {
     PartWs w = part_layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
     const int64_t ntiles = ceil_div(n, kTile);
@@ -846,12 +920,18 @@ static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int6
     const size_t bin_lds = (size_t)P * 4;
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
     static_assert((1 << kPartMaxLog2) <= 4 * kBaseThreads, "one-workgroup bin prefix");
-    hipLaunchKernelGGL(k_dedup_tile<false>, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys, w.tu_count,
-                       w.local, (int32_t*)nullptr, (int64_t*)nullptr, SetClear{});
-    hipLaunchKernelGGL(k_part_count, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count, ntiles,
+    // raw: no stage 1 -- the tiles' survivors are their keys, in place
+    const int64_t* tkeys = raw ? keys : w.tu_keys;
+    const uint16_t* local = raw ? nullptr : w.local;
+    if (raw)
+        hipLaunchKernelGGL(k_tile_lengths, dim3(grid_for(ntiles, 256)), dim3(256), 0, stream, w.tu_count, n, ntiles);
+    else
+        hipLaunchKernelGGL(k_dedup_tile<false>, dim3(gt), dim3(kTileThreads), 0, stream, keys, n, w.tu_keys,
+                           w.tu_count, w.local, (int32_t*)nullptr, (int64_t*)nullptr, SetClear{});
+    hipLaunchKernelGGL(k_part_count, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, tkeys, w.tu_count, ntiles,
                        w.tpr, w.plog2, w.cnt);
     hipLaunchKernelGGL(k_col_scan, dim3(P / kColBins), dim3(1024), 0, stream, w.cnt, w.rows, w.plog2, w.btotal);
-    hipLaunchKernelGGL(k_part_scatter, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, w.tu_keys, w.tu_count,
+    hipLaunchKernelGGL(k_part_scatter, dim3(w.rows), dim3(kRowThreads), bin_lds, stream, tkeys, w.tu_count,
                        ntiles, w.cnt, w.btotal, w.rows, w.tpr, w.plog2, w.ent);
     hipLaunchKernelGGL(k_part_dedup, dim3(P), dim3(kBinThreads), 0, stream, w.ent, w.btotal, w.base, bin_max_keys(),
                        w.tu_l, w.ustage, w.ucount, w.fb_keys, w.fb_ids);
@@ -860,19 +940,23 @@ static htl_status run_part(const char* who, const int64_t* keys, int64_t n, int6
     // split: the packing only (the compose runs after find-or-insert)
     const unsigned grid = split ? P : P + gt;
     hipLaunchKernelGGL(k_part_finish, dim3(grid), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
-                       w.ucount, w.uoff, unique, n_unique_dev, w.tu_keys, w.tu_count, w.tu_l, w.local, n, inverse, P,
+                       w.ucount, w.uoff, unique, n_unique_dev, tkeys, w.tu_count, w.tu_l, local, n, inverse, P,
                        (const int32_t*)nullptr, (int32_t*)nullptr);
-    if (split) *split = DedupRun{kRunPart, n, ws};
+    if (sink.dev)
+        hipLaunchKernelGGL(k_dedup_stats, dim3(1), dim3(1024), 0, stream, sink.dev, sink.call, n,
+                           raw ? (int)kBinsOnly : (int)kBins, raw ? (const int32_t*)nullptr : w.tu_count, ntiles,
+                           (const int64_t*)n_unique_dev);
+    if (split) *split = DedupRun{kRunPart, n, ws, raw ? keys : nullptr};
     return check_launch(who);
 }
 
 static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, int64_t n, int64_t* unique,
                             int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream,
-                            DedupRun* split = nullptr) {
+                            DedupRun* split = nullptr, int path = -1, const StatsSink& sink = StatsSink{}) {
     clear_error();
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 30), std::string(who) + ": n must be in [0, 2^30)");
     HTL_REQUIRE(n_unique_dev && aligned(n_unique_dev, 8), std::string(who) + ": null or misaligned n_unique_dev");
-    if (split) *split = DedupRun{kRunDone, n, ws};
+    if (split) *split = DedupRun{kRunDone, n, ws, nullptr};
     if (n == 0) {
         hipLaunchKernelGGL(k_write_zero, dim3(1), dim3(1), 0, stream, n_unique_dev);
         return check_launch(who);
@@ -880,16 +964,22 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     HTL_REQUIRE(keys && unique && inverse && ws, std::string(who) + ": null pointer");
     HTL_REQUIRE(aligned(keys, 8) && aligned(unique, 8) && aligned(inverse, 4) && aligned(ws, 256),
                 std::string(who) + ": misaligned pointer");
-    if (use_part_path(ordered, n))
-        return run_part(who, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream, split);
+    if (path < 0) path = default_path(ordered, n);
+    path = forced_path(ordered, n, path);
+    if (path == kBins || path == kBinsOnly)
+        return run_part(who, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream, split, path == kBinsOnly,
+                        sink);
     DedupWs w = layout(n, (char*)ws);
     HTL_REQUIRE(ws_bytes >= w.bytes, std::string(who) + ": workspace too small");
-    if (n <= kTile) {
+    if (path == kOneTile) {
         // A batch of one tile: the LDS stage alone is the answer (one
         // launch, no device set to clear), in first-occurrence order, which
         // both modes accept.  Nothing is left for a split's second half.
         hipLaunchKernelGGL(k_dedup_tile<true>, dim3(1), dim3(kTileThreads), 0, stream, keys, n, unique,
                            (int32_t*)nullptr, (uint16_t*)nullptr, inverse, n_unique_dev, SetClear{});
+        if (sink.dev)
+            hipLaunchKernelGGL(k_dedup_stats, dim3(1), dim3(1024), 0, stream, sink.dev, sink.call, n, (int)kOneTile,
+                               (const int32_t*)nullptr, (int64_t)1, (const int64_t*)n_unique_dev);
         return check_launch(who);
     }
     const int64_t ntiles = ceil_div(n, kTile);
@@ -917,8 +1007,11 @@ static htl_status run_dedup(const char* who, bool ordered, const int64_t* keys, 
     else
         hipLaunchKernelGGL(k_dedup_assign<false>, dim3(gt), dim3(kGlobalThreads), 0, stream, w.tu_keys, w.tu_count,
                            w.tu_slot, w.tu_own, ntiles, w.set_owner, w.tile_off, w.set_ids, unique, n_unique_dev);
+    if (sink.dev)
+        hipLaunchKernelGGL(k_dedup_stats, dim3(1), dim3(1024), 0, stream, sink.dev, sink.call, n, (int)kSet,
+                           (const int32_t*)w.tu_count, ntiles, (const int64_t*)n_unique_dev);
     if (split) {
-        *split = DedupRun{kRunSet, n, ws};
+        *split = DedupRun{kRunSet, n, ws, nullptr};
         return check_launch(who);
     }
     hipLaunchKernelGGL(k_dedup_compose, dim3(gt), dim3(kTileThreads), 0, stream, w.local, n, w.tu_count, w.tu_slot,
@@ -941,9 +1034,12 @@ htl_status dedup_compose(const char* who, const DedupRun& run, const int32_t* sl
     const unsigned gt = grid_for(ntiles, 1, 1 << 16);
     if (run.path == kRunPart) {
         PartWs w = part_layout(n, (char*)run.ws);
+        // raw_keys: no stage 1 ran; the survivors are the keys themselves
+        const int64_t* tkeys = run.raw_keys ? run.raw_keys : w.tu_keys;
+        const uint16_t* local = run.raw_keys ? nullptr : w.local;
         hipLaunchKernelGGL(k_part_finish, dim3(gt), dim3(kTileThreads), 0, stream, w.ustage, w.base, w.plog2,
-                           w.ucount, w.uoff, (int64_t*)nullptr, (int64_t*)nullptr, w.tu_keys, w.tu_count, w.tu_l,
-                           w.local, n, inverse, 0, slots, sid);
+                           w.ucount, w.uoff, (int64_t*)nullptr, (int64_t*)nullptr, tkeys, w.tu_count, w.tu_l, local,
+                           n, inverse, 0, slots, sid);
     } else {
         DedupWs w = layout(n, (char*)run.ws);
         hipLaunchKernelGGL(k_dedup_compose, dim3(gt), dim3(kTileThreads), 0, stream, w.local, n, w.tu_count,
@@ -953,6 +1049,42 @@ htl_status dedup_compose(const char* who, const DedupRun& run, const int32_t* sl
 }
 
 }  // namespace htl
+
+// ------------------------------------------------------- adaptive unique --
+// The TensorFlow article's section 3.6: a heuristic picks the Unique
+// implementation.  Here the plan remembers the statistics of its previous
+// calls (written by the device into pinned host memory at the end of each
+// call, read by the host at the next call without waiting for the device),
+// and picks the stage-2 form from the batch size and the duplicates that
+// stage 1 found in the last measured batch:
+//   n <= 2^11                 one tile (one launch);
+//   2^11 < n <= 2^23          hash bins, without stage 1 when too few
+//                             duplicates were found for any key to overfill
+//                             a bin, else with it;
+//   n > 2^23                  the device-wide set.
+// Why that bound: stage 1 keeps one copy of a key per tile, so it removes at
+// least c - ntiles copies of a key that occurs c times; a measured duplicate
+// share d = (n - survivors) / n therefore bounds the hottest key by
+// d n + ntiles.  Without stage 1 every copy of a key lands in its one bin,
+// whose workgroup dedups them in turn; stage 1 is skipped only while
+// d n + ntiles <= 3 n / P (P bins), so no key can bring a bin past about
+// four times the mean load.  (On the sweep of hash_table_lookup_amd.tune:
+// skipping saves 12-17% at 2^20..2^23 keys when the tiles hold almost no
+// duplicates, and costs 3-14x under Zipf skew, where a hot key fills one bin.)
+// A batch run without stage 1 cannot measure d, so while the plan skips it,
+// every kRemeasure-th call runs both stages again to renew the measurement.
+struct htl_dedup_plan {
+    DedupStatsDev* host = nullptr;   // pinned, mapped
+    DedupStatsDev* dev = nullptr;    // its device address
+    int64_t calls = 0;               // calls enqueued with statistics
+    mutable double dup = -1.0;       // last measured (n - survivors) / n (-1: none yet)
+    mutable int64_t kept_call = 0;   // the call that measured it
+    int device = -1;
+};
+
+namespace {
+constexpr int64_t kRemeasure = 8;
+}
 
 extern "C" {
 
@@ -965,6 +1097,95 @@ htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t*
                                         int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
     return run_dedup("dedup_unique_inverse_ordered", true, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes,
                      stream);
+}
+
+htl_status dedup_plan_create(htl_dedup_plan** plan) {
+    clear_error();
+    HTL_REQUIRE(plan != nullptr, "dedup_plan_create: null plan");
+    *plan = nullptr;
+    htl_dedup_plan* p = new (std::nothrow) htl_dedup_plan();
+    if (!p) return fail(HTL_ERR_NOMEM, "dedup_plan_create: out of host memory");
+    void* h = nullptr;
+    if (hipHostMalloc(&h, sizeof(DedupStatsDev), hipHostMallocMapped) != hipSuccess || !h) {
+        delete p;
+        return fail(HTL_ERR_NOMEM, "dedup_plan_create: hipHostMalloc of the statistics failed");
+    }
+    std::memset(h, 0, sizeof(DedupStatsDev));
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || !d) {
+        (void)hipHostFree(h);
+        delete p;
+        return fail(HTL_ERR_DEVICE, "dedup_plan_create: no device address for the pinned statistics");
+    }
+    p->host = (DedupStatsDev*)h;
+    p->dev = (DedupStatsDev*)d;
+    (void)hipGetDevice(&p->device);
+    *plan = p;
+    return HTL_OK;
+}
+
+htl_status dedup_plan_destroy(htl_dedup_plan* plan) {
+    clear_error();
+    if (!plan) return HTL_OK;
+    // the device may still write the statistics of an enqueued call
+    HTL_HIP(hipDeviceSynchronize());
+    (void)hipHostFree(plan->host);
+    delete plan;
+    return HTL_OK;
+}
+
+htl_status dedup_plan_stats(const htl_dedup_plan* plan, htl_dedup_stats* out) {
+    clear_error();
+    HTL_REQUIRE(plan && out, "dedup_plan_stats: null argument");
+    // seqlock read of what the device last wrote (no wait for the device)
+    for (int attempt = 0; attempt < 64; ++attempt) {
+        const int64_t s1 = plan->host->seq;
+        if (s1 & 1) continue;
+        std::atomic_thread_fence(std::memory_order_acquire);
+        htl_dedup_stats v;
+        v.calls = s1 / 2;
+        v.n = plan->host->n;
+        v.survivors = plan->host->survivors;
+        v.n_unique = plan->host->n_unique;
+        v.path = (int32_t)plan->host->path;
+        std::atomic_thread_fence(std::memory_order_acquire);
+        if (plan->host->seq == s1) {
+            *out = v;
+            return HTL_OK;
+        }
+    }
+    *out = htl_dedup_stats{};   // being written: report nothing seen yet
+    return HTL_OK;
+}
+
+int32_t dedup_plan_choose(const htl_dedup_plan* plan, int64_t n) {
+    if (n <= kTile) return kOneTile;
+    if (n > kPartMaxN) return kSet;
+    if (!plan) return kBins;
+    htl_dedup_stats v{};
+    if (dedup_plan_stats(plan, &v) == HTL_OK && v.calls > plan->kept_call && v.n > 0 && v.path != kBinsOnly) {
+        plan->dup = (double)(v.n - v.survivors) / (double)v.n;    // a fresh measurement of stage 1
+        plan->kept_call = v.calls;
+    }
+    if (plan->dup < 0) return kBins;
+    const double P = (double)((int64_t)1 << part_layout(n, nullptr).plog2);
+    const double ntiles = (double)ceil_div(n, kTile);
+    if (plan->dup * (double)n + ntiles > 3.0 * (double)n / P) return kBins;
+    // skipping stage 1: every kRemeasure-th call measures it again
+    return ((plan->calls + 1) % kRemeasure == 0) ? kBins : kBinsOnly;
+}
+
+htl_status dedup_unique_inverse_adaptive(htl_dedup_plan* plan, const int64_t* keys, int64_t n, int64_t* unique,
+                                         int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(plan != nullptr, "dedup_unique_inverse_adaptive: null plan");
+    const int path = dedup_plan_choose(plan, n);
+    StatsSink sink{plan->dev, plan->calls + 1};
+    const htl_status st = run_dedup("dedup_unique_inverse_adaptive", false, keys, n, unique, inverse, n_unique_dev,
+                                    ws, ws_bytes, stream, nullptr, path, n > 0 ? sink : StatsSink{});
+    if (st == HTL_OK && n > 0) ++plan->calls;
+    return st;
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ struct DedupRun {
     int path;    // kRunDone: nothing left (a one-tile batch, or n == 0)
     int64_t n;
     void* ws;
+    const int64_t* raw_keys;   // not null: stage 1 was skipped; the survivors are these keys
 };
 
 // First half: the unordered dedup up to unique[] and its count U (device).

@@ -54,7 +54,10 @@ typedef enum {
     HTL_ERR_DEVICE = 3   /* HIP runtime or launch error */
 } htl_status;
 
-typedef enum { HTL_F32 = 0, HTL_BF16 = 1 } htl_dtype;
+/* The last enumerator gives the type the whole int range, so a value out of
+ * range passed from C is a checked argument error, not undefined behaviour
+ * in the library's C++ (the same for htl_dedup_path below). */
+typedef enum { HTL_F32 = 0, HTL_BF16 = 1, HTL_DTYPE_RANGE_ = 0x7FFFFFFF } htl_dtype;
 
 /* Per-key status of ht_find_or_insert (uint8 each). */
 enum { HT_FOUND = 0, HT_INSERTED = 1, HT_FULL = 2, HT_RESERVED = 3 };
@@ -284,6 +287,63 @@ htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique,
 htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t* unique,
                                         int32_t* inverse, int64_t* n_unique_dev, void* ws,
                                         size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------- adaptive unique --
+ * dedup_unique_inverse_adaptive -- dedup_unique_inverse whose second stage
+ * is chosen per call by a heuristic, as the TensorFlow article's adaptive
+ * Unique is ([TF-PS] section 3.6: a heuristic picks the Unique
+ * implementation).  Same arguments, workspace (dedup_workspace_bytes(n)) and
+ * results; unique is in an unspecified order.  The plan carries the
+ * statistics of its previous calls: at the end of each call the device
+ * writes n, the number of stage-1 survivors, U and the form it ran into
+ * pinned host memory, and the next call reads them there without waiting
+ * for the device (so the choice follows the stream one or a few batches
+ * behind).  Forms (htl_dedup_path):
+ *   HTL_DEDUP_ONE_TILE        n <= 2048: one workgroup, one launch;
+ *   HTL_DEDUP_TWO_STAGE_BINS  per-tile dedup in LDS, then hash bins each
+ *                             deduplicated in LDS (2048 < n <= 2^23);
+ *   HTL_DEDUP_BINS_ONLY       the hash bins straight from the keys, no
+ *                             stage 1 -- chosen while the duplicates stage 1
+ *                             found in the plan's last measured batch (a
+ *                             share d of its keys) are too few for any key
+ *                             to overfill a bin: d n + n/2048 <= 3 n / P for
+ *                             the P bins of the batch (every copy of a key
+ *                             goes to one bin when stage 1 is skipped); a
+ *                             batch run this way cannot measure d, so every
+ *                             8th call of the plan runs both stages again;
+ *   HTL_DEDUP_DEVICE_SET      per-tile dedup, then one device-wide set
+ *                             (n > 2^23).
+ * The first call of a plan, knowing nothing, takes the N-based default
+ * (two-stage bins, or the form its size requires).  A plan belongs to one
+ * device and one stream at a time; calls on it must be ordered.
+ *
+ * dedup_plan_create allocates the plan (a few bytes of pinned host memory);
+ * dedup_plan_destroy synchronises the device, then frees it (null: no-op).
+ * dedup_plan_stats returns what the device last reported (calls = 0 before
+ * the first report lands); dedup_plan_choose the form the plan would take
+ * for a batch of n keys now. */
+typedef struct htl_dedup_plan htl_dedup_plan;
+typedef enum {
+    HTL_DEDUP_ONE_TILE = 0,
+    HTL_DEDUP_TWO_STAGE_BINS = 1,
+    HTL_DEDUP_BINS_ONLY = 2,
+    HTL_DEDUP_DEVICE_SET = 3,
+    HTL_DEDUP_PATH_RANGE_ = 0x7FFFFFFF
+} htl_dedup_path;
+typedef struct {
+    int64_t calls;      /* calls whose statistics have landed */
+    int64_t n;          /* keys of the last of them */
+    int64_t survivors;  /* keys that left stage 1 (n when stage 1 was skipped) */
+    int64_t n_unique;   /* U */
+    int32_t path;       /* the htl_dedup_path it ran */
+} htl_dedup_stats;
+htl_status dedup_plan_create(htl_dedup_plan** plan);
+htl_status dedup_plan_destroy(htl_dedup_plan* plan);
+htl_status dedup_plan_stats(const htl_dedup_plan* plan, htl_dedup_stats* out);
+int32_t dedup_plan_choose(const htl_dedup_plan* plan, int64_t n);
+htl_status dedup_unique_inverse_adaptive(htl_dedup_plan* plan, const int64_t* keys, int64_t n, int64_t* unique,
+                                         int32_t* inverse, int64_t* n_unique_dev, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
 
 /* dedup_unique_inverse_noalloc -- dedup_unique_inverse with no workspace
  * argument and no allocation, for callers that cannot allocate device memory

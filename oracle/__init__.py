@@ -18,6 +18,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# The same source built with AddressSanitizer and UndefinedBehaviorSanitizer;
+# HTL_ORACLE_LIB loads it (with gcc's ASan runtime preloaded) in place of
+# liboracle.so.
+SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
 
 FOUND, INSERTED, FULL, RESERVED = 0, 1, 2, 3
 NOT_FOUND, ERASED = 0, 1
@@ -25,15 +29,20 @@ F32, BF16 = 0, 1
 EMPTY_KEY, TOMBSTONE_KEY = -1, -2
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with g++ (single-threaded, no FP contraction)."""
-    if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
-        tmp = LIB_PATH + ".tmp"
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile liboracle.so with g++ (single-threaded, no FP contraction);
+    sanitize: liboracle_san.so under ASan + UBSan."""
+    out = SAN_LIB_PATH if sanitize else LIB_PATH
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp"
         cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
                "-Wall", "-Wextra", _SRC, "-o", tmp]
+        if sanitize:
+            cmd[3:3] = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=undefined"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -47,9 +56,12 @@ _U32 = ctypes.c_uint32
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(LIB_PATH)
+        path = os.environ.get("HTL_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            path = LIB_PATH
+        L = ctypes.CDLL(path)
         sig = {
             "orc_mix64": (_U64, [_U64]),
             "orc_splitmix64": (None, [_U64, _I64, _P]),
@@ -72,6 +84,8 @@ def lib():
                                 ctypes.c_float, ctypes.c_float, _I64]),
             "orc_adam_arrays": (None, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, _I64]),
+            "orc_adam_arrays_f32": (None, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_float, _I64]),
             "orc_live": (_I64, [_P, _P, _P]),
             "orc_lru_victims": (_I64, [_P, _I64, _I64, _P]),
         }
@@ -161,6 +175,18 @@ def adam_arrays(theta, m, v, g, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, step=1):
     gg = _c(g, np.float32)
     assert th.shape == mm.shape == vv.shape == gg.shape
     lib().orc_adam_arrays(_ptr(th), _ptr(mm), _ptr(vv), _ptr(gg), th.size, lr, b1, b2, eps, step)
+    return th, mm, vv
+
+
+def adam_arrays_f32(theta, m, v, g, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, step=1):
+    """One Adam step evaluated in fp32, each operation rounded as written;
+    returns (theta, m, v)."""
+    th = np.array(theta, dtype=np.float32, copy=True, order="C")
+    mm = np.array(m, dtype=np.float32, copy=True, order="C")
+    vv = np.array(v, dtype=np.float32, copy=True, order="C")
+    gg = _c(g, np.float32)
+    assert th.shape == mm.shape == vv.shape == gg.shape
+    lib().orc_adam_arrays_f32(_ptr(th), _ptr(mm), _ptr(vv), _ptr(gg), th.size, lr, b1, b2, eps, step)
     return th, mm, vv
 
 

@@ -414,6 +414,33 @@ void orc_adam_arrays(float* theta, float* m, float* v, const float* g, int64_t n
         adam_elem(theta[i], m[i], v[i], g[i], lr, b1, b2, eps, c1, c2);
 }
 
+// Adam in single precision, every operation rounded to fp32 as written (no
+// fused multiply-add: the oracle is built with -ffp-contract=off), in the
+// order of Kingma & Ba's Algorithm 1 for a table kept in fp32 (the
+// TensorFlow article, section 3.2, keeps Adam's bias terms per server; here
+// they are per-call scalars):
+//   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+//   theta = theta - lr * ((m / c1) / (sqrt(v / c2) + eps)),
+// with 1-b1, 1-b2 in fp32 and c1 = 1-b1^t, c2 = 1-b2^t formed in fp64 and
+// rounded to fp32.  sqrtf and fp32 division are correctly rounded (IEEE
+// 754), so this is one determined value per element.
+void orc_adam_arrays_f32(float* theta, float* m, float* v, const float* g, int64_t n, float lr,
+                         float b1, float b2, float eps, int64_t step) {
+    const float c1 = (float)(1.0 - std::pow((double)b1, (double)step));
+    const float c2 = (float)(1.0 - std::pow((double)b2, (double)step));
+    const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
+    for (int64_t i = 0; i < n; ++i) {
+        const float gi = g[i];
+        const float mi = b1 * m[i] + omb1 * gi;
+        const float vi = b2 * v[i] + omb2 * (gi * gi);
+        const float mh = mi / c1;
+        const float vh = vi / c2;
+        theta[i] = theta[i] - lr * (mh / (std::sqrt(vh) + eps));
+        m[i] = mi;
+        v[i] = vi;
+    }
+}
+
 // Live keys with their last_seen (MTGR section 5, compact key scanning), in
 // ascending key order.  Returns the live count; outputs may be null.
 int64_t orc_live(void* h, int64_t* keys_out, uint32_t* last_seen_out) {

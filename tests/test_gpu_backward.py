@@ -98,6 +98,31 @@ def test_adam_decoupled(htl, orc, dim, cap_log2):
         assert np.all(to_np(status)[:U] == (htl.INSERTED if step == 1 else htl.FOUND))
 
 
+@pytest.mark.parametrize("dim", [128, 6])
+def test_adam_bit_exact_against_fp32_oracle(htl, orc, dim):
+    """The GPU's Adam (fp32, contraction off, correctly rounded division and
+    square root) against the oracle's fp32 Adam in the same order, from
+    identical states (the GPU table's theta, m, v and the GPU's summed
+    gradient): theta, m and v bit for bit over three steps."""
+    w = workloads.backward(n=1 << 14, dim=dim, capacity_log2=16)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    table = htl.Table(w.capacity_log2, w.dim, "f32", adam=True)
+    keys = torch.from_numpy(w.keys).cuda()
+    grad = torch.from_numpy(w.grad).cuda()
+    for step in (1, 2, 3):
+        uniq, inv, nu = htl.dedup_unique_inverse(keys)
+        U = int(nu.item())
+        slots, _ = table.find_or_insert(uniq, n_dev=nu, step=step)
+        g = htl.segment_sum(grad, inv, nu, u_max=keys.numel())
+        sl = to_np(slots)[:U]
+        before = [to_np(htl.table_tensor(table, name))[sl] for name in ("rows", "adam_m", "adam_v")]
+        htl.rowwise_adam(table, slots[:U], g[:U], nu, lr, b1, b2, eps, step)
+        after = [to_np(htl.table_tensor(table, name))[sl] for name in ("rows", "adam_m", "adam_v")]
+        want = orc.adam_arrays_f32(*before, to_np(g)[:U], lr, b1, b2, eps, step)
+        for got, ref in zip(after, want):
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), step
+
+
 def test_adam_closed_form_first_step(htl, orc):
     # from m = v = 0, step 1 moves theta by -lr * g / (|g| + eps)
     table = htl.Table(10, 8, "f32", adam=True)

@@ -241,18 +241,28 @@ def test_duplicate_erase_reports_once(htl, orc):
     assert int((st[:100] == htl.ERASED).sum()) == 1 and st[100] == htl.ERASED
 
 
-def test_repeatable(htl, orc):
-    w = workloads.tiny(seed=3)
-    outs = []
-    for _ in range(5):
+@pytest.mark.parametrize("fused", [True, False])
+def test_repeatable(htl, orc, fused):
+    # the same batch into ten fresh tables: the unique set, every key's status
+    # and every row must come out the same each time (a lost or doubled CAS
+    # claim would change them)
+    w = workloads.tiny(seed=3, n=200_000)
+    keys = torch.from_numpy(w.keys).cuda()
+    first = None
+    for _ in range(10):
         table = htl.Table(w.capacity_log2, w.dim, w.dtype)
-        keys = torch.from_numpy(w.keys).cuda()
-        out, uniq, inv, nu, slots, status = htl.lookup(table, keys)
-        outs.append(to_np(out))
+        out, uniq, inv, nu, slots, status = htl.lookup(table, keys, fused=fused)
         U = int(nu.item())
-        assert np.all(to_np(status)[:U] == htl.INSERTED)
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+        u, st = to_np(uniq)[:U], to_np(status)[:U]
+        order = np.argsort(u)
+        got = (u[order], st[order], to_np(out))
+        assert np.all(got[1] == htl.INSERTED)
+        assert np.unique(to_np(slots)[:U]).size == U              # one slot per key
+        if first is None:
+            first = got
+        else:
+            for a, b in zip(got, first):
+                assert np.array_equal(a, b)
 
 
 def test_pool_merged_tables_small(htl, orc):

@@ -148,3 +148,15 @@ def test_noalloc_dedup_limit_checked_on_the_host(L):
     assert L.dedup_unique_inverse_noalloc(fake, (1 << 20) + 1, fake, fake, fake, None) == 1
     assert b"2^20" in L.htl_last_error()
     assert L.dedup_unique_inverse_noalloc(fake, -1, fake, fake, fake, None) == 1
+
+
+def test_adaptive_dedup_host_checks(L):
+    # no plan: refused before anything is enqueued; the choice without a plan
+    # is the batch-size default
+    fake = ctypes.c_void_p(0x1000)
+    assert L.dedup_unique_inverse_adaptive(None, fake, 10, fake, fake, fake, fake, 1 << 20, None) == 1
+    assert L.dedup_plan_stats(None, None) == 1
+    assert L.dedup_plan_destroy(None) == 0
+    assert L.dedup_plan_choose(None, 100) == 0
+    assert L.dedup_plan_choose(None, 1 << 20) == 1
+    assert L.dedup_plan_choose(None, (1 << 23) + 1) == 3

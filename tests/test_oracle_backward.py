@@ -99,3 +99,40 @@ def test_adam_array_form_matches_table_form(orc):
         for i, k in enumerate(keys):
             row, _, mk, vk = t.lookup(k)
             assert np.array_equal(row, th[i]) and np.array_equal(mk, m[i]) and np.array_equal(vk, v[i])
+
+
+def test_adam_f32_within_fp32_rounding_of_the_fp64_adam(orc):
+    # the fp32 evaluation and the fp64 one agree to within the rounding of
+    # the few fp32 operations each value goes through (2^-24 each, relative to
+    # the terms that make it up), over three steps from random states
+    rng = np.random.default_rng(11)
+    n = 50_000
+    th = rng.normal(0, 0.1, n).astype(np.float32)
+    m = rng.normal(0, 0.01, n).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-4, n)).astype(np.float32)
+    u = 2.0 ** -24
+    for step in (1, 2, 7):
+        g = rng.normal(0, 1, n).astype(np.float32)
+        t32, m32, v32 = orc.adam_arrays_f32(th, m, v, g, step=step)
+        t64, m64, v64 = orc.adam_arrays(th, m, v, g, step=step)
+        d = np.float64
+        assert np.all(np.abs(m32.astype(d) - m64) <= 4 * u * (0.9 * np.abs(m.astype(d)) + 0.1 * np.abs(g.astype(d))))
+        assert np.all(np.abs(v32.astype(d) - v64) <= 4 * u * (0.999 * v.astype(d) + 0.001 * g.astype(d) ** 2))
+        assert np.all(np.abs(t32.astype(d) - t64) <= 16 * u * (np.abs(th.astype(d)) + np.abs(t64.astype(d) - th)))
+        # and they do differ somewhere: the evaluation really is fp32
+        assert not np.array_equal(t32, t64)
+        th, m, v = t32, m32, v32
+
+
+def test_adam_f32_first_step_closed_form(orc):
+    # from m = v = 0 at t = 1: m/c1 = g and v/c2 = g^2 up to rounding, so
+    # theta moves by lr * g / (|g| + eps); a zero gradient moves nothing
+    rng = np.random.default_rng(12)
+    g = rng.normal(0, 1, 20_000).astype(np.float32)
+    g[:5] = 0.0
+    th = rng.normal(0, 0.1, g.size).astype(np.float32)
+    z = np.zeros_like(g)
+    t1, m1, v1 = orc.adam_arrays_f32(th, z, z, g, lr=1e-3, step=1)
+    want = th.astype(np.float64) - 1e-3 * g.astype(np.float64) / (np.abs(g.astype(np.float64)) + 1e-8)
+    np.testing.assert_allclose(t1, want, rtol=0, atol=3e-8)
+    assert np.array_equal(t1[:5], th[:5]) and not m1[:5].any() and not v1[:5].any()
