@@ -43,8 +43,10 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD's published peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
-# Counter-measured HBM bytes of each workload's roofline kernel, per record
-# under profiles/, with the sources that decide them: the kernel's own, and
+# Counter-measured bytes of each workload's roofline kernel (FETCH_SIZE and
+# WRITE_SIZE: what the L2s exchange with the data fabric, Infinity Cache hits
+# included, so an upper bound on HBM bytes), per record under profiles/,
+# with the sources that decide them: the kernel's own, and
 # the dedup's (the order of unique ids it produces decides how the kernel's
 # slot and row reads fall on cache lines).
 _DEDUP_SRC = ("dedup.hip", "tile_dedup.h")
@@ -77,7 +79,7 @@ def _parse():
 
 
 def _measured_traffic(workload):
-    """Counter-measured HBM bytes per launch of the workload's roofline
+    """Counter-measured L2-to-fabric bytes per launch of the workload's roofline
     kernel, or None if its sources or the dedup's changed since the counters
     were taken (or no record exists)."""
     import hashlib
