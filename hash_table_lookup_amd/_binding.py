@@ -24,7 +24,7 @@ HTL_OK, HTL_ERR_INVALID, HTL_ERR_NOMEM, HTL_ERR_DEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 FOUND, INSERTED, FULL, RESERVED = 0, 1, 2, 3
 NOT_FOUND, ERASED = 0, 1
-META_LAST_SEEN, ADAM_STATE, GROWABLE = 1, 2, 4
+META_LAST_SEEN, ADAM_STATE, GROWABLE, META_ACCESS_LOG = 1, 2, 4, 8
 EMPTY_KEY, TOMBSTONE_KEY = -1, -2
 
 _P = ctypes.c_void_p
@@ -63,6 +63,7 @@ _SIGNATURES = {
     "lru_workspace_bytes": [_P],
     "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
     "ht_rows": [_P, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
+    "ht_access_log_state": [_P, _P, _P],
     "ht_view": [_P, ctypes.POINTER(_View)],
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
@@ -190,17 +191,20 @@ class Table:
     """A dynamic embedding table living in device memory (libhtl's ht_* calls).
 
     growable=True: rows live apart from the key index, slots returned are row
-    handles, and resize() grows the index without moving rows."""
+    handles, and resize() grows the index without moving rows.
+    access_log=True (with last_seen): the table keeps an access log that
+    lets lru_select read only the oldest steps' entries."""
 
     def __init__(self, capacity_log2: int, dim: int, dtype="f32", init_seed: int = 0,
-                 last_seen: bool = False, adam: bool = False, growable: bool = False):
+                 last_seen: bool = False, adam: bool = False, growable: bool = False,
+                 access_log: bool = False):
         L = lib()
         self.capacity_log2, self.dim = capacity_log2, dim
         self.dtype = _dtype_code(dtype)
         self.init_seed = init_seed
         self.growable = growable
         flags = ((META_LAST_SEEN if last_seen else 0) | (ADAM_STATE if adam else 0)
-                 | (GROWABLE if growable else 0))
+                 | (GROWABLE if growable else 0) | (META_ACCESS_LOG if access_log else 0))
         h = _P()
         _check(L.ht_create(ctypes.byref(h), capacity_log2, dim, self.dtype,
                            init_seed & 0xFFFFFFFFFFFFFFFF, flags, _stream()))
@@ -351,6 +355,14 @@ class Table:
         _check(lib().ht_lru_select(self._h, num, den, _ptr(victims), cap, _ptr(n), _ptr(ws), nb,
                                    _stream()))
         return victims, n
+
+    def access_log_state(self) -> torch.Tensor:
+        """int64[4] on the device (ht_access_log_state): whether the log
+        serves the next lru_select (1 / 0), its head, its tail, and the
+        oldest step that may still have live keys."""
+        out = torch.empty(4, dtype=torch.int64, device=self.device)
+        _check(lib().ht_access_log_state(self._h, _ptr(out), _stream()))
+        return out
 
     def rows_view(self):
         """(device address of the rows, bytes per row): the read-only row view

@@ -58,6 +58,47 @@ struct TableDev {
     int32_t* rowid;        // growable tables: row handle of each live slot; null: row = slot
 };
 
+// ------------------------------------------------------- access log ----
+// A table created with HT_META_ACCESS_LOG records, at every find-or-insert,
+// one 8-byte entry per key it is given: (slot, step) when the call inserts
+// the key or moves its last_seen to `step`, else kLogNoSlot.  Entries go to
+// a ring in call order, so along the ring the steps never decrease.  Beside
+// the ring, one record per step (indexed by step mod kLogSteps) keeps where
+// the step's entries lie and how many live keys have last_seen == step:
+// each stamp adds one to its step and takes one from the key's previous
+// step, each erase takes one from the erased key's step.  An entry is
+// current iff last_seen[slot] still equals its step; the current entries of
+// steps <= s are exactly the live keys with last_seen <= s (a key gets one
+// entry per step it is stamped in).  The eviction choice reads the step
+// counts to find the cut step, then only the ring entries up to that
+// step's end, instead of last_seen of every slot.
+constexpr int kLogStepsLog2 = 16;
+constexpr int64_t kLogSteps = (int64_t)1 << kLogStepsLog2;
+constexpr uint32_t kLogStepMask = (uint32_t)kLogSteps - 1u;
+constexpr uint32_t kLogNoSlot = 0xFFFFFFFFu;
+constexpr int kLogBins = 256;        // per-block LDS sums of steps left / erased
+
+struct LogSeg {
+    uint32_t step;        // the step this record belongs to (0xFFFFFFFF: none yet)
+    uint32_t pad;
+    int64_t count;        // live keys with last_seen == step
+    uint64_t begin, end;  // ring positions of the step's entries (unwrapped)
+};
+
+struct LogState {
+    uint64_t head[2];     // next ring position, double-buffered by call parity
+    uint64_t tail;        // no current entry lies before it
+    uint32_t s_min;       // no live key has last_seen below it
+    int32_t bad;          // set once the log stopped covering every live key
+};
+
+struct LogDev {
+    uint64_t* entries;    // [cap]: slot | step << 32
+    LogSeg* segs;         // [kLogSteps]
+    LogState* st;
+    uint64_t cap_mask;    // cap - 1 (cap a power of two)
+};
+
 // Row-space index of a live slot.
 __device__ __forceinline__ int64_t row_of(const TableDev& T, int64_t slot) {
     return T.rowid ? (int64_t)T.rowid[slot] : slot;
@@ -107,6 +148,14 @@ struct htl_table {
     int max_capacity_log2;
     htl::VmArray vm_rows, vm_m, vm_v;   // growable tables only
     htl::RowAlloc alloc;                // handles: growable only; temporaries: any table
+    // access log (HT_META_ACCESS_LOG): device storage, and what the host
+    // knows of it
+    htl::LogDev log;
+    bool log_ok;          // false once a call broke the log's premises
+    bool log_first;       // no call logged since create / clear
+    int log_par;          // parity of the next logged call
+    bool erase_pending;   // an erase ran while max_step was erase_step
+    uint32_t erase_step;
 };
 
 namespace htl {

@@ -59,8 +59,14 @@ struct LruState {
     uint32_t pad;
     uint64_t key_prefix;  // selected biased key
     unsigned long long key_and, key_or;   // over the biased keys of the ties
+    int32_t mode;         // kModeLog: candidates from the access log (set by k_lru_log_init)
+    uint32_t pad2;
+    uint64_t win_begin, win_end;          // ring window of the log's candidates
     uint32_t hist[256 * kBinStride];
 };
+
+constexpr int kModeScan = 0;
+constexpr int kModeLog = 1;
 
 struct LruWs {
     LruState* st;
@@ -134,16 +140,87 @@ __device__ __forceinline__ int block_prefix(int& v, int* s_wave) {
 typedef uint32_t u32x4l __attribute__((ext_vector_type(4)));
 constexpr int kQuads = kPerThread / 4;
 
+//
+// With the access log serving (mode kModeLog), chunk c is instead entries
+// [c * kChunk, (c + 1) * kChunk) of the ring window: an entry is a
+// candidate iff its step is at most the cut step and last_seen of its slot
+// still equals that step; chunks past the window get count 0.
 __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nchunks,
                                                          uint32_t* __restrict__ cand_ls,
                                                          uint32_t* __restrict__ cand_slot,
                                                          int32_t* __restrict__ chunk_cnt,
-                                                         uint32_t* __restrict__ chunk_max) {
+                                                         uint32_t* __restrict__ chunk_max, int use_log, LogDev L,
+                                                         const LruState* __restrict__ st) {
     __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_max[kThreads / 64];
     __shared__ uint32_t s_ls[kChunk];
     __shared__ uint16_t s_off[kChunk];
     const int tid = threadIdx.x;
+    if (use_log && st->mode == kModeLog) {
+        const uint64_t wb = st->win_begin;
+        const int64_t W = (int64_t)(st->win_end - wb);
+        const uint32_t thr = st->ls_prefix;
+        for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+            const int64_t e0 = c * kChunk;
+            if (e0 >= W) {                       // the same in the whole block
+                if (tid == 0) {
+                    chunk_cnt[c] = 0;
+                    chunk_max[c] = 0u;
+                }
+                continue;
+            }
+            uint64_t ent[kPerThread];
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const int64_t e = e0 + j * kThreads + tid;
+                ent[j] = e < W ? L.entries[(wb + (uint64_t)e) & L.cap_mask] : ~0ull;
+            }
+            uint32_t now[kPerThread];
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const uint32_t slot = (uint32_t)ent[j], step = (uint32_t)(ent[j] >> 32);
+                // (slot < capacity always holds for entries the table wrote; the
+                // test keeps every read in bounds regardless)
+                now[j] = (slot != kLogNoSlot && (int64_t)slot < T.capacity && step <= thr) ? T.last_seen[slot]
+                                                                                           : kLsDead;
+            }
+            uint32_t live = 0;
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j)
+                if (now[j] != kLsDead && now[j] == (uint32_t)(ent[j] >> 32)) live |= 1u << j;
+            int pos = __popc(live);
+            const int total = block_prefix(pos, s_wave);
+            uint32_t my_max = 0;
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                if (live & (1u << j)) {
+                    my_max = now[j] > my_max ? now[j] : my_max;
+                    s_ls[pos] = now[j];
+                    s_off[pos] = (uint16_t)(j * kThreads + tid);
+                    ++pos;
+                }
+            }
+            for (int off = 32; off > 0; off >>= 1) {
+                const uint32_t y = __shfl_xor(my_max, off);
+                my_max = y > my_max ? y : my_max;
+            }
+            if (lane_id() == 0) s_max[tid >> 6] = my_max;
+            __syncthreads();
+            for (int j = tid; j < total; j += kThreads) {
+                cand_ls[e0 + j] = s_ls[j];
+                // the entry again (just read by this block): its slot
+                cand_slot[e0 + j] = (uint32_t)L.entries[(wb + (uint64_t)(e0 + s_off[j])) & L.cap_mask];
+            }
+            if (tid == 0) {
+                uint32_t m = 0;
+                for (int w = 0; w < kThreads / 64; ++w) m = s_max[w] > m ? s_max[w] : m;
+                chunk_cnt[c] = total;
+                chunk_max[c] = m;
+            }
+            __syncthreads();
+        }
+        return;
+    }
     const u32x4l* ls4 = reinterpret_cast<const u32x4l*>(T.last_seen);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t qbase = c * (kChunk / 4);           // first slot quad of the chunk
@@ -204,10 +281,105 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
     }
 }
 
-// One block: live count, maximum last_seen, k, and a cleared histogram.
+// Live keys of step s by its record (none if the record is another step's).
+__device__ __forceinline__ int64_t log_count(const LogDev& L, uint32_t s) {
+    const LogSeg& g = L.segs[s & kLogStepMask];
+    return g.step == s ? g.count : 0;
+}
+
+// One block, first, on a table with an access log.  If the log serves:
+// the live count from the step counts of [s_min, s_now], k, and the cut
+// step s* (the last_seen of the k-th smallest key): every live key with
+// last_seen < s* is a victim, and k_rem of those with last_seen == s*, by
+// key.  All their entries lie in the ring window [tail, end of s*).  The
+// last_seen digits are then known (ls_digits = 0: their passes skip), and
+// s_min and the tail move up to the oldest step that has live keys.  If
+// the log does not serve, the scan path runs (mode kModeScan).
+__global__ __launch_bounds__(1024) void k_lru_log_init(LruState* st, LogDev L, int par, uint32_t s_now, int64_t num,
+                                                      int64_t den) {
+    __shared__ long long s_sum[1024 / 64];
+    __shared__ uint32_t s_first[1024 / 64];
+    LogState* ls = L.st;
+    const uint32_t s0 = ls->s_min;
+    const int64_t span = (int64_t)(s_now - s0) + 1;
+    if (ls->bad || s_now < s0 || span > kLogSteps) {     // the same in every thread
+        if (threadIdx.x == 0) st->mode = kModeScan;
+        return;
+    }
+    const int64_t per = (span + 1023) / 1024;
+    const int64_t a = threadIdx.x * per;
+    const int64_t b = a + per < span ? a + per : span;
+    long long sum = 0;
+    uint32_t first = 0xFFFFFFFFu;
+    for (int64_t j = a; j < b; ++j) {
+        const int64_t c = log_count(L, s0 + (uint32_t)j);
+        sum += c;
+        if (c > 0 && first == 0xFFFFFFFFu) first = s0 + (uint32_t)j;
+    }
+    // exclusive prefix of the per-thread sums (steps in thread order), total,
+    // and the first step with live keys
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    long long incl = sum;
+    uint32_t fmin = first;
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+        const uint32_t f = __shfl_xor(fmin, off);
+        fmin = f < fmin ? f : fmin;
+    }
+    if (lane == 63) s_sum[wid] = incl;
+    if (lane == 0) s_first[wid] = fmin;
+    if (threadIdx.x < 256) st->hist[threadIdx.x * kBinStride] = 0u;
+    __syncthreads();
+    long long before = incl - sum, total = 0;
+    uint32_t fl = 0xFFFFFFFFu;
+    for (int w = 0; w < 1024 / 64; ++w) {
+        before += w < wid ? s_sum[w] : 0;
+        total += s_sum[w];
+        fl = s_first[w] < fl ? s_first[w] : fl;
+    }
+    const int64_t k = ((int64_t)total * num) / den;
+    if (k > 0 && before < k && k <= before + sum) {
+        long long cum = before;
+        for (int64_t j = a; j < b; ++j) {
+            const uint32_t s = s0 + (uint32_t)j;
+            const int64_t c = log_count(L, s);
+            if (cum + c >= k) {
+                st->ls_prefix = s;
+                st->k_rem = k - cum;
+                st->win_end = L.segs[s & kLogStepMask].end;
+                break;
+            }
+            cum += c;
+        }
+    }
+    if (threadIdx.x == 0) {
+        const uint64_t tail = fl != 0xFFFFFFFFu ? L.segs[fl & kLogStepMask].begin : ls->head[par];
+        ls->s_min = fl != 0xFFFFFFFFu ? fl : s_now;
+        ls->tail = tail;
+        st->win_begin = tail;
+        st->n_live = (int64_t)total;
+        st->k = k;
+        st->ls_max = s_now;
+        st->ls_digits = 0u;
+        st->key_prefix = 0ull;
+        st->key_and = ~0ull;
+        st->key_or = 0ull;
+        st->mode = kModeLog;
+        if (k <= 0) {
+            st->k_rem = 0;
+            st->ls_prefix = 0u;
+            st->win_end = tail;
+        }
+    }
+}
+
+// One block: live count, maximum last_seen, k, and a cleared histogram
+// (the scan path; with the log serving, k_lru_log_init has set them).
 __global__ __launch_bounds__(1024) void k_lru_init(LruState* st, const int32_t* __restrict__ chunk_cnt,
                                                   const uint32_t* __restrict__ chunk_max, int64_t nchunks,
-                                                  int64_t num, int64_t den) {
+                                                  int64_t num, int64_t den, int use_log) {
+    if (use_log && st->mode == kModeLog) return;
     __shared__ unsigned long long s_sum[1024 / 64];
     __shared__ uint32_t s_max[1024 / 64];
     unsigned long long sum = 0;
@@ -561,10 +733,17 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     const unsigned gchunk = grid_for(w.nchunks, 1, 1 << 16);
     const unsigned gwave = grid_for(w.nchunks, kThreads / 64, 1 << 16);   // a chunk per wave
     const unsigned ghist = grid_for(w.nchunks, 1, kHistBlocks);
+    // with an access log that serves, the cut step comes from its step counts
+    // and the candidates from its ring (the log's own kernel decides on the
+    // device whether it serves: the kernels below follow its choice)
+    const int use_log = (t->log.entries && t->log_ok) ? 1 : 0;
+    if (use_log)
+        hipLaunchKernelGGL(k_lru_log_init, dim3(1), dim3(1024), 0, stream, w.st, t->log, t->log_par, t->max_step, num,
+                           den);
     hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_slot,
-                       w.chunk_cnt, w.chunk_max);
+                       w.chunk_cnt, w.chunk_max, use_log, t->log, (const LruState*)w.st);
     hipLaunchKernelGGL(k_lru_init, dim3(1), dim3(1024), 0, stream, w.st, w.chunk_cnt, w.chunk_max, w.nchunks, num,
-                       den);
+                       den, use_log);
     // last_seen digits: as many as the largest step stamped needs (the
     // kernels also skip digits above the live maximum)
     int ls_digits = 1;

@@ -81,14 +81,88 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) 
         p[i] = value;
 }
 
+// ------------------------------------------------------- access log --
+// Thread 0 of block 0 of a logged find-or-insert: the step's record (new
+// when the step is), the head for the next call (the other word of the
+// pair, which no block of this call reads), and the checks that keep the
+// log complete -- the ring must not wrap onto entries at or after the tail,
+// and the live steps must lie within kLogSteps of each other, so that a
+// step record is only reused once its old step has no live key.
+__device__ void log_begin_call(const LogDev& L, int par, uint64_t head0, int64_t n, uint32_t step, int first) {
+    LogState* s = L.st;
+    if (first) {
+        s->s_min = step;
+        s->tail = head0;
+    }
+    LogSeg* g = L.segs + (step & kLogStepMask);
+    if (g->step != step) {
+        g->step = step;
+        g->begin = head0;
+    }
+    g->end = head0 + (uint64_t)n;
+    s->head[par ^ 1] = head0 + (uint64_t)n;
+    if ((int64_t)(step - s->s_min) >= kLogSteps || head0 + (uint64_t)n - s->tail > L.cap_mask + 1) s->bad = 1;
+}
+
+__device__ __forceinline__ void log_count_add(const LogDev& L, uint32_t step, int64_t delta) {
+    atomicAdd((unsigned long long*)&L.segs[step & kLogStepMask].count, (unsigned long long)delta);
+}
+
+// The LDS bins of a block, added to the step records once: bin b holds keys
+// that left step ref - 1 - b (down) or ref + b (up).
+__device__ __forceinline__ void log_flush_bins(const LogDev& L, const int* s_bins, uint32_t ref, bool down) {
+    for (int b = threadIdx.x; b < kLogBins; b += blockDim.x)
+        if (s_bins[b]) log_count_add(L, down ? ref - 1u - (uint32_t)b : ref + (uint32_t)b, -(int64_t)s_bins[b]);
+}
+
+// Lane gl == 0 of key i's group in a logged find-or-insert, before the
+// stamp: key i's ring entry, and its step counts (new stamps summed in
+// s_log[kLogBins], the steps they leave in s_log[step - 1 - old]).  A FOUND
+// key already stamped with `step` (an earlier call of the same step) keeps
+// its entry.
+__device__ __forceinline__ void log_stamp(const LogDev& L, const TableDev& T, int* s_log, uint64_t head0, int64_t i,
+                                          int st, int64_t slot, uint32_t step) {
+    uint64_t e = kLogNoSlot;
+    if (st == HT_FOUND || st == HT_INSERTED) {
+        const uint32_t old = st == HT_FOUND ? T.last_seen[slot] : kLsDead;
+        if (st == HT_INSERTED || old != step) {
+            e = (uint64_t)(uint32_t)slot | ((uint64_t)step << 32);
+            atomicAdd(&s_log[kLogBins], 1);
+            if (old != kLsDead) {
+                const uint32_t d = step - 1u - old;    // old < step: steps of a logged table never decrease
+                if (old < step && d < (uint32_t)kLogBins) atomicAdd(&s_log[d], 1);
+                else log_count_add(L, old, -1);
+            }
+        }
+    }
+    L.entries[(head0 + (uint64_t)i) & L.cap_mask] = e;
+}
+
+// Block-level set-up and commit of a logged call's counts.
+__device__ __forceinline__ void log_block_init(int* s_log) {
+    for (int b = threadIdx.x; b <= kLogBins; b += blockDim.x) s_log[b] = 0;
+}
+__device__ __forceinline__ void log_block_commit(const LogDev& L, const int* s_log, uint32_t step) {
+    log_flush_bins(L, s_log, step, true);
+    if (threadIdx.x == 0 && s_log[kLogBins]) log_count_add(L, step, s_log[kLogBins]);
+}
+
 // WAVE_ROWS (rows of a multiple of 16 bytes): the whole wave writes the new
 // rows of its groups together, after the probes; else each group writes its
-// own key's row.
-template <int G, bool WAVE_ROWS>
+// own key's row.  LOG: the table keeps an access log (above).
+template <int G, bool WAVE_ROWS, bool LOG>
 __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
     TableDev T, const int64_t* __restrict__ keys, int64_t n_max, const int64_t* __restrict__ n_dev,
-    uint32_t step, int32_t* __restrict__ slots, uint8_t* __restrict__ status) {
+    uint32_t step, int32_t* __restrict__ slots, uint8_t* __restrict__ status, LogDev L, int par, int first) {
     const int64_t n = clamp_count(n_max, n_dev);
+    __shared__ int s_log[LOG ? kLogBins + 1 : 1];
+    uint64_t head0 = 0;
+    if (LOG) {
+        log_block_init(s_log);
+        head0 = L.st->head[par];
+        if (blockIdx.x == 0 && threadIdx.x == 0) log_begin_call(L, par, head0, n, step, first);
+        __syncthreads();
+    }
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
@@ -107,6 +181,7 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
             st = find_or_insert_key<G>(T, k, gl, gshift, &slot);
             if (!WAVE_ROWS && st == HT_INSERTED) write_initial_row<G>(T, slot, k, gl);
             if (gl == 0) {
+                if (LOG) log_stamp(L, T, s_log, head0, i, st, slot, step);
                 if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
                 slots[i] = (int32_t)slot;
                 status[i] = (uint8_t)st;
@@ -114,12 +189,25 @@ __global__ __launch_bounds__(kProbeBlock) void k_find_or_insert(
         }
         if (WAVE_ROWS) write_initial_rows_wave<G>(T, st == HT_INSERTED, slot, k);
     }
+    if (LOG) {
+        __syncthreads();
+        log_block_commit(L, s_log, step);
+    }
 }
 
-template <int G>
+// LOG: each erased key takes one from its last_seen step's count (LDS bins
+// from s_min up, which is where eviction victims come from).
+template <int G, bool LOG>
 __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t* __restrict__ keys,
                                                        int64_t n, uint8_t* __restrict__ status,
-                                                       int32_t* __restrict__ row_tmp) {
+                                                       int32_t* __restrict__ row_tmp, LogDev L) {
+    __shared__ int s_log[LOG ? kLogBins : 1];
+    uint32_t smin = 0;
+    if (LOG) {
+        for (int b = threadIdx.x; b < kLogBins; b += blockDim.x) s_log[b] = 0;
+        smin = L.st->s_min;
+        __syncthreads();
+    }
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
@@ -146,6 +234,14 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
                     old = __shfl(old, gshift);
                     st = (old == k) ? HT_ERASED : HT_NOT_FOUND;
                     if (gl == 0 && st == HT_ERASED && row_tmp) row_tmp[i] = T.rowid[base + hit];
+                    if (LOG && gl == 0 && st == HT_ERASED) {
+                        const uint32_t old = T.last_seen[base + hit];
+                        if (old != kLsDead) {
+                            const uint32_t d = old - smin;
+                            if (old >= smin && d < (uint32_t)kLogBins) atomicAdd(&s_log[d], 1);
+                            else log_count_add(L, old, -1);
+                        }
+                    }
                     if (gl == 0 && st == HT_ERASED && T.last_seen) T.last_seen[base + hit] = kLsDead;
                     break;
                 }
@@ -154,6 +250,10 @@ __global__ __launch_bounds__(kProbeBlock) void k_erase(TableDev T, const int64_t
             }
         }
         if (gl == 0 && status) status[i] = (uint8_t)st;
+    }
+    if (LOG) {
+        __syncthreads();
+        log_flush_bins(L, s_log, smin, false);
     }
 }
 
@@ -164,12 +264,21 @@ constexpr int kAssignLanes = 4;   // lanes per key in the assign pass: 64 keys p
 // Pass 1 of an insert into a growable table: probe and claim slots, stamp
 // last_seen (kept per slot); the slot goes to slots[i] for pass 3, no row
 // is written yet.
-template <int G>
+template <int G, bool LOG>
 __global__ __launch_bounds__(kProbeBlock) void k_foi_claim(TableDev T, const int64_t* __restrict__ keys,
                                                           int64_t n_max, const int64_t* __restrict__ n_dev,
                                                           uint32_t step, int32_t* __restrict__ slots,
-                                                          uint8_t* __restrict__ status) {
+                                                          uint8_t* __restrict__ status, LogDev L, int par,
+                                                          int first) {
     const int64_t n = clamp_count(n_max, n_dev);
+    __shared__ int s_log[LOG ? kLogBins + 1 : 1];
+    uint64_t head0 = 0;
+    if (LOG) {
+        log_block_init(s_log);
+        head0 = L.st->head[par];
+        if (blockIdx.x == 0 && threadIdx.x == 0) log_begin_call(L, par, head0, n, step, first);
+        __syncthreads();
+    }
     const int lane = lane_id();
     const int gl = lane & (G - 1);
     const int gshift = lane & ~(G - 1);
@@ -179,10 +288,15 @@ __global__ __launch_bounds__(kProbeBlock) void k_foi_claim(TableDev T, const int
         int64_t slot;
         const int st = find_or_insert_key<G>(T, keys[i], gl, gshift, &slot);
         if (gl == 0) {
+            if (LOG) log_stamp(L, T, s_log, head0, i, st, slot, step);
             if ((st == HT_FOUND || st == HT_INSERTED) && T.last_seen) T.last_seen[slot] = step;
             slots[i] = (int32_t)slot;
             status[i] = (uint8_t)st;
         }
+    }
+    if (LOG) {
+        __syncthreads();
+        log_block_commit(L, s_log, step);
     }
 }
 
@@ -535,6 +649,85 @@ htl_status fill_keys_empty(const TableDev& T, hipStream_t s) {
     return check_launch("clear table keys");
 }
 
+// Access log: every step record empty, the ring empty.
+__global__ void k_log_reset(LogSeg* __restrict__ segs, LogState* __restrict__ st) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < kLogSteps; i += (int64_t)gridDim.x * blockDim.x) {
+        segs[i].step = 0xFFFFFFFFu;
+        segs[i].pad = 0u;
+        segs[i].count = 0;
+        segs[i].begin = 0;
+        segs[i].end = 0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->head[0] = st->head[1] = 0;
+        st->tail = 0;
+        st->s_min = 0u;
+        st->bad = 0;
+    }
+}
+
+__global__ void k_log_state(const LogState* __restrict__ st, int par, int host_ok, int64_t* __restrict__ out) {
+    out[0] = (host_ok && !st->bad) ? 1 : 0;
+    out[1] = (int64_t)st->head[par];
+    out[2] = (int64_t)st->tail;
+    out[3] = (int64_t)st->s_min;
+}
+
+// Ring entries of a table's access log: a quarter of the slots, at least 4096.
+int64_t log_capacity(int capacity_log2) {
+    return (int64_t)1 << (capacity_log2 - 2 > 12 ? capacity_log2 - 2 : 12);
+}
+
+htl_status log_reset(htl_table* t, hipStream_t stream) {
+    if (!t->log.entries) return HTL_OK;
+    hipLaunchKernelGGL(k_log_reset, dim3(grid_for(kLogSteps, 256, 64)), dim3(256), 0, stream, t->log.segs, t->log.st);
+    t->log_ok = true;
+    t->log_first = true;
+    t->log_par = 0;
+    t->erase_pending = false;
+    return check_launch("access log reset");
+}
+
+htl_status log_alloc(htl_table* t, hipStream_t stream) {
+    const int64_t cap = log_capacity(t->capacity_log2);
+    if (hipMalloc((void**)&t->log.entries, (size_t)cap * 8) != hipSuccess ||
+        hipMalloc((void**)&t->log.segs, (size_t)kLogSteps * sizeof(LogSeg)) != hipSuccess ||
+        hipMalloc((void**)&t->log.st, sizeof(LogState)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(HTL_ERR_NOMEM, "ht_create: access log allocation failed");
+    }
+    t->log.cap_mask = (uint64_t)cap - 1u;
+    return log_reset(t, stream);
+}
+
+void log_free(htl_table* t) {
+    if (t->log.entries) (void)hipFree(t->log.entries);
+    if (t->log.segs) (void)hipFree(t->log.segs);
+    if (t->log.st) (void)hipFree(t->log.st);
+    t->log = LogDev{};
+}
+
+// Whether a find-or-insert at `step` is logged.  Turns the log off (until
+// ht_clear) when the call would break its premises: steps never decrease
+// along the ring, and no key is inserted at a step that an erase already
+// saw (a slot freed and claimed again within one step would give two
+// current entries).  Called before max_step is raised.
+bool log_foi(htl_table* t, uint32_t step) {
+    if (!t->log.entries || !t->log_ok) return false;
+    if (!t->log_first && step < t->max_step) {
+        t->log_ok = false;
+        return false;
+    }
+    if (t->erase_pending) {
+        if (step <= t->erase_step) {
+            t->log_ok = false;
+            return false;
+        }
+        t->erase_pending = false;
+    }
+    return true;
+}
+
 hipMemAllocationProp vm_prop(int device) {
     hipMemAllocationProp prop = {};
     prop.type = hipMemAllocationTypePinned;
@@ -725,8 +918,10 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
                 "ht_create: capacity_log2 must be in [1, 31]");
     HTL_REQUIRE(dim >= 1 && dim <= 65536, "ht_create: dim must be in [1, 65536]");
     HTL_REQUIRE(dtype == HTL_F32 || dtype == HTL_BF16, "ht_create: dtype must be HTL_F32 or HTL_BF16");
-    HTL_REQUIRE((flags & ~(uint32_t)(HT_META_LAST_SEEN | HT_ADAM_STATE | HT_GROWABLE)) == 0,
+    HTL_REQUIRE((flags & ~(uint32_t)(HT_META_LAST_SEEN | HT_ADAM_STATE | HT_GROWABLE | HT_META_ACCESS_LOG)) == 0,
                 "ht_create: unknown flag");
+    HTL_REQUIRE(!(flags & HT_META_ACCESS_LOG) || ((flags & HT_META_LAST_SEEN) && capacity_log2 <= 30),
+                "ht_create: an access log needs HT_META_LAST_SEEN and capacity_log2 <= 30");
     HTL_REQUIRE(!(flags & HT_ADAM_STATE) || dtype == HTL_F32, "ht_create: Adam state needs an fp32 table");
     const bool growable = (flags & HT_GROWABLE) != 0;
     HTL_REQUIRE(!growable || capacity_log2 <= 30, "ht_create: a growable table needs capacity_log2 <= 30");
@@ -751,6 +946,7 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
     T.salt = kProbeSalt;
 
     auto cleanup = [&]() {
+        log_free(t);
         if (T.keys) (void)hipFree(T.keys);
         if (T.last_seen && growable) (void)hipFree(T.last_seen);
         if (growable) {
@@ -798,6 +994,7 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
             st = check_launch("ht_create: row allocator");
         }
         if (st == HTL_OK) st = fill_keys_empty(T, stream);
+        if (st == HTL_OK && (flags & HT_META_ACCESS_LOG)) st = log_alloc(t, stream);
         if (st != HTL_OK) {
             std::string msg = g_last_error;
             cleanup();
@@ -816,6 +1013,7 @@ htl_status ht_create(htl_table** out, int capacity_log2, int dim, htl_dtype dtyp
         return fail(HTL_ERR_NOMEM, "ht_create: device allocation failed");
     }
     htl_status st = fill_keys_empty(T, stream);
+    if (st == HTL_OK && (flags & HT_META_ACCESS_LOG)) st = log_alloc(t, stream);
     if (st != HTL_OK) {
         std::string msg = g_last_error;
         cleanup();
@@ -833,6 +1031,7 @@ htl_status ht_destroy(htl_table* t) {
     HTL_HIP(hipSetDevice(t->device));
     HTL_HIP(hipDeviceSynchronize());
     TableDev& T = t->dev;
+    log_free(t);
     (void)hipFree(T.keys);
     if (t->flags & HT_GROWABLE) {
         if (T.last_seen) (void)hipFree(T.last_seen);
@@ -858,6 +1057,8 @@ htl_status ht_clear(htl_table* t, hipStream_t stream) {
         htl_status st = check_launch("ht_clear: row allocator");
         if (st != HTL_OK) return st;
     }
+    htl_status st = log_reset(t, stream);
+    if (st != HTL_OK) return st;
     return fill_keys_empty(t->dev, stream);
 }
 
@@ -865,6 +1066,7 @@ htl_status ht_resize(htl_table* t, int new_capacity_log2, hipStream_t stream) {
     clear_error();
     HTL_REQUIRE(t != nullptr, "ht_resize: null table");
     HTL_REQUIRE(t->flags & HT_GROWABLE, "ht_resize: the table was not created with HT_GROWABLE");
+    t->log_ok = false;   // the rehash moves keys to other slots: logged slots go stale
     HTL_REQUIRE(new_capacity_log2 >= t->capacity_log2 && new_capacity_log2 <= t->max_capacity_log2,
                 "ht_resize: new_capacity_log2 must be in [current, created + 8] and <= 30");
     TableDev& O = t->dev;
@@ -934,7 +1136,16 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
     HTL_REQUIRE(keys && slots && status, "ht_find_or_insert: null keys/slots/status");
     HTL_REQUIRE(aligned(keys, 8) && aligned(slots, 4) && (!n_dev || aligned(n_dev, 8)),
                 "ht_find_or_insert: misaligned pointer");
+    const bool logged = log_foi(t, step);
     if (step > t->max_step) t->max_step = step;
+    const int par = t->log_par, first = t->log_first ? 1 : 0;
+    // a logged launch wrote the other head word: the next call reads it
+    auto logged_launch = [&]() {
+        if (logged) {
+            t->log_par ^= 1;
+            t->log_first = false;
+        }
+    };
     const int G = probe_lanes();
     // n_max is an upper bound (the dedup output's size: N, with U < N keys
     // real); a persistent grid keeps the blocks past U from costing launches.
@@ -945,9 +1156,13 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         if (st != HTL_OK) return st;
         RowAlloc& A = t->alloc;
         const int64_t nchunks = ceil_div(n_max, kChunkKeys);
-#define HTL_CLAIM(GG)                                                                                        \
-    hipLaunchKernelGGL(k_foi_claim<GG>, dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys, n_max, n_dev, \
-                       step, slots, status)
+#define HTL_CLAIM(GG)                                                                                          \
+    if (logged)                                                                                                \
+        hipLaunchKernelGGL((k_foi_claim<GG, true>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys,    \
+                           n_max, n_dev, step, slots, status, t->log, par, first);                            \
+    else                                                                                                       \
+        hipLaunchKernelGGL((k_foi_claim<GG, false>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, keys,   \
+                           n_max, n_dev, step, slots, status, t->log, par, first)
         switch (G) {
             case 1: HTL_CLAIM(1); break;
             case 2: HTL_CLAIM(2); break;
@@ -956,6 +1171,7 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
             default: HTL_CLAIM(4); break;
         }
 #undef HTL_CLAIM
+        logged_launch();
         hipLaunchKernelGGL(k_chunk_count, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, status, n_max,
                            n_dev, (int)HT_INSERTED, A.chunk_cnt, nchunks);
         st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
@@ -971,13 +1187,19 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         hipLaunchKernelGGL(k_foi_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
         return check_launch("ht_find_or_insert");
     }
-#define HTL_FOI(GG)                                                                                      \
-    if (wave_rows)                                                                                       \
-        hipLaunchKernelGGL((k_find_or_insert<GG, true>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, \
-                           keys, n_max, n_dev, step, slots, status);                                       \
-    else                                                                                                 \
-        hipLaunchKernelGGL((k_find_or_insert<GG, false>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, \
-                           keys, n_max, n_dev, step, slots, status)
+#define HTL_FOI_L(GG, WR, LG)                                                                             \
+    hipLaunchKernelGGL((k_find_or_insert<GG, WR, LG>), dim3(grid), dim3(kProbeBlock), 0, stream, t->dev, \
+                       keys, n_max, n_dev, step, slots, status, t->log, par, first)
+#define HTL_FOI(GG)                  \
+    if (logged) {                    \
+        if (wave_rows)               \
+            HTL_FOI_L(GG, true, true);  \
+        else                         \
+            HTL_FOI_L(GG, false, true); \
+    } else if (wave_rows)            \
+        HTL_FOI_L(GG, true, false);     \
+    else                             \
+        HTL_FOI_L(GG, false, false)
     const bool wave_rows = ((t->dev.dim * t->dev.elem_bytes) & 15) == 0;
     switch (G) {
         case 1: HTL_FOI(1); break;
@@ -987,6 +1209,8 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         default: HTL_FOI(4); break;
     }
 #undef HTL_FOI
+#undef HTL_FOI_L
+    logged_launch();
     return check_launch("ht_find_or_insert");
 }
 
@@ -996,6 +1220,19 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
     HTL_REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "ht_erase: n out of range");
     if (n == 0) return HTL_OK;
     HTL_REQUIRE(keys && aligned(keys, 8), "ht_erase: null or misaligned keys");
+    const bool logged = t->log.entries && t->log_ok;
+    if (logged && !t->log_first) {
+        t->erase_pending = true;
+        t->erase_step = t->max_step;
+    }
+    auto erase = [&](uint8_t* stat, int32_t* row_tmp) {
+        if (logged)
+            hipLaunchKernelGGL((k_erase<8, true>), dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream,
+                               t->dev, keys, n, stat, row_tmp, t->log);
+        else
+            hipLaunchKernelGGL((k_erase<8, false>), dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream,
+                               t->dev, keys, n, stat, row_tmp, t->log);
+    };
     if (t->flags & HT_GROWABLE) {
         // erased keys' row handles go back on the free stack, in key order
         htl_status st = ensure_tmp(t, n);
@@ -1003,8 +1240,7 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
         RowAlloc& A = t->alloc;
         uint8_t* stat = status ? status : A.status_tmp;
         const int64_t nchunks = ceil_div(n, kChunkKeys);
-        hipLaunchKernelGGL(k_erase<8>, dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream, t->dev,
-                           keys, n, stat, A.row_tmp);
+        erase(stat, A.row_tmp);
         hipLaunchKernelGGL(k_chunk_count, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, stat, n,
                            (const int64_t*)nullptr, (int)HT_ERASED, A.chunk_cnt, nchunks);
         st = scan_exclusive_i32(A.chunk_cnt, A.chunk_off, nchunks, nullptr, kScanIdentity, 1, A.scan_tmp, stream);
@@ -1014,8 +1250,7 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
         hipLaunchKernelGGL(k_erase_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
         return check_launch("ht_erase");
     }
-    hipLaunchKernelGGL(k_erase<8>, dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream, t->dev, keys,
-                       n, status, (int32_t*)nullptr);
+    erase(status, (int32_t*)nullptr);
     return check_launch("ht_erase");
 }
 
@@ -1094,6 +1329,7 @@ htl_status ht_import(htl_table* t, const int64_t* keys, int64_t n, const void* r
     if (st != HTL_OK) return st;
     int32_t* handles = t->alloc.row_tmp;
     const uint32_t keep_step = t->max_step;
+    t->log_ok = false;   // last_seen values set from outside: the log no longer covers them
     st = ht_find_or_insert(t, keys, n, nullptr, 0u, handles, status, stream);
     if (st != HTL_OK) return st;
     t->max_step = keep_step;
@@ -1116,6 +1352,14 @@ htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes) {
     if (rows) *rows = t->dev.rows;
     if (row_bytes) *row_bytes = (int64_t)t->dim * t->dev.elem_bytes;
     return HTL_OK;
+}
+
+htl_status ht_access_log_state(const htl_table* t, int64_t* out_dev, hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(t && out_dev && aligned(out_dev, 8), "ht_access_log_state: null or misaligned argument");
+    HTL_REQUIRE(t->log.entries != nullptr, "ht_access_log_state: the table keeps no access log");
+    hipLaunchKernelGGL(k_log_state, dim3(1), dim3(1), 0, stream, t->log.st, t->log_par, t->log_ok ? 1 : 0, out_dev);
+    return check_launch("ht_access_log_state");
 }
 
 htl_status ht_view(const htl_table* t, htl_view* out) {

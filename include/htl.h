@@ -64,7 +64,7 @@ enum { HT_FOUND = 0, HT_INSERTED = 1, HT_FULL = 2, HT_RESERVED = 3 };
 /* Per-key status of ht_erase (uint8 each). */
 enum { HT_NOT_FOUND = 0, HT_ERASED = 1 };
 /* ht_create flags. */
-enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u };
+enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACCESS_LOG = 8u };
 
 /* Key values the table keeps for itself (slot markers). */
 #define HT_EMPTY_KEY ((int64_t)-1)
@@ -85,7 +85,9 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u };
  *                  row is a function of (key, init_seed) only.
  *   flags          HT_META_LAST_SEEN: keep a uint32 last_seen per slot;
  *                  HT_ADAM_STATE: keep fp32 Adam moments m, v (needs HTL_F32);
- *                  HT_GROWABLE: a table that ht_resize can grow (below).
+ *                  HT_GROWABLE: a table that ht_resize can grow (below);
+ *                  HT_META_ACCESS_LOG: keep an access log for eviction
+ *                  (needs HT_META_LAST_SEEN, capacity_log2 <= 30; below).
  *   stream         the table is cleared (all slots EMPTY) on this stream.
  * Storage, all on the current device: keys int64[M]; rows dtype[M][dim];
  * last_seen uint32[M]; m, v float[M][dim].  *t receives the handle.
@@ -102,6 +104,23 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u };
  * long as its key stays live, across resizes; the handle of an erased key is
  * reused by a later insert.  capacity_log2 <= 30 (the row handles are int32
  * and the reservation must fit).
+ *
+ * Access log ([MTGR] section 5: per-key metadata, and scanning only what is
+ * needed; the eviction policy is this library's, see ht_lru_select).  Each
+ * find-or-insert appends one 8-byte entry per key, (slot, step) for keys it
+ * inserts or re-stamps, to a ring of max(2^12, M/4) entries, and keeps per
+ * step the number of live keys whose last_seen is that step (a record per
+ * step, 2^16 of them, 32 bytes each).  ht_lru_select then finds the cut
+ * step from those counts and reads only the ring entries of the oldest
+ * steps up to it, instead of the last_seen of all M slots; its result is
+ * the same.  The log serves while steps never decrease from one
+ * find-or-insert to the next, no key is inserted at a step during which an
+ * erase ran, the live keys' last_seen span fewer than 2^16 steps and the
+ * entries from the oldest live step on fit in the ring; ht_import and
+ * ht_resize end it.  Once it stops serving, ht_lru_select scans last_seen
+ * as on a table without the log, until ht_clear restarts the log.  Writing
+ * keys or last_seen through ht_view also ends what the log can vouch for,
+ * without the library knowing: do not, on a logged table.
  * Errors: INVALID for a bad size/flag combination or null t; NOMEM; DEVICE
  * if the device cannot map virtual memory (HT_GROWABLE only). */
 htl_status ht_create(htl_table** t, int capacity_log2, int dim, htl_dtype dtype,
@@ -111,7 +130,8 @@ htl_status ht_create(htl_table** t, int capacity_log2, int dim, htl_dtype dtype,
 htl_status ht_destroy(htl_table* t);
 
 /* ht_clear -- mark every slot EMPTY again (rows, metadata are left as they
- * are; a growable table also takes back every row handle). */
+ * are; a growable table also takes back every row handle; an access log
+ * restarts empty). */
 htl_status ht_clear(htl_table* t, hipStream_t stream);
 
 /* ht_resize -- grow a growable table to 2^new_capacity_log2 slots ([MTGR]
@@ -227,6 +247,14 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
  * space never moves: ht_resize maps more rows behind it).  Either output may
  * be null.  Errors: INVALID for a null table. */
 htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes);
+
+/* ht_access_log_state -- where a table's access log stands (see ht_create),
+ * for tests and monitoring.  Writes int64[4] to out_dev on `stream`: [0] 1
+ * if the log serves the next eviction choice, else 0; [1] its head and [2]
+ * its tail (ring positions, unwrapped); [3] the oldest step that may still
+ * have live keys.  Errors: INVALID for a null table or output, or a table
+ * created without HT_META_ACCESS_LOG; DEVICE. */
+htl_status ht_access_log_state(const htl_table* t, int64_t* out_dev, hipStream_t stream);
 
 /* ht_view -- every storage array of the table, for checkpoint tooling,
  * tests and measurement.  Any output may be null.  rows is dtype[M][dim]; m,

@@ -101,7 +101,11 @@ def test_invalid_arguments_rejected_on_host(L):
     assert L.ht_create(ctypes.byref(h), 10, 0, 0, 0, 0, None) == INVALID
     assert L.ht_create(ctypes.byref(h), 10, 16, 7, 0, 0, None) == INVALID
     assert L.ht_create(ctypes.byref(h), 10, 16, 1, 0, 2, None) == INVALID   # Adam needs fp32
-    assert L.ht_create(ctypes.byref(h), 10, 16, 0, 0, 8, None) == INVALID   # unknown flag
+    assert L.ht_create(ctypes.byref(h), 10, 16, 0, 0, 16, None) == INVALID   # unknown flag
+    assert L.ht_create(ctypes.byref(h), 10, 16, 0, 0, 8, None) == INVALID    # access log without last_seen
+    assert b"access log" in L.htl_last_error()
+    assert L.ht_create(ctypes.byref(h), 31, 16, 0, 0, 9, None) == INVALID    # access log above 2^30 slots
+    assert L.ht_access_log_state(None, None, None) == INVALID
     assert not h.value
     assert L.ht_find_or_insert(None, None, 4, None, 0, None, None, None) == INVALID
     assert L.ht_erase(None, None, 4, None, None) == INVALID
