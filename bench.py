@@ -73,6 +73,8 @@ def _parse():
                     help="dynamic_online: time a full export / host copy / import of the table")
     ap.add_argument("--growable", action="store_true",
                     help="dynamic_online: use a growable table and time one capacity doubling")
+    ap.add_argument("--no-access-log", action="store_true",
+                    help="dynamic_online: a table without the access log (eviction scans last_seen)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22,
                     help="IDs of the batch the CPU oracle processes (timed)")
     return ap.parse_args()
@@ -401,9 +403,12 @@ def run_backward(args, torch, htl, workloads, dev):
 def run_online(args, torch, htl, workloads, dev):
     spec = workloads.DynamicOnlineSpec()
     steps = args.warmup + args.steps
-    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=args.growable)
+    use_log = not args.no_access_log
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=args.growable,
+                      access_log=use_log)
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.n, spec.dim), dtype=torch.bfloat16, device=dev)
+    log_served = 0
     bufs = _lookup_bufs(torch, spec.n, dev)
     fwd, lru, ers, gat = [], [], [], []
     U_last = 0
@@ -433,6 +438,8 @@ def run_online(args, torch, htl, workloads, dev):
             ers.append(e[3].elapsed_time(e[4]))
             gat.append(e[5].elapsed_time(e[1]))
             U_last = int(nu.item())
+            if use_log:       # outside the timed events: did the log serve this step's choice?
+                log_served += int(table.access_log_state()[0].item())
         print(f"online step {s} done", file=sys.stderr, flush=True)
     ms = float(np.mean(fwd))
     M = 1 << spec.capacity_log2
@@ -460,21 +467,26 @@ def run_online(args, torch, htl, workloads, dev):
     fwd_bytes = spec.n * (16 + row) + U_last * (33 + row)
     gather_bytes = spec.n * (4 + row) + U_last * row
     live_now = int(table.scan()[3].item())
-    # the selection reads last_seen of every slot (dead slots are marked
-    # there) and writes then reads back each live slot's (last_seen, slot)
+    # the scan reads last_seen of every slot (dead slots are marked there)
+    # and writes then reads back each live slot's (last_seen, slot); with
+    # the access log the selection reads only the ring entries of the oldest
+    # steps (a window the device chooses), so no fixed byte count applies
     lru_bytes = M * 4 + live_now * 8 * 2
     config = {"workload": "dynamic_online", "ids_per_step": spec.n, "window": spec.window,
               "new_ids_per_step": spec.delta, "zipf_a": spec.zipf_a, "table_slots_log2": spec.capacity_log2,
               "dim": spec.dim, "row_dtype": "bf16", "evict_fraction": f"{spec.evict_num}/{spec.evict_den}",
-              "parallelism": "single GPU"}
+              "access_log": use_log, "parallelism": "single GPU"}
     ckpt = None
     if args.checkpoint:
         ckpt = _time_checkpoint(torch, htl, table, spec, stream)
     path = {"unique_last_step": U_last, "forward_ms": round(ms, 4),
             "lru_select_ms": round(float(np.mean(lru)), 4), "erase_ms": round(float(np.mean(ers)), 4),
             "live_keys": live_now,
-            "lru_select_roofline": _roofline("ht_lru_select (last_seen scan + radix select, all its kernels)",
-                                             lru_bytes, float(np.mean(lru))),
+            "lru_select_path": ("access log (cut step from per-step live counts, candidates from the ring "
+                                "entries of the oldest steps)" if use_log else "last_seen scan"),
+            "lru_select_log_served_steps": f"{log_served}/{args.steps}" if use_log else None,
+            "lru_select_roofline": None if use_log else _roofline(
+                "ht_lru_select (last_seen scan + radix select, all its kernels)", lru_bytes, float(np.mean(lru))),
             "forward_algorithmic_bytes": fwd_bytes,
             "table": "growable (row handles, mapped row space)" if args.growable else "fixed",
             "resize": resize,

@@ -18,25 +18,35 @@
 //              that tie on the selected last_seen and for the victims;
 //   init    -- one block sums the counts (live L), takes the maximum
 //              last_seen and sets k = floor(L * num / den);
-//   select  -- radix select with 8-bit digits: per digit, LDS histograms of
-//              the candidates that match the digits chosen so far (a
-//              persistent grid, so each of the 256 global bins, one cache
-//              line apart, gets one add per block), then one block scans the
-//              bins for the bucket holding the k-th smallest.  last_seen
-//              digits go first (only as many as its maximum needs), then the
-//              64-bit keys (sign bit flipped so unsigned order is signed
-//              order) over the candidates that tie on last_seen, compacted
-//              per chunk the same way, and compacted again in place to those
-//              matching the top key digit before the second one is counted.
-//              (A pick fused into the histogram pass by a last-block ticket
-//              needs a device-scope fence per block, which writes back L2 on
-//              this multi-die part and cost far more than the extra launch.)
+//   select  -- the cut last_seen by radix select with 8-bit digits: per
+//              digit, LDS histograms of the candidates that match the digits
+//              chosen so far (a persistent grid, so each of the 256 global
+//              bins, one cache line apart, gets one add per block), then one
+//              block scans the bins for the bucket holding the k-th smallest
+//              (only as many digits as the largest last_seen needs).  Then
+//              the cut key among the candidates that tie on last_seen (keys
+//              with the sign bit flipped, so unsigned order is signed order),
+//              compacted per chunk: one histogram of a 12-bit window that
+//              starts at the highest bit in which the ties differ (their
+//              AND and OR say which), in LDS per block and then 4096 global
+//              bins; a one-block pick of the bucket that holds the cut; the
+//              ties in that bucket gathered (and compacted in place); and
+//              one block that ranks them in LDS (at most kFinalCap of them:
+//              uniform keys leave about ties / 4096) or, for a larger
+//              bucket (keys that share more high bits, such as a table id
+//              over small ids), takes the bits below the window by 8-bit
+//              radix passes of its own.
+//              Every launch here costs a few microseconds even with little
+//              to do, so the passes are few.  (A pick fused into the
+//              histogram pass by a last-block ticket needs a device-scope
+//              fence per block, which writes back L2 on this multi-die part
+//              and cost far more than the extra launch.)
 //   emit    -- victims (candidates at or below the selected (last_seen,
 //              key)) are counted per chunk, the counts prefix-summed, and
 //              written densely.
 // Every pass after the collect takes one chunk per wave, with wave-wide
 // prefixes: no block barrier per chunk.
-#include "scan.h"
+#include "htl_common.h"
 
 namespace htl {
 namespace {
@@ -52,7 +62,10 @@ constexpr int kBinStride = 32;             // words between global histogram bin
 struct LruState {
     int64_t n_live;
     int64_t k;            // victims wanted
-    int64_t k_rem;        // rank (1-based) still to find inside the current prefix
+    int64_t k_rem;        // rank (1-based) still to find inside the current last_seen prefix
+    int64_t k_tie;        // rank (1-based) of the cut among the ties, then inside the key prefix
+    uint32_t ls_cut;      // the cut last_seen (set by k_lru_ties)
+    uint32_t pad3;
     uint32_t ls_max;
     uint32_t ls_digits;   // last_seen digits in use
     uint32_t ls_prefix;   // selected last_seen (complete after its last digit)
@@ -60,13 +73,27 @@ struct LruState {
     uint64_t key_prefix;  // selected biased key
     unsigned long long key_and, key_or;   // over the biased keys of the ties
     int32_t mode;         // kModeLog: candidates from the access log (set by k_lru_log_init)
-    uint32_t pad2;
+    int32_t ksel_state;   // cut key: 0 histogram pending, 1 final rank pending, 2 known
+    int32_t ksel_fix;     // bits >= ksel_fix of key_prefix are fixed
+    int32_t ksel_n;       // keys gathered for the final rank
     uint64_t win_begin, win_end;          // ring window of the log's candidates
     uint32_t hist[256 * kBinStride];
 };
 
 constexpr int kModeScan = 0;
 constexpr int kModeLog = 1;
+constexpr int kKeyWin = 12;            // bits of the cut-key histogram window
+constexpr int kKeyBins = 1 << kKeyWin;
+constexpr int kFinalCap = 4096;        // keys the final rank holds in LDS
+
+// Chunks that can hold candidates: all of them, or with the access log the
+// window's (the later ones have none).
+__device__ __forceinline__ int64_t busy_chunks(const struct LruState* st, int64_t nchunks, int use_log, int log_chunk) {
+    if (!use_log || st->mode != kModeLog) return nchunks;
+    const int64_t nw = (int64_t)(st->win_end - st->win_begin + (uint64_t)log_chunk - 1) / log_chunk;
+    return nw < nchunks ? nw : nchunks;
+}
+
 
 struct LruWs {
     LruState* st;
@@ -78,7 +105,8 @@ struct LruWs {
     int32_t* tie_cnt;      // [nchunks]
     int32_t* vic_cnt;      // [nchunks]
     int32_t* vic_off;      // [nchunks + 1]
-    void* scan_tmp;
+    uint32_t* khist;       // [kKeyBins]: cut-key histogram
+    uint64_t* sel;         // [kFinalCap]: ties of the cut bucket
     int64_t nchunks;
     size_t bytes;
 };
@@ -102,7 +130,8 @@ LruWs lru_layout(int64_t M, char* base) {
     w.tie_cnt = (int32_t*)take((size_t)w.nchunks * 4);
     w.vic_cnt = (int32_t*)take((size_t)w.nchunks * 4);
     w.vic_off = (int32_t*)take((size_t)(w.nchunks + 1) * 4);
-    w.scan_tmp = take(scan_temp_bytes(w.nchunks));
+    w.khist = (uint32_t*)take((size_t)kKeyBins * 4);
+    w.sel = (uint64_t*)take((size_t)kFinalCap * 8);
     w.bytes = off;
     return w;
 }
@@ -142,15 +171,24 @@ constexpr int kQuads = kPerThread / 4;
 
 //
 // With the access log serving (mode kModeLog), chunk c is instead entries
-// [c * kChunk, (c + 1) * kChunk) of the ring window: an entry is a
-// candidate iff its step is at most the cut step and last_seen of its slot
-// still equals that step; chunks past the window get count 0.
+// [c * E, (c + 1) * E) of the ring window (E = log_chunk <= kChunk: the ring
+// holds at most nchunks * E entries): an entry is a candidate iff its step
+// is at most the cut step and last_seen of its slot still equals that step;
+// chunks past the window are neither written nor read by the passes after
+// (they stop at the window's chunks).  E below kChunk spreads the window's
+// candidates over more chunks, so the passes that take one chunk per wave
+// have more waves at work.  An entry found stale is overwritten with
+// kLogNoSlot: it can never be current again (its slot's last_seen only
+// moves to later steps, or the key is erased, and a slot freed and claimed
+// again within one step ends the log), and the oldest steps' entries, most
+// of them stale, are read again by every selection until their last live
+// key goes -- this way without a last_seen read each.
 __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nchunks,
                                                          uint32_t* __restrict__ cand_ls,
                                                          uint32_t* __restrict__ cand_slot,
                                                          int32_t* __restrict__ chunk_cnt,
                                                          uint32_t* __restrict__ chunk_max, int use_log, LogDev L,
-                                                         const LruState* __restrict__ st) {
+                                                         const LruState* __restrict__ st, int log_chunk) {
     __shared__ int s_wave[kThreads / 64];
     __shared__ uint32_t s_max[kThreads / 64];
     __shared__ uint32_t s_ls[kChunk];
@@ -160,20 +198,16 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
         const uint64_t wb = st->win_begin;
         const int64_t W = (int64_t)(st->win_end - wb);
         const uint32_t thr = st->ls_prefix;
-        for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-            const int64_t e0 = c * kChunk;
-            if (e0 >= W) {                       // the same in the whole block
-                if (tid == 0) {
-                    chunk_cnt[c] = 0;
-                    chunk_max[c] = 0u;
-                }
-                continue;
-            }
+        const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);   // chunks past them are not read
+        for (int64_t c = blockIdx.x; c < nb; c += gridDim.x) {
+            const int64_t e0 = c * log_chunk;    // window entry of the chunk's first
+            const int64_t r0 = c * kChunk;       // the chunk's candidate region
             uint64_t ent[kPerThread];
 #pragma unroll
             for (int j = 0; j < kPerThread; ++j) {
                 const int64_t e = e0 + j * kThreads + tid;
-                ent[j] = e < W ? L.entries[(wb + (uint64_t)e) & L.cap_mask] : ~0ull;
+                ent[j] = (j * kThreads + tid < log_chunk && e < W) ? L.entries[(wb + (uint64_t)e) & L.cap_mask]
+                                                                   : ~0ull;
             }
             uint32_t now[kPerThread];
 #pragma unroll
@@ -186,8 +220,14 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
             }
             uint32_t live = 0;
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j)
+            for (int j = 0; j < kPerThread; ++j) {
+                const uint32_t slot = (uint32_t)ent[j];
                 if (now[j] != kLsDead && now[j] == (uint32_t)(ent[j] >> 32)) live |= 1u << j;
+                else if (slot != kLogNoSlot && (int64_t)slot < T.capacity && (uint32_t)(ent[j] >> 32) <= thr)
+                    // read, and stale
+                    L.entries[(wb + (uint64_t)(e0 + j * kThreads + tid)) & L.cap_mask] =
+                        (ent[j] & 0xFFFFFFFF00000000ull) | kLogNoSlot;
+            }
             int pos = __popc(live);
             const int total = block_prefix(pos, s_wave);
             uint32_t my_max = 0;
@@ -207,9 +247,9 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
             if (lane_id() == 0) s_max[tid >> 6] = my_max;
             __syncthreads();
             for (int j = tid; j < total; j += kThreads) {
-                cand_ls[e0 + j] = s_ls[j];
+                cand_ls[r0 + j] = s_ls[j];
                 // the entry again (just read by this block): its slot
-                cand_slot[e0 + j] = (uint32_t)L.entries[(wb + (uint64_t)(e0 + s_off[j])) & L.cap_mask];
+                cand_slot[r0 + j] = (uint32_t)L.entries[(wb + (uint64_t)(e0 + s_off[j])) & L.cap_mask];
             }
             if (tid == 0) {
                 uint32_t m = 0;
@@ -281,10 +321,15 @@ __global__ __launch_bounds__(kThreads) void k_lru_collect(TableDev T, int64_t nc
     }
 }
 
-// Live keys of step s by its record (none if the record is another step's).
+// Live keys of step s: the sum of its partial counts (none if the record is
+// another step's: that step has no live key left, its counts are zero).
 __device__ __forceinline__ int64_t log_count(const LogDev& L, uint32_t s) {
-    const LogSeg& g = L.segs[s & kLogStepMask];
-    return g.step == s ? g.count : 0;
+    if (L.segs[s & kLogStepMask].step != s) return 0;
+    const int64_t* c = L.cnt + (int64_t)(s & kLogStepMask) * kLogSubs * kLogCntStride;
+    int64_t sum = 0;
+#pragma unroll 8
+    for (int q = 0; q < kLogSubs; ++q) sum += c[q * kLogCntStride];
+    return sum;
 }
 
 // One block, first, on a table with an access log.  If the log serves:
@@ -365,6 +410,7 @@ __global__ __launch_bounds__(1024) void k_lru_log_init(LruState* st, LogDev L, i
         st->key_prefix = 0ull;
         st->key_and = ~0ull;
         st->key_or = 0ull;
+        st->ksel_state = 0;
         st->mode = kModeLog;
         if (k <= 0) {
             st->k_rem = 0;
@@ -430,6 +476,7 @@ __global__ __launch_bounds__(1024) void k_lru_init(LruState* st, const int32_t* 
         st->key_prefix = 0ull;
         st->key_and = ~0ull;
         st->key_or = 0ull;
+        st->ksel_state = 0;
     }
 }
 
@@ -441,22 +488,16 @@ __device__ __forceinline__ void commit_hist(LruState* st, const uint32_t* s_h) {
     if (c) atomicAdd(&st->hist[threadIdx.x * kBinStride], c);
 }
 
-// One block of 256 threads after each digit's histogram: a block-wide scan
-// of the 256 bins finds the bucket that holds rank k_rem; the prefix is
-// narrowed and the histogram cleared for the next digit.
-__global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d, int is_key) {
+// One block of 256 threads after each last_seen digit's histogram: a
+// block-wide scan of the 256 bins finds the bucket that holds rank k_rem;
+// the prefix is narrowed and the histogram cleared for the next digit.
+__global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d) {
     __shared__ int64_t s_wave[4];
     const int t = threadIdx.x, lane = lane_id(), wid = t >> 6;
-    const bool active = st->k > 0 && (is_key || (uint32_t)d < st->ls_digits);
+    const bool active = st->k > 0 && (uint32_t)d < st->ls_digits;
     const int64_t rem = st->k_rem;                // read before any thread may update it
     const int64_t c = st->hist[t * kBinStride];
     st->hist[t * kBinStride] = 0u;
-    if (is_key && active && (((st->key_or ^ st->key_and) >> (8 * d)) & 255u) == 0) {
-        // every tie has this digit (the top digit's histogram is taken all
-        // the same, the others are skipped): the rank within stays
-        if (t == 0) st->key_prefix |= st->key_and & (0xFFull << (8 * d));
-        return;
-    }
     int64_t incl = c;
     for (int off = 1; off < 64; off <<= 1) {
         const int64_t y = __shfl_up(incl, off);
@@ -468,8 +509,7 @@ __global__ __launch_bounds__(256) void k_lru_pick(LruState* st, int d, int is_ke
     const int64_t excl = incl - c;
     if (active && excl < rem && (incl >= rem || t == 255)) {
         st->k_rem = rem - excl;
-        if (is_key) st->key_prefix |= (uint64_t)t << (8 * d);
-        else st->ls_prefix |= (uint32_t)t << (8 * d);
+        st->ls_prefix |= (uint32_t)t << (8 * d);
     }
 }
 
@@ -526,29 +566,68 @@ __global__ __launch_bounds__(kThreads) void k_lru_hist_ls(LruState* __restrict__
     commit_hist(st, s_h);
 }
 
-// Candidates tying on the selected last_seen, compacted per chunk, with
-// their keys (read through the slot); the histogram of their top key digit
-// (7); and the AND and OR of all their keys (digits where the two agree are
-// the same in every tie and need no pass).
+// Candidates tying on the cut last_seen, compacted per chunk, with their
+// keys (read through the slot), and the AND and OR of all their keys (the
+// highest bit where the two differ is where the cut-key window starts).
+// Every block first takes the pick of the last last_seen digit from the 256
+// histogram bins itself (the same in every block; block 0 records it in
+// ls_cut and k_tie, fields no other block reads here), which saves the
+// launch of a one-block pick; with the access log serving, the cut is
+// already known.  Also clears the cut-key histogram.
 __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st,
                                                       const uint32_t* __restrict__ cand_ls,
                                                       const uint32_t* __restrict__ cand_slot,
                                                       const int64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
-                                                      uint64_t* __restrict__ ties, int32_t* __restrict__ tie_cnt) {
-    __shared__ uint32_t s_h[256];
+                                                      uint64_t* __restrict__ ties, int32_t* __restrict__ tie_cnt,
+                                                      uint32_t* __restrict__ khist, int use_log, int log_chunk) {
     __shared__ unsigned long long s_and[kThreads / 64], s_or[kThreads / 64];
+    __shared__ int64_t s_wv[kThreads / 64];
+    __shared__ uint32_t s_thr;
+    __shared__ int64_t s_rem;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < kKeyBins; i += (int64_t)gridDim.x * kThreads)
+        khist[i] = 0u;
+    const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
     if (st->k <= 0) {
-        for (int64_t c = blockIdx.x * (int64_t)kThreads + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * kThreads)
+        for (int64_t c = blockIdx.x * (int64_t)kThreads + threadIdx.x; c < nb; c += (int64_t)gridDim.x * kThreads)
             tie_cnt[c] = 0;
         return;
     }
-    const uint32_t thr = st->ls_prefix;
     const int lane = lane_id();
-    s_h[threadIdx.x] = 0u;
+    {
+        // the cut last_seen: the last digit's bucket (kThreads == 256 bins)
+        const int64_t rem = st->k_rem;
+        const uint32_t pre = st->ls_prefix;
+        if (threadIdx.x == 0) {
+            s_thr = pre;
+            s_rem = rem;
+        }
+        if (st->ls_digits > 0) {
+            const int t = threadIdx.x, wid = t >> 6;
+            const int64_t c = st->hist[t * kBinStride];
+            int64_t incl = c;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int64_t y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            if (lane == 63) s_wv[wid] = incl;
+            __syncthreads();
+            for (int w = 0; w < wid; ++w) incl += s_wv[w];
+            const int64_t excl = incl - c;
+            if (excl < rem && (incl >= rem || t == 255)) {
+                s_thr = pre | (uint32_t)t;
+                s_rem = rem - excl;
+            }
+        }
+        __syncthreads();
+    }
+    const uint32_t thr = s_thr;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->ls_cut = thr;
+        st->k_tie = s_rem;
+    }
     unsigned long long k_and = ~0ull, k_or = 0ull;
-    __syncthreads();
-    for_wave_chunks(chunk_cnt, nchunks, tie_cnt, [&](int64_t c, int cnt) {
+    for_wave_chunks(chunk_cnt, nb, tie_cnt, [&](int64_t c, int cnt) {
         int run = 0;
         for (int j0 = 0; j0 < cnt; j0 += 64) {
             const int j = j0 + lane;
@@ -561,7 +640,6 @@ __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st
             uint64_t key = 0;
             if (tie) {
                 key = bias(keys[slot]);
-                atomicAdd(&s_h[(uint32_t)(key >> 56)], 1u);
                 k_and &= key;
                 k_or |= key;
             }
@@ -588,52 +666,260 @@ __global__ __launch_bounds__(kThreads) void k_lru_ties(LruState* __restrict__ st
         if (k_and != ~0ull) atomicAnd(&st->key_and, k_and);
         if (k_or != 0ull) atomicOr(&st->key_or, k_or);
     }
-    commit_hist(st, s_h);
 }
 
-// Key digit d over the tied candidates matching the higher digits.  Skipped
-// when every tie has the same digit d.  When a higher digit varied among the
-// ties, the entries that match the prefix chosen so far are first compacted
-// in place in each chunk, so the passes after it read only those.
-__global__ __launch_bounds__(kThreads) void k_lru_hist_key(LruState* __restrict__ st, uint64_t* __restrict__ ties,
-                                                          int32_t* __restrict__ tie_cnt, int64_t nchunks, int d) {
+// The cut-key window: bits [lo, fix) of the biased key, where fix is one
+// past the highest bit in which the ties differ (they all agree above it).
+__device__ __forceinline__ void ksel_window(const LruState* st, int& fix, int& lo) {
+    const uint64_t diff = st->key_and ^ st->key_or;
+    fix = diff ? 64 - __clzll((long long)diff) : 0;
+    lo = fix > kKeyWin ? fix - kKeyWin : 0;
+}
+
+// Does a key match the bits >= fix of the prefix?
+__device__ __forceinline__ bool ksel_match(uint64_t key, uint64_t prefix, int fix) {
+    return fix >= 64 || (key >> fix) == (prefix >> fix);
+}
+
+// Histogram of the ties' window digits: LDS bins per block (a chunk per
+// wave), the nonzero ones then added to the global bins.
+__global__ __launch_bounds__(kThreads) void k_lru_hist_key(const LruState* __restrict__ st,
+                                                          const uint64_t* __restrict__ ties,
+                                                          const int32_t* __restrict__ tie_cnt, int64_t nchunks,
+                                                          uint32_t* __restrict__ khist, int use_log, int log_chunk) {
+    __shared__ uint32_t s_h[kKeyBins];
     if (st->k <= 0) return;
-    const uint64_t diff = st->key_or ^ st->key_and;
-    if (((diff >> (8 * d)) & 255u) == 0) return;
-    const bool compact = (diff >> (8 * (d + 1))) != 0;     // d < 7 here: digit 7 is counted by k_lru_ties
-    __shared__ uint32_t s_h[256];
-    s_h[threadIdx.x] = 0u;
+    const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
+    int fix, lo;
+    ksel_window(st, fix, lo);
+    if (fix == 0) return;                      // one tie: nothing to count
+    for (int b = threadIdx.x; b < kKeyBins; b += kThreads) s_h[b] = 0u;
     __syncthreads();
-    const uint64_t want = st->key_prefix >> (8 * (d + 1));
+    const uint64_t mask = (1ull << (fix - lo)) - 1ull;
     const int lane = lane_id();
-    for_wave_chunks(tie_cnt, nchunks, nullptr, [&](int64_t c, int cnt) {
-        if (!compact) {
-            for (int j = lane; j < cnt; j += 64) {
-                const uint64_t x = ties[c * kChunk + j];
-                atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
-            }
-            return;
+    for_wave_chunks(tie_cnt, nb, nullptr, [&](int64_t c, int cnt) {
+        for (int j = lane; j < cnt; j += 64) atomicAdd(&s_h[(uint32_t)((ties[c * kChunk + j] >> lo) & mask)], 1u);
+    });
+    __syncthreads();
+    for (int b = threadIdx.x; b < kKeyBins; b += kThreads)
+        if (s_h[b]) atomicAdd(&khist[b], s_h[b]);
+}
+
+// Block-wide inclusive scan over 1024 threads of one count each; s_w holds
+// 16 partial sums.  Returns the inclusive prefix of this thread.
+__device__ __forceinline__ int64_t scan1024(int64_t v, int64_t* s_w) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    int64_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_w[wid] = incl;
+    __syncthreads();
+    for (int w = 0; w < wid; ++w) incl += s_w[w];
+    __syncthreads();
+    return incl;
+}
+
+// One block: the bucket of the window that holds rank k_rem among the ties
+// (four bins per thread); its digit joins the prefix.  Done when the window
+// reaches bit 0, else the bucket's ties are ranked next.
+__global__ __launch_bounds__(1024) void k_lru_pick_key(LruState* st, const uint32_t* __restrict__ khist) {
+    __shared__ int64_t s_w[1024 / 64];
+    if (st->k <= 0) return;
+    int fix, lo;
+    ksel_window(st, fix, lo);
+    const int t = threadIdx.x;
+    if (fix == 0) {                            // a single tie: it is the cut key
+        if (t == 0) {
+            st->key_prefix = st->key_and;
+            st->ksel_state = 2;
         }
-        // in place, one wave per chunk: a round's writes land below the
-        // next round's reads, and each store waits for its own round's load
+        return;
+    }
+    const int nbins = 1 << (fix - lo);
+    const int64_t rem = st->k_tie;
+    const uint64_t base = st->key_and & ~((fix >= 64 ? 0ull : (1ull << fix)) - 1ull);
+    static_assert(kKeyBins == 4 * 1024, "four bins per thread");
+    uint32_t v[4];
+    int64_t c = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        v[u] = 4 * t + u < nbins ? khist[4 * t + u] : 0u;
+        c += v[u];
+    }
+    const int64_t incl = scan1024(c, s_w);
+    int64_t run = incl - c;
+    if (run < rem && rem <= incl) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (run + (int64_t)v[u] >= rem) {
+                st->key_prefix = base | ((uint64_t)(4 * t + u) << lo);
+                st->k_tie = rem - run;
+                st->ksel_fix = lo;
+                st->ksel_n = 0;
+                st->ksel_state = lo == 0 ? 2 : 1;
+                break;
+            }
+            run += v[u];
+        }
+    }
+}
+
+// The ties in the cut bucket (bits >= ksel_fix equal the prefix): counted,
+// gathered into sel while they fit, and compacted in place in each chunk
+// (one wave per chunk: a round's writes land below the next round's reads,
+// and each store waits for its own round's load) for a bucket too large.
+__global__ __launch_bounds__(kThreads) void k_lru_bucket(LruState* __restrict__ st, uint64_t* __restrict__ ties,
+                                                        int32_t* __restrict__ tie_cnt, int64_t nchunks,
+                                                        uint64_t* __restrict__ sel, int use_log, int log_chunk) {
+    if (st->k <= 0 || st->ksel_state != 1) return;
+    const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
+    const uint64_t want = st->key_prefix;
+    const int fix = st->ksel_fix;
+    const int lane = lane_id();
+    for_wave_chunks(tie_cnt, nb, nullptr, [&](int64_t c, int cnt) {
         int run = 0;
         for (int j0 = 0; j0 < cnt; j0 += 64) {
             const int j = j0 + lane;
             uint64_t x = 0;
-            bool keep = false;
+            bool in = false;
             if (j < cnt) {
                 x = ties[c * kChunk + j];
-                keep = (x >> (8 * (d + 1))) == want;
-                if (keep) atomicAdd(&s_h[(uint32_t)(x >> (8 * d)) & 255u], 1u);
+                in = ksel_match(x, want, fix);
             }
-            const uint64_t m = __ballot(keep);
-            if (keep) ties[c * kChunk + run + __popcll(m & lanemask_lt())] = x;
+            const uint64_t m = __ballot(in);
+            if (in) ties[c * kChunk + run + __popcll(m & lanemask_lt())] = x;
+            if (m) {
+                int at = 0;
+                if (lane == 0) at = atomicAdd(&st->ksel_n, __popcll(m));
+                at = __shfl(at, 0) + __popcll(m & lanemask_lt());
+                if (in && at < kFinalCap) sel[at] = x;
+            }
             run += __popcll(m);
         }
         if (lane == 0) tie_cnt[c] = run;
     });
+}
+
+// Calls f(c, cnt) for every chunk c < n with a nonzero count, over the 16
+// waves of a 1024-thread block, 64 counts loaded at once per wave.
+template <class F>
+__device__ __forceinline__ void for_block_chunks(const int32_t* __restrict__ cnts, int64_t n, F&& f) {
+    const int lane = lane_id();
+    for (int64_t c0 = (int64_t)(threadIdx.x >> 6) * 64; c0 < n; c0 += 1024) {
+        const int64_t c = c0 + lane;
+        const int32_t cnt = c < n ? cnts[c] : 0;
+        uint64_t busy = __ballot(cnt > 0);
+        while (busy) {
+            const int j = __ffsll((long long)busy) - 1;
+            busy &= busy - 1;
+            f(c0 + j, __shfl(cnt, j));
+        }
+    }
+}
+
+// One block: the cut key among the bucket's ties.  Up to kFinalCap of them
+// were gathered into sel: ranked in LDS (keys are distinct: exactly one has
+// k_rem - 1 smaller ones).  More are narrowed by 8-bit radix passes over the
+// bits below the window, each a pass over the compacted chunks.
+__global__ __launch_bounds__(1024) void k_lru_final(LruState* __restrict__ st, const uint64_t* __restrict__ ties,
+                                                   const int32_t* __restrict__ tie_cnt, int64_t nchunks,
+                                                   const uint64_t* __restrict__ sel, int use_log, int log_chunk) {
+    __shared__ uint64_t s_k[kFinalCap];
+    __shared__ uint32_t s_h[256];
+    __shared__ int64_t s_w[1024 / 64];
+    __shared__ uint64_t s_prefix;
+    __shared__ int64_t s_rem;
+    if (st->k <= 0 || st->ksel_state != 1) return;
+    const int t = threadIdx.x;
+    const int m = st->ksel_n;
+    if (m <= kFinalCap) {
+        for (int i = t; i < m; i += 1024) s_k[i] = sel[i];
+        __syncthreads();
+        const int64_t rem = st->k_tie;
+        for (int i = t; i < m; i += 1024) {
+            const uint64_t x = s_k[i];
+            int below = 0;
+            for (int j = 0; j < m; ++j) below += s_k[j] < x ? 1 : 0;
+            if (below == rem - 1) st->key_prefix = x;
+        }
+        if (t == 0) st->ksel_state = 2;
+        return;
+    }
+    const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
+    if (t == 0) {
+        s_prefix = st->key_prefix;
+        s_rem = st->k_tie;
+    }
+    int fix = st->ksel_fix;
     __syncthreads();
-    commit_hist(st, s_h);
+    while (fix > 0) {
+        const int lo = fix > 8 ? fix - 8 : 0;
+        const uint32_t mask = (1u << (fix - lo)) - 1u;
+        const uint64_t want = s_prefix;
+        if (t < 256) s_h[t] = 0u;
+        __syncthreads();
+        const int lane = lane_id();
+        for_block_chunks(tie_cnt, nb, [&](int64_t c, int cnt) {
+            for (int j = lane; j < cnt; j += 64) {
+                const uint64_t x = ties[c * kChunk + j];
+                if (ksel_match(x, want, fix)) atomicAdd(&s_h[(uint32_t)(x >> lo) & mask], 1u);
+            }
+        });
+        __syncthreads();
+        const int64_t h = t < 256 ? (int64_t)s_h[t] : 0;
+        const int64_t incl = scan1024(h, s_w);
+        const int64_t rem = s_rem;
+        __syncthreads();
+        if (t < 256 && incl - h < rem && rem <= incl) {
+            s_prefix = want | ((uint64_t)t << lo);
+            s_rem = rem - (incl - h);
+        }
+        __syncthreads();
+        fix = lo;
+    }
+    if (t == 0) {
+        st->key_prefix = s_prefix;
+        st->k_tie = s_rem;
+        st->ksel_state = 2;
+    }
+}
+
+// One block: exclusive prefix of the per-chunk victim counts, in rounds of
+// 4096 chunks (four per thread, loaded as one 16-byte vector), carrying the
+// running total; with the access log only the window's chunks (the others
+// hold no candidate and their offsets are not read).
+__global__ __launch_bounds__(1024) void k_lru_offsets(const LruState* __restrict__ st, const int32_t* __restrict__ cnt,
+                                                     int64_t nchunks, int32_t* __restrict__ off, int use_log,
+                                                     int log_chunk) {
+    __shared__ int64_t s_w[1024 / 64];
+    __shared__ int64_t s_carry;
+    const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
+    const int t = threadIdx.x;
+    if (t == 0) s_carry = 0;
+    for (int64_t c0 = 0; c0 < nb; c0 += 4096) {
+        const int64_t c = c0 + 4 * t;
+        int32_t v[4];
+        if (c + 3 < nchunks && (nchunks & 3) == 0) {
+            const int4 x = *reinterpret_cast<const int4*>(cnt + c);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = c + u < nchunks ? cnt[c + u] : 0;
+        }
+        const int64_t sum = (int64_t)v[0] + v[1] + v[2] + v[3];
+        const int64_t incl = scan1024(sum, s_w);      // its barriers also order s_carry
+        int64_t run = s_carry + incl - sum;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c + u < nchunks) off[c + u] = (int32_t)run;
+            run += v[u];
+        }
+        __syncthreads();
+        if (t == 1023) s_carry = run;
+        __syncthreads();
+    }
 }
 
 // Victim test of a candidate; its key is read (through its slot) only when
@@ -650,9 +936,11 @@ __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* 
                                                                const uint32_t* __restrict__ cand_slot,
                                                                const int64_t* __restrict__ keys,
                                                                const int32_t* __restrict__ chunk_cnt,
-                                                               int64_t nchunks, int32_t* __restrict__ vic_cnt) {
+                                                               int64_t nchunks, int32_t* __restrict__ vic_cnt,
+                                                               int use_log, int log_chunk) {
     const bool any = st->k > 0;
-    const uint32_t thr = st->ls_prefix;
+    const uint32_t thr = st->ls_cut;
+    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const uint64_t kthr = st->key_prefix;
     const int lane = lane_id();
     const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
@@ -674,10 +962,12 @@ __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restric
                                                       const int64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
                                                       const int32_t* __restrict__ vic_off, int64_t* __restrict__ victims,
-                                                      int64_t cap, int64_t* __restrict__ n_victims) {
+                                                      int64_t cap, int64_t* __restrict__ n_victims, int use_log,
+                                                      int log_chunk) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_victims = st->k;
     const bool any = st->k > 0;
-    const uint32_t thr = st->ls_prefix;
+    const uint32_t thr = st->ls_cut;
+    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const uint64_t kthr = st->key_prefix;
     const int lane = lane_id();
     const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
@@ -740,8 +1030,13 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     if (use_log)
         hipLaunchKernelGGL(k_lru_log_init, dim3(1), dim3(1024), 0, stream, w.st, t->log, t->log_par, t->max_step, num,
                            den);
+    int log_chunk = kChunk;
+    if (use_log) {
+        const int64_t per = (int64_t)(t->log.cap_mask + 1) / w.nchunks;
+        log_chunk = per < kChunk ? (int)per : kChunk;
+    }
     hipLaunchKernelGGL(k_lru_collect, dim3(gchunk), dim3(kThreads), 0, stream, T, w.nchunks, w.cand_ls, w.cand_slot,
-                       w.chunk_cnt, w.chunk_max, use_log, t->log, (const LruState*)w.st);
+                       w.chunk_cnt, w.chunk_max, use_log, t->log, (const LruState*)w.st, log_chunk);
     hipLaunchKernelGGL(k_lru_init, dim3(1), dim3(1024), 0, stream, w.st, w.chunk_cnt, w.chunk_max, w.nchunks, num,
                        den, use_log);
     // last_seen digits: as many as the largest step stamped needs (the
@@ -751,23 +1046,24 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
     for (int d = ls_digits - 1; d >= 0; --d) {
         hipLaunchKernelGGL(k_lru_hist_ls, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.chunk_cnt,
                            w.nchunks, d);
-        hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 0);
+        // the last digit's pick runs inside k_lru_ties
+        if (d > 0) hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d);
     }
     hipLaunchKernelGGL(k_lru_ties, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
-                       w.chunk_cnt, w.nchunks, w.ties, w.tie_cnt);
-    hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, 7, 1);
-    for (int d = 6; d >= 0; --d) {
-        hipLaunchKernelGGL(k_lru_hist_key, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.ties, w.tie_cnt,
-                           w.nchunks, d);
-        hipLaunchKernelGGL(k_lru_pick, dim3(1), dim3(256), 0, stream, w.st, d, 1);
-    }
+                       w.chunk_cnt, w.nchunks, w.ties, w.tie_cnt, w.khist, use_log, log_chunk);
+    hipLaunchKernelGGL(k_lru_hist_key, dim3(ghist), dim3(kThreads), 0, stream, (const LruState*)w.st, w.ties,
+                       w.tie_cnt, w.nchunks, w.khist, use_log, log_chunk);
+    hipLaunchKernelGGL(k_lru_pick_key, dim3(1), dim3(1024), 0, stream, w.st, w.khist);
+    hipLaunchKernelGGL(k_lru_bucket, dim3(ghist), dim3(kThreads), 0, stream, w.st, w.ties, w.tie_cnt, w.nchunks,
+                       w.sel, use_log, log_chunk);
+    hipLaunchKernelGGL(k_lru_final, dim3(1), dim3(1024), 0, stream, w.st, w.ties, w.tie_cnt, w.nchunks, w.sel,
+                       use_log, log_chunk);
     hipLaunchKernelGGL(k_lru_count_victims, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot,
-                       T.keys, w.chunk_cnt, w.nchunks, w.vic_cnt);
-    htl_status st = scan_exclusive_i32(w.vic_cnt, w.vic_off, w.nchunks, nullptr, kScanIdentity, 1, w.scan_tmp,
-                                       stream);
-    if (st != HTL_OK) return st;
+                       T.keys, w.chunk_cnt, w.nchunks, w.vic_cnt, use_log, log_chunk);
+    hipLaunchKernelGGL(k_lru_offsets, dim3(1), dim3(1024), 0, stream, (const LruState*)w.st, w.vic_cnt, w.nchunks,
+                       w.vic_off, use_log, log_chunk);
     hipLaunchKernelGGL(k_lru_emit, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
-                       w.chunk_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev);
+                       w.chunk_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev, use_log, log_chunk);
     return check_launch("ht_lru_select");
 }
 

@@ -1,4 +1,4 @@
-// Device-wide exclusive prefix sum used by the segment-sum and eviction paths.
+// Device-wide exclusive prefix sum (segment-sum, dedup and growable-table paths).
 #pragma once
 
 #include "htl_common.h"

@@ -104,8 +104,10 @@ __device__ void log_begin_call(const LogDev& L, int par, uint64_t head0, int64_t
     if ((int64_t)(step - s->s_min) >= kLogSteps || head0 + (uint64_t)n - s->tail > L.cap_mask + 1) s->bad = 1;
 }
 
+// Partial count `blockIdx.x mod kLogSubs` of the step.
 __device__ __forceinline__ void log_count_add(const LogDev& L, uint32_t step, int64_t delta) {
-    atomicAdd((unsigned long long*)&L.segs[step & kLogStepMask].count, (unsigned long long)delta);
+    const int64_t at = ((int64_t)(step & kLogStepMask) * kLogSubs + (blockIdx.x & (kLogSubs - 1))) * kLogCntStride;
+    atomicAdd((unsigned long long*)&L.cnt[at], (unsigned long long)delta);
 }
 
 // The LDS bins of a block, added to the step records once: bin b holds keys
@@ -649,15 +651,17 @@ htl_status fill_keys_empty(const TableDev& T, hipStream_t s) {
     return check_launch("clear table keys");
 }
 
-// Access log: every step record empty, the ring empty.
-__global__ void k_log_reset(LogSeg* __restrict__ segs, LogState* __restrict__ st) {
+// Access log: every step record empty, every count zero, the ring empty.
+__global__ void k_log_reset(LogSeg* __restrict__ segs, int64_t* __restrict__ cnt, LogState* __restrict__ st) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < kLogSteps; i += (int64_t)gridDim.x * blockDim.x) {
         segs[i].step = 0xFFFFFFFFu;
         segs[i].pad = 0u;
-        segs[i].count = 0;
         segs[i].begin = 0;
         segs[i].end = 0;
     }
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < kLogSteps * kLogSubs;
+         i += (int64_t)gridDim.x * blockDim.x)
+        cnt[i * kLogCntStride] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         st->head[0] = st->head[1] = 0;
         st->tail = 0;
@@ -680,7 +684,8 @@ int64_t log_capacity(int capacity_log2) {
 
 htl_status log_reset(htl_table* t, hipStream_t stream) {
     if (!t->log.entries) return HTL_OK;
-    hipLaunchKernelGGL(k_log_reset, dim3(grid_for(kLogSteps, 256, 64)), dim3(256), 0, stream, t->log.segs, t->log.st);
+    hipLaunchKernelGGL(k_log_reset, dim3(grid_for(kLogSteps * kLogSubs, 256, 256)), dim3(256), 0, stream, t->log.segs,
+                       t->log.cnt, t->log.st);
     t->log_ok = true;
     t->log_first = true;
     t->log_par = 0;
@@ -692,6 +697,7 @@ htl_status log_alloc(htl_table* t, hipStream_t stream) {
     const int64_t cap = log_capacity(t->capacity_log2);
     if (hipMalloc((void**)&t->log.entries, (size_t)cap * 8) != hipSuccess ||
         hipMalloc((void**)&t->log.segs, (size_t)kLogSteps * sizeof(LogSeg)) != hipSuccess ||
+        hipMalloc((void**)&t->log.cnt, (size_t)kLogSteps * kLogSubs * kLogCntStride * 8) != hipSuccess ||
         hipMalloc((void**)&t->log.st, sizeof(LogState)) != hipSuccess) {
         (void)hipGetLastError();
         return fail(HTL_ERR_NOMEM, "ht_create: access log allocation failed");
@@ -703,6 +709,7 @@ htl_status log_alloc(htl_table* t, hipStream_t stream) {
 void log_free(htl_table* t) {
     if (t->log.entries) (void)hipFree(t->log.entries);
     if (t->log.segs) (void)hipFree(t->log.segs);
+    if (t->log.cnt) (void)hipFree(t->log.cnt);
     if (t->log.st) (void)hipFree(t->log.st);
     t->log = LogDev{};
 }

@@ -110,12 +110,12 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACC
  * find-or-insert appends one 8-byte entry per key, (slot, step) for keys it
  * inserts or re-stamps, to a ring of max(2^12, M/4) entries, and keeps per
  * step the number of live keys whose last_seen is that step (a record per
- * step, 2^16 of them, 32 bytes each).  ht_lru_select then finds the cut
+ * step mod 2^12, with 32 partial counts of one cache line each: 16 MiB).  ht_lru_select then finds the cut
  * step from those counts and reads only the ring entries of the oldest
  * steps up to it, instead of the last_seen of all M slots; its result is
  * the same.  The log serves while steps never decrease from one
  * find-or-insert to the next, no key is inserted at a step during which an
- * erase ran, the live keys' last_seen span fewer than 2^16 steps and the
+ * erase ran, the live keys' last_seen span fewer than 2^12 steps and the
  * entries from the oldest live step on fit in the ring; ht_import and
  * ht_resize end it.  Once it stops serving, ht_lru_select scans last_seen
  * as on a table without the log, until ht_clear restarts the log.  Writing

@@ -219,7 +219,7 @@ def test_log_ends_when_the_ring_fills(htl, orc):
 
 
 def test_log_ends_when_steps_span_too_far(htl, orc):
-    # live keys 70,000 steps apart: more than the 2^16 step records
+    # live keys 70,000 steps apart: more than the 4096 step records
     table, otab, rng = _filled(htl, orc)
     ks = np.arange(50_000, 50_500, dtype=np.int64)
     table.find_or_insert(torch.from_numpy(ks).cuda(), step=70_000)
@@ -245,3 +245,26 @@ def test_log_ring_reused_over_many_steps(htl, orc):
     st = to_np(table.access_log_state())
     assert st[1] > 4 * 4096          # the ring has wrapped several times
     _check_live(table, otab)
+
+
+@pytest.mark.parametrize("access_log", [False, True])
+def test_cut_among_keys_that_share_high_bits(htl, orc, access_log):
+    # keys (table << 48) | id: the ties differ from bit 52 down, so the cut
+    # key's first window (20 bits from there) leaves one table's ties -- up to
+    # 30,000, more than the final rank holds in LDS -- for its radix passes
+    table = htl.Table(19, 4, "bf16", last_seen=True, access_log=access_log)
+    otab = orc.Table(1 << 19, 4, orc.BF16)
+    rng = np.random.default_rng(12)
+    old = (np.arange(8, dtype=np.int64)[:, None] << 48 | rng.integers(0, 1 << 30, (8, 2000))).ravel()
+    new = (np.arange(26, dtype=np.int64)[:, None] << 48 | rng.integers(0, 30_000, (26, 3000))).ravel()
+    dense = np.arange(30_000, dtype=np.int64) | (3 << 48)               # one table dense in [0, 30000)
+    new = np.unique(np.concatenate([new, dense]))
+    old = np.unique(old)
+    old = np.setdiff1d(old, new)
+    for ks, step in ((old, 1), (new, 2)):
+        table.find_or_insert(torch.from_numpy(ks).cuda(), step=step)
+        otab.find_or_insert(ks, step=step)
+    for num, den in ((1, 5), (1, 3), (1, 2), (2, 3), (99, 100)):
+        _check_select(htl, table, otab, num, den)
+    if access_log:
+        assert _serves(table)
