@@ -767,11 +767,9 @@ __global__ __launch_bounds__(1024) void k_lru_pick_key(LruState* st, const uint3
 }
 
 // The ties in the cut bucket (bits >= ksel_fix equal the prefix): counted,
-// gathered into sel while they fit, and compacted in place in each chunk
-// (one wave per chunk: a round's writes land below the next round's reads,
-// and each store waits for its own round's load) for a bucket too large.
-__global__ __launch_bounds__(kThreads) void k_lru_bucket(LruState* __restrict__ st, uint64_t* __restrict__ ties,
-                                                        int32_t* __restrict__ tie_cnt, int64_t nchunks,
+// and gathered into sel while they fit.
+__global__ __launch_bounds__(kThreads) void k_lru_bucket(LruState* __restrict__ st, const uint64_t* __restrict__ ties,
+                                                        const int32_t* __restrict__ tie_cnt, int64_t nchunks,
                                                         uint64_t* __restrict__ sel, int use_log, int log_chunk) {
     if (st->k <= 0 || st->ksel_state != 1) return;
     const int64_t nb = busy_chunks(st, nchunks, use_log, log_chunk);
@@ -779,7 +777,6 @@ __global__ __launch_bounds__(kThreads) void k_lru_bucket(LruState* __restrict__ 
     const int fix = st->ksel_fix;
     const int lane = lane_id();
     for_wave_chunks(tie_cnt, nb, nullptr, [&](int64_t c, int cnt) {
-        int run = 0;
         for (int j0 = 0; j0 < cnt; j0 += 64) {
             const int j = j0 + lane;
             uint64_t x = 0;
@@ -789,16 +786,13 @@ __global__ __launch_bounds__(kThreads) void k_lru_bucket(LruState* __restrict__ 
                 in = ksel_match(x, want, fix);
             }
             const uint64_t m = __ballot(in);
-            if (in) ties[c * kChunk + run + __popcll(m & lanemask_lt())] = x;
             if (m) {
                 int at = 0;
                 if (lane == 0) at = atomicAdd(&st->ksel_n, __popcll(m));
                 at = __shfl(at, 0) + __popcll(m & lanemask_lt());
                 if (in && at < kFinalCap) sel[at] = x;
             }
-            run += __popcll(m);
         }
-        if (lane == 0) tie_cnt[c] = run;
     });
 }
 
@@ -822,7 +816,8 @@ __device__ __forceinline__ void for_block_chunks(const int32_t* __restrict__ cnt
 // One block: the cut key among the bucket's ties.  Up to kFinalCap of them
 // were gathered into sel: ranked in LDS (keys are distinct: exactly one has
 // k_rem - 1 smaller ones).  More are narrowed by 8-bit radix passes over the
-// bits below the window, each a pass over the compacted chunks.
+// bits below the window, each a pass over all the ties (those off the
+// prefix are skipped).
 __global__ __launch_bounds__(1024) void k_lru_final(LruState* __restrict__ st, const uint64_t* __restrict__ ties,
                                                    const int32_t* __restrict__ tie_cnt, int64_t nchunks,
                                                    const uint64_t* __restrict__ sel, int use_log, int log_chunk) {
@@ -922,35 +917,35 @@ __global__ __launch_bounds__(1024) void k_lru_offsets(const LruState* __restrict
     }
 }
 
-// Victim test of a candidate; its key is read (through its slot) only when
-// its last_seen equals the selected one.
-__device__ __forceinline__ bool is_victim(uint32_t ls, uint32_t slot, const int64_t* __restrict__ keys,
-                                          uint32_t thr, uint64_t kthr) {
-    return ls < thr || (ls == thr && bias(keys[slot]) <= kthr);
-}
-
-// The victim passes take one chunk per wave (c = w + i * W over the grid's
-// waves), with wave-wide prefixes.
+// A chunk's victims: its candidates below the cut last_seen, then its ties
+// at or below the cut key -- taken from the ties array, which holds their
+// keys, so that keys are read through the slot only for the victims below
+// the cut.  The victim passes take one chunk per wave (c = w + i * W over
+// the grid's waves), with wave-wide prefixes.
 __global__ __launch_bounds__(kThreads) void k_lru_count_victims(const LruState* __restrict__ st,
                                                                const uint32_t* __restrict__ cand_ls,
-                                                               const uint32_t* __restrict__ cand_slot,
-                                                               const int64_t* __restrict__ keys,
                                                                const int32_t* __restrict__ chunk_cnt,
+                                                               const uint64_t* __restrict__ ties,
+                                                               const int32_t* __restrict__ tie_cnt,
                                                                int64_t nchunks, int32_t* __restrict__ vic_cnt,
                                                                int use_log, int log_chunk) {
     const bool any = st->k > 0;
     const uint32_t thr = st->ls_cut;
-    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const uint64_t kthr = st->key_prefix;
     const int lane = lane_id();
+    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
     for (int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); c < nchunks; c += W) {
         const int cnt = any ? chunk_cnt[c] : 0;
+        const int tc = any ? tie_cnt[c] : 0;
         int tot = 0;
         for (int j0 = 0; j0 < cnt; j0 += 64) {
             const int j = j0 + lane;
-            const bool v = j < cnt && is_victim(cand_ls[c * kChunk + j], cand_slot[c * kChunk + j], keys, thr, kthr);
-            tot += __popcll(__ballot(v));
+            tot += __popcll(__ballot(j < cnt && cand_ls[c * kChunk + j] < thr));
+        }
+        for (int j0 = 0; j0 < tc; j0 += 64) {
+            const int j = j0 + lane;
+            tot += __popcll(__ballot(j < tc && ties[c * kChunk + j] <= kthr));
         }
         if (lane == 0) vic_cnt[c] = tot;
     }
@@ -960,34 +955,41 @@ __global__ __launch_bounds__(kThreads) void k_lru_emit(const LruState* __restric
                                                       const uint32_t* __restrict__ cand_ls,
                                                       const uint32_t* __restrict__ cand_slot,
                                                       const int64_t* __restrict__ keys,
-                                                      const int32_t* __restrict__ chunk_cnt, int64_t nchunks,
+                                                      const int32_t* __restrict__ chunk_cnt,
+                                                      const uint64_t* __restrict__ ties,
+                                                      const int32_t* __restrict__ tie_cnt, int64_t nchunks,
                                                       const int32_t* __restrict__ vic_off, int64_t* __restrict__ victims,
                                                       int64_t cap, int64_t* __restrict__ n_victims, int use_log,
                                                       int log_chunk) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_victims = st->k;
     const bool any = st->k > 0;
     const uint32_t thr = st->ls_cut;
-    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const uint64_t kthr = st->key_prefix;
     const int lane = lane_id();
+    nchunks = busy_chunks(st, nchunks, use_log, log_chunk);
     const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
     for (int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); c < nchunks; c += W) {
         const int cnt = any ? chunk_cnt[c] : 0;
+        const int tc = any ? tie_cnt[c] : 0;
         int64_t run = vic_off[c];
         for (int j0 = 0; j0 < cnt; j0 += 64) {
             const int j = j0 + lane;
+            const bool v = j < cnt && cand_ls[c * kChunk + j] < thr;
             int64_t key = 0;
-            bool v = false;
-            if (j < cnt) {
-                const uint32_t ls = cand_ls[c * kChunk + j];
-                if (ls <= thr) {
-                    key = keys[cand_slot[c * kChunk + j]];
-                    v = ls < thr || bias(key) <= kthr;
-                }
-            }
+            if (v) key = keys[cand_slot[c * kChunk + j]];
             const uint64_t m = __ballot(v);
             const int64_t at = run + __popcll(m & lanemask_lt());
             if (v && at < cap) victims[at] = key;
+            run += __popcll(m);
+        }
+        for (int j0 = 0; j0 < tc; j0 += 64) {
+            const int j = j0 + lane;
+            uint64_t x = 0;
+            if (j < tc) x = ties[c * kChunk + j];
+            const bool v = j < tc && x <= kthr;
+            const uint64_t m = __ballot(v);
+            const int64_t at = run + __popcll(m & lanemask_lt());
+            if (v && at < cap) victims[at] = (int64_t)bias((int64_t)x);   // unbias: the flip is its own inverse
             run += __popcll(m);
         }
     }
@@ -1058,12 +1060,13 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
                        w.sel, use_log, log_chunk);
     hipLaunchKernelGGL(k_lru_final, dim3(1), dim3(1024), 0, stream, w.st, w.ties, w.tie_cnt, w.nchunks, w.sel,
                        use_log, log_chunk);
-    hipLaunchKernelGGL(k_lru_count_victims, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot,
-                       T.keys, w.chunk_cnt, w.nchunks, w.vic_cnt, use_log, log_chunk);
+    hipLaunchKernelGGL(k_lru_count_victims, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.chunk_cnt,
+                       w.ties, w.tie_cnt, w.nchunks, w.vic_cnt, use_log, log_chunk);
     hipLaunchKernelGGL(k_lru_offsets, dim3(1), dim3(1024), 0, stream, (const LruState*)w.st, w.vic_cnt, w.nchunks,
                        w.vic_off, use_log, log_chunk);
     hipLaunchKernelGGL(k_lru_emit, dim3(gwave), dim3(kThreads), 0, stream, w.st, w.cand_ls, w.cand_slot, T.keys,
-                       w.chunk_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev, use_log, log_chunk);
+                       w.chunk_cnt, w.ties, w.tie_cnt, w.nchunks, w.vic_off, victims, victims_cap, n_victims_dev,
+                       use_log, log_chunk);
     return check_launch("ht_lru_select");
 }
 
