@@ -19,7 +19,8 @@ import torch
 from ._binding import (  # noqa: F401
     DEDUP_BINS_ONLY, DEDUP_DEVICE_SET, DEDUP_ONE_TILE, DEDUP_TWO_STAGE_BINS, DedupPlan,
     ADAM_STATE, BF16, EMPTY_KEY, ERASED, EXPORTED, F32, FOUND, FULL, GROWABLE, HTLError, INSERTED, LIB_PATH,
-    copy_probe,
+    META_ACCESS_LOG, DEBUG_DEDUP, DEBUG_DUP, DEBUG_FULL, DEBUG_LOG, DEBUG_SLOT, DEBUG_WALK, copy_probe,
+    copy_to_device_ptr, debug_build, debug_flags,
     META_LAST_SEEN, NOT_FOUND, RESERVED, TOMBSTONE_KEY, Table, dedup_unique_inverse, gather,
     gather_pool, lib, lookup_fused, lookup_slots, release_workspaces, rowwise_adam, segment_sum, segment_sum_adam, table_keys,
     table_tensor,

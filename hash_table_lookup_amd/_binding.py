@@ -64,6 +64,8 @@ _SIGNATURES = {
     "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
     "ht_rows": [_P, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
     "ht_access_log_state": [_P, _P, _P],
+    "htl_debug_build": [],
+    "htl_debug_flags": [ctypes.POINTER(_U32)],
     "ht_view": [_P, ctypes.POINTER(_View)],
     "dedup_workspace_bytes": [_I64],
     "dedup_unique_inverse": [_P, _I64, _P, _P, _P, _P, _SZ, _P],
@@ -619,6 +621,22 @@ def copy_to_device_ptr(dst_ptr: int, src: torch.Tensor):
                                    _stream())
     if rc != 0:
         raise HTLError(HTL_ERR_DEVICE, f"hipMemcpyAsync failed ({rc})")
+
+
+def debug_build() -> bool:
+    """Whether the loaded library is the debug build (device-side checks)."""
+    return bool(lib().htl_debug_build())
+
+
+def debug_flags() -> int:
+    """The current device's invariant-violation bits (HTL_DEBUG_*; always 0
+    in a release build), cleared by reading them; synchronises the device."""
+    f = _U32(0)
+    _check(lib().htl_debug_flags(ctypes.byref(f)))
+    return int(f.value)
+
+
+DEBUG_SLOT, DEBUG_DUP, DEBUG_WALK, DEBUG_FULL, DEBUG_DEDUP, DEBUG_LOG = 1, 2, 4, 8, 16, 32
 
 
 def table_keys(table: Table) -> torch.Tensor:

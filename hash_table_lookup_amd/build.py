@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libhtl.so")
 ARCH = os.environ.get("HTL_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["table.hip", "dedup.hip", "lookup.hip", "gather.hip", "pool.hip", "scan.hip", "backward.hip", "lru.hip",
-           "copy.hip", "noalloc.hip"]
+           "copy.hip", "noalloc.hip", "debug.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -47,11 +47,19 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=und
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 SAN_BUILD_DIR = os.path.join(HERE, "_build_san")
 SAN_LIB_PATH = os.path.join(HERE, "libhtl_san.so")
+# debug build: the same kernels plus device-side invariant checks after each
+# find-or-insert, dedup and logged erase (htl_debug_flags reads what they
+# found), loaded in place of libhtl.so through HTL_LIB
+DEBUG_BUILD_DIR = os.path.join(HERE, "_build_dbg")
+DEBUG_LIB_PATH = os.path.join(HERE, "libhtl_debug.so")
 
 
-def _compile(src: str, san: bool = False) -> str:
-    obj = os.path.join(SAN_BUILD_DIR if san else BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, san: bool = False, debug: bool = False) -> str:
+    out_dir = SAN_BUILD_DIR if san else (DEBUG_BUILD_DIR if debug else BUILD_DIR)
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     flags = [f for f in HIPCC_FLAGS if not (san and f == "-O3")] + (["-O1", "-g"] + SAN_FLAGS if san else [])
+    if debug:
+        flags = flags + ["-DHTL_DEBUG"]
     cmd = [_hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -59,13 +67,19 @@ def _compile(src: str, san: bool = False) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = True, sanitize: bool = False) -> str:
+def build(jobs: int = 8, verbose: bool = True, sanitize: bool = False, debug: bool = False) -> str:
     """Compile every HIP source and link libhtl.so (sanitize: libhtl_san.so,
-    host code under ASan + UBSan); returns its path."""
-    out_dir, lib = (SAN_BUILD_DIR, SAN_LIB_PATH) if sanitize else (BUILD_DIR, LIB_PATH)
+    host code under ASan + UBSan; debug: libhtl_debug.so, with the device-side
+    invariant checks); returns its path."""
+    if sanitize:
+        out_dir, lib = SAN_BUILD_DIR, SAN_LIB_PATH
+    elif debug:
+        out_dir, lib = DEBUG_BUILD_DIR, DEBUG_LIB_PATH
+    else:
+        out_dir, lib = BUILD_DIR, LIB_PATH
     os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, sanitize, debug), SOURCES))
     tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if sanitize:
@@ -80,5 +94,5 @@ def build(jobs: int = 8, verbose: bool = True, sanitize: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    args = [a for a in sys.argv[1:] if a != "--sanitize"]
-    build(jobs=int(args[0]) if args else 8, sanitize="--sanitize" in sys.argv)
+    args = [a for a in sys.argv[1:] if a not in ("--sanitize", "--debug")]
+    build(jobs=int(args[0]) if args else 8, sanitize="--sanitize" in sys.argv, debug="--debug" in sys.argv)

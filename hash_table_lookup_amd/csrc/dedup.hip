@@ -72,6 +72,7 @@
 #include <cstring>
 #include <new>
 
+#include "debug.h"
 #include "lookup.h"
 #include "scan.h"
 #include "tile_dedup.h"
@@ -1090,13 +1091,18 @@ extern "C" {
 
 htl_status dedup_unique_inverse(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
                                 int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
-    return run_dedup("dedup_unique_inverse", false, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream);
+    const htl_status st =
+        run_dedup("dedup_unique_inverse", false, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes, stream);
+    if (st == HTL_OK) debug_check_dedup(keys, n, unique, inverse, n_unique_dev, stream);
+    return st;
 }
 
 htl_status dedup_unique_inverse_ordered(const int64_t* keys, int64_t n, int64_t* unique, int32_t* inverse,
                                         int64_t* n_unique_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
-    return run_dedup("dedup_unique_inverse_ordered", true, keys, n, unique, inverse, n_unique_dev, ws, ws_bytes,
-                     stream);
+    const htl_status st = run_dedup("dedup_unique_inverse_ordered", true, keys, n, unique, inverse, n_unique_dev, ws,
+                                    ws_bytes, stream);
+    if (st == HTL_OK) debug_check_dedup(keys, n, unique, inverse, n_unique_dev, stream);
+    return st;
 }
 
 htl_status dedup_plan_create(htl_dedup_plan** plan) {
@@ -1185,6 +1191,7 @@ htl_status dedup_unique_inverse_adaptive(htl_dedup_plan* plan, const int64_t* ke
     const htl_status st = run_dedup("dedup_unique_inverse_adaptive", false, keys, n, unique, inverse, n_unique_dev,
                                     ws, ws_bytes, stream, nullptr, path, n > 0 ? sink : StatsSink{});
     if (st == HTL_OK && n > 0) ++plan->calls;
+    if (st == HTL_OK) debug_check_dedup(keys, n, unique, inverse, n_unique_dev, stream);
     return st;
 }
 

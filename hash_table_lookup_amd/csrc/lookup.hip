@@ -15,6 +15,7 @@
 // The gather then walks sid in sequence (one dependent load per row, not
 // two), and the random slot loads drop from one per ID to one per tile
 // survivor.
+#include "debug.h"
 #include "lookup.h"
 
 namespace htl {
@@ -63,9 +64,12 @@ htl_status emb_lookup_slots(htl_table* t, const int64_t* keys, int64_t n, uint32
     if (n == 0) return HTL_OK;
     if (run.path == kRunDone) {   // one tile: the dedup wrote the inverse already
         hipLaunchKernelGGL(k_id_slots, dim3(grid_for(n, 256)), dim3(256), 0, stream, slots, inverse, n, id_slots);
-        return check_launch("emb_lookup_slots");
+        st = check_launch("emb_lookup_slots");
+    } else {
+        st = dedup_compose("emb_lookup_slots", run, slots, inverse, id_slots, stream);
     }
-    return dedup_compose("emb_lookup_slots", run, slots, inverse, id_slots, stream);
+    if (st == HTL_OK) debug_check_dedup(keys, n, unique, inverse, n_unique_dev, stream);
+    return st;
 }
 
 size_t emb_lookup_workspace_bytes(int64_t n) {

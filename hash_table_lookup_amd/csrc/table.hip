@@ -37,6 +37,7 @@
 #include <cstdlib>
 
 #include "probe.h"
+#include "debug.h"
 #include "scan.h"
 
 namespace htl {
@@ -1192,6 +1193,8 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
         hipLaunchKernelGGL(k_foi_found, dim3(grid_for(n_max, 256 * 4)), dim3(256), 0, stream, t->dev, n_max, n_dev,
                            slots, status);
         hipLaunchKernelGGL(k_foi_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
+        debug_check_foi(t->dev, keys, n_max, n_dev, slots, status, stream);
+        debug_check_log(t, stream);
         return check_launch("ht_find_or_insert");
     }
 #define HTL_FOI_L(GG, WR, LG)                                                                             \
@@ -1218,6 +1221,8 @@ htl_status ht_find_or_insert(htl_table* t, const int64_t* keys, int64_t n_max, c
 #undef HTL_FOI
 #undef HTL_FOI_L
     logged_launch();
+    debug_check_foi(t->dev, keys, n_max, n_dev, slots, status, stream);
+    debug_check_log(t, stream);
     return check_launch("ht_find_or_insert");
 }
 
@@ -1255,9 +1260,11 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
         hipLaunchKernelGGL(k_erase_push, dim3(grid_for(nchunks, 4, 1 << 16)), dim3(256), 0, stream, stat, A.row_tmp,
                            n, A.chunk_off, A.state, A.free_stack);
         hipLaunchKernelGGL(k_erase_finish, dim3(1), dim3(1), 0, stream, A.state, A.chunk_off + nchunks);
+        debug_check_log(t, stream);
         return check_launch("ht_erase");
     }
     erase(status, (int32_t*)nullptr);
+    debug_check_log(t, stream);
     return check_launch("ht_erase");
 }
 

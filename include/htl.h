@@ -248,6 +248,29 @@ htl_status ht_lru_select(const htl_table* t, int64_t num, int64_t den, int64_t* 
  * be null.  Errors: INVALID for a null table. */
 htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes);
 
+/* htl_debug_build -- 1 if the library was built with -DHTL_DEBUG, else 0.
+ * A debug build enqueues, after each find-or-insert, dedup and logged erase,
+ * a kernel that checks the table's invariants on the device and records
+ * violations as bits of a per-device flag word (it never stops a kernel):
+ *   HTL_DEBUG_SLOT   a FOUND / INSERTED key is not in the slot returned
+ *   HTL_DEBUG_DUP    a FOUND / INSERTED key occurs other than once on its walk
+ *   HTL_DEBUG_WALK   a walk took more than M/16 buckets (Theorem 1 of [MTGenRec]
+ *                    at bucket level: M/16 buckets reach every slot)
+ *   HTL_DEBUG_FULL   a FULL key's walk holds a free slot or a copy of the key
+ *   HTL_DEBUG_DEDUP  unique[inverse[i]] != keys[i], or n_unique out of [1, n]
+ *   HTL_DEBUG_LOG    an access log's live count of a step is negative
+ * htl_debug_flags -- synchronise the current device, write its flag word to
+ * *flags_out and clear it (0 in a release build).  Errors: INVALID for a
+ * null output; DEVICE. */
+#define HTL_DEBUG_SLOT 1u
+#define HTL_DEBUG_DUP 2u
+#define HTL_DEBUG_WALK 4u
+#define HTL_DEBUG_FULL 8u
+#define HTL_DEBUG_DEDUP 16u
+#define HTL_DEBUG_LOG 32u
+int htl_debug_build(void);
+htl_status htl_debug_flags(uint32_t* flags_out);
+
 /* ht_access_log_state -- where a table's access log stands (see ht_create),
  * for tests and monitoring.  Writes int64[4] to out_dev on `stream`: [0] 1
  * if the log serves the next eviction choice, else 0; [1] its head and [2]

@@ -164,3 +164,15 @@ def test_adaptive_dedup_host_checks(L):
     assert L.dedup_plan_choose(None, 100) == 0
     assert L.dedup_plan_choose(None, 1 << 20) == 1
     assert L.dedup_plan_choose(None, (1 << 23) + 1) == 3
+
+
+def test_debug_build_reports_itself(L):
+    # the release library is no debug build; the debug variant (if built)
+    # says it is -- a host-only call in both
+    assert L.htl_debug_build() == 0
+    dbg = os.path.join(ROOT, "hash_table_lookup_amd", "libhtl_debug.so")
+    if not os.path.exists(dbg):
+        pytest.skip("libhtl_debug.so not built")
+    D = ctypes.CDLL(dbg)
+    assert D.htl_debug_build() == 1
+    assert D.htl_debug_flags(None) == 1                   # null output: INVALID, before any device call
