@@ -46,15 +46,17 @@ CSRC = os.path.join(ROOT, "hash_table_lookup_amd", "csrc")
 # Counter-measured bytes of each workload's roofline kernel (FETCH_SIZE and
 # WRITE_SIZE: what the L2s exchange with the data fabric, Infinity Cache hits
 # included, so an upper bound on HBM bytes), per record under profiles/,
-# with the sources that decide them: the kernel's own, and
-# the dedup's (the order of unique ids it produces decides how the kernel's
-# slot and row reads fall on cache lines).
+# with the sources that decide them: the kernel's own, the
+# dedup's (the order of unique ids it produces decides how the kernel's slot
+# and row reads fall on cache lines), and for the row reads the probe header
+# (how find-or-insert stores the new rows decides whether the gather finds
+# them in L2).
 _DEDUP_SRC = ("dedup.hip", "tile_dedup.h")
 TRAFFIC_RECORDS = {
-    "single_large_table": ("gather_single_large_table_traffic.txt", ("gather.hip",) + _DEDUP_SRC),
-    "merged_tables": ("pool_merged_tables_traffic.txt", ("pool.hip",) + _DEDUP_SRC),
+    "single_large_table": ("gather_single_large_table_traffic.txt", ("gather.hip",) + _DEDUP_SRC + ("probe.h",)),
+    "merged_tables": ("pool_merged_tables_traffic.txt", ("pool.hip",) + _DEDUP_SRC + ("probe.h",)),
     "backward": ("backward_fused_traffic.txt", ("backward.hip", "scan.hip") + _DEDUP_SRC),
-    "dynamic_online": ("gather_dynamic_online_traffic.txt", ("gather.hip",) + _DEDUP_SRC),
+    "dynamic_online": ("gather_dynamic_online_traffic.txt", ("gather.hip",) + _DEDUP_SRC + ("probe.h",)),
 }
 METRIC = "dedup+lookup+gather Mkeys/s and achieved HBM GB/s vs peak on 1 MI355X"
 

@@ -38,7 +38,7 @@ __device__ void write_initial_row(const TableDev& T, int64_t slot, int64_t key, 
     if ((row_bytes & 15) == 0) {
         const int vpr = (int)(row_bytes >> 4);
         u32x4* dst = reinterpret_cast<u32x4*>(T.rows) + slot * vpr;
-        for (int v = gl; v < vpr; v += G) dst[v] = init_vec(base, v, T.dtype);
+        for (int v = gl; v < vpr; v += G) __builtin_nontemporal_store(init_vec(base, v, T.dtype), dst + v);
     } else if (T.dtype == HTL_F32) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(T.rows) + slot * T.dim;
         for (int j = gl; j < T.dim; j += G) dst[j] = init_elem_bits(base, j, T.dtype);
@@ -57,7 +57,11 @@ __device__ void write_initial_row(const TableDev& T, int64_t slot, int64_t key, 
 // Writes the initial rows (and zeroed Adam moments) of every key that the
 // groups of this wave have just inserted, with all 64 lanes: each 16-byte
 // vector of those rows is one lane's store, so the stores of a row leave
-// together and no lane of a group that found its key sits idle.  Must be
+// together and no lane of a group that found its key sits idle.  The stores
+// are non-temporal: nothing in this kernel reads the rows again, and kept
+// out of L2 they are not written back while the next kernels run (the
+// large-table step 0.627 -> 0.610 ms, its gather 0.304 -> 0.289 ms; the
+// merged-tables step 2.847 -> 2.775 ms).  Must be
 // called by the whole wave; `ins` marks a group that inserted key `k` at
 // `slot` (every lane of the group passes the same values).  Needs 16-byte
 // rows (dim*elem_bytes % 16 == 0).
@@ -90,12 +94,12 @@ __device__ void write_initial_rows_wave(const TableDev& T, bool ins, int64_t slo
         if (w < total) {
             const int u = w - r * per;
             if (u < vpr) {
-                rows[s * vpr + u] = init_vec(base, u, T.dtype);
+                __builtin_nontemporal_store(init_vec(base, u, T.dtype), rows + s * vpr + u);
             } else {
                 const u32x4 z = {0u, 0u, 0u, 0u};
                 float* mv = (u < vpr + mvv) ? T.m : T.v;
                 const int q = (u < vpr + mvv) ? u - vpr : u - vpr - mvv;
-                reinterpret_cast<u32x4*>(mv)[s * mvv + q] = z;
+                __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(mv) + s * mvv + q);
             }
         }
     }
