@@ -64,6 +64,7 @@ _SIGNATURES = {
     "ht_lru_select": [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P],
     "ht_rows": [_P, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
     "ht_access_log_state": [_P, _P, _P],
+    "ht_access_log_rebuild": [_P, _P],
     "htl_debug_build": [],
     "htl_debug_flags": [ctypes.POINTER(_U32)],
     "ht_view": [_P, ctypes.POINTER(_View)],
@@ -365,6 +366,10 @@ class Table:
         out = torch.empty(4, dtype=torch.int64, device=self.device)
         _check(lib().ht_access_log_state(self._h, _ptr(out), _stream()))
         return out
+
+    def rebuild_access_log(self):
+        """ht_access_log_rebuild: the log again from the live keys (synchronises)."""
+        _check(lib().ht_access_log_rebuild(self._h, _stream()))
 
     def rows_view(self):
         """(device address of the rows, bytes per row): the read-only row view

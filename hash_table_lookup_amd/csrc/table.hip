@@ -678,6 +678,85 @@ __global__ void k_log_state(const LogState* __restrict__ st, int par, int host_o
     out[3] = (int64_t)st->s_min;
 }
 
+// Rebuild of an access log from the table itself: [0] min and [1] max
+// last_seen over the live slots, [2] their count (one atomic of each per
+// block, over a persistent grid).
+__global__ void k_log_range(const uint32_t* __restrict__ ls, int64_t M, unsigned long long* __restrict__ out) {
+    __shared__ uint32_t s_lo, s_hi;
+    __shared__ unsigned long long s_n;
+    if (threadIdx.x == 0) {
+        s_lo = 0xFFFFFFFFu;
+        s_hi = 0u;
+        s_n = 0ull;
+    }
+    __syncthreads();
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    unsigned long long n = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < M; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t v = ls[i];
+        if (v == kLsDead) continue;
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
+        ++n;
+    }
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+    atomicAdd(&s_n, n);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        atomicMin(reinterpret_cast<unsigned int*>(out), s_lo);
+        atomicMax(reinterpret_cast<unsigned int*>(out + 1), s_hi);
+        atomicAdd(out + 2, s_n);
+    }
+}
+
+// Pass 1 (cursor == nullptr): live slots per step (step - lo < kLogSteps),
+// summed in LDS per block and added to cnt.  Pass 2: each block reserves a
+// run per step with one add to the step's cursor, then writes its slots'
+// entries (slot | step << 32) into the runs.
+__global__ __launch_bounds__(256) void k_log_fill(const uint32_t* __restrict__ ls, int64_t M, uint32_t lo,
+                                                  uint32_t* __restrict__ cnt, unsigned long long* __restrict__ cursor,
+                                                  uint64_t* __restrict__ entries, uint64_t cap_mask) {
+    __shared__ uint32_t s_c[kLogSteps];
+    __shared__ unsigned long long s_at[kLogSteps];
+    for (int b = threadIdx.x; b < kLogSteps; b += blockDim.x) s_c[b] = 0u;
+    __syncthreads();
+    const int64_t per = (M + gridDim.x - 1) / gridDim.x;       // each block a contiguous range of slots
+    const int64_t a = blockIdx.x * per, e = a + per < M ? a + per : M;
+    for (int64_t i = a + threadIdx.x; i < e; i += blockDim.x) {
+        const uint32_t v = ls[i];
+        if (v != kLsDead) atomicAdd(&s_c[v - lo], 1u);
+    }
+    __syncthreads();
+    if (!cursor) {
+        for (int b = threadIdx.x; b < kLogSteps; b += blockDim.x)
+            if (s_c[b]) atomicAdd(&cnt[b], s_c[b]);
+        return;
+    }
+    for (int b = threadIdx.x; b < kLogSteps; b += blockDim.x)
+        s_at[b] = s_c[b] ? atomicAdd(&cursor[b], (unsigned long long)s_c[b]) : 0ull;
+    __syncthreads();
+    for (int64_t i = a + threadIdx.x; i < e; i += blockDim.x) {
+        const uint32_t v = ls[i];
+        if (v == kLsDead) continue;
+        const unsigned long long at = atomicAdd(&s_at[v - lo], 1ull);
+        entries[at & cap_mask] = (uint64_t)(uint32_t)i | ((uint64_t)v << 32);
+    }
+}
+
+// The rebuilt log's step counts (partial count 0 of each step) and state.
+__global__ void k_log_set(int64_t* __restrict__ cntp, const uint32_t* __restrict__ cnt, uint32_t lo, int64_t span,
+                          LogState* __restrict__ st, int par, uint64_t head, uint32_t s_min) {
+    for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < span; b += (int64_t)gridDim.x * blockDim.x)
+        cntp[(int64_t)((lo + (uint32_t)b) & kLogStepMask) * kLogSubs * kLogCntStride] = cnt[b];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->head[par] = head;
+        st->tail = 0;
+        st->s_min = s_min;
+        st->bad = 0;
+    }
+}
+
 // Ring entries of a table's access log: a quarter of the slots, at least 4096.
 int64_t log_capacity(int capacity_log2) {
     return (int64_t)1 << (capacity_log2 - 2 > 12 ? capacity_log2 - 2 : 12);
@@ -1365,6 +1444,111 @@ htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes) {
     HTL_REQUIRE(t, "ht_rows: null table");
     if (rows) *rows = t->dev.rows;
     if (row_bytes) *row_bytes = (int64_t)t->dim * t->dev.elem_bytes;
+    return HTL_OK;
+}
+
+htl_status ht_access_log_rebuild(htl_table* t, hipStream_t stream) {
+    clear_error();
+    HTL_REQUIRE(t != nullptr, "ht_access_log_rebuild: null table");
+    HTL_REQUIRE(t->log.entries != nullptr, "ht_access_log_rebuild: the table keeps no access log");
+    const TableDev& T = t->dev;
+    const int64_t M = T.capacity;
+    const uint64_t cap = t->log.cap_mask + 1;
+    // device temporaries: range [3], per-step counts and cursors [kLogSteps]
+    unsigned long long* range = nullptr;
+    uint32_t* cnt = nullptr;
+    unsigned long long* cursor = nullptr;
+    auto release = [&]() {
+        if (range) (void)hipFree(range);
+        if (cnt) (void)hipFree(cnt);
+        if (cursor) (void)hipFree(cursor);
+    };
+    if (hipMalloc((void**)&range, 3 * sizeof(unsigned long long)) != hipSuccess ||
+        hipMalloc((void**)&cnt, (size_t)kLogSteps * 4) != hipSuccess ||
+        hipMalloc((void**)&cursor, (size_t)kLogSteps * 8) != hipSuccess) {
+        (void)hipGetLastError();
+        release();
+        return fail(HTL_ERR_NOMEM, "ht_access_log_rebuild: temporaries allocation failed");
+    }
+    const unsigned long long init[3] = {0xFFFFFFFFull, 0ull, 0ull};
+    unsigned long long host[3] = {0, 0, 0};
+    htl_status st = HTL_OK;
+    auto hip = [&](hipError_t e, const char* what) {
+        if (st == HTL_OK && e != hipSuccess) st = fail(HTL_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+    };
+    hip(hipMemcpyAsync(range, init, sizeof(init), hipMemcpyHostToDevice, stream), "ht_access_log_rebuild: copy");
+    if (st == HTL_OK)
+        hipLaunchKernelGGL(k_log_range, dim3(grid_for(M, 256 * 16, 2048)), dim3(256), 0, stream, T.last_seen, M, range);
+    hip(hipMemcpyAsync(host, range, sizeof(host), hipMemcpyDeviceToHost, stream), "ht_access_log_rebuild: copy");
+    hip(hipStreamSynchronize(stream), "ht_access_log_rebuild: synchronize");
+    if (st != HTL_OK) {
+        release();
+        return st;
+    }
+    const uint32_t lo = (uint32_t)host[0], hi = (uint32_t)host[1];
+    const uint64_t live = host[2];
+    if (live == 0) {                          // nothing live: an empty log
+        release();
+        st = log_reset(t, stream);
+        if (st == HTL_OK && t->max_step == 0xFFFFFFFFu) t->max_step = 0u;
+        return st;
+    }
+    if ((int64_t)(hi - lo) >= kLogSteps || live > cap) {
+        release();
+        return fail(HTL_ERR_INVALID, "ht_access_log_rebuild: the live keys' last_seen span 4096 steps or more, or "
+                                     "they outnumber the ring's entries; the eviction choice keeps scanning");
+    }
+    const int64_t span = (int64_t)(hi - lo) + 1;
+    std::vector<uint32_t> hc(span);
+    std::vector<unsigned long long> hcur(kLogSteps, 0ull);
+    std::vector<LogSeg> segs(kLogSteps);
+    for (auto& g : segs) g = LogSeg{0xFFFFFFFFu, 0u, 0ull, 0ull};
+    hip(hipMemsetAsync(cnt, 0, (size_t)kLogSteps * 4, stream), "ht_access_log_rebuild: clear");
+    const unsigned gfill = grid_for(M, 256 * 64, 1024);
+    if (st == HTL_OK)
+        hipLaunchKernelGGL(k_log_fill, dim3(gfill), dim3(256), 0, stream, T.last_seen, M, lo, cnt,
+                           (unsigned long long*)nullptr, t->log.entries, t->log.cap_mask);
+    hip(hipMemcpyAsync(hc.data(), cnt, (size_t)span * 4, hipMemcpyDeviceToHost, stream), "ht_access_log_rebuild: copy");
+    hip(hipStreamSynchronize(stream), "ht_access_log_rebuild: synchronize");
+    if (st != HTL_OK) {
+        release();
+        return st;
+    }
+    // the steps' runs in step order from ring position 0
+    uint64_t at = 0;
+    uint32_t s_min = lo;
+    bool first = true;
+    for (int64_t b = 0; b < span; ++b) {
+        if (!hc[b]) continue;
+        const uint32_t s = lo + (uint32_t)b;
+        if (first) {
+            s_min = s;
+            first = false;
+        }
+        hcur[b] = at;
+        segs[s & kLogStepMask] = LogSeg{s, 0u, at, at + hc[b]};
+        at += hc[b];
+    }
+    hip(hipMemcpyAsync(cursor, hcur.data(), (size_t)kLogSteps * 8, hipMemcpyHostToDevice, stream),
+        "ht_access_log_rebuild: copy");
+    hip(hipMemcpyAsync(t->log.segs, segs.data(), (size_t)kLogSteps * sizeof(LogSeg), hipMemcpyHostToDevice, stream),
+        "ht_access_log_rebuild: copy");
+    hip(hipMemsetAsync(t->log.cnt, 0, (size_t)kLogSteps * kLogSubs * kLogCntStride * 8, stream),
+        "ht_access_log_rebuild: clear");
+    if (st == HTL_OK) {
+        hipLaunchKernelGGL(k_log_fill, dim3(gfill), dim3(256), 0, stream, T.last_seen, M, lo, cnt, cursor,
+                           t->log.entries, t->log.cap_mask);
+        hipLaunchKernelGGL(k_log_set, dim3(grid_for(span, 256, 16)), dim3(256), 0, stream, t->log.cnt, cnt, lo, span,
+                           t->log.st, t->log_par, (uint64_t)live, s_min);
+        st = check_launch("ht_access_log_rebuild");
+    }
+    hip(hipStreamSynchronize(stream), "ht_access_log_rebuild: synchronize");
+    release();
+    if (st != HTL_OK) return st;
+    t->log_ok = true;
+    t->log_first = false;
+    t->erase_pending = false;
+    if (t->max_step == 0xFFFFFFFFu || t->max_step < hi) t->max_step = hi;
     return HTL_OK;
 }
 

@@ -118,7 +118,8 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACC
  * erase ran, the live keys' last_seen span fewer than 2^12 steps and the
  * entries from the oldest live step on fit in the ring; ht_import and
  * ht_resize end it.  Once it stops serving, ht_lru_select scans last_seen
- * as on a table without the log, until ht_clear restarts the log.  Writing
+ * as on a table without the log, until ht_clear restarts the log empty or
+ * ht_access_log_rebuild rebuilds it from the live keys.  Writing
  * keys or last_seen through ht_view also ends what the log can vouch for,
  * without the library knowing: do not, on a logged table.
  * Errors: INVALID for a bad size/flag combination or null t; NOMEM; DEVICE
@@ -270,6 +271,16 @@ htl_status ht_rows(const htl_table* t, const void** rows, int64_t* row_bytes);
 #define HTL_DEBUG_LOG 32u
 int htl_debug_build(void);
 htl_status htl_debug_flags(uint32_t* flags_out);
+
+/* ht_access_log_rebuild -- rebuild a table's access log from its live keys
+ * and their last_seen (after ht_import, ht_resize or an overflow ended it):
+ * the live keys' entries go to the ring in step order and each step's count
+ * is set, so that the log serves the next eviction choice again.  Reads
+ * last_seen of every slot twice; allocates small temporaries and
+ * synchronises `stream`.  Errors: INVALID for a null table, a table without
+ * HT_META_ACCESS_LOG, or live keys whose last_seen span 4096 steps or more or
+ * that outnumber the ring's entries (the log then stays off); NOMEM; DEVICE. */
+htl_status ht_access_log_rebuild(htl_table* t, hipStream_t stream);
 
 /* ht_access_log_state -- where a table's access log stands (see ht_create),
  * for tests and monitoring.  Writes int64[4] to out_dev on `stream`: [0] 1

@@ -268,3 +268,65 @@ def test_cut_among_keys_that_share_high_bits(htl, orc, access_log):
         _check_select(htl, table, otab, num, den)
     if access_log:
         assert _serves(table)
+
+
+def _continue_stream(htl, orc, table, otab, spec, steps):
+    for s in steps:
+        keys_np = workloads.dynamic_online_step(spec, s)
+        out, uniq, inv, nu, slots, status = htl.lookup(table, torch.from_numpy(keys_np).cuda(), step=s)
+        U = int(nu.item())
+        assert np.array_equal(to_np(status)[:U], otab.find_or_insert(to_np(uniq)[:U], step=s))
+        assert _serves(table)
+        victims, k, ref = _check_select(htl, table, otab, spec.evict_num, spec.evict_den)
+        table.erase(victims[:k])
+        otab.erase(ref)
+    _check_live(table, otab)
+
+
+def test_log_rebuilt_after_a_checkpoint_restore(htl, orc):
+    # a stream, a checkpoint, the restore into a fresh logged table (which
+    # ends its log), the rebuild, and the stream going on with the log serving
+    spec = workloads.DynamicOnlineSpec(window=1 << 13, n=1 << 12, capacity_log2=16, dim=8)
+    src = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, access_log=True)
+    otab = orc.Table(1 << spec.capacity_log2, spec.dim, orc.BF16)
+    _continue_stream(htl, orc, src, otab, spec, range(5))
+    ck = src.checkpoint()
+    dst = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, access_log=True)
+    dst.restore(ck)
+    assert not _serves(dst)
+    _check_select(htl, dst, otab, spec.evict_num, spec.evict_den)    # the scan, exact
+    dst.rebuild_access_log()
+    assert _serves(dst)
+    st = to_np(dst.access_log_state())
+    assert st[1] == len(otab) and st[2] == 0 and st[3] == otab.live()[1].min()
+    _check_select(htl, dst, otab, 1, 3)
+    _continue_stream(htl, orc, dst, otab, spec, range(5, 9))
+
+
+def test_log_rebuilt_after_a_resize(htl, orc):
+    spec = workloads.DynamicOnlineSpec(window=1 << 13, n=1 << 12, capacity_log2=15, dim=8)
+    table = htl.Table(spec.capacity_log2, spec.dim, "bf16", last_seen=True, growable=True, access_log=True)
+    otab = orc.Table(1 << spec.capacity_log2, spec.dim, orc.BF16)
+    _continue_stream(htl, orc, table, otab, spec, range(4))
+    table.resize(spec.capacity_log2 + 1)
+    otab.resize(table.capacity)
+    assert not _serves(table)
+    table.rebuild_access_log()
+    _continue_stream(htl, orc, table, otab, spec, range(4, 8))
+
+
+def test_log_rebuild_refuses_a_wide_step_span_and_tables_without_a_log(htl, orc):
+    table, otab, rng = _filled(htl, orc)
+    ks = np.arange(50_000, 50_500, dtype=np.int64)
+    table.find_or_insert(torch.from_numpy(ks).cuda(), step=70_000)     # ends the log (span)
+    otab.find_or_insert(ks, step=70_000)
+    with pytest.raises(htl.HTLError):
+        table.rebuild_access_log()
+    assert not _serves(table)
+    _check_select(htl, table, otab, 1, 2)
+    plain = htl.Table(10, 4, "bf16", last_seen=True)
+    with pytest.raises(htl.HTLError):
+        plain.rebuild_access_log()
+    empty = htl.Table(12, 4, "bf16", last_seen=True, access_log=True)
+    empty.rebuild_access_log()
+    assert _serves(empty)

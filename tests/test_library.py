@@ -106,6 +106,7 @@ def test_invalid_arguments_rejected_on_host(L):
     assert b"access log" in L.htl_last_error()
     assert L.ht_create(ctypes.byref(h), 31, 16, 0, 0, 9, None) == INVALID    # access log above 2^30 slots
     assert L.ht_access_log_state(None, None, None) == INVALID
+    assert L.ht_access_log_rebuild(None, None) == INVALID
     assert not h.value
     assert L.ht_find_or_insert(None, None, 4, None, 0, None, None, None) == INVALID
     assert L.ht_erase(None, None, 4, None, None) == INVALID
