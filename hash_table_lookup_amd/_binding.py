@@ -531,7 +531,11 @@ def gather(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor] = 
 
 def gather_pool(table: Table, slots: torch.Tensor, inverse: Optional[torch.Tensor],
                 offsets: torch.Tensor, out_dtype="f32", out: Optional[torch.Tensor] = None):
-    """Bag sums: out[b] = sum of rows of IDs offsets[b]..offsets[b+1]-1."""
+    """Bag sums: out[b] = sum of rows of IDs offsets[b]..offsets[b+1]-1.
+
+    The kernels clamp every bag to [0, n), so offsets that break the CSR
+    rules read no ID outside the batch; they are not checked on the host
+    (reading offsets[-1] back would synchronise every call)."""
     slots = _dev(slots, torch.int32, "slots")
     offsets = _dev(offsets, torch.int32, "offsets")
     n = slots.numel() if inverse is None else inverse.numel()
