@@ -121,7 +121,11 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACC
  * as on a table without the log, until ht_clear restarts the log empty or
  * ht_access_log_rebuild rebuilds it from the live keys.  Writing
  * keys or last_seen through ht_view also ends what the log can vouch for,
- * without the library knowing: do not, on a logged table.
+ * without the library knowing: do not, on a logged table.  Part of the
+ * log's bookkeeping is kept by the host at each call (which of two head
+ * words the call reads, the step order, the erase rule above), so the
+ * find-or-insert and erase calls of a logged table must be enqueued call by
+ * call, not replayed from a captured HIP graph.
  * Errors: INVALID for a bad size/flag combination or null t; NOMEM; DEVICE
  * if the device cannot map virtual memory (HT_GROWABLE only). */
 htl_status ht_create(htl_table** t, int capacity_log2, int dim, htl_dtype dtype,
