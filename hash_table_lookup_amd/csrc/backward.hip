@@ -37,10 +37,15 @@
 namespace htl {
 namespace {
 
-constexpr int kCThreads = 256;             // threads of a counting block
-// IDs per counting tile (on the backward workload: 2048 -> 235 us, 4096 ->
-// 196 us, 8192 -> 245 us, where its 128 KB of LDS leaves one block per CU)
-constexpr int kCTile = 4096;
+// Counting tile: IDs per tile and threads per block.  Its LDS (8 bytes per
+// hash slot, 2 slots per ID) is 128 KB at 8192 IDs, one block per CU, so the
+// block is 1024 threads to keep 16 waves per CU in flight.  On the backward
+// workload (2^23 IDs, fused step): 4096 IDs x 256 threads (two blocks per
+// CU) 1.640 ms; 4096 x 512 or x 1024 within noise of it; 8192 x 512
+// 1.613 ms; 8192 x 1024 1.606 ms (five runs on two boxes); 8192 x 256 was
+// slower (4 waves per CU).
+constexpr int kCThreads = 1024;
+constexpr int kCTile = 8192;
 constexpr int kSmallMax = 32;              // longest segment summed by one team
 constexpr int kChunk = 1024;               // rows per workgroup in long segments
 constexpr int kRBlock = 256;
