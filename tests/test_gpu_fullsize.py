@@ -6,7 +6,9 @@ the eviction victims of every step.
 Merged tables: 65,536 samples x 26 bags of Poisson(20) IDs (34.08M IDs), one
 2^26-slot bf16 table of dim 128 warmed by an earlier batch.  Online: the
 2^27-slot bf16 table of dim 64 over all 50 steps of the drifting stream,
-the oracle table stepped beside it.
+the oracle table stepped beside it, once on a table whose eviction choice
+scans last_seen and once on a table with the access log (the form bench.py
+times), whose choice is served by the log at every step.
 """
 import numpy as np
 import pytest
@@ -54,15 +56,17 @@ class _OnlineRun:
 
     FULL_ROWS = (0, 10, 20, 30, 40, 49)
 
-    def __init__(self, htl, orc):
+    def __init__(self, htl, orc, access_log):
         import concurrent.futures as cf
         self.htl, self.orc = htl, orc
+        self.access_log = access_log
         self.spec = workloads.DynamicOnlineSpec()
         self.gen = workloads.DynamicOnlineStream(self.spec, self.spec.steps)
         # the host draws the key batches ahead on a few threads
         self.pool = cf.ThreadPoolExecutor(max_workers=4)
         self.batches = {s: self.pool.submit(self.gen.keys, s) for s in range(self.spec.steps)}
-        self.table = htl.Table(self.spec.capacity_log2, self.spec.dim, "bf16", last_seen=True)
+        self.table = htl.Table(self.spec.capacity_log2, self.spec.dim, "bf16", last_seen=True,
+                               access_log=access_log)
         self.otab = orc.Table(1 << self.spec.capacity_log2, self.spec.dim, orc.BF16)
         self.sample = np.random.default_rng(17).integers(0, self.spec.n, 1 << 16)
         self.next = 0
@@ -94,6 +98,9 @@ class _OnlineRun:
         assert np.array_equal(to_np(lk), ok), s
         assert np.array_equal(to_np(lls).astype(np.uint32), ols), s
         del k_all, ls_all, lk, lls, order
+        if self.access_log:
+            # the log still vouches for every live key, so it serves the choice
+            assert int(self.table.access_log_state()[0].item()) == 1, s
         victims, nv = self.table.lru_select(spec.evict_num, spec.evict_den)
         k = int(nv.item())
         want_v = self.otab.lru_victims(spec.evict_num, spec.evict_den)
@@ -112,11 +119,13 @@ class _OnlineRun:
         self.pool.shutdown(wait=True, cancel_futures=True)
 
 
-@pytest.fixture(scope="module")
-def online_run(htl, orc):
-    run = _OnlineRun(htl, orc)
+@pytest.fixture(scope="module", params=[False, True], ids=["scan", "access_log"])
+def online_run(htl, orc, request):
+    run = _OnlineRun(htl, orc, request.param)
     yield run
     run.close()
+    del run.table
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
