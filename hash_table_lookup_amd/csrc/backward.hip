@@ -65,6 +65,7 @@ struct SegWs {
     int32_t* rel;          // [n]
     int32_t* perm;         // [n]
     int32_t* large;        // [large_max]
+    int32_t* large_n;      // [large_max]: chunks of each listed segment, ceil(count / kChunk)
     int32_t* large_off;    // [large_max + 1]: chunks before each listed segment
     int32_t* part_off;     // [large_max + 1]: the same, counting multi-chunk segments only
     unsigned long long* n_large;
@@ -92,6 +93,7 @@ SegWs seg_layout(int64_t n, int64_t u_max, int dim, char* base) {
     w.rel = (int32_t*)take((size_t)n * 4);
     w.perm = (int32_t*)take((size_t)n * 4);
     w.large = (int32_t*)take((size_t)w.large_max * 4);
+    w.large_n = (int32_t*)take((size_t)w.large_max * 4);
     w.large_off = (int32_t*)take((size_t)(w.large_max + 1) * 4);
     w.part_off = (int32_t*)take((size_t)(w.large_max + 1) * 4);
     w.n_large = (unsigned long long*)take(8);
@@ -342,14 +344,15 @@ __device__ __forceinline__ void sum_rows(const u32x4* __restrict__ grad, int vpr
 // One team of TEAM lanes per segment (in spread order): most segments of a
 // Zipf batch hold one to a few IDs, so a team, not a whole wavefront, takes
 // each, and a wavefront keeps 64/TEAM segments' rows in flight.  Segments
-// longer than kSmallMax are listed, by their spread index, for the chunked
-// path.
+// longer than kSmallMax are listed, by their spread index and chunk count,
+// for the chunked path.
 template <int TEAM, int QMAX, bool ADAM>
 __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__ grad, int vpr,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ seg_off, int64_t u_max,
                                                       const int64_t* __restrict__ n_dev, u32x4* __restrict__ out,
                                                       AdamArgs A, int32_t* __restrict__ large,
+                                                      int32_t* __restrict__ large_n,
                                                       unsigned long long* __restrict__ n_large) {
     const int64_t U = dev_count(u_max, n_dev);
     const int64_t C = spread_c(U);
@@ -361,7 +364,11 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
         if (u >= U) continue;                    // a hole of the spread order
         const int64_t beg = seg_off[q], end = seg_off[q + 1];
         if (end - beg > kSmallMax) {
-            if (tl == 0) large[atomicAdd(n_large, 1ull)] = (int32_t)q;
+            if (tl == 0) {
+                const unsigned long long at = atomicAdd(n_large, 1ull);
+                large[at] = (int32_t)q;
+                large_n[at] = (int32_t)((end - beg + kChunk - 1) / kChunk);
+            }
             continue;
         }
         AdamVec st[QMAX];
@@ -386,9 +393,15 @@ __global__ __launch_bounds__(kRBlock) void k_seg_small(const u32x4* __restrict__
 // One block: large_off = exclusive scan of the chunk counts ceil(count /
 // kChunk) over the list, part_off = the same over the segments of more than
 // one chunk only (a one-chunk segment's sum goes straight to the output).
-__global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__ large,
+// The chunk counts were listed beside the segments, so a round reads one
+// coalesced array; each thread takes kLScanPer consecutive entries per round.
+// On the backward workload (7,827 long segments) the scan took 29.5 us when
+// it read each segment's two offsets itself (two dependent random loads per
+// round of 1024 entries), 40 us with those loads issued 8 per thread at
+// once (one workgroup cannot keep that many misses in flight).
+constexpr int kLScanPer = 8;
+__global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__ large_n,
                                                     const unsigned long long* __restrict__ n_large,
-                                                    const int32_t* __restrict__ seg_off,
                                                     int32_t* __restrict__ large_off,
                                                     int32_t* __restrict__ part_off) {
     __shared__ int32_t s_warp[16], s_warp2[16];
@@ -396,17 +409,21 @@ __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__
     const int64_t nl = (int64_t)*n_large;
     if (threadIdx.x == 0) s_carry = s_carry2 = 0;
     __syncthreads();
-    for (int64_t b0 = 0; b0 <= nl; b0 += 1024) {
-        const int64_t i = b0 + threadIdx.x;
-        int32_t x = 0;
-        if (i < nl) {
-            const int32_t q = large[i];
-            x = (seg_off[q + 1] - seg_off[q] + kChunk - 1) / kChunk;
+    constexpr int64_t kRound = 1024 * kLScanPer;
+    for (int64_t b0 = 0; b0 <= nl; b0 += kRound) {
+        const int64_t i0 = b0 + (int64_t)threadIdx.x * kLScanPer;
+        int32_t x[kLScanPer];
+#pragma unroll
+        for (int k = 0; k < kLScanPer; ++k) x[k] = i0 + k < nl ? large_n[i0 + k] : 0;
+        int32_t tot = 0, tot2 = 0;
+#pragma unroll
+        for (int k = 0; k < kLScanPer; ++k) {
+            tot += x[k];
+            tot2 += x[k] > 1 ? x[k] : 0;
         }
-        const int32_t x2 = x > 1 ? x : 0;
         const int lane = lane_id();
         const int wid = threadIdx.x >> 6;
-        int32_t incl = x, incl2 = x2;
+        int32_t incl = tot, incl2 = tot2;
         for (int off = 1; off < 64; off <<= 1) {
             const int32_t y = __shfl_up(incl, off);
             const int32_t y2 = __shfl_up(incl2, off);
@@ -430,9 +447,15 @@ __global__ __launch_bounds__(1024) void k_large_scan(const int32_t* __restrict__
             total2 += s_warp2[w];
         }
         const int32_t carry = s_carry, carry2 = s_carry2;
-        if (i <= nl) {
-            large_off[i] = carry + before + incl - x;
-            part_off[i] = carry2 + before2 + incl2 - x2;
+        int32_t run = carry + before + incl - tot, run2 = carry2 + before2 + incl2 - tot2;
+#pragma unroll
+        for (int k = 0; k < kLScanPer; ++k) {
+            if (i0 + k <= nl) {
+                large_off[i0 + k] = run;
+                part_off[i0 + k] = run2;
+            }
+            run += x[k];
+            run2 += x[k] > 1 ? x[k] : 0;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -616,9 +639,8 @@ void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, co
     // 753K segments for u_max = 8.4M), and idle workgroups cost launch time.
     hipLaunchKernelGGL((k_seg_small<TEAM, QMAX, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM, 1 << 15)),
                        dim3(kRBlock), 0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, (u32x4*)out, A,
-                       w.large, w.n_large);
-    hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large, w.n_large, w.seg_off, w.large_off,
-                       w.part_off);
+                       w.large, w.large_n, w.n_large);
+    hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large_n, w.n_large, w.large_off, w.part_off);
     hipLaunchKernelGGL((k_large_reduce<TEAM, QMAX, ADAM>), dim3(grid_for(w.max_chunks, 1, 1 << 14)), dim3(kRBlock),
                        0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, w.large, w.n_large, w.large_off, w.part_off,
                        w.max_chunks, u_max, n_dev, (u32x4*)w.partial, (u32x4*)out, A);
