@@ -13,7 +13,11 @@ namespace {
 
 constexpr int kTile = 2048;            // keys per stage-1 tile
 constexpr int kTileLog2 = 11;
-constexpr int kTileThreads = 256;
+// Threads per tile (and per block of the tile-wise stage-2 kernels).  The
+// tile's LDS (48 KB) allows three blocks per CU: 512 threads keep 24 waves
+// per CU in flight.  Large-table step 0.608 / 0.597 / 0.602 ms and
+// merged-tables step 2.771 / 2.759 / 2.814 ms with 256 / 512 / 1024.
+constexpr int kTileThreads = 512;
 constexpr int kKeysPerThread = kTile / kTileThreads;
 constexpr int kLdsCap = 2 * kTile;     // LDS set slots (load <= 1/2); slot kLdsCap holds key -1
 constexpr int kLdsCapLog2 = kTileLog2 + 1;
