@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kTileThreads) void k_dedup_tile(const int64_t* __re
         for (int j = 0; j < kKeysPerThread; ++j)
             if ((valid & (1u << j)) && s_tag[pos[j]] == j * kTileThreads + tid) first |= 1u << j;
         __syncthreads();
-        // ids in position order: positions j*256 + tid run j-major.  One
+        // ids in position order: positions j*kTileThreads + tid run j-major.  One
         // ballot per j; the per-wave counts of every j go through LDS at once.
         uint64_t bal[kKeysPerThread];
 #pragma unroll
