@@ -52,6 +52,7 @@ constexpr uint64_t kProbeSalt = 0x2545F4914F6CDD1Dull;
 // with 2^13 / 2^14 / 2^15: large table 0.594 / 0.597 / 0.597 ms, online
 // forward (logged) 0.381 / - / 0.391 ms, merged tables unchanged; 2^12 0.600.
 constexpr int64_t kProbeGridMax = 1 << 13;
+constexpr int64_t kEraseGridMax = 1 << 11;   // workgroups of the erase kernel at most
 }  // namespace
 
 int probe_lanes() {
@@ -1322,13 +1323,16 @@ htl_status ht_erase(htl_table* t, const int64_t* keys, int64_t n, uint8_t* statu
         t->erase_pending = true;
         t->erase_step = t->max_step;
     }
+    // at most 2^11 workgroups, each looping: fewer blocks flush their LDS step
+    // counts (online erase of 5% of the live keys: 28.7 -> 27.6 us; 2^12 28.0)
+    const unsigned egrid = grid_for(n, kProbeBlock / 8, kEraseGridMax);
     auto erase = [&](uint8_t* stat, int32_t* row_tmp) {
         if (logged)
-            hipLaunchKernelGGL((k_erase<8, true>), dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream,
-                               t->dev, keys, n, stat, row_tmp, t->log);
+            hipLaunchKernelGGL((k_erase<8, true>), dim3(egrid), dim3(kProbeBlock), 0, stream, t->dev, keys, n, stat,
+                               row_tmp, t->log);
         else
-            hipLaunchKernelGGL((k_erase<8, false>), dim3(grid_for(n, kProbeBlock / 8)), dim3(kProbeBlock), 0, stream,
-                               t->dev, keys, n, stat, row_tmp, t->log);
+            hipLaunchKernelGGL((k_erase<8, false>), dim3(egrid), dim3(kProbeBlock), 0, stream, t->dev, keys, n, stat,
+                               row_tmp, t->log);
     };
     if (t->flags & HT_GROWABLE) {
         // erased keys' row handles go back on the free stack, in key order
