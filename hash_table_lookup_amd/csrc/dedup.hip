@@ -1070,7 +1070,7 @@ htl_status dedup_compose(const char* who, const DedupRun& run, const int32_t* sl
 // whose workgroup dedups them in turn; stage 1 is skipped only while
 // d n + ntiles <= 3 n / P (P bins), so no key can bring a bin past about
 // four times the mean load.  (On the sweep of hash_table_lookup_amd.tune:
-// skipping saves 12-17% at 2^20..2^23 keys when the tiles hold almost no
+// skipping saves up to 15% at 2^20..2^23 keys when the tiles hold almost no
 // duplicates, and costs 3-14x under Zipf skew, where a hot key fills one bin.)
 // A batch run without stage 1 cannot measure d, so while the plan skips it,
 // every kRemeasure-th call runs both stages again to renew the measurement.

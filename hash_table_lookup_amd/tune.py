@@ -2,8 +2,8 @@
 GPU across batch sizes and duplicate patterns, the measurement behind the
 adaptive dedup's rule (skip stage 1 only while the duplicate share d that
 stage 1 measured bounds the hottest key so that it cannot overfill a bin:
-d * n + ntiles <= 3 n / P for P bins; the sweep shows the skip saving
-12-17% where tiles hold almost no duplicates and costing 3-14x under skew).
+d * n + ntiles <= 3 n / P for P bins; the sweep shows the skip saving up
+to 15% where tiles hold almost no duplicates and costing 3-14x under skew).
 
     python -m hash_table_lookup_amd.tune [--reps 10] [--max-log2 23]
 
