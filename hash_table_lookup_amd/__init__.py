@@ -2,8 +2,8 @@
 
 Python face of libhtl.so (include/htl.h).  The library implements, as HIP
 kernels for gfx950, the embedding path described by MTGenRec (arXiv
-2505.12663: dynamic hash embedding table, table merging, two-stage ID
-deduplication) and MTGR (arXiv 2505.18654, section 5): feature-ID dedup,
+2505.12663: embeddings in a dynamic hash table, feature tables merged into
+one, IDs deduplicated in two stages) and MTGR (arXiv 2505.18654, section 5): feature-ID dedup,
 find-or-insert into an open-addressing table with odd-step probing, row
 gather with optional bag sum-pooling, gradient segment-sum and row-wise Adam,
 erase and least-recently-used eviction.

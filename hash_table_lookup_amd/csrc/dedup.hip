@@ -1,8 +1,9 @@
 // Two-stage feature-ID deduplication: unique keys plus inverse index.
 //
 // MTGenRec (arXiv 2505.12663), TL;DR and section 6 of its contents ("Embedding
-// Table Lookup Acceleration"): two-stage ID deduplication for faster
-// embedding lookups.  MTGR (arXiv 2505.18654) section 5, "Embedding Lookup":
+// Table Lookup Acceleration"): the IDs are deduplicated in two stages so
+// that the embedding lookup is quicker.  MTGR (arXiv 2505.18654) section 5,
+// "Embedding Lookup":
 // IDs are made unique before and after the cross-device all-to-all so that no
 // duplicate crosses the link.  On one device the two stages become:
 //

@@ -1,12 +1,12 @@
 // Dynamic open-addressing embedding table: create/clear/destroy/resize,
 // find-or-insert, erase, compact scan, export / import (checkpoint).
 //
-// MTGenRec (arXiv 2505.12663): Abstract and Figure 5 (a hash-based dynamic
-// embedding table replaces static tables so embeddings can be inserted and
-// deleted in real time), Theorem 1 (in a table of 2^n slots the walk
+// MTGenRec (arXiv 2505.12663): Abstract and Figure 5 (embeddings held in a
+// table indexed by a hash of the key, in place of fixed-size tables, so that
+// they can be added and removed while training runs), Theorem 1 (in a table of 2^n slots the walk
 // h_t = h_0 + t*S mod 2^n visits every slot iff S is odd).  MTGR (arXiv
-// 2505.18654) section 5, "Embedding Management": keys map to embedding
-// vectors plus metadata, and live keys can be scanned compactly.
+// 2505.18654) section 5, "Embedding Management": each key leads to its
+// embedding row and its metadata, and live keys can be scanned compactly.
 //
 // Layout in HBM: keys int64[M] (EMPTY = -1, TOMBSTONE = -2), rows
 // dtype[M][dim] indexed by slot, optional last_seen uint32[M], optional Adam

@@ -74,10 +74,11 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACC
 
 /* ------------------------------------------------------------------ table --
  * ht_create -- allocate an empty dynamic embedding table.
- * [MTGenRec] Abstract and Figure 5: a hash-based dynamic embedding table
- * replaces static tables; [MTGR] section 5 "Embedding Management": keys map to
- * embedding vectors and metadata.  Theorem 1 of [MTGenRec] fixes the shape:
- * M = 2^capacity_log2 slots probed with an odd step.
+ * [MTGenRec] Abstract and Figure 5: embeddings kept in a table indexed by a
+ * hash of the key, in place of fixed-size tables; [MTGR] section 5
+ * "Embedding Management": each key leads to its embedding row and its
+ * per-key metadata.  Theorem 1 of [MTGenRec] fixes the shape: M =
+ * 2^capacity_log2 slots probed with an odd step.
  *   capacity_log2  1..HT_MAX_CAPACITY_LOG2; M = 2^capacity_log2 slots.
  *   dim            row length, 1..65536 elements.
  *   dtype          HTL_F32 or HTL_BF16 row elements.
@@ -92,8 +93,9 @@ enum { HT_META_LAST_SEEN = 1u, HT_ADAM_STATE = 2u, HT_GROWABLE = 4u, HT_META_ACC
  * Storage, all on the current device: keys int64[M]; rows dtype[M][dim];
  * last_seen uint32[M]; m, v float[M][dim].  *t receives the handle.
  *
- * Growable tables ([MTGR] section 5: keys map to vectors and metadata, and
- * capacity grows by copying the key storage, not the embeddings): the key
+ * Growable tables ([MTGR] section 5: each key leads to its row and
+ * metadata, and the table grows by copying what indexes the keys while the
+ * embedding rows stay where they are): the key
  * index (keys int64[M], a row handle int32[M] and last_seen uint32[M] per
  * slot) is separate from the row space (rows, m, v indexed by row handle).
  * The row space is a reserved virtual range of up to

@@ -14,9 +14,9 @@
 //    (power-of-two table, odd probe step covers every slot), Figure 5 caption
 //    (dynamic embedding table).
 //  * MTGR: Industrial-Scale Generative Recommendation Framework in Meituan
-//    (arXiv 2505.18654), section 5 "Training System": keys map to embedding
-//    vectors and metadata, compact key scanning, ID de-duplication before and
-//    after the all-to-all.
+//    (arXiv 2505.18654), section 5 "Training System": each key leads to its
+//    embedding row and metadata; live keys are scanned compactly; IDs are
+//    made unique on both sides of the all-to-all.
 //  * Deep Customization of TensorFlow for Large-Scale Sparse Training at
 //    Meituan, section 3.1 (hash table instead of Variables) and 3.2 (Adam).
 //

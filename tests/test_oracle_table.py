@@ -2,8 +2,8 @@
 
 MTGenRec (arXiv 2505.12663), Abstract: dynamic hash tables replace static
 ones so sparse embeddings can be inserted and deleted in real time; MTGR
-(arXiv 2505.18654) section 5, "Embedding Management": keys map to embedding
-vectors and metadata.  The table contract read from these: FOUND for a live
+(arXiv 2505.18654) section 5, "Embedding Management": each key leads to its
+embedding row and its metadata.  The table contract read from these: FOUND for a live
 key, INSERTED (with the closed-form initial row) for a new one, FULL when all
 M slots are live, RESERVED for the two key values the table keeps for itself
 (-1 empty, -2 tombstone); erase gives ERASED or NOT_FOUND; FOUND and INSERTED
