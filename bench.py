@@ -325,7 +325,7 @@ def run_pooled(args, torch, htl, workloads, dev):
                                               "emb_gather_pool(slots, inverse, offsets)"},
             "timing": "HIP events per step; table keys restored between steps outside the events"}
     res = _result(args, n / (ms * 1e-3) / 1e6, ms, config, "int64 keys, bf16 rows, fp32 accumulate", path,
-                  _roofline("k_pool (emb_gather_pool with bags)", pool_bytes, p_ms,
+                  _roofline("k_pool_team (emb_gather_pool with bags)", pool_bytes, p_ms,
                             _measured_traffic("merged_tables")))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline_pooled(w, warm)

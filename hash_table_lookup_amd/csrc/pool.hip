@@ -33,7 +33,8 @@ int team_for(int vpr) {
 }
 
 // ------------------------------------------------------------- pooling --
-// One wavefront per bag.  The wave splits into 64/TEAM teams; team q takes
+// One wavefront per bag (rows of more than 32 vectors; shorter rows take
+// k_pool_team below).  The wave splits into 64/TEAM teams; team q takes
 // IDs q, q + 64/TEAM, ... of the bag, kPoolUnroll of them per round so that
 // their three dependent loads (inverse, slot, row) overlap; every lane
 // accumulates its 16-byte vectors in fp32; a butterfly over the teams then
@@ -164,12 +165,110 @@ __global__ void k_pool_elem(const TIn* __restrict__ rows, int dim, int64_t M, co
     }
 }
 
+// One team of TEAM lanes per bag, for rows of at most 32 vectors: the team
+// walks its own bag kPoolUnroll IDs at a time and keeps the sum, so a
+// wave keeps the rows of 64/TEAM bags in flight (a ~20-ID bag alone would
+// leave a third of a wave's 32 row loads idle) and needs no combine across
+// teams.  The pooling is bound by how many row loads are in flight: on the
+// 26-table bf16 workload, 1.160 ms per launch with a wave per bag, 1.065 ms
+// with a team per bag, 1.084 / 1.22 ms with 6 / 12 rows per team (12 costs
+// two waves per SIMD), and a wave per bag at half the waves took 1.79 ms.
+template <int TEAM, bool IN_BF16>
+__global__ __launch_bounds__(kBlock) void k_pool_team(const u32x4* __restrict__ rows, int vpr, int64_t M,
+                                                     const int32_t* __restrict__ slots,
+                                                     const int32_t* __restrict__ inverse, int64_t n,
+                                                     const int32_t* __restrict__ offsets, int64_t nbags,
+                                                     bool out_bf16, void* __restrict__ out) {
+    constexpr int E = IN_BF16 ? 8 : 4;
+    const int tl = threadIdx.x & (TEAM - 1);
+    const int64_t team = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / TEAM;
+    const int64_t nteams = (int64_t)gridDim.x * kBlock / TEAM;
+    const bool lane_on = tl < vpr;
+    for (int64_t bag = team; bag < nbags; bag += nteams) {
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+        const int64_t beg = clamp_pos(offsets[bag], n), end = clamp_pos(offsets[bag + 1], n);
+        for (int64_t i0 = beg; i0 < end; i0 += kPoolUnroll) {
+            int32_t sl[kPoolUnroll];
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) {
+                const int64_t i = i0 + u;
+                sl[u] = i < end ? (inverse ? inverse[i] : (int32_t)i) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) {
+                if (sl[u] >= 0) sl[u] = slots[sl[u]];
+                if (sl[u] >= M) sl[u] = -1;
+            }
+            u32x4 x[kPoolUnroll];
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u)
+                x[u] = (lane_on && sl[u] >= 0) ? rows[(int64_t)sl[u] * vpr + tl] : zero4();
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) {
+                if (IN_BF16) {
+                    const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        acc[2 * c] += bf16_lo(w[c]);
+                        acc[2 * c + 1] += bf16_hi(w[c]);
+                    }
+                } else {
+                    acc[0] += __uint_as_float(x[u].x);
+                    acc[1] += __uint_as_float(x[u].y);
+                    acc[2] += __uint_as_float(x[u].z);
+                    acc[3] += __uint_as_float(x[u].w);
+                }
+            }
+        }
+        if (!lane_on) continue;
+        const int64_t e0 = (bag * vpr + tl) * E;
+        if (out_bf16) {
+            uint32_t p[E / 2];
+#pragma unroll
+            for (int c = 0; c < E / 2; ++c) p[c] = f32_to_bf16_bits(acc[2 * c]) | (f32_to_bf16_bits(acc[2 * c + 1]) << 16);
+            uint16_t* o = (uint16_t*)out + e0;
+            if (E == 8) {
+                u32x4 w;
+                w.x = p[0]; w.y = p[1]; w.z = p[2]; w.w = p[3];
+                __builtin_nontemporal_store(w, (u32x4*)o);
+            } else {
+                __builtin_nontemporal_store(p[0], (uint32_t*)o);
+                __builtin_nontemporal_store(p[1], (uint32_t*)o + 1);
+            }
+        } else {
+            float* o = (float*)out + e0;
+#pragma unroll
+            for (int c = 0; c < E / 4; ++c) {
+                u32x4 w;
+                w.x = __float_as_uint(acc[4 * c]);
+                w.y = __float_as_uint(acc[4 * c + 1]);
+                w.z = __float_as_uint(acc[4 * c + 2]);
+                w.w = __float_as_uint(acc[4 * c + 3]);
+                __builtin_nontemporal_store(w, (u32x4*)o + c);
+            }
+        }
+    }
+}
+
 template <int TEAM, int QMAX>
 void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t* inverse, int64_t n,
                  const int32_t* offsets, int64_t nbags, bool out_bf16, void* out, hipStream_t s) {
-    // A persistent grid (each wavefront strides over bags): on the 1.7M-bag
-    // pooled workload, 16K workgroups ran 10% faster than one wavefront per
-    // bag (426K workgroups); for the per-ID gather the full grid was best.
+    // A persistent grid (each team or wavefront strides over bags): on the
+    // 1.7M-bag pooled workload, 16K workgroups ran 10% faster than one
+    // wavefront per bag (426K workgroups); for the per-ID gather the full
+    // grid was best.
+    if (QMAX == 1 && TEAM <= 32) {
+        const unsigned tgrid = grid_for(nbags, kBlock / TEAM, kPoolBlocks);
+        if (T.dtype == HTL_BF16)
+            hipLaunchKernelGGL((k_pool_team<TEAM, true>), dim3(tgrid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
+                               vpr, T.capacity, slots, inverse, n, offsets, nbags, out_bf16, out);
+        else
+            hipLaunchKernelGGL((k_pool_team<TEAM, false>), dim3(tgrid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
+                               vpr, T.capacity, slots, inverse, n, offsets, nbags, out_bf16, out);
+        return;
+    }
     const unsigned grid = grid_for(nbags, kBlock / 64, kPoolBlocks);
     if (T.dtype == HTL_BF16)
         hipLaunchKernelGGL((k_pool<TEAM, QMAX, true>), dim3(grid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
@@ -185,10 +284,10 @@ htl_status launch_pooling(const TableDev& T, int dtype, bool vec, int vpr, const
                           const int32_t* inverse, int64_t n, const int32_t* offsets, int64_t nbags, bool out_bf16,
                           void* out, hipStream_t stream) {
     if (vec && vpr <= 256) {
-        // One 16-byte vector per lane.  (Narrower teams with two vectors
-        // per lane, which keep a whole 20-ID bag in flight in one round,
-        // measured 3% slower on the 26-table bf16 workload: the pooled rows
-        // come from cache and the loop is not latency-bound.)
+        // One 16-byte vector per lane.  (With a wave per bag, narrower
+        // teams with two vectors per lane, which keep a whole 20-ID bag in
+        // flight in one round, measured 3% slower on the 26-table bf16
+        // workload; a team per bag keeps more rows in flight instead.)
         switch (team_for(vpr)) {
             case 1: launch_pool<1, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
             case 2: launch_pool<2, 1>(T, vpr, slots, inverse, n, offsets, nbags, out_bf16, out, stream); break;
