@@ -637,7 +637,14 @@ void launch_reduce(const float* grad, int vpr, const SegWs& w, int64_t u_max, co
                    const AdamArgs& A, hipStream_t s) {
     // Persistent grids: u_max bounds the segments from above (often by far:
     // 753K segments for u_max = 8.4M), and idle workgroups cost launch time.
-    hipLaunchKernelGGL((k_seg_small<TEAM, QMAX, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / TEAM, 1 << 15)),
+    // Without Adam the short-segment sum is bound by the rows in flight (at
+    // half its waves it took 390 against 240 us), so for rows of 16+ vectors
+    // it runs half-width teams with two vectors per lane: twice the segments
+    // per wave, 240 -> 222 us on the backward workload.  With Adam it is
+    // bound by its bytes (half its waves: 590 -> 638 us) and keeps full teams.
+    constexpr bool kHalf = !ADAM && QMAX == 1 && TEAM >= 16;
+    constexpr int kSTeam = kHalf ? TEAM / 2 : TEAM, kSQmax = kHalf ? 2 : QMAX;
+    hipLaunchKernelGGL((k_seg_small<kSTeam, kSQmax, ADAM>), dim3(grid_for(u_max + kSpread, kRBlock / kSTeam, 1 << 15)),
                        dim3(kRBlock), 0, s, (const u32x4*)grad, vpr, w.perm, w.seg_off, u_max, n_dev, (u32x4*)out, A,
                        w.large, w.large_n, w.n_large);
     hipLaunchKernelGGL(k_large_scan, dim3(1), dim3(1024), 0, s, w.large_n, w.n_large, w.large_off, w.part_off);
