@@ -279,6 +279,47 @@ def test_pool_merged_tables_small(htl, orc):
         assert np.array_equal(to_np(out), ref)
 
 
+@pytest.mark.parametrize("dim,dtype", [(64, "bf16"), (16, "f32"), (512, "bf16"), (6, "bf16")])
+def test_pool_offsets_that_break_the_rules(htl, orc, dim, dtype):
+    # emb_gather_pool's contract for offsets outside the CSR rules: every bag
+    # is clamped to [0, n) on its own, and a bag whose clamped start is not
+    # below its clamped end sums nothing.  Offsets below 0, above n and
+    # decreasing pairs, through the team-per-bag (dim 64, 16), wave-per-bag
+    # (dim 512) and element-wise (dim 6) kernels; rows from the oracle.
+    rng = np.random.default_rng(100 + dim)
+    n, nb = 5000, 600
+    keys = rng.integers(0, 700, n).astype(np.int64)
+    offsets = np.sort(rng.integers(0, n + 1, nb + 1)).astype(np.int64)
+    offsets[rng.choice(nb + 1, 40, replace=False)] = rng.integers(-50, 0, 40)
+    offsets[rng.choice(nb + 1, 40, replace=False)] = rng.integers(n + 1, n + 100, 40)
+    for s in rng.choice(nb, 40, replace=False):
+        offsets[s], offsets[s + 1] = offsets[s + 1], offsets[s]
+    beg, end = np.clip(offsets[:-1], 0, n), np.clip(offsets[1:], 0, n)
+    assert (beg > end).sum() > 10 and (offsets < 0).any() and (offsets > n).any()
+    uk, inv = np.unique(keys, return_inverse=True)
+    table = htl.Table(12, dim, dtype)
+    slots, st = table.find_or_insert(torch.from_numpy(uk).cuda())
+    assert (to_np(st) == htl.INSERTED).all()
+    got = to_np(htl.gather_pool(table, slots, torch.from_numpy(inv.astype(np.int32)).cuda(),
+                                torch.from_numpy(offsets.astype(np.int32)).cuda(), out_dtype="f32"))
+    otab = orc.Table(1 << 12, dim, orc.F32 if dtype == "f32" else orc.BF16)
+    otab.find_or_insert(uk)
+    rows = otab.gather(keys)
+    rows = (orc.bf16_bits_to_f32(rows) if dtype == "bf16" else rows).astype(np.float64)
+    want, bound = np.zeros((nb, dim)), np.zeros((nb, dim))
+    for b in range(nb):
+        if beg[b] < end[b]:
+            want[b] = rows[beg[b]:end[b]].sum(axis=0)
+            # recursive fp32 summation of L terms: |error| <= (L - 1) u sum|x|
+            bound[b] = (end[b] - beg[b]) * 2.0**-24 * np.abs(rows[beg[b]:end[b]]).sum(axis=0)
+    if dtype == "bf16":
+        assert np.array_equal(got.astype(np.float64), want)   # sums of bf16 rows are exact in fp32
+    else:
+        assert (np.abs(got.astype(np.float64) - want) <= bound).all()
+        assert np.array_equal(got[beg >= end], np.zeros(((beg >= end).sum(), dim), np.float32))
+    table.close()
+
+
 @pytest.mark.parametrize("dim,dtype", [(16, "f32"), (64, "bf16"), (6, "bf16"), (7, "f32"), (512, "bf16")])
 def test_pool_shapes_and_empty_bags(htl, orc, dim, dtype):
     rng = np.random.default_rng(dim)
