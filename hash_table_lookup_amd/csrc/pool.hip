@@ -13,7 +13,11 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kPoolUnroll = 8;             // IDs per team in flight (merged-tables step: 4 -> 1.40 ms, 8 -> 1.29, 16 -> 1.89)
-constexpr int64_t kPoolBlocks = 1 << 14;   // workgroups of the pooling kernel (persistent grid)
+constexpr int64_t kPoolBlocks = 1 << 14;   // workgroups of the wave-per-bag kernel (persistent grid)
+// Workgroups of the team-per-bag kernel (persistent grid).  On the 26-table
+// bf16 workload (1.70M bags): 2^13 / 2^14 / 2^15 / 2^16 / one team per bag
+// 1.068 / 1.063 / 1.056 / 1.061 / 1.078 ms.
+constexpr int64_t kPoolTeamBlocks = 1 << 15;
 
 __device__ __forceinline__ u32x4 zero4() {
     u32x4 z;
@@ -260,7 +264,7 @@ void launch_pool(const TableDev& T, int vpr, const int32_t* slots, const int32_t
     // wavefront per bag (426K workgroups); for the per-ID gather the full
     // grid was best.
     if (QMAX == 1 && TEAM <= 32) {
-        const unsigned tgrid = grid_for(nbags, kBlock / TEAM, kPoolBlocks);
+        const unsigned tgrid = grid_for(nbags, kBlock / TEAM, kPoolTeamBlocks);
         if (T.dtype == HTL_BF16)
             hipLaunchKernelGGL((k_pool_team<TEAM, true>), dim3(tgrid), dim3(kBlock), 0, s, (const u32x4*)T.rows,
                                vpr, T.capacity, slots, inverse, n, offsets, nbags, out_bf16, out);
